@@ -1,0 +1,477 @@
+"""Step-by-step protocol simulation of the collectives on the oracle's state.
+
+Each virtual rank runs a program (a Python generator) that yields the
+primitive operations it issues, in the order the pages give them; the
+scheduler executes one operation at a time, choosing the next rank from a
+seeded random generator (``run``) or trying every choice (``all_runs``).
+A wait is executable only once its condition holds; a barrier only once
+every unfinished rank has reached it. If no rank can move while some are
+unfinished, ``Deadlock`` is raised.
+
+The programs follow the pages:
+* AlltoAll -- GIN page, pure-GIN AlltoAll kernel: read the signal's base
+  value, enter a barrier, put one block to every peer with a SignalInc,
+  wait until the signal reaches base + nRanks, leave through a barrier.
+* AllReduce -- reduce-scatter by gets (each owner pulls its chunk from
+  every rank and sums in rank order), then all-gather by puts with a
+  SignalInc to every rank (the one-sided put/get of the GIN page over the
+  symmetric windows of the Symmetric-memory page).
+* AllGather -- Symmetric-memory page, AllGather example, as one put per
+  (source, destination) with a SignalInc.
+* Dispatch -- GPUDirect Async survey (opening MoE dispatch; section 4, a
+  batch of puts followed by one trailing signal): exchange per-expert
+  counts with SignalInc, compute offsets, put each expert's packed rows,
+  then one strong SignalAdd(rows) per destination.
+* Ring -- GPUDirect Async survey, section 4: each rank puts to its successor
+  with a strong SignalInc and a CounterInc per put, then waits.
+"""
+from __future__ import annotations
+
+import hashlib
+import random
+from dataclasses import dataclass
+from typing import Callable
+
+import numpy as np
+
+from .primitives import (COUNTER_BITS, SIGNAL_BITS, CounterInc, Deadlock,
+                         InvalidArgument, SignalAdd, SignalInc, World)
+
+
+# -- operations ----------------------------------------------------------------
+@dataclass
+class Put:
+    peer: int
+    dst: int
+    doff: int
+    src: int
+    soff: int
+    nbytes: int
+    remote: object = None
+    local: object = None
+
+
+@dataclass
+class Get:
+    peer: int
+    rwin: int
+    roff: int
+    lwin: int
+    loff: int
+    nbytes: int
+    local: object = None
+
+
+@dataclass
+class Signal:
+    peer: int
+    remote: object
+
+
+@dataclass
+class ReadSignal:
+    id: int
+    bits: int = SIGNAL_BITS
+
+
+@dataclass
+class ReadCounter:
+    id: int
+    bits: int = COUNTER_BITS
+
+
+@dataclass
+class WaitSignal:
+    id: int
+    least: int
+    bits: int = SIGNAL_BITS
+
+
+@dataclass
+class WaitCounter:
+    id: int
+    least: int
+    bits: int = COUNTER_BITS
+
+
+@dataclass
+class ResetSignal:
+    id: int
+
+
+@dataclass
+class Barrier:
+    """Every unfinished rank must arrive before any of them continues."""
+
+
+@dataclass
+class Local:
+    """A computation on the calling rank's own memory: ``fn(world, rank)``."""
+    fn: Callable
+    label: str = ""
+
+
+# -- scheduler -----------------------------------------------------------------
+class Sim:
+    def __init__(self, world: World, programs):
+        self.world = world
+        self.gens = list(programs)
+        self.pending = [None] * len(self.gens)
+        self.barrier_gen = [0] * len(self.gens)
+        self.generation = 0
+        self.done_ops = [0] * len(self.gens)   # operations each rank has completed
+        self.reads = [[] for _ in self.gens]   # values its reads returned, in order
+        for r, g in enumerate(self.gens):
+            self.pending[r] = self._advance(r, None, first=True)
+
+    def _advance(self, r, value, first=False):
+        if not first:
+            self.done_ops[r] += 1
+        try:
+            return next(self.gens[r]) if first else self.gens[r].send(value)
+        except StopIteration:
+            return None
+
+    def done(self) -> bool:
+        return all(p is None for p in self.pending)
+
+    def _ready(self, r) -> bool:
+        op = self.pending[r]
+        w = self.world
+        if op is None:
+            return False
+        if isinstance(op, WaitSignal):
+            return w.signal_reached(r, op.id, op.least, op.bits)
+        if isinstance(op, WaitCounter):
+            return w.counter_reached(r, op.id, op.least, op.bits)
+        if isinstance(op, Barrier):
+            live = [q for q in range(len(self.pending)) if self.pending[q] is not None]
+            return all(isinstance(self.pending[q], Barrier) for q in live)
+        return True
+
+    def runnable(self) -> list[int]:
+        return [r for r in range(len(self.pending)) if self._ready(r)]
+
+    def step(self, r: int) -> None:
+        op = self.pending[r]
+        w = self.world
+        result = None
+        if isinstance(op, Put):
+            w.put(r, op.peer, op.dst, op.doff, op.src, op.soff, op.nbytes, op.remote, op.local)
+        elif isinstance(op, Get):
+            w.get(r, op.peer, op.rwin, op.roff, op.lwin, op.loff, op.nbytes, op.local)
+        elif isinstance(op, Signal):
+            w.signal(r, op.peer, op.remote)
+        elif isinstance(op, ReadSignal):
+            result = w.read_signal(r, op.id, op.bits)
+            self.reads[r].append(result)
+        elif isinstance(op, ReadCounter):
+            result = w.read_counter(r, op.id, op.bits)
+            self.reads[r].append(result)
+        elif isinstance(op, (WaitSignal, WaitCounter)):
+            pass
+        elif isinstance(op, ResetSignal):
+            w.reset_signal(r, op.id)
+        elif isinstance(op, Barrier):
+            # releasing one rank releases all that wait at this barrier
+            live = [q for q in range(len(self.pending)) if self.pending[q] is not None]
+            for q in live:
+                if q != r:
+                    self.pending[q] = self._advance(q, None)
+        elif isinstance(op, Local):
+            op.fn(w, r)
+        else:
+            raise InvalidArgument(f"unknown operation {op!r}")
+        self.pending[r] = self._advance(r, result)
+
+
+def run(world: World, programs, seed: int = 0) -> World:
+    """Execute the programs under one seeded random interleaving."""
+    sim = Sim(world, programs)
+    rng = random.Random(seed)
+    while not sim.done():
+        ready = sim.runnable()
+        if not ready:
+            raise Deadlock("every unfinished rank is blocked")
+        sim.step(ready[rng.randrange(len(ready))])
+    return world
+
+
+def _fingerprint(sim: "Sim") -> tuple:
+    w = sim.world
+    h = hashlib.blake2b(digest_size=16)
+    for key in sorted(w.windows):
+        for b in w.windows[key]:
+            h.update(b.tobytes())
+    h.update(repr((w.sig, w.cnt, w._sig_mode)).encode())
+    return (tuple(sim.done_ops), tuple(tuple(x) for x in sim.reads), h.hexdigest())
+
+
+def distinct_final_states(setup: Callable, limit: int = 500000):
+    """Yield the final world of every distinct outcome over all interleavings.
+
+    A depth-first search over schedule prefixes that skips a prefix when an
+    earlier one reached the same node: the same number of operations done
+    by each rank, the same values returned to each rank by its reads, and
+    the same memory, signals and counters. Two such prefixes have identical
+    futures (the programs here read shared memory directly only after a
+    wait that fixes what they read), so every interleaving's outcome is
+    still reached. Returns nothing else; raises ``Deadlock`` if any
+    interleaving blocks every unfinished rank.
+    """
+    seen = set()
+    finals = set()
+    stack: list[list[int]] = [[]]
+    nodes = 0
+    while stack:
+        prefix = stack.pop()
+        world, programs = setup()
+        sim = Sim(world, programs)
+        for c in prefix:
+            sim.step(c)
+        key = _fingerprint(sim)
+        if key in seen:
+            continue
+        seen.add(key)
+        nodes += 1
+        if nodes > limit:
+            raise RuntimeError("too many states")
+        if sim.done():
+            fk = key[2]
+            if fk not in finals:
+                finals.add(fk)
+                yield world
+            continue
+        ready = sim.runnable()
+        if not ready:
+            raise Deadlock(f"every unfinished rank is blocked after schedule {prefix}")
+        for r in ready:
+            stack.append(prefix + [r])
+
+
+def all_runs(setup: Callable, limit: int = 200000):
+    """Yield ``(world, schedule)`` for every interleaving of the programs.
+
+    ``setup()`` returns a fresh ``(world, programs)``; each interleaving is
+    replayed from scratch, so programs may hold arbitrary local state.
+    """
+    stack: list[list[int]] = [[]]
+    count = 0
+    while stack:
+        prefix = stack.pop()
+        world, programs = setup()
+        sim = Sim(world, programs)
+        for c in prefix:
+            sim.step(c)
+        path = list(prefix)
+        while not sim.done():
+            ready = sim.runnable()
+            if not ready:
+                raise Deadlock(f"every unfinished rank is blocked after schedule {path}")
+            for alt in ready[1:]:
+                stack.append(path + [alt])
+            sim.step(ready[0])
+            path.append(ready[0])
+        count += 1
+        if count > limit:
+            raise RuntimeError("too many interleavings")
+        yield world, path
+
+
+# -- collective programs -----------------------------------------------------------
+def alltoall_programs(world: World, send: int, recv: int, block: int, sig: int, strong: bool = True):
+    R = world.nranks
+
+    def prog(rank):
+        base = yield ReadSignal(sig)
+        yield Barrier()
+        for peer in range(R):
+            yield Put(peer, recv, rank * block, send, peer * block, block, SignalInc(sig, strong))
+        yield WaitSignal(sig, base + R)
+        yield Barrier()
+
+    return [prog(r) for r in range(R)]
+
+
+def allgather_programs(world: World, send: int, recv: int, nbytes: int, sig: int):
+    R = world.nranks
+
+    def prog(rank):
+        base = yield ReadSignal(sig)
+        yield Barrier()
+        for peer in range(R):
+            yield Put(peer, recv, rank * nbytes, send, 0, nbytes, SignalInc(sig))
+        yield WaitSignal(sig, base + R)
+        yield Barrier()
+
+    return [prog(r) for r in range(R)]
+
+
+def chunk_bounds(count: int, nranks: int, owner: int) -> tuple[int, int]:
+    """Elements ``[start, stop)`` reduced by ``owner``: ceil(count / R) per owner."""
+    per = -(-count // nranks)
+    start = min(count, owner * per)
+    return start, min(count, start + per)
+
+
+def allreduce_scratch_bytes(count: int, nranks: int, dtype: str) -> int:
+    esize = 4 if dtype == "f32" else 2
+    per = -(-count // nranks)
+    return nranks * per * esize + per * esize
+
+
+def allreduce_programs(world: World, send: int, recv: int, scratch: int, count: int,
+                       dtype: str, sig: int):
+    """Reduce-scatter by gets into per-owner scratch slots, then all-gather by puts.
+
+    Scratch layout per rank: R slots of ``ceil(count/R)`` input elements,
+    followed by one slot holding the reduced chunk in the output type.
+    """
+    from .definitions import allreduce  # the rank-order sum of one chunk
+    R = world.nranks
+    esize = 4 if dtype == "f32" else 2
+    per = -(-count // R)
+    res_off = R * per * esize
+    np_t = np.float32 if dtype == "f32" else np.uint16
+
+    def prog(rank):
+        start, stop = chunk_bounds(count, R, rank)
+        n = stop - start
+        base = yield ReadSignal(sig)
+        yield Barrier()
+        for r in range(R):  # pull chunk `rank` of every rank's input
+            yield Get(r, send, start * esize, scratch, r * per * esize, n * esize)
+
+        def reduce_chunk(w, me, n=n):
+            buf = w.buf(scratch, me)
+            slots = [buf[r * per * esize:(r * per + n) * esize].view(np_t) for r in range(R)]
+            buf[res_off:res_off + n * esize] = allreduce(slots, dtype).view(np.uint8)
+
+        yield Local(reduce_chunk, "sum in rank order")
+        for peer in range(R):
+            yield Put(peer, recv, start * esize, scratch, res_off, n * esize, SignalInc(sig))
+        yield WaitSignal(sig, base + R)
+        yield Barrier()
+
+    return [prog(r) for r in range(R)]
+
+
+def ring_programs(world: World, send: int, recv: int, puts_per_rank: int, put_bytes: int,
+                  contexts: int, sig_base: int, cnt_base: int, reset: bool = False):
+    R = world.nranks
+    if puts_per_rank % contexts:
+        raise InvalidArgument("puts_per_rank must be a multiple of contexts")
+    per_ctx = puts_per_rank // contexts
+
+    def prog(rank):
+        sbase = []
+        cbase = []
+        for c in range(contexts):
+            sbase.append((yield ReadSignal(sig_base + c)))
+            cbase.append((yield ReadCounter(cnt_base + c)))
+        yield Barrier()
+        peer = (rank + 1) % R
+        for k in range(puts_per_rank):
+            c = k // per_ctx
+            yield Put(peer, recv, k * put_bytes, send, k * put_bytes, put_bytes,
+                      SignalInc(sig_base + c, True), CounterInc(cnt_base + c))
+        for c in range(contexts):
+            yield WaitSignal(sig_base + c, sbase[c] + per_ctx)
+            yield WaitCounter(cnt_base + c, cbase[c] + per_ctx)
+        if reset:
+            for c in range(contexts):
+                yield ResetSignal(sig_base + c)
+        yield Barrier()
+
+    return [prog(r) for r in range(R)]
+
+
+class DispatchBuffers:
+    """Windows and local arrays one dispatch needs on the oracle's world."""
+
+    def __init__(self, world: World, x_bits: np.ndarray, topk_idx: np.ndarray,
+                 num_experts: int, capacity_rows: int):
+        R, T, K = topk_idx.shape
+        self.R, self.T, self.K, self.E = R, T, K, num_experts
+        self.epr = num_experts // R
+        self.cap = capacity_rows
+        xb = [np.ascontiguousarray(x_bits[s]).reshape(T, -1).view(np.uint8) for s in range(R)]
+        self.row_bytes = xb[0].shape[1] if T else 0
+        self.topk = np.asarray(topk_idx)
+        self.x = world.register([b.reshape(-1).copy() for b in xb])
+        self.cnt_send = world.register_zeros(4 * num_experts)
+        self.cnt_all = world.register_zeros(4 * num_experts * R)
+        self.stage = world.register_zeros(max(1, T * K * self.row_bytes))
+        self.stage_src = world.register_zeros(max(4, 4 * T * K))
+        self.recv = world.register_zeros(max(1, capacity_rows * self.row_bytes))
+        self.recv_src = world.register_zeros(max(4, 4 * capacity_rows))
+        self.counts = np.zeros((R, self.epr), dtype=np.int32)
+        self.overflow = [False] * R
+
+
+def dispatch_programs(world: World, b: DispatchBuffers, sig_counts: int, sig_rows: int):
+    R, T, K, E, epr, rb = b.R, b.T, b.K, b.E, b.epr, b.row_bytes
+
+    def prog(s):
+        base_c = yield ReadSignal(sig_counts)
+        base_r = yield ReadSignal(sig_rows)
+        yield Barrier()
+
+        # step 1: this rank's tokens per expert, sent to every rank
+        def histogram(w, me):
+            c = np.zeros(E, dtype=np.int32)
+            for t in range(T):
+                for k in range(K):
+                    e = int(b.topk[me, t, k])
+                    if e >= 0:
+                        c[e] += 1
+            w.buf(b.cnt_send, me)[:] = c.view(np.uint8)
+
+        yield Local(histogram, "histogram")
+        for d in range(R):
+            yield Put(d, b.cnt_all, s * E * 4, b.cnt_send, 0, E * 4, SignalInc(sig_counts))
+        yield WaitSignal(sig_counts, base_c + R)
+
+        # step 2: offsets from the full count matrix
+        C = world.buf(b.cnt_all, s).view(np.int32).reshape(R, E).astype(np.int64)
+        tot = C.sum(axis=0)
+        seg = np.zeros(E, dtype=np.int64)
+        for e in range(E):
+            first = (e // epr) * epr
+            seg[e] = tot[first:e].sum()
+        off = seg + C[:s].sum(axis=0)
+        b.counts[s] = tot[s * epr:(s + 1) * epr].astype(np.int32)
+        my_rows = int(tot[s * epr:(s + 1) * epr].sum())
+        b.overflow[s] = my_rows > b.cap
+
+        # step 3: one put per expert of the packed rows (ascending token), no signal
+        rows_to = [0] * R
+        so = 0
+        for e in range(E):
+            n = int(C[s, e])
+            if n == 0:
+                continue
+            d = e // epr
+            toks = [t for t in range(T) if e in b.topk[s, t]]
+
+            def pack(w, me, toks=toks, so=so):
+                xs = w.buf(b.x, me).reshape(T, rb)
+                w.buf(b.stage, me)[so * rb:(so + len(toks)) * rb] = xs[toks].reshape(-1)
+                tags = np.array([(me << 16) | t for t in toks], dtype=np.int32)
+                w.buf(b.stage_src, me)[so * 4:(so + len(toks)) * 4] = tags.view(np.uint8)
+
+            yield Local(pack, f"pack e={e}")
+            keep = max(0, min(n, b.cap - int(off[e])))  # rows past the capacity are dropped
+            if keep:
+                yield Put(d, b.recv, int(off[e]) * rb, b.stage, so * rb, keep * rb)
+                yield Put(d, b.recv_src, int(off[e]) * 4, b.stage_src, so * 4, keep * 4)
+            rows_to[d] += n
+            so += n
+        # one trailing strong signal per destination covers all earlier puts to it
+        for d in range(R):
+            if rows_to[d]:
+                yield Signal(d, SignalAdd(sig_rows, rows_to[d], True))
+        yield WaitSignal(sig_rows, base_r + my_rows)
+        yield Barrier()
+
+    return [prog(s) for s in range(R)]

@@ -1,0 +1,275 @@
+"""Pins for the oracle's plain definitions.
+
+Against the pages' worked examples (tests/golden/*.json), hand-worked
+binary32 cases, closed forms, library routines (numpy reductions, torch's
+bf16 conversion, numpy stable argsort, block transposes) and brute force.
+"""
+import itertools
+import json
+import struct
+
+import numpy as np
+import pytest
+
+from oracle import definitions as D
+import workloads as W
+
+from conftest import golden
+
+
+def _load(name):
+    with open(golden(name)) as f:
+        return json.load(f)
+
+
+# -- AllReduce -------------------------------------------------------------------
+def test_allreduce_worked_example_rank_fill():
+    g = _load("allreduce_rank_fill.json")
+    R, N = g["ranks"], g["count"]
+    xs = W.allreduce_f32_inputs(R, N, run="A")
+    assert xs[0].nbytes == g["bytes_per_buffer"]
+    out = D.allreduce_sum_f32(xs)
+    assert out.shape == (N,)
+    assert np.all(np.abs(out - g["expected"]) <= g["tolerance"])
+    assert np.all(out == np.float32(g["expected"]))  # small integers: the sum is exact
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 8, 16])
+def test_allreduce_rank_fill_closed_form(R):
+    out = D.allreduce_sum_f32(W.allreduce_f32_inputs(R, 4096, run="A"))
+    assert np.all(out == np.float32(R * (R - 1) // 2))
+
+
+def test_allreduce_summation_order_hand_worked():
+    g = _load("summation_order.json")
+    for case in g["cases"]:
+        xs = [np.array([v], dtype=np.float32) for v in case["ranks_values"]]
+        out = D.allreduce_sum_f32(xs)
+        if "expected" in case:
+            assert out[0] == np.float32(case["expected"]), case
+        bits = struct.unpack("<I", struct.pack("<f", float(out[0])))[0]
+        if "expected_bits_hex" in case:
+            assert bits == int(case["expected_bits_hex"], 16), case
+
+
+def test_allreduce_matches_numpy_axis0_reduction():
+    # numpy reduces a C-contiguous [R, N] array over axis 0 row by row
+    # (checked here on data where order matters), an independent route to
+    # the same fixed-order fp32 sum.
+    xs = W.allreduce_f32_inputs(8, 1 << 15, run="B", seed=7)
+    xs = [x * np.float32(1e4 ** (r % 3)) for r, x in enumerate(xs)]
+    stacked = np.ascontiguousarray(np.stack(xs))
+    assert np.array_equal(D.allreduce_sum_f32(xs), np.add.reduce(stacked, axis=0))
+    # and a different order really would differ somewhere on this data
+    assert not np.array_equal(D.allreduce_sum_f32(xs[::-1]), D.allreduce_sum_f32(xs))
+
+
+def test_allreduce_matches_exact_sum_rounded_each_step():
+    # Rounding each exact partial sum to binary32 with Python's struct (an
+    # independent RNE implementation) must reproduce the oracle.
+    def r32(v):
+        return struct.unpack("<f", struct.pack("<f", v))[0]
+    rng = np.random.default_rng(3)
+    xs = [(rng.standard_normal(200) * 10.0 ** rng.integers(-3, 6, 200)).astype(np.float32) for _ in range(5)]
+    out = D.allreduce_sum_f32(xs)
+    for i in range(200):
+        acc = float(xs[0][i])
+        for r in range(1, 5):
+            acc = r32(acc + float(xs[r][i]))  # exact double add of two floats, then one rounding
+        assert np.float32(acc) == out[i] or (np.isnan(acc) and np.isnan(out[i]))
+
+
+def test_allreduce_error_bound_random():
+    xs = W.allreduce_f32_inputs(8, 1 << 14, run="B", seed=11)
+    out = D.allreduce_sum_f32(xs).astype(np.float64)
+    exact = np.sum(np.stack(xs).astype(np.float64), axis=0)
+    bound = 7 * 2.0 ** -24 * np.sum(np.abs(np.stack(xs).astype(np.float64)), axis=0) * 1.0001
+    assert np.all(np.abs(out - exact) <= bound + 1e-45)
+
+
+def test_bf16_widening_is_exact():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = D.bf16_bits_to_f32(bits)
+    assert np.array_equal(f.view(np.uint32) >> 16, bits.astype(np.uint32))
+    assert np.all(f.view(np.uint32) & 0xFFFF == 0)
+
+
+def test_bf16_rounding_matches_torch_on_non_nan():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    u = rng.integers(0, 1 << 32, 1 << 18, dtype=np.uint64).astype(np.uint32)
+    specials = np.array([0x00000000, 0x80000000, 0x3F808000, 0x3F818000, 0x3F807FFF,
+                         0x3F808001, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F8000, 0x7F800000,
+                         0xFF800000, 0x00000001, 0x00008000, 0x00018000, 0x807FFFFF],
+                        dtype=np.uint32)
+    u = np.concatenate([u, specials])
+    f = u.view(np.float32)
+    keep = ~np.isnan(f)
+    f = f[keep]
+    ours = D.f32_to_bf16_bits_rne(f)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_rounding_hand_worked_and_nan_reading():
+    cases = {0x3F808000: 0x3F80,  # 1 + 2^-8: tie, keep even 0x3F80
+             0x3F818000: 0x3F82,  # tie with odd low bit -> round up
+             0x3F808001: 0x3F81,  # just above the tie -> up
+             0x7F7FFFFF: 0x7F80,  # max finite fp32 overflows bf16 -> +inf
+             0x80000000: 0x8000,  # -0 stays -0
+             0x7FC00001: 0x7FC0, 0xFFC12345: 0x7FC0, 0x7F800001: 0x7FC0}  # NaN -> canonical
+    u = np.array(list(cases), dtype=np.uint32)
+    out = D.f32_to_bf16_bits_rne(u.view(np.float32))
+    assert [int(v) for v in out] == list(cases.values())
+
+
+# -- AlltoAll -------------------------------------------------------------------------
+def test_alltoall_page_fill_pattern():
+    g = _load("alltoall_fill.json")
+    R, count = 4, 16
+    wr, wd, we = (g["fill"][k] for k in ("rank_weight", "dest_weight", "element_weight"))
+    sends = []
+    for s in range(R):
+        blocks = [np.array([s * wr + d * wd + i * we for i in range(count)], dtype=np.int32)
+                  for d in range(R)]
+        sends.append(np.concatenate(blocks).view(np.uint8))
+    out = D.alltoall(sends, count * 4)
+    for d in range(R):
+        got = out[d].view(np.int32).reshape(R, count)
+        for s in range(R):
+            assert list(got[s]) == [s * wr + d * wd + i * we for i in range(count)]
+
+
+def test_alltoall_is_block_transpose_and_bijection():
+    R, B = 5, 24
+    sends = W.alltoall_inputs(R, B, seed=1)
+    out = D.alltoall(sends, B)
+    ref = np.stack(sends).reshape(R, R, B).swapaxes(0, 1).reshape(R, R * B)
+    assert all(np.array_equal(out[d], ref[d]) for d in range(R))
+    # index-tagged payload: every (source, dest, word) lands exactly once
+    tagged = [np.array([(s << 20) | (d << 10) | w for d in range(R) for w in range(B // 4)],
+                       dtype=np.uint32).view(np.uint8) for s in range(R)]
+    got = np.concatenate([o.view(np.uint32) for o in D.alltoall(tagged, B)])
+    assert sorted(got.tolist()) == sorted(np.concatenate([t.view(np.uint32) for t in tagged]).tolist())
+
+
+# -- AllGather -------------------------------------------------------------------------
+def test_allgather_page_segments():
+    g = _load("allgather_segments.json")
+    R = g["ranks"]
+    n = g["send_bytes"] // 4
+    sends = [np.full(n, float(r), dtype=np.float32).view(np.uint8) for r in range(R)]
+    out = D.allgather(sends)
+    for d in range(R):
+        assert out[d].nbytes == g["recv_bytes"]
+        segs = out[d].view(np.float32).reshape(R, n)
+        for k, v in enumerate(g["segment_values"]):
+            assert np.all(segs[k] == np.float32(v))
+
+
+def test_allgather_matches_tile():
+    sends = W.allgather_inputs(3, 36, seed=3)
+    out = D.allgather(sends)
+    ref = np.tile(np.concatenate(sends), (3, 1))
+    assert all(np.array_equal(out[d], ref[d]) for d in range(3))
+
+
+# -- Ring --------------------------------------------------------------------------------
+def test_ring_is_cyclic_shift():
+    R, P, pb = 5, 6, 8
+    sends = W.ring_inputs(R, P, pb, seed=2)
+    before = [np.full(P * pb + 5, 0xEE, dtype=np.uint8) for _ in range(R)]
+    out = D.ring(sends, before, P, pb)
+    ref = np.roll(np.stack(sends), 1, axis=0)
+    for d in range(R):
+        assert np.array_equal(out[d][:P * pb], ref[d])
+        assert np.all(out[d][P * pb:] == 0xEE)
+
+
+# -- Dispatch ------------------------------------------------------------------------------
+def _dispatch_by_loops(topk, x, E):
+    """Destination-major loops: for d, for expert e of d, for source s, for token t."""
+    R, T, K = topk.shape
+    epr = E // R
+    res = []
+    for d in range(R):
+        rows, tags = [], []
+        for e in range(d * epr, (d + 1) * epr):
+            for s in range(R):
+                for t in range(T):
+                    if e in list(topk[s, t]):
+                        rows.append(x[s, t].view(np.uint8))
+                        tags.append((s << 16) | t)
+        res.append((rows, tags))
+    return res
+
+
+def test_dispatch_brute_force_all_routings_tiny():
+    # Every routing for R=2, T=2, K=2, E=4 with distinct experts per token.
+    R, T, K, E = 2, 2, 2, 4
+    pairs = [p for p in itertools.permutations(range(E), K)]
+    x = np.arange(R * T * 2, dtype=np.uint16).reshape(R, T, 2)
+    n = 0
+    for choice in itertools.product(pairs, repeat=R * T):
+        topk = np.array(choice, dtype=np.int32).reshape(R, T, K)
+        rows, src, counts, over = D.dispatch(topk, x, E)
+        ref = _dispatch_by_loops(topk, x, E)
+        for d in range(R):
+            rr, tt = ref[d]
+            assert rows[d].shape[0] == len(rr)
+            if rr:
+                assert np.array_equal(rows[d], np.stack(rr))
+            assert src[d].tolist() == tt
+            assert int(counts[d].sum()) == len(rr)
+            assert not over[d]
+        n += 1
+    assert n == len(pairs) ** (R * T)
+
+
+def test_dispatch_brute_force_three_ranks_one_slot():
+    R, T, K, E = 3, 2, 1, 6
+    x = (np.arange(R * T * 3, dtype=np.uint16) * 7).reshape(R, T, 3)
+    for choice in itertools.product(range(E), repeat=R * T):
+        topk = np.array(choice, dtype=np.int32).reshape(R, T, K)
+        rows, src, _, _ = D.dispatch(topk, x, E)
+        ref = _dispatch_by_loops(topk, x, E)
+        for d in range(R):
+            assert src[d].tolist() == ref[d][1]
+
+
+def test_dispatch_matches_numpy_stable_argsort_and_invariants():
+    R, T, H, E, K = 4, 300, 8, 32, 4
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=12)
+    rows, src, counts, over = D.dispatch(topk, x, E)
+    s_idx, t_idx, _ = np.meshgrid(np.arange(R), np.arange(T), np.arange(K), indexing="ij")
+    e = topk.reshape(-1).astype(np.int64)
+    key = (e * R + s_idx.reshape(-1)) * T + t_idx.reshape(-1)
+    order = np.argsort(key, kind="stable")
+    epr = E // R
+    xb = x.reshape(R, T, -1).view(np.uint8)
+    start = 0
+    for d in range(R):
+        n = int(np.sum(e // epr == d))
+        sel = order[start:start + n]
+        start += n
+        ss, tt = s_idx.reshape(-1)[sel], t_idx.reshape(-1)[sel]
+        assert np.array_equal(src[d], ((ss << 16) | tt).astype(np.int32))
+        assert np.array_equal(rows[d], xb[ss, tt])
+        assert np.array_equal(counts[d], np.bincount(e[e // epr == d] - d * epr, minlength=epr))
+    # bijection between routing slots and received rows; totals
+    assert sum(r.shape[0] for r in rows) == R * T * K
+    got = sorted((int(tag) >> 16, int(tag) & 0xFFFF) for d in range(R) for tag in src[d])
+    want = sorted((s, t) for s in range(R) for t in range(T) for _ in range(K))
+    assert got == want
+    assert np.array_equal(D.dispatch_rows_per_rank(topk, E), [r.shape[0] for r in rows])
+
+
+def test_dispatch_skips_unrouted_and_flags_capacity():
+    topk = np.array([[[0, -1], [1, 0]], [[-1, -1], [0, 3]]], dtype=np.int32)  # R=2,T=2,K=2,E=4
+    x = np.arange(2 * 2 * 1, dtype=np.uint16).reshape(2, 2, 1)
+    rows, src, counts, over = D.dispatch(topk, x, 4, capacity_rows=2)
+    assert counts[0].tolist() == [3, 1] and counts[1].tolist() == [0, 1]
+    assert over == [True, False]
+    assert src[0].tolist() == [(0 << 16) | 0, (0 << 16) | 1]  # third row dropped
+    with pytest.raises(ValueError):
+        D.dispatch(np.array([[[4]]], dtype=np.int32), np.zeros((1, 1, 1), np.uint16), 4)

@@ -1,0 +1,128 @@
+"""Planted mistakes in the oracle must be caught by its pins (run on the CPU).
+
+Each test swaps one oracle function for a plausible wrong version and
+checks that the corresponding pin test fails.
+"""
+import numpy as np
+import pytest
+
+from oracle import definitions as D, ordering as O
+import test_oracle_definitions as TD
+import test_oracle_ordering as TO
+import test_oracle_primitives as TP
+
+
+def _fails(fn, *a):
+    with pytest.raises(AssertionError):
+        fn(*a)
+
+
+def test_sum_started_from_zero_is_caught(monkeypatch):
+    def bad(xs):
+        acc = np.zeros_like(np.asarray(xs[0], np.float32))
+        for x in xs:
+            acc = acc + np.asarray(x, np.float32)
+        return acc
+    monkeypatch.setattr(D, "allreduce_sum_f32", bad)
+    _fails(TD.test_allreduce_summation_order_hand_worked)
+
+
+def test_reversed_rank_order_is_caught(monkeypatch):
+    orig = D.allreduce_sum_f32
+    monkeypatch.setattr(D, "allreduce_sum_f32", lambda xs: orig(list(xs)[::-1]))
+    _fails(TD.test_allreduce_summation_order_hand_worked)
+    _fails(TD.test_allreduce_matches_numpy_axis0_reduction)
+
+
+def test_pairwise_summation_is_caught(monkeypatch):
+    def pairwise(xs):
+        xs = [np.asarray(x, np.float32) for x in xs]
+        while len(xs) > 1:
+            xs = [xs[i] + xs[i + 1] if i + 1 < len(xs) else xs[i] for i in range(0, len(xs), 2)]
+        return xs[0]
+    monkeypatch.setattr(D, "allreduce_sum_f32", pairwise)
+    _fails(TD.test_allreduce_matches_numpy_axis0_reduction)
+
+
+def test_dropped_rank_is_caught(monkeypatch):
+    orig = D.allreduce_sum_f32
+    monkeypatch.setattr(D, "allreduce_sum_f32", lambda xs: orig(list(xs)[:-1]) if len(xs) > 1 else orig(xs))
+    _fails(TD.test_allreduce_worked_example_rank_fill)
+
+
+def test_bf16_truncation_is_caught(monkeypatch):
+    def trunc(x):
+        return (np.ascontiguousarray(x, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    monkeypatch.setattr(D, "f32_to_bf16_bits_rne", trunc)
+    _fails(TD.test_bf16_rounding_matches_torch_on_non_nan)
+    _fails(TD.test_bf16_rounding_hand_worked_and_nan_reading)
+
+
+def test_bf16_round_half_up_is_caught(monkeypatch):
+    def half_up(x):
+        u = np.ascontiguousarray(x, np.float32).view(np.uint32)
+        return ((u + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16)
+    monkeypatch.setattr(D, "f32_to_bf16_bits_rne", half_up)
+    _fails(TD.test_bf16_rounding_hand_worked_and_nan_reading)
+
+
+def test_alltoall_transposed_index_is_caught(monkeypatch):
+    def transposed(sends, B):
+        R = len(sends)
+        return [np.concatenate([np.asarray(sends[d]).reshape(-1)[s * B:(s + 1) * B] for s in range(R)])
+                for d in range(R)]
+    monkeypatch.setattr(D, "alltoall", transposed)
+    _fails(TD.test_alltoall_page_fill_pattern)
+    _fails(TD.test_alltoall_is_block_transpose_and_bijection)
+
+
+def test_allgather_wrong_segment_is_caught(monkeypatch):
+    def shifted(sends):
+        R = len(sends)
+        return [np.concatenate([np.asarray(sends[(s + 1) % R]).reshape(-1) for s in range(R)]) for _ in range(R)]
+    monkeypatch.setattr(D, "allgather", shifted)
+    _fails(TD.test_allgather_page_segments)
+
+
+def test_dispatch_unstable_order_is_caught(monkeypatch):
+    orig = D.dispatch
+
+    def token_major(topk, x, E, capacity_rows=None):
+        rows, src, counts, over = orig(topk, x, E, capacity_rows)
+        # same multiset per destination, but ordered by (source, token) only
+        for d in range(len(rows)):
+            order = np.argsort(src[d], kind="stable")
+            rows[d], src[d] = rows[d][order], src[d][order]
+        return rows, src, counts, over
+    monkeypatch.setattr(D, "dispatch", token_major)
+    _fails(TD.test_dispatch_matches_numpy_stable_argsort_and_invariants)
+
+
+def test_dispatch_wrong_owner_is_caught(monkeypatch):
+    orig = D.dispatch
+
+    def rotated(topk, x, E, capacity_rows=None):
+        rows, src, counts, over = orig(topk, x, E, capacity_rows)
+        return rows[1:] + rows[:1], src[1:] + src[:1], counts[1:] + counts[:1], over
+    monkeypatch.setattr(D, "dispatch", rotated)
+    _fails(TD.test_dispatch_brute_force_all_routings_tiny)
+
+
+def test_rolling_compare_off_by_one_is_caught(monkeypatch):
+    def bad(a, b, bits):
+        m = (1 << bits) - 1
+        return ((b - a) & m) <= (1 << (bits - 1))
+    monkeypatch.setattr(TP, "rolling_le", bad)
+    _fails(TP.test_rolling_le_small_width_brute_force)
+
+
+def test_weak_rule_treated_as_strong_is_caught(monkeypatch):
+    orig = O._prereqs
+    monkeypatch.setattr(O, "_prereqs", lambda n, strong: orig(n, True))
+    _fails(TO.test_weak_signal_admits_a_missing_earlier_payload, 3)
+
+
+def test_strong_rule_treated_as_weak_is_caught(monkeypatch):
+    orig = O._prereqs
+    monkeypatch.setattr(O, "_prereqs", lambda n, strong: orig(n, False))
+    _fails(TO.test_strong_signal_prefix_property_holds_in_every_state, 3)

@@ -1,0 +1,239 @@
+"""The protocol simulation reaches the plain definitions under every schedule tried."""
+import numpy as np
+import pytest
+
+from oracle import definitions as D, protocol as pr
+from oracle.primitives import Deadlock, SignalInc, World
+import workloads as W
+
+
+def _alltoall_setup(R, B, sends):
+    def setup():
+        w = World(R, signal_count=2)
+        s = w.register([x.copy() for x in sends])
+        r = w.register_zeros(R * B)
+        return w, pr.alltoall_programs(w, s, r, B, 1)
+    return setup
+
+
+@pytest.mark.parametrize("R", [3])
+def test_alltoall_every_interleaving_state_search(R):
+    B = 4
+    sends = W.alltoall_inputs(R, B, seed=R)
+    exp = D.alltoall(sends, B)
+    finals = list(pr.distinct_final_states(_alltoall_setup(R, B, sends)))
+    assert len(finals) == 1
+    w = finals[0]
+    recv = list(w.windows)[1]
+    assert all(np.array_equal(w.buf(recv, d), exp[d]) for d in range(R))
+
+
+@pytest.mark.parametrize("R", [2])
+def test_alltoall_every_interleaving(R):
+    B = 8
+    sends = W.alltoall_inputs(R, B, seed=R)
+    exp = D.alltoall(sends, B)
+    n = 0
+    for w, _ in pr.all_runs(_alltoall_setup(R, B, sends)):
+        recv = [h for h in w.windows][1]
+        for d in range(R):
+            assert np.array_equal(w.buf(recv, d), exp[d])
+            assert w.sig[d][1] == R
+        n += 1
+    assert n > 1
+
+
+@pytest.mark.parametrize("R", [3, 5, 8])
+def test_alltoall_random_interleavings(R):
+    B = 12
+    sends = W.alltoall_inputs(R, B, seed=R)
+    exp = D.alltoall(sends, B)
+    for seed in range(20):
+        w, progs = _alltoall_setup(R, B, sends)()
+        pr.run(w, progs, seed=seed)
+        recv = list(w.windows)[1]
+        assert all(np.array_equal(w.buf(recv, d), exp[d]) for d in range(R))
+        assert [w.sig[d][1] for d in range(R)] == [R] * R
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_allreduce_every_interleaving_two_ranks(dtype):
+    R, N = 2, 37
+    xs = W.allreduce_f32_inputs(R, N) if dtype == "f32" else W.allreduce_bf16_inputs(R, N)
+    exp = D.allreduce(xs, dtype).view(np.uint8)
+    es = 4 if dtype == "f32" else 2
+
+    def setup():
+        w = World(R)
+        s = w.register([x.view(np.uint8).copy() for x in xs])
+        r = w.register_zeros(N * es)
+        sc = w.register_zeros(pr.allreduce_scratch_bytes(N, R, dtype))
+        return w, pr.allreduce_programs(w, s, r, sc, N, dtype, 0)
+
+    n = 0
+    for w, _ in pr.all_runs(setup):
+        recv = list(w.windows)[1]
+        assert all(np.array_equal(w.buf(recv, d), exp) for d in range(R))
+        assert [w.sig[d][0] for d in range(R)] == [R] * R
+        n += 1
+    assert n > 10
+
+
+@pytest.mark.parametrize("R,N,dtype", [(3, 1001, "f32"), (4, 64, "bf16"), (8, 1000, "bf16"),
+                                       (5, 3, "f32"), (1, 17, "f32")])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_allreduce_random_interleavings(R, N, dtype, seed):
+    xs = W.allreduce_f32_inputs(R, N, seed=seed) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=seed)
+    es = 4 if dtype == "f32" else 2
+    w = World(R)
+    s = w.register([x.view(np.uint8).copy() for x in xs])
+    r = w.register_zeros(N * es)
+    sc = w.register_zeros(pr.allreduce_scratch_bytes(N, R, dtype))
+    pr.run(w, pr.allreduce_programs(w, s, r, sc, N, dtype, 0), seed=seed)
+    exp = D.allreduce(xs, dtype).view(np.uint8)
+    assert all(np.array_equal(w.buf(r, d), exp) for d in range(R))
+    assert [w.sig[d][0] for d in range(R)] == [R] * R
+
+
+def test_allreduce_worked_example_through_protocol():
+    R, N = 4, 1 << 20
+    xs = W.allreduce_f32_inputs(R, N, run="A")
+    w = World(R)
+    s = w.register([x.view(np.uint8).copy() for x in xs])
+    r = w.register_zeros(N * 4)
+    sc = w.register_zeros(pr.allreduce_scratch_bytes(N, R, "f32"))
+    pr.run(w, pr.allreduce_programs(w, s, r, sc, N, "f32", 0), seed=0)
+    for d in range(R):
+        assert np.all(w.buf(r, d).view(np.float32) == np.float32(6.0))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_allgather_protocol(seed):
+    R, M = 4, 52
+    sends = W.allgather_inputs(R, M, seed=seed)
+    w = World(R)
+    s = w.register([x.copy() for x in sends])
+    r = w.register_zeros(R * M)
+    pr.run(w, pr.allgather_programs(w, s, r, M, 3), seed=seed)
+    exp = D.allgather(sends)
+    assert all(np.array_equal(w.buf(r, d), exp[d]) for d in range(R))
+    assert [w.sig[d][3] for d in range(R)] == [R] * R
+
+
+def test_allgather_every_interleaving_two_ranks():
+    R, M = 2, 12
+    sends = W.allgather_inputs(R, M, seed=4)
+    exp = D.allgather(sends)
+
+    def setup():
+        w = World(R)
+        s = w.register([x.copy() for x in sends])
+        r = w.register_zeros(R * M)
+        return w, pr.allgather_programs(w, s, r, M, 0)
+
+    for w, _ in pr.all_runs(setup):
+        r = list(w.windows)[1]
+        assert all(np.array_equal(w.buf(r, d), exp[d]) for d in range(R))
+
+
+@pytest.mark.parametrize("seed", [0, 3])
+def test_ring_protocol_signals_and_counters(seed):
+    R, P, pb, C = 4, 12, 16, 3
+    sends = W.ring_inputs(R, P, pb, seed=seed)
+    w = World(R, signal_count=C, counter_count=C)
+    s = w.register([x.copy() for x in sends])
+    r = w.register([np.full(P * pb, 7, np.uint8) for _ in range(R)])
+    pr.run(w, pr.ring_programs(w, s, r, P, pb, C, 0, 0), seed=seed)
+    exp = D.ring(sends, [np.full(P * pb, 7, np.uint8)] * R, P, pb)
+    assert all(np.array_equal(w.buf(r, d), exp[d]) for d in range(R))
+    assert w.sig == [[P // C] * C] * R
+    assert w.cnt == [[P // C] * C] * R
+
+
+def test_ring_with_reset_returns_signals_to_zero():
+    R, P, pb, C = 3, 4, 8, 2
+    sends = W.ring_inputs(R, P, pb, seed=1)
+    w = World(R, signal_count=C, counter_count=C)
+    s = w.register([x.copy() for x in sends])
+    r = w.register_zeros(P * pb)
+    pr.run(w, pr.ring_programs(w, s, r, P, pb, C, 0, 0, reset=True), seed=1)
+    assert w.sig == [[0] * C] * R
+    assert w.cnt == [[P // C] * C] * R
+
+
+def _run_dispatch(R, T, H, E, K, seed, cap=None):
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    cap = cap if cap is not None else R * T * min(K, E // R)
+    w = World(R)
+    b = pr.DispatchBuffers(w, x, topk, E, cap)
+    pr.run(w, pr.dispatch_programs(w, b, 0, 1), seed=seed)
+    return topk, x, w, b, cap
+
+
+@pytest.mark.parametrize("R,T,H,E,K,seed", [(4, 37, 8, 16, 3, 0), (2, 50, 4, 8, 2, 1),
+                                             (3, 20, 2, 6, 2, 2), (8, 64, 4, 64, 8, 3)])
+def test_dispatch_protocol_matches_definition(R, T, H, E, K, seed):
+    topk, x, w, b, cap = _run_dispatch(R, T, H, E, K, seed)
+    rows, src, counts, over = D.dispatch(topk, x, E, cap)
+    for d in range(R):
+        n, rb = rows[d].shape
+        assert np.array_equal(w.buf(b.recv, d)[:n * rb], rows[d].reshape(-1))
+        assert np.array_equal(w.buf(b.recv_src, d)[:n * 4].view(np.int32), src[d])
+        assert np.array_equal(b.counts[d], counts[d])
+        assert w.sig[d][0] == R            # count exchange: one SignalInc per source
+        assert w.sig[d][1] == n            # rows: SignalAdd totals aimed at d
+        assert b.overflow[d] == over[d]
+
+
+def test_dispatch_protocol_capacity_overflow():
+    R, T, H, E, K = 2, 40, 2, 4, 2
+    topk, x, w, b, cap = _run_dispatch(R, T, H, E, K, 5, cap=30)
+    rows, src, counts, over = D.dispatch(topk, x, E, cap)
+    assert any(over)
+    for d in range(R):
+        n, rb = rows[d].shape
+        assert np.array_equal(w.buf(b.recv, d)[:n * rb], rows[d].reshape(-1))
+        assert b.overflow[d] == over[d]
+
+
+def test_dispatch_every_interleaving_two_ranks():
+    R, T, H, E, K = 2, 3, 1, 4, 2
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=8)
+    rows, src, counts, _ = D.dispatch(topk, x, E, R * T * K)
+    bufs = []
+
+    def setup():
+        w = World(R)
+        b = pr.DispatchBuffers(w, x, topk, E, R * T * K)
+        bufs.append(b)
+        return w, pr.dispatch_programs(w, b, 0, 1)
+
+    n = 0
+    for w in pr.distinct_final_states(setup):
+        b = bufs[-1]
+        for d in range(R):
+            k, rb = rows[d].shape
+            assert np.array_equal(w.buf(b.recv, d)[:k * rb], rows[d].reshape(-1))
+            assert np.array_equal(w.buf(b.recv_src, d)[:k * 4].view(np.int32), src[d])
+            assert w.sig[d][1] == k
+        n += 1
+    assert n == 1  # one outcome, whatever the interleaving
+
+
+def test_deadlock_is_detected_when_a_put_is_missing():
+    R, B = 3, 4
+    w = World(R)
+    s = w.register_zeros(R * B)
+    r = w.register_zeros(R * B)
+
+    def prog(rank):
+        base = yield pr.ReadSignal(0)
+        yield pr.Barrier()
+        for peer in range(R):
+            if (rank, peer) == (1, 2):
+                continue  # the dropped put
+            yield pr.Put(peer, r, rank * B, s, peer * B, B, SignalInc(0))
+        yield pr.WaitSignal(0, base + R)
+
+    with pytest.raises(Deadlock):
+        pr.run(w, [prog(q) for q in range(R)], seed=0)
