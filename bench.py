@@ -1,0 +1,378 @@
+"""Throughput of the window put/get collectives on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
+
+A step is one sum-AllReduce of 8 virtual ranks x 64 Mi bf16 elements each
+(fp32 accumulation in fixed rank order, bf16 output): reduce-scatter by gets
+and all-gather by puts with a SignalInc per (owner, receiver), receivers
+waiting in-kernel -- the whole hot path, one kernel launch. Inputs are
+seeded normal(0, 1) values already resident in HBM when the timed region
+starts. The metric is achieved HBM GB/s over the algorithmic bytes
+2 * R * N * 2 (every input byte read once, every output byte written once).
+
+Printed: one JSON line with the metric, the roofline of the AllReduce kernel
+(its algorithmic bytes over its event-timed duration, against the 8 TB/s
+HBM3E peak), the CPU oracle timed on a bounded sample, and -- unless
+--no-rows -- the other workloads (AllReduce fp32 R=4, AlltoAll, dispatch,
+AllGather, ring exchange) each measured the same way, with the 256 MiB
+Infinity Cache flushed before every timed repetition.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (and % of peak) for R-rank AllReduce/AlltoAll/dispatch"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "k_allreduce": "allreduce.hip", "k_alltoall": "alltoall.hip", "k_allgather": "allgather.hip",
+    "k_dispatch_put": "dispatch.hip", "k_ring": "ring.hip",
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    """Hash of a kernel's source and the shared device header (to age traffic figures)."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "vr_device.hpp"):
+        with open(os.path.join(ROOT, "collective_window_put_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter runs, if they match this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(f"{kernel}:{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Bench:
+    def __init__(self):
+        import torch
+        import collective_window_put_amd as vr
+        self.torch, self.vr = torch, vr
+        torch.cuda.set_device(0)
+        self.stream = torch.cuda.current_stream()
+        self.flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def slices(self, R: int, nbytes: int, arrays=None, fill=None):
+        torch = self.torch
+        a = self.vr.VR_WIN_REQUIRED_ALIGNMENT
+        stride = (nbytes + a - 1) // a * a
+        slab = torch.empty(R * stride + a, dtype=torch.uint8, device="cuda")
+        s = (-slab.data_ptr()) % a
+        views = [slab[s + r * stride: s + r * stride + nbytes] for r in range(R)]
+        if arrays is not None:
+            for v, x in zip(views, arrays):
+                v.copy_(torch.from_numpy(np.ascontiguousarray(x).reshape(-1).view(np.uint8)))
+        elif fill is not None:
+            slab.fill_(fill)
+        return slab, views
+
+    def flush_cache(self):
+        self.flush_buf.fill_(1)  # 1 GiB write evicts the 256 MiB Infinity Cache and the L2s
+
+    def timed(self, fn, reps: int, flush: bool):
+        """Per-repetition durations (ms) from events recorded on the launch stream."""
+        torch = self.torch
+        out = []
+        for _ in range(reps):
+            if flush:
+                self.flush_cache()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            fn()
+            e1.record(self.stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return out
+
+
+def row_entry(name, bytes_alg, times_ms, kernel, workload, extra=None):
+    med = float(np.median(times_ms))
+    gbs = bytes_alg / (med * 1e-3) / 1e9
+    d = {"algorithmic_bytes": int(bytes_alg), "median_ms": round(med, 5), "min_ms": round(float(np.min(times_ms)), 5),
+         "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "kernel": kernel,
+         "traffic_bytes_per_launch": measured_traffic(kernel, workload) if kernel in KERNEL_SOURCES else None}
+    if extra:
+        d.update(extra)
+    log(f"{name}: {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), median {med:.4f} ms")
+    return d
+
+
+# ---- the headline workload -------------------------------------------------------------------
+def run_allreduce_headline(b: Bench, steps: int, warmup: int):
+    import workloads as W
+    vr = b.vr
+    c = W.CONFIGS["c2"]
+    R, N = c["ranks"], c["count"]
+    log(f"generating AllReduce inputs R={R} N={N} bf16")
+    xs = W.allreduce_bf16_inputs(R, N, seed=c["seed"])
+    comm = vr.vr_comm_create(R, signal_count=4)
+    s_slab, sv = b.slices(R, N * 2, arrays=xs)
+    r_slab, rv = b.slices(R, N * 2, fill=0)
+    sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], N * 2)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], N * 2)
+    stream = b.stream.cuda_stream
+
+    def step():
+        vr.vr_allreduce(comm, sw, 0, rw, 0, N, vr.VR_DT_BF16, sig=0, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    b.torch.cuda.synchronize()
+    # timed region: K steps, events around each one on the launch stream
+    evs = [(b.torch.cuda.Event(enable_timing=True), b.torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    b.torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(b.stream)
+        step()
+        e1.record(b.stream)
+    b.torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    code, bits = vr.vr_comm_get_async_error(comm)
+    if code != vr.VR_OK:
+        raise RuntimeError(f"device error during the AllReduce: {vr.vr_error_string(code)} bits={bits:#x}")
+    # spot-check the last result against the fixed rank-order sum on a sample of elements
+    idx = np.random.default_rng(0).integers(0, N, 4096)
+    acc = (xs[0][idx].astype(np.uint32) << 16).view(np.float32)
+    for r in range(1, R):
+        acc = acc + (xs[r][idx].astype(np.uint32) << 16).view(np.float32)
+    u = acc.view(np.uint32)
+    exp = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    for d in (0, R - 1):
+        got = rv[d].view(b.torch.int16).cpu().numpy().view(np.uint16)[idx]
+        if not np.array_equal(got, exp):
+            raise RuntimeError(f"AllReduce result mismatch on rank {d}")
+    bytes_alg = 2 * R * N * 2
+    ms_per_step = wall * 1e3 / steps
+    vr.vr_window_deregister(comm, sw)
+    vr.vr_window_deregister(comm, rw)
+    vr.vr_comm_destroy(comm)
+    del s_slab, r_slab
+    return dict(xs=xs, R=R, N=N, bytes_alg=bytes_alg, ms_per_step=ms_per_step, kern_ms=kern_ms)
+
+
+# ---- the other workloads ------------------------------------------------------------------------
+def run_rows(b: Bench, reps: int = 10):
+    import workloads as W
+    vr = b.vr
+    torch = b.torch
+    stream = b.stream.cuda_stream
+    rows = {}
+
+    def comm_for(R, **kw):
+        return vr.vr_comm_create(R, **kw)
+
+    # AllReduce fp32, R=4, 1 Mi elements (the worked-example shape)
+    c = W.CONFIGS["c1"]
+    R, N = c["ranks"], c["count"]
+    xs = W.allreduce_f32_inputs(R, N, run="B", seed=c["seed"])
+    comm = comm_for(R, signal_count=2)
+    s1, sv = b.slices(R, N * 4, arrays=xs)
+    r1, rv = b.slices(R, N * 4, fill=0)
+    sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], N * 4)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], N * 4)
+    f = lambda: vr.vr_allreduce(comm, sw, 0, rw, 0, N, vr.VR_DT_F32, sig=0, stream=stream)  # noqa: E731
+    f()
+    rows["allreduce_f32_r4_1Mi"] = row_entry("AllReduce fp32 R=4 N=1Mi", 2 * R * N * 4, b.timed(f, reps, True),
+                                             "k_allreduce", "allreduce_f32_r4_1Mi")
+    vr.vr_window_deregister(comm, sw)
+    vr.vr_window_deregister(comm, rw)
+    vr.vr_comm_destroy(comm)
+    del s1, r1
+
+    # AlltoAll R=8, 4 MiB blocks
+    c = W.CONFIGS["c3"]
+    R, B = c["ranks"], c["block_bytes"]
+    sends = W.alltoall_inputs(R, B, seed=c["seed"])
+    comm = comm_for(R, signal_count=2)
+    s1, sv = b.slices(R, R * B, arrays=sends)
+    r1, rv = b.slices(R, R * B, fill=0)
+    sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], R * B)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], R * B)
+    f = lambda: vr.vr_alltoall(comm, sw, 0, rw, 0, B, sig=0, stream=stream)  # noqa: E731
+    f()
+    rows["alltoall_r8_4MiB"] = row_entry("AlltoAll R=8 B=4MiB", 2 * R * R * B, b.timed(f, reps, True),
+                                         "k_alltoall", "alltoall_r8_4MiB")
+    vr.vr_window_deregister(comm, sw)
+    vr.vr_window_deregister(comm, rw)
+    vr.vr_comm_destroy(comm)
+    del s1, r1
+
+    # MoE dispatch R=8, 4096 tokens x 512 B, 256 experts, top-8 Zipf(1.1)
+    c = W.CONFIGS["c4"]
+    R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
+    topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
+    rb = H * 2
+    cap = R * T * min(K, E // R)
+    comm = comm_for(R, signal_count=4)
+    s1, xv = b.slices(R, T * rb, arrays=[x[r] for r in range(R)])
+    r1, rv = b.slices(R, cap * rb, fill=0)
+    xw = vr.vr_window_register(comm, [v.data_ptr() for v in xv], T * rb)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], cap * rb)
+    tk = torch.from_numpy(topk).cuda()
+    counts = torch.zeros(R, E // R, dtype=torch.int32, device="cuda")
+    src = torch.zeros(R, cap, dtype=torch.int32, device="cuda")
+    f = lambda: vr.vr_dispatch(comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, 0, 1, stream=stream)  # noqa
+    f()
+    nrows = int((topk >= 0).sum())
+    bytes_alg = R * T * rb + topk.nbytes + nrows * rb + nrows * 4 + R * (E // R) * 4
+    rows["dispatch_r8_t4096_e256_k8"] = row_entry("dispatch R=8 T=4096 512B E=256 K=8", bytes_alg,
+                                                  b.timed(f, reps, True), "k_dispatch_put",
+                                                  "dispatch_r8_t4096_e256_k8", {"rows": nrows})
+    vr.vr_window_deregister(comm, xw)
+    vr.vr_window_deregister(comm, rw)
+    vr.vr_comm_destroy(comm)
+    del s1, r1, tk, counts, src
+
+    # AllGather R=16, 64 MiB per rank
+    c = W.CONFIGS["c5a"]
+    R, M = c["ranks"], c["bytes_per_rank"]
+    sends = W.allgather_inputs(R, M, seed=c["seed"])
+    comm = comm_for(R, signal_count=2)
+    s1, sv = b.slices(R, M, arrays=sends)
+    r1, rv = b.slices(R, R * M, fill=None)
+    sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], M)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], R * M)
+    f = lambda: vr.vr_allgather(comm, sw, 0, rw, 0, M, sig=0, stream=stream)  # noqa: E731
+    f()
+    rows["allgather_r16_64MiB"] = row_entry("AllGather R=16 M=64MiB", R * M + R * R * M,
+                                            b.timed(f, max(3, reps // 2), True), "k_allgather",
+                                            "allgather_r16_64MiB")
+    vr.vr_window_deregister(comm, sw)
+    vr.vr_window_deregister(comm, rw)
+    vr.vr_comm_destroy(comm)
+    del s1, r1
+
+    # Ring exchange R=16, 65536 x 256 B per rank, 64 contexts, litmus on
+    c = W.CONFIGS["c5b"]
+    R, P, pb, C = c["ranks"], c["puts_per_rank"], c["put_bytes"], c["contexts"]
+    sends = W.ring_inputs(R, P, pb, seed=c["seed"])
+    comm = comm_for(R, signal_count=C, counter_count=C, context_count=C)
+    s1, sv = b.slices(R, P * pb, arrays=sends)
+    r1, rv = b.slices(R, P * pb, fill=0)
+    sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], P * pb)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], P * pb)
+    lit = torch.zeros(2, dtype=torch.int64, device="cuda")
+    f = lambda: vr.vr_ring_exchange(comm, sw, rw, pb, P, C, 0, 0, lit, stream=stream)  # noqa: E731
+    f()
+    t = b.timed(f, reps, True)
+    med = float(np.median(t))
+    lh = lit.cpu().numpy()
+    rows["ring_r16_1Mi_x_256B"] = row_entry("ring R=16 2^20 puts x 256B", 2 * R * P * pb, t, "k_ring",
+                                            "ring_r16_1Mi_x_256B",
+                                            {"Mputs_per_s": round(R * P / (med * 1e-3) / 1e6, 1),
+                                             "litmus_checks": int(lh[0]), "litmus_violations": int(lh[1])})
+    code, bits = vr.vr_comm_get_async_error(comm)
+    if code != vr.VR_OK:
+        raise RuntimeError(f"device error in the ring exchange: {vr.vr_error_string(code)} bits={bits:#x}")
+    vr.vr_window_deregister(comm, sw)
+    vr.vr_window_deregister(comm, rw)
+    vr.vr_comm_destroy(comm)
+    del s1, r1
+    return rows
+
+
+# ---- the CPU oracle beside it ---------------------------------------------------------------------
+def cpu_baseline(xs, R: int, N: int, budget_s: float = 20.0):
+    """Time the oracle's protocol simulation of the same AllReduce on one host core.
+
+    Bounded sample: the first n elements of every rank's input, n growing
+    until one run takes at least ~2 s (capped by the budget), then scaled to
+    GB/s over the sample's algorithmic bytes.
+    """
+    from oracle import primitives as P, protocol as pr
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    n = 1 << 20
+    t_used = 0.0
+    best = None
+    while True:
+        w = P.World(R, signal_count=1)
+        sw = w.register([x[:n].view(np.uint8).copy() for x in xs])
+        rw = w.register_zeros(n * 2)
+        sc = w.register_zeros(pr.allreduce_scratch_bytes(n, R, "bf16"))
+        t0 = time.perf_counter()
+        pr.run(w, pr.allreduce_programs(w, sw, rw, sc, n, "bf16", 0), seed=0)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        best = (n, dt)
+        del w
+        if dt >= 2.0 or n >= N or t_used + 4 * dt > budget_s:
+            break
+        n = min(N, n * 4)
+    n, dt = best
+    gbs = 2 * R * n * 2 / dt / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"protocol simulation of the bf16 AllReduce, R={R}, first {n} of {N} elements per rank "
+                      f"({dt:.2f} s on one pinned host core, numpy single-threaded)",
+            "seconds": round(dt, 3), "host_cpu_count": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--reps", type=int, default=10, help="repetitions per other workload")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the R virtual ranks share one device, and no collectives cross "
+              "GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+    b = Bench()
+    head = run_allreduce_headline(b, args.steps, args.warmup)
+    kern = float(np.mean(head["kern_ms"]))
+    achieved = head["bytes_alg"] / (kern * 1e-3) / 1e9
+    value = head["bytes_alg"] / (head["ms_per_step"] * 1e-3) / 1e9
+    workload = "allreduce_bf16_r8_64Mi"
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": workload, "ranks": head["R"], "count_per_rank": head["N"], "elem": "bf16",
+                   "accumulate": "f32 in rank order", "algorithmic_bytes": head["bytes_alg"],
+                   "frac_of_peak": round(value / HBM_PEAK_GBS, 4), "inputs": "seeded normal(0,1) -> bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("k_allreduce", workload), "kernel": "k_allreduce",
+                     "kernel_ms_mean": round(kern, 5)},
+    }
+    if not args.no_rows:
+        out["rows"] = run_rows(b, args.reps)
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(head["xs"], head["R"], head["N"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

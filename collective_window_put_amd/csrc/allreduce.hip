@@ -1,0 +1,231 @@
+// Sum-AllReduce over symmetric windows: reduce-scatter by gets, all-gather by
+// puts, fused in one kernel so a reduced chunk never round-trips through HBM.
+//
+// Symmetric page (zwxr.cn/news/250719), AllReduce example: every rank ends
+// with the element-wise sum over all ranks. GIN page (lpnh.cn/news/2681042):
+// get pulls a peer's window bytes, put pushes them with a SignalInc.
+//
+// Owner c reduces elements [c*csz, (c+1)*csz) (csz = ceil(N/R) rounded up to
+// a whole number of tiles). Each workgroup takes one tile of one owner's
+// chunk: it reads the tile from every rank's send window (the gets of the
+// reduce-scatter), sums in rank order in fp32 -- acc = x_0, then acc += x_r
+// for r = 1..R-1, each an IEEE binary32 addition rounded to nearest even --
+// converts, and stores the tile into every rank's receive window (the puts of
+// the all-gather). The workgroup completing the chunk's relay applies one
+// SignalInc at every rank, so each rank's signal rises by R (one per owner).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "vr_device.hpp"
+#include "vr_internal.hpp"
+
+namespace vr {
+namespace {
+
+constexpr int kU = 2;  // 16-byte vectors per thread per tile
+
+struct ARArgs {
+  WinTab send, recv;
+  U64Tab target;
+  uint64_t send_off, recv_off;
+  uint64_t count;   // elements
+  uint64_t csz;     // elements per owner chunk (multiple of the tile)
+  uint32_t tpc;     // tiles per chunk
+  uint64_t* sig;
+  uint32_t sig_stride;
+  uint32_t* relay;  // [R]
+  uint32_t* err;
+  uint64_t timeout_ns;
+  int R;
+  int wait;
+};
+
+template <int DT> struct Elem;
+template <> struct Elem<VR_DT_F32> {
+  static constexpr int kSize = 4, kPerVec = 4;
+  __device__ static void widen(v4u w, float* f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = __uint_as_float(w[j]);
+  }
+  __device__ static v4u narrow(const float* f) {
+    v4u w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = __float_as_uint(f[j]);
+    return w;
+  }
+  __device__ static float load1(const char* p) { return *reinterpret_cast<const float*>(p); }
+  __device__ static void store1(__amdgpu_buffer_rsrc_t r, uint32_t off, float f) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, off, 0, kStoreAgent);
+  }
+};
+template <> struct Elem<VR_DT_BF16> {
+  static constexpr int kSize = 2, kPerVec = 8;
+  __device__ static void widen(v4u w, float* f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = bf16lo(w[j]);
+      f[2 * j + 1] = bf16hi(w[j]);
+    }
+  }
+  __device__ static v4u narrow(const float* f) {
+    v4u w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = bf16_rne(f[2 * j]) | (bf16_rne(f[2 * j + 1]) << 16);
+    return w;
+  }
+  __device__ static float load1(const char* p) {
+    return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
+  }
+  __device__ static void store1(__amdgpu_buffer_rsrc_t r, uint32_t off, float f) {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bf16_rne(f)), r, off, 0, kStoreAgent);
+  }
+};
+
+// One tile [start, end) of the owner's chunk. RT: compile-time rank count, or
+// 0 for any R. ALIGNED: every rank's (base + offset) is 16-byte aligned.
+template <int DT, int RT, bool ALIGNED>
+__device__ void reduce_tile(const ARArgs& a, uint64_t start, uint64_t end) {
+  using E = Elem<DT>;
+  constexpr int V = E::kPerVec;
+  const int R = RT ? RT : a.R;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t nbytes = static_cast<uint32_t>((end - start) * E::kSize);
+  if (ALIGNED) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint64_t i = start + (uint64_t)(u * 256 + tid) * V;
+      if (i + V <= end) {
+        float acc[V];
+        const uint64_t sb = a.send_off + i * E::kSize;
+        if (RT) {
+          v4u x[RT ? RT : 1];
+#pragma unroll
+          for (int r = 0; r < (RT ? RT : 1); ++r)
+            x[r] = load16_stream(reinterpret_cast<const v4u*>(a.send.p[r] + sb));
+          E::widen(x[0], acc);
+#pragma unroll
+          for (int r = 1; r < (RT ? RT : 1); ++r) {
+            float f[V];
+            E::widen(x[r], f);
+#pragma unroll
+            for (int j = 0; j < V; ++j) acc[j] = acc[j] + f[j];
+          }
+        } else {
+          E::widen(load16_stream(reinterpret_cast<const v4u*>(a.send.p[0] + sb)), acc);
+          for (int r0 = 1; r0 < R; r0 += 4) {
+            v4u x[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (r0 + q < R) x[q] = load16_stream(reinterpret_cast<const v4u*>(a.send.p[r0 + q] + sb));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (r0 + q < R) {
+                float f[V];
+                E::widen(x[q], f);
+#pragma unroll
+                for (int j = 0; j < V; ++j) acc[j] = acc[j] + f[j];
+              }
+          }
+        }
+        const v4u out = E::narrow(acc);
+        const uint32_t off = static_cast<uint32_t>((i - start) * E::kSize);
+        for (int d = 0; d < R; ++d)
+          store16_agent(rsrc(a.recv.p[d] + a.recv_off + start * E::kSize, nbytes), off, out);
+      } else if (i < end) {  // ragged tail of the whole vector: element by element
+        for (uint64_t k = i; k < end; ++k) {
+          const uint64_t sb = a.send_off + k * E::kSize;
+          float acc = E::load1(a.send.p[0] + sb);
+          for (int r = 1; r < R; ++r) acc = acc + E::load1(a.send.p[r] + sb);
+          const uint32_t off = static_cast<uint32_t>((k - start) * E::kSize);
+          for (int d = 0; d < R; ++d)
+            E::store1(rsrc(a.recv.p[d] + a.recv_off + start * E::kSize, nbytes), off, acc);
+        }
+      }
+    }
+  } else {
+    for (uint64_t k = start + tid; k < end; k += 256) {
+      const uint64_t sb = a.send_off + k * E::kSize;
+      float acc = E::load1(a.send.p[0] + sb);
+      for (int r = 1; r < R; ++r) acc = acc + E::load1(a.send.p[r] + sb);
+      const uint32_t off = static_cast<uint32_t>((k - start) * E::kSize);
+      for (int d = 0; d < R; ++d) E::store1(rsrc(a.recv.p[d] + a.recv_off + start * E::kSize, nbytes), off, acc);
+    }
+  }
+}
+
+template <int DT, int RT, bool ALIGNED>
+__global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
+  const uint32_t R = RT ? RT : a.R;
+  const uint32_t nwork = R * a.tpc;
+  const uint32_t b = blockIdx.x;
+  if (b >= nwork) {  // receiver d waits for one SignalInc per owner
+    const uint32_t d = b - nwork;
+    if (threadIdx.x == 0)
+      wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
+    return;
+  }
+  const uint32_t c = b / a.tpc, j = b % a.tpc;
+  constexpr uint64_t tile = 256ull * kU * Elem<DT>::kPerVec;
+  const uint64_t cbeg = (uint64_t)c * a.csz;
+  const uint64_t cend = std::min<uint64_t>(a.count, cbeg + a.csz);
+  const uint64_t start = cbeg + (uint64_t)j * tile;
+  const uint64_t end = std::min<uint64_t>(cend, start + tile);
+  if (start < end) reduce_tile<DT, RT, ALIGNED>(a, start, end);
+  wg_stores_complete();
+  if (threadIdx.x == 0 && relay_arrive(a.relay + c, a.tpc))
+    for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
+}
+
+template <int DT, int RT, bool AL>
+void launch_t(const ARArgs& a, uint32_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_allreduce<DT, RT, AL>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int DT>
+void launch_dt(const ARArgs& a, bool aligned, uint32_t grid, hipStream_t st) {
+  if (!aligned) return launch_t<DT, 0, false>(a, grid, st);
+  switch (a.R) {
+    case 2: return launch_t<DT, 2, true>(a, grid, st);
+    case 4: return launch_t<DT, 4, true>(a, grid, st);
+    case 8: return launch_t<DT, 8, true>(a, grid, st);
+    case 16: return launch_t<DT, 16, true>(a, grid, st);
+    default: return launch_t<DT, 0, true>(a, grid, st);
+  }
+}
+
+}  // namespace
+
+vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, const vrWindow* recv, size_t recv_off,
+                            size_t count, int dtype, uint32_t sig, const U64Tab& target, bool wait, hipStream_t st) {
+  ARArgs a;
+  const int R = c->nranks;
+  bool aligned = ((send_off | recv_off) & 15) == 0;
+  for (int r = 0; r < VR_MAX_RANKS; ++r) {
+    a.send.p[r] = send->base[r];
+    a.recv.p[r] = recv->base[r];
+  }
+  a.target = target;
+  a.send_off = send_off;
+  a.recv_off = recv_off;
+  a.count = count;
+  const uint64_t tile = 256ull * kU * (dtype == VR_DT_F32 ? 4 : 8);
+  const uint64_t per = (count + R - 1) / R;
+  a.csz = (per + tile - 1) / tile * tile;
+  const uint64_t tpc = std::max<uint64_t>(1, a.csz / tile);
+  if (tpc * R > 0x7FFFFFFFull) return VR_ERR_INVALID_ARGUMENT;
+  a.tpc = static_cast<uint32_t>(tpc);
+  a.sig = c->sig + sig;
+  a.sig_stride = c->req.signal_count;
+  a.relay = c->relay + kRelayColl;
+  a.err = c->err;
+  a.timeout_ns = kDefaultTimeoutNs;
+  a.R = R;
+  a.wait = wait;
+  const uint32_t grid = a.tpc * R + (wait ? R : 0);
+  if (dtype == VR_DT_F32) launch_dt<VR_DT_F32>(a, aligned, grid, st);
+  else launch_dt<VR_DT_BF16>(a, aligned, grid, st);
+  return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;
+}
+
+}  // namespace vr

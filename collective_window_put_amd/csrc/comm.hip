@@ -1,0 +1,616 @@
+// Communicator, windows, one-sided primitives and the C ABI entry points.
+//
+// GIN page (lpnh.cn/news/2681042): one-sided transfers (put/get), signals
+// and counters, signal and counter methods. Symmetric page
+// (zwxr.cn/news/250719): window registration flags, alignment and the
+// deregister-before-free cleanup order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <new>
+#include <set>
+#include <vector>
+
+#include "vr_device.hpp"
+#include "vr_internal.hpp"
+
+using namespace vr;
+
+namespace {
+
+std::mutex g_mu;
+std::set<vrComm*> g_comms;
+
+constexpr uint32_t kPutTile = 16384;  // bytes per workgroup of a put
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool valid_req(int nranks, const vrCommRequirements* req) {
+  if (nranks < 1 || nranks > VR_MAX_RANKS || !req) return false;
+  if (req->signal_count < 1 || req->signal_count > 65536) return false;
+  if (req->counter_count > 65536) return false;
+  if (req->context_count < 1 || req->context_count > 1024) return false;
+  return true;
+}
+
+struct Layout {
+  size_t sig, cnt, err, relay, total;
+};
+Layout layout(int R, const vrCommRequirements& q) {
+  Layout l;
+  l.sig = 0;
+  l.cnt = align_up(l.sig + sizeof(uint64_t) * R * q.signal_count, 256);
+  l.err = align_up(l.cnt + sizeof(uint64_t) * R * std::max<uint32_t>(q.counter_count, 1), 256);
+  l.relay = align_up(l.err + 256, 256);
+  l.total = align_up(l.relay + sizeof(uint32_t) * kRelaySlots, 256);
+  return l;
+}
+
+bool live(vrComm* c) {
+  std::lock_guard<std::mutex> g(g_mu);
+  return c && g_comms.count(c);
+}
+bool has_win(vrComm* c, vrWindow* w) { return w && c->windows.count(w); }
+bool rank_ok(vrComm* c, int r) { return r >= 0 && r < c->nranks; }
+bool span_ok(const vrWindow* w, size_t off, size_t n) { return off <= w->bytes && n <= w->bytes - off; }
+bool overlap(const char* a, size_t an, const char* b, size_t bn) {
+  if (!an || !bn) return false;
+  return a < b + bn && b < a + an;
+}
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+vrResult_t hip_ok(hipError_t e) { return e == hipSuccess ? VR_OK : VR_ERR_HIP; }
+
+size_t sidx(const vrComm* c, int rank, uint32_t id) { return (size_t)rank * c->req.signal_count + id; }
+
+// Checks that a signal action may be applied (Inc/Add not mixed since the
+// last reset: GIN page, strong and weak signals).
+vrResult_t check_signal_mode(const vrComm* c, int peer, uint32_t id, uint32_t kind) {
+  const uint8_t m = c->sig_mode[sidx(c, peer, id)];
+  const uint8_t want = kind == VR_SIGNAL_INC ? 1 : 2;
+  return (m && m != want) ? VR_ERR_INVALID_USAGE : VR_OK;
+}
+void note_signal(vrComm* c, int peer, uint32_t id, uint32_t kind, uint64_t amount, bool known) {
+  const size_t i = sidx(c, peer, id);
+  c->sig_mode[i] = kind == VR_SIGNAL_INC ? 1 : 2;
+  c->expect[i] += amount;
+  if (!known) c->expect_known[i] = 0;
+}
+
+vrResult_t check_remote(vrComm* c, int peer, const vrRemoteAction& a) {
+  if (a.reserved) return VR_ERR_INVALID_ARGUMENT;
+  if (a.kind == VR_ACTION_NONE) return VR_OK;
+  if (a.kind != VR_SIGNAL_INC && a.kind != VR_SIGNAL_ADD) return VR_ERR_INVALID_ARGUMENT;
+  if (a.id >= c->req.signal_count) return VR_ERR_INVALID_ARGUMENT;
+  return check_signal_mode(c, peer, a.id, a.kind);
+}
+vrResult_t check_local(vrComm* c, const vrLocalAction& a) {
+  if (a.kind == VR_ACTION_NONE) return VR_OK;
+  if (a.kind != VR_COUNTER_INC) return VR_ERR_INVALID_ARGUMENT;
+  if (a.id >= c->req.counter_count) return VR_ERR_INVALID_ARGUMENT;
+  return VR_OK;
+}
+
+// ---- kernels -------------------------------------------------------------------
+struct PutArgs {
+  char* dst;
+  const char* src;
+  uint64_t bytes;
+  uint32_t parts;
+  int dir;           // 0: disjoint ranges; +1 / -1: overlapping, copy forward / backward
+  uint32_t* relay;
+  uint64_t* sig;     // remote action target or null
+  uint64_t add;
+  uint64_t* cnt;     // local action target or null
+};
+
+// Overlapping copy by one workgroup, in the direction that never overwrites
+// bytes not yet read: each round loads a chunk into registers, waits for the
+// loads, meets at a barrier, then stores.
+__device__ void memmove_wg(char* dst, const char* src, uint64_t n, int dir) {
+  constexpr uint32_t kChunk = 256 * 16;
+  const uint32_t t = threadIdx.x;
+  const uint64_t nchunks = (n + kChunk - 1) / kChunk;
+  for (uint64_t k = 0; k < nchunks; ++k) {
+    const uint64_t c = dir > 0 ? k : nchunks - 1 - k;
+    const uint64_t base = c * kChunk;
+    const uint32_t len = static_cast<uint32_t>(std::min<uint64_t>(kChunk, n - base));
+    uint8_t v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t i = t * 16 + j;
+      v[j] = i < len ? static_cast<uint8_t>(src[base + i]) : 0;
+    }
+    wait_vmem();
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rd = rsrc(dst + base, len);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t i = t * 16 + j;
+      if (i < len) store1_agent(rd, i, v[j]);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_put(PutArgs a) {
+  if (a.dir == 0) {
+    const uint64_t off = (uint64_t)blockIdx.x * kPutTile;
+    if (off < a.bytes) {
+      const uint32_t n = static_cast<uint32_t>(std::min<uint64_t>(kPutTile, a.bytes - off));
+      copy_any<4>(a.dst + off, a.src + off, n, threadIdx.x, 256);
+    }
+  } else {
+    memmove_wg(a.dst, a.src, a.bytes, a.dir);
+  }
+  wg_stores_complete();
+  if (threadIdx.x == 0 && relay_arrive(a.relay, a.parts)) {
+    if (a.sig) atomic_add_u64(a.sig, a.add);
+    if (a.cnt) atomic_add_u64(a.cnt, 1ull);
+  }
+}
+
+__global__ void k_signal(uint64_t* sig, uint64_t add) {
+  if (threadIdx.x == 0) atomic_add_u64(sig, add);
+}
+
+__global__ void k_wait(const uint64_t* word, uint64_t least, int bits, uint64_t timeout_ns, uint32_t* err) {
+  if (threadIdx.x == 0) wait_reached(word, least, bits, timeout_ns, err, VR_ASYNC_TIMEOUT);
+}
+
+__global__ void k_store0(uint64_t* word) {
+  if (threadIdx.x == 0) store8_agent(word, 0ull);
+}
+
+vrResult_t enqueue_copy(vrComm* c, char* dst, const char* src, size_t bytes, uint64_t* sig,
+                        uint64_t add, uint64_t* cnt, hipStream_t st) {
+  PutArgs a;
+  a.dst = dst;
+  a.src = src;
+  a.bytes = bytes;
+  a.dir = 0;
+  if (overlap(dst, bytes, src, bytes) && dst != src) a.dir = dst < src ? 1 : -1;
+  const uint64_t tiles = a.dir ? 1 : std::max<uint64_t>(1, (bytes + kPutTile - 1) / kPutTile);
+  if (tiles > 0xFFFFFFFFull) return VR_ERR_INVALID_ARGUMENT;
+  a.parts = static_cast<uint32_t>(tiles);
+  a.relay = c->relay + kRelaySingle;
+  a.sig = sig;
+  a.add = add;
+  a.cnt = cnt;
+  hipLaunchKernelGGL(k_put, dim3(a.parts), dim3(256), 0, st, a);
+  return hip_ok(hipGetLastError());
+}
+
+}  // namespace
+
+// ---- internal helpers used by the collectives ---------------------------------------
+namespace vr {
+vrResult_t ensure_scratch(vrComm* c, size_t bytes) {
+  if (bytes <= c->scratch_bytes) return VR_OK;
+  // the previous scratch may still be in use by enqueued work
+  if (c->scratch) {
+    if (hipDeviceSynchronize() != hipSuccess) return VR_ERR_HIP;
+    if (hipFree(c->scratch) != hipSuccess) return VR_ERR_HIP;
+    c->scratch = nullptr;
+    c->scratch_bytes = 0;
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) return VR_ERR_OUT_OF_RESOURCES;
+  if (hipMemset(p, 0, bytes) != hipSuccess) return VR_ERR_HIP;
+  c->scratch = static_cast<char*>(p);
+  c->scratch_bytes = bytes;
+  return VR_OK;
+}
+}  // namespace vr
+
+// ---- C ABI -------------------------------------------------------------------------------
+extern "C" {
+
+const char* vr_error_string(vrResult_t r) {
+  switch (r) {
+    case VR_OK: return "VR_OK";
+    case VR_ERR_INVALID_ARGUMENT: return "VR_ERR_INVALID_ARGUMENT";
+    case VR_ERR_INVALID_USAGE: return "VR_ERR_INVALID_USAGE";
+    case VR_ERR_OUT_OF_RESOURCES: return "VR_ERR_OUT_OF_RESOURCES";
+    case VR_ERR_HIP: return "VR_ERR_HIP";
+    case VR_ERR_TIMEOUT: return "VR_ERR_TIMEOUT";
+    case VR_ERR_UNSUPPORTED_DEVICE: return "VR_ERR_UNSUPPORTED_DEVICE";
+    case VR_ERR_INTERNAL: return "VR_ERR_INTERNAL";
+    case VR_ERR_DEVICE_CHECK: return "VR_ERR_DEVICE_CHECK";
+    default: return "VR_ERR_UNKNOWN";
+  }
+}
+
+int vr_version(void) { return 100; }
+
+size_t vr_comm_workspace_bytes(int nranks, const vrCommRequirements* req) {
+  if (!valid_req(nranks, req)) return 0;
+  return layout(nranks, *req).total;
+}
+
+vrResult_t vr_comm_create(int nranks, const vrCommRequirements* req, void* workspace,
+                          size_t workspace_bytes, vrComm_t* out) {
+  if (!out || !valid_req(nranks, req)) return VR_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  const Layout l = layout(nranks, *req);
+  if (workspace && (workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 255)))
+    return VR_ERR_INVALID_ARGUMENT;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return VR_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return VR_ERR_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return VR_ERR_UNSUPPORTED_DEVICE;
+  vrComm* c = new (std::nothrow) vrComm();
+  if (!c) return VR_ERR_OUT_OF_RESOURCES;
+  c->device = dev;
+  c->nranks = nranks;
+  c->req = *req;
+  c->owns_ws = workspace == nullptr;
+  c->ws_bytes = l.total;
+  if (workspace) {
+    c->ws = static_cast<char*>(workspace);
+  } else {
+    void* p = nullptr;
+    if (hipMalloc(&p, l.total) != hipSuccess) {
+      delete c;
+      return VR_ERR_OUT_OF_RESOURCES;
+    }
+    c->ws = static_cast<char*>(p);
+  }
+  if (hipMemset(c->ws, 0, l.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (c->owns_ws) (void)hipFree(c->ws);
+    delete c;
+    return VR_ERR_HIP;
+  }
+  c->sig = reinterpret_cast<uint64_t*>(c->ws + l.sig);
+  c->cnt = reinterpret_cast<uint64_t*>(c->ws + l.cnt);
+  c->err = reinterpret_cast<uint32_t*>(c->ws + l.err);
+  c->relay = reinterpret_cast<uint32_t*>(c->ws + l.relay);
+  c->scratch = nullptr;
+  c->scratch_bytes = 0;
+  const size_t ns = (size_t)nranks * req->signal_count;
+  c->expect.assign(ns, 0);
+  c->expect_known.assign(ns, 1);
+  c->sig_mode.assign(ns, 0);
+  {
+    std::lock_guard<std::mutex> g(g_mu);
+    g_comms.insert(c);
+  }
+  *out = c;
+  return VR_OK;
+}
+
+vrResult_t vr_comm_destroy(vrComm_t c) {
+  if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
+  if (!c->windows.empty()) return VR_ERR_INVALID_USAGE;
+  (void)hipDeviceSynchronize();
+  if (c->owns_ws) (void)hipFree(c->ws);
+  if (c->scratch) (void)hipFree(c->scratch);
+  {
+    std::lock_guard<std::mutex> g(g_mu);
+    g_comms.erase(c);
+  }
+  delete c;
+  return VR_OK;
+}
+
+vrResult_t vr_comm_get_async_error(vrComm_t c, vrResult_t* out, uint32_t* bits) {
+  if (!live(c) || !out) return VR_ERR_INVALID_ARGUMENT;
+  uint32_t b = 0;
+  if (hipMemcpy(&b, c->err, sizeof(b), hipMemcpyDeviceToHost) != hipSuccess) return VR_ERR_HIP;
+  if (b && hipMemset(c->err, 0, sizeof(uint32_t)) != hipSuccess) return VR_ERR_HIP;
+  if (bits) *bits = b;
+  if (b & VR_ASYNC_TIMEOUT) *out = VR_ERR_TIMEOUT;
+  else if (b & VR_ASYNC_CAPACITY) *out = VR_ERR_OUT_OF_RESOURCES;
+  else if (b) *out = VR_ERR_DEVICE_CHECK;
+  else *out = VR_OK;
+  return VR_OK;
+}
+
+vrResult_t vr_comm_query(vrComm_t c, int* nranks, vrCommRequirements* req) {
+  if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
+  if (nranks) *nranks = c->nranks;
+  if (req) *req = c->req;
+  return VR_OK;
+}
+
+vrResult_t vr_window_register(vrComm_t c, void* const* bases, size_t bytes, uint32_t flags,
+                              vrWindow_t* out) {
+  if (!live(c) || !bases || !out || bytes == 0) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~(VR_WIN_COLL_SYMMETRIC | VR_WIN_STRICT_ORDERING)) return VR_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  const int R = c->nranks;
+  for (int r = 0; r < R; ++r) {
+    char* b = static_cast<char*>(bases[r]);
+    if (!b || (reinterpret_cast<uintptr_t>(b) % VR_WIN_REQUIRED_ALIGNMENT)) return VR_ERR_INVALID_ARGUMENT;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, b) != hipSuccess) return VR_ERR_INVALID_ARGUMENT;
+    if (attr.type != hipMemoryTypeDevice || attr.device != c->device) return VR_ERR_INVALID_ARGUMENT;
+    hipDeviceptr_t pbase = nullptr;
+    size_t psize = 0;
+    if (hipMemGetAddressRange(&pbase, &psize, b) != hipSuccess) return VR_ERR_INVALID_ARGUMENT;
+    if (b + bytes > static_cast<char*>(pbase) + psize) return VR_ERR_INVALID_ARGUMENT;
+    for (int q = 0; q < r; ++q)
+      if (overlap(b, bytes, static_cast<char*>(bases[q]), bytes)) return VR_ERR_INVALID_ARGUMENT;
+  }
+  vrWindow* w = new (std::nothrow) vrWindow();
+  if (!w) return VR_ERR_OUT_OF_RESOURCES;
+  w->comm = c;
+  w->bytes = bytes;
+  w->flags = flags;
+  w->nranks = R;
+  for (int r = 0; r < VR_MAX_RANKS; ++r) w->base[r] = r < R ? static_cast<char*>(bases[r]) : nullptr;
+  c->windows.insert(w);
+  *out = w;
+  return VR_OK;
+}
+
+vrResult_t vr_window_deregister(vrComm_t c, vrWindow_t w) {
+  if (!live(c) || !has_win(c, w)) return VR_ERR_INVALID_ARGUMENT;
+  (void)hipDeviceSynchronize();  // no enqueued work may still use the window
+  c->windows.erase(w);
+  delete w;
+  return VR_OK;
+}
+
+vrResult_t vr_put(vrComm_t c, int ctx, int rank, int peer, vrWindow_t dst, size_t dst_off,
+                  vrWindow_t src, size_t src_off, size_t bytes, vrRemoteAction remote,
+                  vrLocalAction local, void* stream) {
+  if (!live(c) || !rank_ok(c, rank) || !rank_ok(c, peer)) return VR_ERR_INVALID_ARGUMENT;
+  if (ctx < 0 || (uint32_t)ctx >= c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
+  if (!has_win(c, dst) || !has_win(c, src)) return VR_ERR_INVALID_ARGUMENT;
+  if (!span_ok(dst, dst_off, bytes) || !span_ok(src, src_off, bytes)) return VR_ERR_INVALID_ARGUMENT;
+  vrResult_t r = check_remote(c, peer, remote);
+  if (r != VR_OK) return r;
+  if ((r = check_local(c, local)) != VR_OK) return r;
+  uint64_t* sig = nullptr;
+  uint64_t add = 0;
+  if (remote.kind != VR_ACTION_NONE) {
+    sig = c->sig + sidx(c, peer, remote.id);
+    add = remote.kind == VR_SIGNAL_INC ? 1 : remote.value;
+  }
+  uint64_t* cnt = local.kind == VR_COUNTER_INC ? c->cnt + (size_t)rank * c->req.counter_count + local.id : nullptr;
+  r = enqueue_copy(c, dst->base[peer] + dst_off, src->base[rank] + src_off, bytes, sig, add, cnt, S(stream));
+  if (r == VR_OK && sig) note_signal(c, peer, remote.id, remote.kind, add, true);
+  return r;
+}
+
+vrResult_t vr_get(vrComm_t c, int ctx, int rank, int peer, vrWindow_t remote, size_t remote_off,
+                  vrWindow_t localw, size_t local_off, size_t bytes, vrLocalAction local, void* stream) {
+  if (!live(c) || !rank_ok(c, rank) || !rank_ok(c, peer)) return VR_ERR_INVALID_ARGUMENT;
+  if (ctx < 0 || (uint32_t)ctx >= c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
+  if (!has_win(c, remote) || !has_win(c, localw)) return VR_ERR_INVALID_ARGUMENT;
+  if (!span_ok(remote, remote_off, bytes) || !span_ok(localw, local_off, bytes)) return VR_ERR_INVALID_ARGUMENT;
+  vrResult_t r = check_local(c, local);
+  if (r != VR_OK) return r;
+  uint64_t* cnt = local.kind == VR_COUNTER_INC ? c->cnt + (size_t)rank * c->req.counter_count + local.id : nullptr;
+  return enqueue_copy(c, localw->base[rank] + local_off, remote->base[peer] + remote_off, bytes, nullptr, 0,
+                      cnt, S(stream));
+}
+
+vrResult_t vr_signal(vrComm_t c, int ctx, int rank, int peer, vrRemoteAction remote, void* stream) {
+  if (!live(c) || !rank_ok(c, rank) || !rank_ok(c, peer)) return VR_ERR_INVALID_ARGUMENT;
+  if (ctx < 0 || (uint32_t)ctx >= c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
+  if (remote.kind == VR_ACTION_NONE) return VR_ERR_INVALID_ARGUMENT;
+  vrResult_t r = check_remote(c, peer, remote);
+  if (r != VR_OK) return r;
+  const uint64_t add = remote.kind == VR_SIGNAL_INC ? 1 : remote.value;
+  hipLaunchKernelGGL(k_signal, dim3(1), dim3(64), 0, S(stream), c->sig + sidx(c, peer, remote.id), add);
+  r = hip_ok(hipGetLastError());
+  if (r == VR_OK) note_signal(c, peer, remote.id, remote.kind, add, true);
+  return r;
+}
+
+static vrResult_t wait_word(vrComm* c, uint64_t* word, uint64_t least, int bits, uint64_t timeout_ns,
+                            void* stream) {
+  if (timeout_ns == 0) timeout_ns = kDefaultTimeoutNs;
+  hipLaunchKernelGGL(k_wait, dim3(1), dim3(64), 0, S(stream), word, least, bits, timeout_ns, c->err);
+  return hip_ok(hipGetLastError());
+}
+
+vrResult_t vr_signal_wait(vrComm_t c, int rank, uint32_t id, uint64_t least, int bits, uint64_t timeout_ns,
+                          void* stream) {
+  if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count) return VR_ERR_INVALID_ARGUMENT;
+  if (bits < 1 || bits > VR_SIGNAL_BITS) return VR_ERR_INVALID_ARGUMENT;
+  return wait_word(c, c->sig + sidx(c, rank, id), least, bits, timeout_ns, stream);
+}
+
+vrResult_t vr_counter_wait(vrComm_t c, int rank, uint32_t id, uint64_t least, int bits, uint64_t timeout_ns,
+                           void* stream) {
+  if (!live(c) || !rank_ok(c, rank) || id >= c->req.counter_count) return VR_ERR_INVALID_ARGUMENT;
+  if (bits < 1 || bits > VR_COUNTER_BITS) return VR_ERR_INVALID_ARGUMENT;
+  return wait_word(c, c->cnt + (size_t)rank * c->req.counter_count + id, least, bits, timeout_ns, stream);
+}
+
+static vrResult_t read_word(const uint64_t* word, int bits, uint64_t* out) {
+  uint64_t v = 0;
+  if (hipMemcpy(&v, word, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return VR_ERR_HIP;
+  *out = bits >= 64 ? v : (v & ((1ull << bits) - 1));
+  return VR_OK;
+}
+
+vrResult_t vr_signal_read(vrComm_t c, int rank, uint32_t id, int bits, uint64_t* out) {
+  if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count || !out) return VR_ERR_INVALID_ARGUMENT;
+  if (bits < 1 || bits > VR_SIGNAL_BITS) return VR_ERR_INVALID_ARGUMENT;
+  return read_word(c->sig + sidx(c, rank, id), bits, out);
+}
+
+vrResult_t vr_counter_read(vrComm_t c, int rank, uint32_t id, int bits, uint64_t* out) {
+  if (!live(c) || !rank_ok(c, rank) || id >= c->req.counter_count || !out) return VR_ERR_INVALID_ARGUMENT;
+  if (bits < 1 || bits > VR_COUNTER_BITS) return VR_ERR_INVALID_ARGUMENT;
+  return read_word(c->cnt + (size_t)rank * c->req.counter_count + id, bits, out);
+}
+
+vrResult_t vr_signal_reset(vrComm_t c, int rank, uint32_t id, void* stream) {
+  if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count) return VR_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(k_store0, dim3(1), dim3(64), 0, S(stream), c->sig + sidx(c, rank, id));
+  vrResult_t r = hip_ok(hipGetLastError());
+  if (r == VR_OK) {
+    const size_t i = sidx(c, rank, id);
+    c->expect[i] = 0;
+    c->expect_known[i] = 1;
+    c->sig_mode[i] = 0;
+  }
+  return r;
+}
+
+vrResult_t vr_counter_reset(vrComm_t c, int rank, uint32_t id, void* stream) {
+  if (!live(c) || !rank_ok(c, rank) || id >= c->req.counter_count) return VR_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(k_store0, dim3(1), dim3(64), 0, S(stream),
+                     c->cnt + (size_t)rank * c->req.counter_count + id);
+  return hip_ok(hipGetLastError());
+}
+
+vrResult_t vr_signal_expected(vrComm_t c, int rank, uint32_t id, uint64_t* out) {
+  if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count || !out) return VR_ERR_INVALID_ARGUMENT;
+  const size_t i = sidx(c, rank, id);
+  if (!c->expect_known[i]) return VR_ERR_INVALID_USAGE;
+  *out = c->expect[i];
+  return VR_OK;
+}
+
+// ---- collectives: validation and bookkeeping; kernels live in their own files ---------------
+static bool any_overlap(const vrWindow* a, size_t aoff, size_t an, const vrWindow* b, size_t boff, size_t bn,
+                        int R) {
+  for (int i = 0; i < R; ++i)
+    for (int j = 0; j < R; ++j)
+      if (overlap(a->base[i] + aoff, an, b->base[j] + boff, bn)) return true;
+  return false;
+}
+
+// Targets for an Inc-type completion signal that rises by `amount` at every rank.
+static vrResult_t inc_targets(vrComm* c, uint32_t sig, uint64_t amount, bool wait, U64Tab* t) {
+  if (sig >= c->req.signal_count) return VR_ERR_INVALID_ARGUMENT;
+  for (int d = 0; d < c->nranks; ++d) {
+    if (check_signal_mode(c, d, sig, VR_SIGNAL_INC) != VR_OK) return VR_ERR_INVALID_USAGE;
+    if (wait && !c->expect_known[sidx(c, d, sig)]) return VR_ERR_INVALID_USAGE;
+  }
+  for (int d = 0; d < VR_MAX_RANKS; ++d)
+    t->v[d] = d < c->nranks ? c->expect[sidx(c, d, sig)] + amount : 0;
+  return VR_OK;
+}
+static void commit_inc(vrComm* c, uint32_t sig, uint64_t amount) {
+  for (int d = 0; d < c->nranks; ++d) note_signal(c, d, sig, VR_SIGNAL_INC, amount, true);
+}
+
+vrResult_t vr_allreduce(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
+                        size_t count, int dtype, int op, uint32_t sig, uint32_t flags, void* stream) {
+  if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if ((dtype != VR_DT_F32 && dtype != VR_DT_BF16) || op != VR_OP_SUM) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
+  const size_t es = dtype == VR_DT_F32 ? 4 : 2;
+  if (count > (size_t(1) << 40) || (send_off % es) || (recv_off % es)) return VR_ERR_INVALID_ARGUMENT;
+  const size_t n = count * es;
+  if (!span_ok(send, send_off, n) || !span_ok(recv, recv_off, n)) return VR_ERR_INVALID_ARGUMENT;
+  if (any_overlap(send, send_off, n, recv, recv_off, n, c->nranks)) return VR_ERR_INVALID_ARGUMENT;
+  const bool wait = !(flags & VR_COLL_NO_WAIT);
+  U64Tab t;
+  vrResult_t r = inc_targets(c, sig, c->nranks, wait, &t);
+  if (r != VR_OK) return r;
+  r = launch_allreduce(c, send, send_off, recv, recv_off, count, dtype, sig, t, wait, S(stream));
+  if (r == VR_OK) commit_inc(c, sig, c->nranks);
+  return r;
+}
+
+vrResult_t vr_alltoall(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
+                       size_t block, uint32_t sig, uint32_t flags, void* stream) {
+  if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
+  const int R = c->nranks;
+  if (block > (size_t(1) << 40)) return VR_ERR_INVALID_ARGUMENT;
+  const size_t n = block * R;
+  if (!span_ok(send, send_off, n) || !span_ok(recv, recv_off, n)) return VR_ERR_INVALID_ARGUMENT;
+  if (any_overlap(send, send_off, n, recv, recv_off, n, R)) return VR_ERR_INVALID_ARGUMENT;
+  const bool wait = !(flags & VR_COLL_NO_WAIT);
+  U64Tab t;
+  vrResult_t r = inc_targets(c, sig, R, wait, &t);
+  if (r != VR_OK) return r;
+  r = launch_alltoall(c, send, send_off, recv, recv_off, block, sig, t, wait, S(stream));
+  if (r == VR_OK) commit_inc(c, sig, R);
+  return r;
+}
+
+vrResult_t vr_allgather(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
+                        size_t bytes, uint32_t sig, uint32_t flags, void* stream) {
+  if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
+  const int R = c->nranks;
+  if (bytes > (size_t(1) << 40)) return VR_ERR_INVALID_ARGUMENT;
+  if (!span_ok(send, send_off, bytes) || !span_ok(recv, recv_off, bytes * R)) return VR_ERR_INVALID_ARGUMENT;
+  if (any_overlap(send, send_off, bytes, recv, recv_off, bytes * R, R)) return VR_ERR_INVALID_ARGUMENT;
+  const bool wait = !(flags & VR_COLL_NO_WAIT);
+  U64Tab t;
+  vrResult_t r = inc_targets(c, sig, R, wait, &t);
+  if (r != VR_OK) return r;
+  r = launch_allgather(c, send, send_off, recv, recv_off, bytes, sig, t, wait, S(stream));
+  if (r == VR_OK) commit_inc(c, sig, R);
+  return r;
+}
+
+vrResult_t vr_dispatch(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes, const int32_t* topk,
+                       int T, int K, int E, vrWindow_t recv, size_t recv_off, size_t cap, int32_t* counts_out,
+                       int32_t* src_out, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags, void* stream) {
+  if (!live(c) || !has_win(c, x) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
+  const int R = c->nranks;
+  if ((!topk && T > 0) || !counts_out || (!src_out && cap > 0)) return VR_ERR_INVALID_ARGUMENT;
+  if (T < 0 || T >= 65536 || K < 1 || K > 64 || E < R || E % R || E > 1024)
+    return VR_ERR_INVALID_ARGUMENT;
+  if (row_bytes == 0 || row_bytes > (size_t(1) << 30) || cap > (size_t(1) << 31)) return VR_ERR_INVALID_ARGUMENT;
+  if (!span_ok(x, x_off, row_bytes * T) || !span_ok(recv, recv_off, row_bytes * cap)) return VR_ERR_INVALID_ARGUMENT;
+  if (any_overlap(x, x_off, row_bytes * T, recv, recv_off, row_bytes * cap, R)) return VR_ERR_INVALID_ARGUMENT;
+  if (sig_counts >= c->req.signal_count || sig_rows >= c->req.signal_count || sig_counts == sig_rows)
+    return VR_ERR_INVALID_ARGUMENT;
+  const bool wait = !(flags & VR_COLL_NO_WAIT);
+  U64Tab tc;
+  vrResult_t r = inc_targets(c, sig_counts, R, true, &tc);
+  if (r != VR_OK) return r;
+  for (int d = 0; d < R; ++d)
+    if (check_signal_mode(c, d, sig_rows, VR_SIGNAL_ADD) != VR_OK) return VR_ERR_INVALID_USAGE;
+  r = ensure_scratch(c, dispatch_scratch_bytes(R, T, E));
+  if (r != VR_OK) return r;
+  r = launch_dispatch(c, x, x_off, row_bytes, topk, T, K, E, recv, recv_off, cap, counts_out, src_out, sig_counts,
+                      sig_rows, tc, wait, S(stream));
+  if (r == VR_OK) {
+    commit_inc(c, sig_counts, R);
+    for (int d = 0; d < R; ++d) note_signal(c, d, sig_rows, VR_SIGNAL_ADD, 0, false);
+  }
+  return r;
+}
+
+vrResult_t vr_ring_exchange(vrComm_t c, vrWindow_t send, vrWindow_t recv, size_t put_bytes, size_t puts_per_rank,
+                            int contexts, uint32_t sig_base, uint32_t cnt_base, uint64_t* litmus, uint32_t flags,
+                            void* stream) {
+  if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
+  const int R = c->nranks;
+  if (contexts < 1 || (uint32_t)contexts > c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
+  if (put_bytes == 0 || put_bytes % 16 || put_bytes > 65536) return VR_ERR_INVALID_ARGUMENT;
+  if (puts_per_rank == 0 || puts_per_rank % contexts || puts_per_rank > (size_t(1) << 32)) return VR_ERR_INVALID_ARGUMENT;
+  if ((uint64_t)sig_base + contexts > c->req.signal_count || (uint64_t)cnt_base + contexts > c->req.counter_count)
+    return VR_ERR_INVALID_ARGUMENT;
+  const size_t n = put_bytes * puts_per_rank;
+  if (!span_ok(send, 0, n) || !span_ok(recv, 0, n)) return VR_ERR_INVALID_ARGUMENT;
+  if (any_overlap(send, 0, n, recv, 0, n, R)) return VR_ERR_INVALID_ARGUMENT;
+  const uint64_t per_ctx = puts_per_rank / contexts;
+  std::vector<uint64_t> target((size_t)R * contexts);
+  for (int d = 0; d < R; ++d)
+    for (int k = 0; k < contexts; ++k) {
+      const size_t i = sidx(c, d, sig_base + k);
+      if (check_signal_mode(c, d, sig_base + k, VR_SIGNAL_INC) != VR_OK) return VR_ERR_INVALID_USAGE;
+      if (!c->expect_known[i]) return VR_ERR_INVALID_USAGE;
+      target[(size_t)d * contexts + k] = c->expect[i] + per_ctx;
+    }
+  const bool wait = !(flags & VR_COLL_NO_WAIT);
+  vrResult_t r = launch_ring(c, send, recv, put_bytes, puts_per_rank, contexts, sig_base, cnt_base,
+                             wait ? target : std::vector<uint64_t>(), litmus, S(stream));
+  if (r == VR_OK)
+    for (int d = 0; d < R; ++d)
+      for (int k = 0; k < contexts; ++k) note_signal(c, d, sig_base + k, VR_SIGNAL_INC, per_ctx, true);
+  return r;
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// Fine-grained ring exchange with strong signals, counters and a litmus check.
+//
+// GDA survey (10100.com/article/158785524), section 4: the GIN paper's ring
+// exchange is put (with SignalInc), waitSignal, resetSignal; signals and
+// counters are addressed by integer ids; a strong signal on a context makes
+// every earlier put of that context to the peer visible. GIN page
+// (lpnh.cn/news/2681042), counter methods: a counter counts puts whose source
+// has been consumed.
+//
+// Rank r sends puts_per_rank messages to rank (r+1) mod R, split into
+// `contexts` contiguous ranges. One wavefront owns each (rank, context) and
+// issues its messages in order, in rounds of up to 4 KiB: it loads the
+// round's messages, stores them with agent-coherent stores, waits for its
+// stores, then applies one SignalInc per message at the receiver and one
+// CounterInc per message at itself. Every signal is therefore applied after
+// the payloads of all earlier messages of its context are visible (strong).
+// One waiting wavefront per receiving (rank, context) polls the signal until
+// it has grown by the context's message count; with the litmus on, each time
+// it sees a new value v it acquires and checks that message v-1 and one
+// earlier message of the context are present, counting violations.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "vr_device.hpp"
+#include "vr_internal.hpp"
+
+namespace vr {
+namespace {
+
+constexpr uint32_t kRoundBytes = 4096;
+
+struct RingArgs {
+  WinTab send, recv;
+  uint64_t put_bytes, per_ctx;
+  uint64_t* sig;        // &sig[0][sig_base]
+  uint64_t* cnt;        // &cnt[0][cnt_base]
+  uint32_t sig_stride, cnt_stride;
+  uint64_t* bases;      // [R][C] signal values before this exchange
+  uint64_t* litmus;     // [2] checks, violations; or null
+  uint32_t* err;
+  uint64_t timeout_ns;
+  int R, C, waiters;
+};
+
+__global__ void k_ring_snapshot(const RingArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < a.R * a.C) {
+    const int d = i / a.C, k = i % a.C;
+    store8_agent(a.bases + i, load_relaxed_u64(a.sig + (size_t)d * a.sig_stride + k));
+  }
+}
+
+// Compare message m at receiver d with its source at sender; true if equal.
+__device__ bool message_present(const RingArgs& a, int d, int sender, uint64_t m) {
+  const v4u* got = reinterpret_cast<const v4u*>(a.recv.p[d] + m * a.put_bytes);
+  const v4u* want = reinterpret_cast<const v4u*>(a.send.p[sender] + m * a.put_bytes);
+  bool same = true;
+  for (uint64_t i = threadIdx.x; i < a.put_bytes / 16; i += 64) {
+    const v4u x = got[i], y = want[i];
+    same &= (x[0] == y[0]) & (x[1] == y[1]) & (x[2] == y[2]) & (x[3] == y[3]);
+  }
+  return ballot(!same) == 0;
+}
+
+__global__ __launch_bounds__(64) void k_ring(const RingArgs a) {
+  const int R = a.R, C = a.C;
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (w < R * C) {  // producer: rank r, context k
+    const int r = w / C, k = w % C, peer = (r + 1) % R;
+    const uint64_t P = a.put_bytes;
+    // one lane applies each message's signal, so a round holds at most 64 messages
+    const uint64_t per_round = std::min<uint64_t>(64, std::max<uint64_t>(1, kRoundBytes / P));
+    const uint64_t m0 = (uint64_t)k * a.per_ctx, m1 = m0 + a.per_ctx;
+    uint64_t* sig = a.sig + (size_t)peer * a.sig_stride + k;
+    uint64_t* cnt = a.cnt + (size_t)r * a.cnt_stride + k;
+    for (uint64_t m = m0; m < m1; m += per_round) {
+      const uint64_t nm = std::min<uint64_t>(per_round, m1 - m);
+      const uint32_t bytes = static_cast<uint32_t>(nm * P);
+      copy16<4>(a.recv.p[peer] + m * P, a.send.p[r] + m * P, bytes, lane, 64);
+      wait_vmem();  // this round's payloads are visible at agent scope
+      if ((uint64_t)lane < nm) {
+        atomic_add_u64(sig, 1ull);  // strong SignalInc of message m + lane
+        atomic_add_u64(cnt, 1ull);  // CounterInc: its source has been read
+      }
+    }
+    return;
+  }
+  // receiver d, context k: wait (and check prefixes when the litmus is on)
+  const int i = w - R * C;
+  if (i >= a.waiters) return;
+  const int d = i / C, k = i % C, sender = (d + R - 1) % R;
+  const uint64_t base = a.bases[(size_t)d * C + k];
+  const uint64_t* sig = a.sig + (size_t)d * a.sig_stride + k;
+  const uint64_t m0 = (uint64_t)k * a.per_ctx;
+  const uint64_t t0 = now_ns();
+  uint64_t seen = 0;
+  for (;;) {
+    const uint64_t v = load_relaxed_u64(sig);
+    const uint64_t n = static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v - base))) |
+                       (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>((v - base) >> 32))) << 32);
+    // n: messages of this context the signal vouches for
+    if (a.litmus && n > seen && n <= a.per_ctx) {
+      acquire_agent();
+      const uint64_t earlier = ((n * 2654435761ull) >> 7) % n;
+      const bool ok = message_present(a, d, sender, m0 + n - 1) && message_present(a, d, sender, m0 + earlier);
+      if (lane == 0) {
+        atomic_add_u64(a.litmus, 2ull);
+        if (!ok) {
+          atomic_add_u64(a.litmus + 1, 1ull);
+          atomic_or_u32(a.err, VR_ASYNC_LITMUS);
+        }
+      }
+      seen = n;
+    }
+    if (rolling_le(base + a.per_ctx, base + n, 64)) break;
+    if (now_ns() - t0 > a.timeout_ns) {
+      if (lane == 0) atomic_or_u32(a.err, VR_ASYNC_TIMEOUT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  acquire_agent();
+}
+
+}  // namespace
+
+vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, size_t put_bytes, size_t puts_per_rank,
+                       int contexts, uint32_t sig_base, uint32_t cnt_base, const std::vector<uint64_t>& target,
+                       uint64_t* litmus, hipStream_t st) {
+  const int R = c->nranks;
+  vrResult_t r = ensure_scratch(c, sizeof(uint64_t) * R * contexts);
+  if (r != VR_OK) return r;
+  RingArgs a;
+  for (int q = 0; q < VR_MAX_RANKS; ++q) {
+    a.send.p[q] = send->base[q];
+    a.recv.p[q] = recv->base[q];
+  }
+  a.put_bytes = put_bytes;
+  a.per_ctx = puts_per_rank / contexts;
+  a.sig = c->sig + sig_base;
+  a.cnt = c->cnt + cnt_base;
+  a.sig_stride = c->req.signal_count;
+  a.cnt_stride = c->req.counter_count;
+  a.bases = reinterpret_cast<uint64_t*>(c->scratch);
+  a.litmus = litmus;
+  a.err = c->err;
+  a.timeout_ns = kDefaultTimeoutNs;
+  a.R = R;
+  a.C = contexts;
+  a.waiters = target.empty() ? 0 : R * contexts;
+  if (a.waiters) {
+    const int n = R * contexts;
+    hipLaunchKernelGGL(k_ring_snapshot, dim3((n + 255) / 256), dim3(256), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return VR_ERR_HIP;
+  }
+  hipLaunchKernelGGL(k_ring, dim3(R * contexts + a.waiters), dim3(64), 0, st, a);
+  return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;
+}
+
+}  // namespace vr

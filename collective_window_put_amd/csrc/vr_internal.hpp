@@ -1,0 +1,88 @@
+// Host-side state of a communicator and the launch entry points each kernel
+// file provides. Shared by the .hip files of libvrcomm; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <set>
+#include <vector>
+
+#include "../../include/vrcomm.h"
+
+namespace vr {
+
+// Relay counters: one region per kind of operation, so that a collective and
+// a single put enqueued back to back never share a counter.
+constexpr uint32_t kRelaySingle = 0;       // vr_put / vr_get: 1 counter
+constexpr uint32_t kRelayColl = 64;        // collectives: up to R*R counters
+constexpr uint32_t kRelayDispatch = 64 + VR_MAX_RANKS * VR_MAX_RANKS;  // 2 per source rank
+constexpr uint32_t kRelaySlots = kRelayDispatch + 2 * VR_MAX_RANKS;
+
+constexpr uint64_t kDefaultTimeoutNs = 5ull * 1000 * 1000 * 1000;
+
+struct WinTab {
+  char* p[VR_MAX_RANKS];
+};
+struct U64Tab {
+  uint64_t v[VR_MAX_RANKS];
+};
+
+}  // namespace vr
+
+struct vrWindow {
+  vrComm* comm;
+  size_t bytes;
+  uint32_t flags;
+  int nranks;
+  char* base[VR_MAX_RANKS];
+};
+
+struct vrComm {
+  int device;
+  int nranks;
+  vrCommRequirements req;
+  // device words (one allocation, or the caller's workspace)
+  char* ws;
+  size_t ws_bytes;
+  bool owns_ws;
+  uint64_t* sig;    // [R][signal_count]
+  uint64_t* cnt;    // [R][counter_count]
+  uint32_t* err;    // error bits
+  uint32_t* relay;  // [kRelaySlots]
+  // growable scratch for dispatch (histograms, count exchange)
+  char* scratch;
+  size_t scratch_bytes;
+  // host view of the signals: the value each will hold once all enqueued work has run
+  std::vector<uint64_t> expect;      // [R][S]
+  std::vector<uint8_t> expect_known; // 0 when a device-computed amount was added
+  std::vector<uint8_t> sig_mode;     // 0 none, 1 SignalInc, 2 SignalAdd (since the last reset)
+  std::set<vrWindow*> windows;
+};
+
+namespace vr {
+
+// launch entry points (each returns VR_OK or VR_ERR_HIP)
+vrResult_t launch_alltoall(vrComm* c, const vrWindow* send, size_t send_off, const vrWindow* recv,
+                           size_t recv_off, size_t block, uint32_t sig, const U64Tab& target,
+                           bool wait, hipStream_t st);
+vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, const vrWindow* recv,
+                            size_t recv_off, size_t count, int dtype, uint32_t sig,
+                            const U64Tab& target, bool wait, hipStream_t st);
+vrResult_t launch_allgather(vrComm* c, const vrWindow* send, size_t send_off, const vrWindow* recv,
+                            size_t recv_off, size_t bytes, uint32_t sig, const U64Tab& target,
+                            bool wait, hipStream_t st);
+vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t row_bytes,
+                           const int32_t* topk, int T, int K, int E, const vrWindow* recv,
+                           size_t recv_off, size_t cap, int32_t* counts_out, int32_t* src_out,
+                           uint32_t sig_counts, uint32_t sig_rows, const U64Tab& target_counts,
+                           bool wait, hipStream_t st);
+size_t dispatch_scratch_bytes(int R, int T, int E);
+vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, size_t put_bytes,
+                       size_t puts_per_rank, int contexts, uint32_t sig_base, uint32_t cnt_base,
+                       const std::vector<uint64_t>& target, uint64_t* litmus, hipStream_t st);
+
+// helpers in comm.hip
+vrResult_t ensure_scratch(vrComm* c, size_t bytes);
+
+}  // namespace vr

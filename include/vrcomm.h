@@ -1,0 +1,302 @@
+/*
+ * vrcomm.h -- one-sided window put/get with integer signals and counters,
+ * and the collectives built on them, for R virtual ranks that share one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page and section (the pages are not reproduced here):
+ *   GIN page         NCCL GIN device API walkthrough, lpnh.cn/news/2681042
+ *   Symmetric page   NCCL symmetric-memory examples, zwxr.cn/news/250719
+ *   GDA survey       "GPUDirect Async" survey, 10100.com/article/158785524
+ *
+ * Model. A communicator (vrComm_t) holds R virtual ranks on the current HIP
+ * device. Each rank owns a slice of every registered window: R device
+ * pointers, one per rank, all of the same size ("symmetric": one offset names
+ * the same slot on every rank). Every rank can address every other rank's
+ * slices directly (on one GPU all memory is load/store accessible), so a put
+ * or get is a copy performed by GPU workgroups, and a signal is an atomic add
+ * at agent scope on a 64-bit word owned by the receiving rank.
+ *
+ * Conventions (every function):
+ *   - Returns a vrResult_t; nothing throws across this interface.
+ *   - Argument errors are reported synchronously, before anything is
+ *     enqueued, and leave the communicator unchanged.
+ *   - Errors found by device code (a wait that timed out, a dispatch that
+ *     overflowed its receive capacity, an expert id out of range, a litmus
+ *     violation) set bits in the communicator's device error word; read them
+ *     with vr_comm_get_async_error after synchronizing the stream.
+ *   - Memory: windows, inputs and outputs are owned by the caller; the
+ *     library owns only its signal/counter words and small scratch buffers.
+ *   - Device pointers are plain device addresses on the communicator's device.
+ *     A stream is a hipStream_t passed as void* (NULL = the null stream).
+ *   - A communicator is not thread-safe, and the operations issued on one
+ *     communicator must execute in issue order: use one stream per
+ *     communicator, or order the streams yourself. Operations that share a
+ *     signal id must be stream-ordered.
+ */
+#ifndef VRCOMM_H
+#define VRCOMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- result codes ---------------------------------------------------------- */
+typedef int vrResult_t;
+#define VR_OK                      0
+#define VR_ERR_INVALID_ARGUMENT    1  /* a value is out of range, misaligned or NULL */
+#define VR_ERR_INVALID_USAGE       2  /* legal values, but the call breaks a usage rule */
+#define VR_ERR_OUT_OF_RESOURCES    3  /* allocation failed, or a dispatch overflowed (async) */
+#define VR_ERR_HIP                 4  /* a HIP runtime call failed */
+#define VR_ERR_TIMEOUT             5  /* a device-side wait gave up (async) */
+#define VR_ERR_UNSUPPORTED_DEVICE  6  /* the current device is not gfx950 */
+#define VR_ERR_INTERNAL            7
+#define VR_ERR_DEVICE_CHECK        8  /* a device-side check failed (async): bad expert id, litmus */
+
+/* Human-readable name of a result code. Never NULL. */
+const char* vr_error_string(vrResult_t r);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int vr_version(void);
+
+/* ---- limits and flags --------------------------------------------------------- */
+#define VR_MAX_RANKS               64
+#define VR_WIN_DEFAULT             0x00u
+#define VR_WIN_COLL_SYMMETRIC      0x01u  /* Symmetric page, window registration flags */
+#define VR_WIN_STRICT_ORDERING     0x02u
+#define VR_WIN_REQUIRED_ALIGNMENT  4096u  /* Symmetric page: required window alignment */
+#define VR_SIGNAL_BITS             64
+#define VR_COUNTER_BITS            56     /* GIN page, counter methods: at most 56 bits */
+
+/* ---- handles and requirement records ------------------------------------------- */
+typedef struct vrComm* vrComm_t;
+typedef struct vrWindow* vrWindow_t;
+
+/* Resources a communicator provides to each rank (GIN page, host-side setup of
+ * the AlltoAll example: signal and barrier counts requested up front).
+ * signal_count   signals per rank (ids 0..signal_count-1), 1..65536
+ * counter_count  counters per rank, 0..65536
+ * context_count  ordering contexts per rank, 1..1024 (GIN page, ncclGin:
+ *                several contexts spread traffic; a context orders the puts
+ *                of the one issuer that owns it). */
+typedef struct {
+  uint32_t signal_count;
+  uint32_t counter_count;
+  uint32_t context_count;
+} vrCommRequirements;
+
+/* Remote action, applied at the peer after the put's payload has landed
+ * (GIN page, one-sided transfers and signals and counters).
+ *   kind  VR_ACTION_NONE, VR_SIGNAL_INC (add 1) or VR_SIGNAL_ADD (add value)
+ *   id    signal id at the peer
+ *   strong nonzero: the signal also covers every earlier put of the same
+ *         context to the same peer (GIN page, strong and weak signals). This
+ *         library always publishes a signal after all earlier stores of the
+ *         issuing context, so weak signals get the strong guarantee too.
+ * A signal id must not receive both SignalInc and SignalAdd without a reset
+ * in between (GIN page, strong and weak signals); the library rejects such a
+ * call with VR_ERR_INVALID_USAGE. */
+#define VR_ACTION_NONE   0u
+#define VR_SIGNAL_INC    1u
+#define VR_SIGNAL_ADD    2u
+#define VR_COUNTER_INC   3u
+typedef struct {
+  uint32_t kind;
+  uint32_t id;
+  uint64_t value;
+  uint32_t strong;
+  uint32_t reserved;  /* must be 0 */
+} vrRemoteAction;
+
+/* Local action, applied at the issuing rank once the source bytes have been
+ * read (GIN page, counter methods): kind VR_ACTION_NONE or VR_COUNTER_INC. */
+typedef struct {
+  uint32_t kind;
+  uint32_t id;
+} vrLocalAction;
+
+/* ---- communicator ---------------------------------------------------------------- */
+/* Device bytes a communicator needs for its signal and counter words, error
+ * word and relay counters; 0 on invalid arguments. */
+size_t vr_comm_workspace_bytes(int nranks, const vrCommRequirements* req);
+
+/* Create a communicator of nranks (1..VR_MAX_RANKS) virtual ranks on the
+ * current HIP device. workspace: caller-owned device memory of at least
+ * vr_comm_workspace_bytes() bytes, 256-byte aligned, or NULL to let the
+ * library allocate it. The words are zeroed (synchronously) before return.
+ * Errors: VR_ERR_INVALID_ARGUMENT, VR_ERR_UNSUPPORTED_DEVICE (not gfx950; the
+ * analog of a device communicator that cannot be created, GIN page, host-side
+ * setup), VR_ERR_HIP, VR_ERR_OUT_OF_RESOURCES. */
+vrResult_t vr_comm_create(int nranks, const vrCommRequirements* req, void* workspace,
+                          size_t workspace_bytes, vrComm_t* out);
+
+/* Destroy a communicator. VR_ERR_INVALID_USAGE while windows are still
+ * registered (Symmetric page, example 1 step 7: deregister windows, then free
+ * memory, then destroy the communicator). Synchronizes the device. */
+vrResult_t vr_comm_destroy(vrComm_t comm);
+
+/* Read and clear the device error word. Synchronize the streams that ran the
+ * communicator's work first. *out is VR_OK, or the code of the first set bit
+ * in the order TIMEOUT, OUT_OF_RESOURCES, DEVICE_CHECK. *bits (may be NULL)
+ * receives the raw bit set. */
+#define VR_ASYNC_TIMEOUT       0x1u
+#define VR_ASYNC_CAPACITY      0x2u
+#define VR_ASYNC_BAD_EXPERT    0x4u
+#define VR_ASYNC_LITMUS        0x8u
+vrResult_t vr_comm_get_async_error(vrComm_t comm, vrResult_t* out, uint32_t* bits);
+
+/* Rank count and requirements of a communicator. */
+vrResult_t vr_comm_query(vrComm_t comm, int* nranks, vrCommRequirements* req);
+
+/* ---- windows ------------------------------------------------------------------------ */
+/* Register a symmetric window: bases[r] is rank r's slice (device memory on
+ * the communicator's device, VR_WIN_REQUIRED_ALIGNMENT-aligned, bytes long);
+ * the R slices must not overlap. flags: VR_WIN_* bits. The memory stays owned
+ * by the caller and must outlive the registration (Symmetric page, window
+ * registration and cleanup order). */
+vrResult_t vr_window_register(vrComm_t comm, void* const* bases, size_t bytes, uint32_t flags,
+                              vrWindow_t* out);
+
+/* Deregister a window; must precede freeing its memory. Synchronizes the device. */
+vrResult_t vr_window_deregister(vrComm_t comm, vrWindow_t win);
+
+/* ---- one-sided primitives (each enqueues one kernel on the stream) --------------------- */
+/* put: copy bytes from src (rank's slice, at src_off) to dst (peer's slice, at
+ * dst_off), then apply the remote action at the peer and the local action at
+ * the rank (GIN page, one-sided transfers: put). peer may equal rank
+ * (loopback); when the source and destination bytes overlap in memory the
+ * copy behaves like memmove (one workgroup copies in the safe direction).
+ * bytes may be 0 (actions only). ctx < context_count. Offsets and sizes are
+ * checked against the window size (VR_ERR_INVALID_ARGUMENT). */
+vrResult_t vr_put(vrComm_t comm, int ctx, int rank, int peer, vrWindow_t dst, size_t dst_off,
+                  vrWindow_t src, size_t src_off, size_t bytes, vrRemoteAction remote,
+                  vrLocalAction local, void* stream);
+
+/* get: copy bytes from remote (peer's slice, at remote_off) into local (rank's
+ * slice, at local_off); the local action runs once the bytes have landed
+ * (GIN page, one-sided transfers: get; completion management: flush). */
+vrResult_t vr_get(vrComm_t comm, int ctx, int rank, int peer, vrWindow_t remote, size_t remote_off,
+                  vrWindow_t local, size_t local_off, size_t bytes, vrLocalAction local_action,
+                  void* stream);
+
+/* signal: a remote action with no payload (GIN page, signal methods). */
+vrResult_t vr_signal(vrComm_t comm, int ctx, int rank, int peer, vrRemoteAction remote, void* stream);
+
+/* Wait on the stream until the low `bits` bits of rank's signal id reach
+ * `least` in rolling (wrap-around) order: value - least, taken modulo
+ * 2^bits, is below 2^(bits-1) (GIN page, signals and counters: rolling
+ * comparison; signal methods: waitSignal). timeout_ns: give up after this
+ * long and set VR_ASYNC_TIMEOUT (0 = 5 s). bits in 1..64. */
+vrResult_t vr_signal_wait(vrComm_t comm, int rank, uint32_t id, uint64_t least, int bits,
+                          uint64_t timeout_ns, void* stream);
+
+/* Read the low `bits` bits of a signal now (synchronous device read; the
+ * caller synchronizes the stream that modified it). */
+vrResult_t vr_signal_read(vrComm_t comm, int rank, uint32_t id, int bits, uint64_t* out);
+
+/* Reset a signal to 0 on the stream. Must not race with updates of the same
+ * signal (GIN page, signal methods: resetSignal). Also clears its Inc/Add mode. */
+vrResult_t vr_signal_reset(vrComm_t comm, int rank, uint32_t id, void* stream);
+
+/* The value a signal will hold once every operation enqueued so far has run,
+ * as tracked by the host (the library's counterpart of the pages' per-signal
+ * shadow value, GIN page, signal methods). VR_ERR_INVALID_USAGE when an
+ * enqueued operation added a device-computed amount (vr_dispatch's row
+ * signal) and no reset followed. */
+vrResult_t vr_signal_expected(vrComm_t comm, int rank, uint32_t id, uint64_t* out);
+
+/* Counters: as the signal calls, with at most 56 bits (GIN page, counter methods). */
+vrResult_t vr_counter_wait(vrComm_t comm, int rank, uint32_t id, uint64_t least, int bits,
+                           uint64_t timeout_ns, void* stream);
+vrResult_t vr_counter_read(vrComm_t comm, int rank, uint32_t id, int bits, uint64_t* out);
+vrResult_t vr_counter_reset(vrComm_t comm, int rank, uint32_t id, void* stream);
+
+/* ---- collectives (all R ranks in one call, stream-ordered) ------------------------------ */
+#define VR_DT_F32   0
+#define VR_DT_BF16  1
+#define VR_OP_SUM   0
+/* flags */
+#define VR_COLL_NO_WAIT  0x1u  /* skip the in-kernel receiver waits (signals are still applied) */
+
+/* Sum-AllReduce over `count` elements at send_off of every rank's send slice;
+ * every rank's recv slice receives the sum at recv_off.
+ * Result, per element: ((x_0 + x_1) + x_2) + ... + x_{R-1}, each addition an
+ * IEEE binary32 addition rounded to nearest even (fixed rank order; the pages
+ * fix no order). VR_DT_BF16: bf16 inputs widened exactly, fp32 accumulation,
+ * bf16 output rounded to nearest even; any NaN becomes 0x7FC0.
+ * Method: reduce-scatter, each owner pulling its chunk from every rank (get),
+ * then all-gather, the owner putting the reduced chunk to every rank, with one
+ * SignalInc on `sig` per (owner, receiver): every rank's signal rises by R.
+ * Unless VR_COLL_NO_WAIT, each receiver waits in-kernel for its signal.
+ * Symmetric page, AllReduce example; GIN page, put/get and signals.
+ * Offsets must be multiples of the element size; send and recv ranges must
+ * not overlap (VR_ERR_INVALID_ARGUMENT). */
+vrResult_t vr_allreduce(vrComm_t comm, vrWindow_t send, size_t send_off, vrWindow_t recv,
+                        size_t recv_off, size_t count, int dtype, int op, uint32_t sig,
+                        uint32_t flags, void* stream);
+
+/* Equal-block AlltoAll: block d of rank s's send slice (at send_off +
+ * d*block_bytes) lands in rank d's recv slice at recv_off + s*block_bytes,
+ * as one put per (s, d) with a SignalInc on `sig` at d: every rank's signal
+ * rises by R, its own loopback block included (GIN page, pure-GIN AlltoAll
+ * kernel). */
+vrResult_t vr_alltoall(vrComm_t comm, vrWindow_t send, size_t send_off, vrWindow_t recv,
+                       size_t recv_off, size_t block_bytes, uint32_t sig, uint32_t flags,
+                       void* stream);
+
+/* AllGather: rank s's bytes_per_rank bytes at send_off land in every rank's
+ * recv slice at recv_off + s*bytes_per_rank, one put + SignalInc per (s, d)
+ * (Symmetric page, AllGather example: segment k holds rank k's data). */
+vrResult_t vr_allgather(vrComm_t comm, vrWindow_t send, size_t send_off, vrWindow_t recv,
+                        size_t recv_off, size_t bytes_per_rank, uint32_t sig, uint32_t flags,
+                        void* stream);
+
+/* MoE token dispatch (GDA survey, opening section: tokens of a few hundred
+ * bytes routed among dozens of experts).
+ *   x, x_off        rank s's T token rows of row_bytes bytes each (window)
+ *   topk_idx        device int32 [R][T][K]: expert ids in [0, num_experts),
+ *                   or -1 for "not routed"; K in 1..64; may be NULL when T == 0
+ *   num_experts     multiple of R, at most 1024; rank d owns experts
+ *                   [d*E/R, (d+1)*E/R)
+ *   recv, recv_off  rank d's receive rows (window), capacity recv_capacity_rows
+ *   recv_expert_counts  device int32 [R][E/R]: rows received per local expert
+ *   recv_src        device int32 [R][recv_capacity_rows]: (s << 16) | t per row
+ * Layout of rank d's rows: by expert, then source rank, then token (a stable
+ * sort of the routing entries on (expert, source, token)).
+ * Method: (1) each rank counts its tokens per expert and puts its count row
+ * to every rank with a SignalInc on sig_counts (each rises by R); (2) every
+ * rank computes its offsets from the full count matrix; (3) each rank puts
+ * every expert's rows, then one strong SignalAdd(rows sent to d) on
+ * sig_rows at each d (GDA survey, section 4: a batch of puts closed by one
+ * signal). Unless VR_COLL_NO_WAIT, each receiver waits in-kernel until
+ * sig_rows has grown by the rows aimed at it. Rows past the capacity are
+ * dropped and set VR_ASYNC_CAPACITY; out-of-range ids set VR_ASYNC_BAD_EXPERT.
+ * T < 65536; row_bytes > 0; sig_counts != sig_rows. */
+vrResult_t vr_dispatch(vrComm_t comm, vrWindow_t x, size_t x_off, size_t row_bytes,
+                       const int32_t* topk_idx, int T, int K, int num_experts, vrWindow_t recv,
+                       size_t recv_off, size_t recv_capacity_rows, int32_t* recv_expert_counts,
+                       int32_t* recv_src, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags,
+                       void* stream);
+
+/* Ring exchange (GDA survey, section 4, the ring-exchange example): rank r
+ * puts puts_per_rank messages of put_bytes each to rank (r+1) mod R, message
+ * k from send offset k*put_bytes to recv offset k*put_bytes. Messages are
+ * split into `contexts` contiguous ranges, each issued in order by one
+ * wavefront; every message carries a strong SignalInc on signal
+ * sig_base + ctx at the receiver and a CounterInc on counter cnt_base + ctx
+ * at the sender. Receivers wait in-kernel until each context signal has
+ * grown by puts_per_rank / contexts. litmus (device uint64[2] or NULL): when
+ * given, the waiting wavefronts repeatedly read a context signal v and check
+ * that messages v-1 and an earlier one are visible, counting checks in
+ * litmus[0] and violations in litmus[1] (and VR_ASYNC_LITMUS).
+ * puts_per_rank must be a multiple of contexts; put_bytes a multiple of 16. */
+vrResult_t vr_ring_exchange(vrComm_t comm, vrWindow_t send, vrWindow_t recv, size_t put_bytes,
+                            size_t puts_per_rank, int contexts, uint32_t sig_base,
+                            uint32_t cnt_base, uint64_t* litmus, uint32_t flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VRCOMM_H */

@@ -1,0 +1,93 @@
+"""The C-ABI library loads, exports every function include/vrcomm.h declares,
+and rejects bad arguments before touching a GPU (runs without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import collective_window_put_amd as vr
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "vrcomm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vr_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vr.LIB_PATH):
+        from collective_window_put_amd.build import build
+        build()
+    return vr.lib()
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_functions() == sorted(vr.SYMBOLS)
+
+
+def test_library_exports_every_declared_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", vr.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_library_is_built_for_gfx950_only(lib):
+    # the offload bundle embedded in our own library names its device targets
+    blob = open(vr.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-[-a-z]*(gfx[0-9a-z]+)", blob))
+    assert targets == {b"gfx950"}
+
+
+def test_error_strings_and_version(lib):
+    assert vr.vr_error_string(vr.VR_OK) == "VR_OK"
+    assert vr.vr_error_string(vr.VR_ERR_TIMEOUT) == "VR_ERR_TIMEOUT"
+    assert vr.vr_error_string(12345) == "VR_ERR_UNKNOWN"
+    assert vr.vr_version() >= 100
+
+
+def test_workspace_bytes_validation(lib):
+    assert vr.vr_comm_workspace_bytes(0) == 0
+    assert vr.vr_comm_workspace_bytes(65) == 0
+    assert vr.vr_comm_workspace_bytes(4, signal_count=0) == 0
+    assert vr.vr_comm_workspace_bytes(4, context_count=0) == 0
+    n = vr.vr_comm_workspace_bytes(8, signal_count=16, counter_count=16)
+    assert n >= 8 * 16 * 8 * 2 and n % 256 == 0
+
+
+def test_argument_errors_without_gpu(lib):
+    for bad in (0, -1, 65):
+        with pytest.raises(vr.VrError) as e:
+            vr.vr_comm_create(bad)
+        assert e.value.code == vr.VR_ERR_INVALID_ARGUMENT
+    with pytest.raises(vr.VrError) as e:
+        vr.vr_comm_create(4, signal_count=0)
+    assert e.value.code == vr.VR_ERR_INVALID_ARGUMENT
+    # handles that were never created are rejected, not dereferenced
+    for fn, args in ((vr.vr_comm_destroy, (0x1234,)), (vr.vr_comm_query, (0,)),
+                     (vr.vr_signal_read, (0x10, 0, 0)), (vr.vr_window_deregister, (0x10, 0x20))):
+        with pytest.raises(vr.VrError) as e:
+            fn(*args)
+        assert e.value.code == vr.VR_ERR_INVALID_ARGUMENT
+    rc = lib.vr_allreduce(None, None, 0, None, 0, 0, 0, 0, 0, 0, None)
+    assert rc == vr.VR_ERR_INVALID_ARGUMENT
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(vr.vrRemoteAction) == 24
+    assert ctypes.sizeof(vr.vrLocalAction) == 8
+    assert ctypes.sizeof(vr.vrCommRequirements) == 12
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(vr, "_lib", None)
+    monkeypatch.setattr(vr, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(vr.VrLibraryMissing):
+        vr.vr_version()

@@ -1,0 +1,81 @@
+"""AllGather on the GPU against the oracle."""
+import json
+
+import numpy as np
+import pytest
+
+import collective_window_put_amd as vr
+from oracle import definitions as D
+import workloads as W
+from conftest import golden
+from gpu_util import Job, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(sends, M, send_off=0, recv_off=0, sig=1):
+    R = len(sends)
+    with Job(R) as job:
+        sw, sv = job.window(send_off + M, fill=0)
+        rw, rv = job.window(recv_off + R * M, fill=0x5A)
+        for r in range(R):
+            sv[r][send_off:].copy_(job.torch.from_numpy(sends[r]))
+        vr.vr_allgather(job.comm, sw, send_off, rw, recv_off, M, sig=sig)
+        out = job.host(rv)
+        sigs = [job.sig(d, sig) for d in range(R)]
+        job.assert_no_async_error()
+    return out, sigs
+
+
+def test_allgather_page_segments():
+    g = json.load(open(golden("allgather_segments.json")))
+    R, n = g["ranks"], g["send_bytes"] // 4
+    say("allgather page segments R=4 4MB")
+    sends = [np.full(n, float(r), np.float32).view(np.uint8) for r in range(R)]
+    out, sigs = _run(sends, g["send_bytes"])
+    for d in range(R):
+        assert out[d].nbytes == g["recv_bytes"]
+        segs = out[d].view(np.float32).reshape(R, n)
+        for k, v in enumerate(g["segment_values"]):
+            assert np.all(segs[k] == np.float32(v))
+    assert sigs == [R] * R
+
+
+@pytest.mark.parametrize("R,M", [(1, 16), (2, 1), (3, 16385), (4, 16384 * 3), (8, 1000), (16, 32768 + 16), (5, 77)])
+def test_allgather_random_vs_oracle(R, M):
+    say(f"allgather R={R} M={M}")
+    sends = W.allgather_inputs(R, M, seed=R * 3 + M)
+    out, sigs = _run(sends, M)
+    exp = D.allgather(sends)
+    for d in range(R):
+        assert np.array_equal(out[d], exp[d]), d
+    assert sigs == [R] * R
+
+
+def test_allgather_offsets():
+    R, M = 4, 20000
+    say("allgather offsets")
+    sends = W.allgather_inputs(R, M, seed=2)
+    out, _ = _run(sends, M, send_off=7, recv_off=4096 + 3)
+    exp = D.allgather(sends)
+    for d in range(R):
+        assert np.array_equal(out[d][4099:], exp[d])
+        assert np.all(out[d][:4099] == 0x5A)
+
+
+def test_allgather_config_c5a_full_size():
+    c = W.CONFIGS["c5a"]
+    R, M = c["ranks"], c["bytes_per_rank"]
+    say(f"allgather c5a full R={R} M={M}")
+    sends = W.allgather_inputs(R, M, seed=c["seed"])
+    with Job(R) as job:
+        sw, sv = job.window(M, fill=None, arrays=sends)
+        rw, rv = job.window(R * M, fill=None)
+        vr.vr_allgather(job.comm, sw, 0, rw, 0, M, sig=0)
+        job.torch.cuda.synchronize()
+        for d in range(R):  # one destination at a time: 1 GiB each
+            got = rv[d].cpu().numpy()
+            assert np.array_equal(got, D.allgather_for_rank(sends, d)), d
+            del got
+        assert [job.sig(d, 0) for d in range(R)] == [R] * R
+        job.assert_no_async_error()

@@ -1,0 +1,121 @@
+"""Sum-AllReduce on the GPU against the oracle: bit-exact in fixed rank order."""
+import json
+
+import numpy as np
+import pytest
+
+import collective_window_put_amd as vr
+from oracle import definitions as D
+import workloads as W
+from conftest import golden
+from gpu_util import Job, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(xs, dtype, send_off=0, recv_off=0, sig=2, repeats=1):
+    R = len(xs)
+    es = 4 if dtype == "f32" else 2
+    N = xs[0].size
+    dt = vr.VR_DT_F32 if dtype == "f32" else vr.VR_DT_BF16
+    with Job(R) as job:
+        sw, sv = job.window(send_off + N * es + 16, fill=0)
+        rw, rv = job.window(recv_off + N * es + 16, fill=0xCD)
+        for r in range(R):
+            sv[r][send_off:send_off + N * es].copy_(job.torch.from_numpy(xs[r].view(np.uint8)))
+        for _ in range(repeats):
+            vr.vr_allreduce(job.comm, sw, send_off, rw, recv_off, N, dt, sig=sig)
+        out = job.host(rv)
+        sigs = [job.sig(d, sig) for d in range(R)]
+        job.assert_no_async_error()
+    return out, sigs
+
+
+def test_allreduce_page_worked_example():
+    g = json.load(open(golden("allreduce_rank_fill.json")))
+    R, N = g["ranks"], g["count"]
+    say("allreduce rank fill R=4 N=1M")
+    out, sigs = _run(W.allreduce_f32_inputs(R, N, run="A"), "f32")
+    for d in range(R):
+        v = out[d][:N * 4].view(np.float32)
+        assert np.all(np.abs(v - g["expected"]) <= g["tolerance"])
+        assert np.all(v == np.float32(g["expected"]))
+        assert np.all(out[d][N * 4:] == 0xCD)
+    assert sigs == [R] * R
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 8, 16])
+def test_allreduce_rank_fill_closed_form(R):
+    say(f"allreduce rank fill R={R}")
+    out, _ = _run(W.allreduce_f32_inputs(R, 5000, run="A"), "f32")
+    for d in range(R):
+        assert np.all(out[d][:20000].view(np.float32) == np.float32(R * (R - 1) // 2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("R,N", [(2, 1), (3, 1001), (4, 4096), (5, 77777), (8, 2048 * 8 + 3), (16, 40000),
+                                 (7, 123457)])
+def test_allreduce_random_bit_exact(dtype, R, N):
+    say(f"allreduce {dtype} R={R} N={N}")
+    xs = W.allreduce_f32_inputs(R, N, seed=R + N) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + N)
+    out, sigs = _run(xs, dtype)
+    es = 4 if dtype == "f32" else 2
+    exp = D.allreduce(xs, dtype).view(np.uint8)
+    for d in range(R):
+        assert np.array_equal(out[d][:N * es], exp), d
+    assert sigs == [R] * R
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_allreduce_unaligned_offsets(dtype):
+    R, N = 4, 3000
+    es = 4 if dtype == "f32" else 2
+    say(f"allreduce unaligned {dtype}")
+    xs = W.allreduce_f32_inputs(R, N, seed=3) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=3)
+    out, _ = _run(xs, dtype, send_off=es * 3, recv_off=es * 5)
+    exp = D.allreduce(xs, dtype).view(np.uint8)
+    for d in range(R):
+        assert np.array_equal(out[d][es * 5:es * 5 + N * es], exp)
+
+
+def test_allreduce_special_values_bf16():
+    # ties, overflow to inf, inf + -inf = NaN (canonical 0x7FC0), signed zeros
+    R = 3
+    vals = np.array([[0x3F80, 0x7F7F, 0x7F80, 0x8000, 0x3F80, 0x0001, 0xFF80, 0x7FC1],
+                     [0x3B80, 0x7F7F, 0xFF80, 0x8000, 0xBF80, 0x0001, 0xFF80, 0x0000],
+                     [0x0000, 0x7F00, 0x0000, 0x8000, 0x0000, 0x8001, 0x3F80, 0x3F80]], dtype=np.uint16)
+    xs = [np.tile(v, 700) for v in vals]
+    say("allreduce bf16 special values")
+    out, _ = _run(xs, "bf16")
+    exp = D.allreduce(xs, "bf16").view(np.uint8)
+    for d in range(R):
+        assert np.array_equal(out[d][:exp.size], exp)
+
+
+def test_allreduce_repeated_signal_accumulates():
+    say("allreduce repeated x3")
+    xs = W.allreduce_f32_inputs(4, 1000, seed=5)
+    out, sigs = _run(xs, "f32", repeats=3)
+    assert sigs == [12] * 4
+
+
+def test_allreduce_config_c1_run_b():
+    c = W.CONFIGS["c1"]
+    say("allreduce c1 run B")
+    xs = W.allreduce_f32_inputs(c["ranks"], c["count"], run="B", seed=c["seed"])
+    out, _ = _run(xs, "f32")
+    exp = D.allreduce(xs, "f32").view(np.uint8)
+    for d in range(c["ranks"]):
+        assert np.array_equal(out[d][:exp.size], exp)
+
+
+def test_allreduce_config_c2_full_size():
+    c = W.CONFIGS["c2"]
+    R, N = c["ranks"], c["count"]
+    say(f"allreduce c2 full R={R} N={N}")
+    xs = W.allreduce_bf16_inputs(R, N, seed=c["seed"])
+    exp = D.allreduce(xs, "bf16").view(np.uint8)
+    out, sigs = _run(xs, "bf16")
+    for d in range(R):
+        assert np.array_equal(out[d][:N * 2], exp), d
+    assert sigs == [R] * R

@@ -1,0 +1,62 @@
+"""Ring exchange on the GPU: cyclic shift, per-context signals and counters, litmus."""
+import numpy as np
+import pytest
+
+import collective_window_put_amd as vr
+from oracle import definitions as D
+import workloads as W
+from gpu_util import Job, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(R, P, pb, C, litmus=True, repeats=1):
+    import torch
+    sends = W.ring_inputs(R, P, pb, seed=R + P)
+    with Job(R, signal_count=C + 2, counter_count=C + 1, context_count=C) as job:
+        sw, _ = job.window(P * pb, fill=None, arrays=sends)
+        rw, rv = job.window(P * pb, fill=0)
+        lit = torch.zeros(2, dtype=torch.int64, device="cuda") if litmus else None
+        for _ in range(repeats):
+            vr.vr_ring_exchange(job.comm, sw, rw, pb, P, C, sig_base=1, cnt_base=1, litmus=lit)
+        out = job.host(rv)
+        sigs = [[job.sig(d, 1 + k) for k in range(C)] for d in range(R)]
+        cnts = [[job.cnt(d, 1 + k) for k in range(C)] for d in range(R)]
+        lit_h = lit.cpu().numpy() if litmus else None
+        err = job.async_error()
+    return sends, out, sigs, cnts, lit_h, err
+
+
+@pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 2), (3, 96, 256, 4), (4, 1000, 48, 10), (16, 4096, 256, 64),
+                                      (5, 64, 8192, 2)])
+def test_ring_vs_oracle(R, P, pb, C):
+    say(f"ring R={R} P={P} pb={pb} C={C}")
+    sends, out, sigs, cnts, lit, err = _run(R, P, pb, C)
+    exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
+    for d in range(R):
+        assert np.array_equal(out[d], exp[d]), d
+    assert sigs == [[P // C] * C] * R
+    assert cnts == [[P // C] * C] * R
+    assert lit[1] == 0 and lit[0] > 0
+    assert err[0] == vr.VR_OK
+
+
+def test_ring_repeated_accumulates():
+    say("ring repeated x2")
+    R, P, pb, C = 4, 64, 256, 4
+    sends, out, sigs, cnts, lit, err = _run(R, P, pb, C, repeats=2)
+    assert sigs == [[2 * P // C] * C] * R and cnts == [[2 * P // C] * C] * R
+    assert err[0] == vr.VR_OK
+
+
+def test_ring_config_c5b_full_size():
+    c = W.CONFIGS["c5b"]
+    say("ring c5b full")
+    R, P, pb, C = c["ranks"], c["puts_per_rank"], c["put_bytes"], c["contexts"]
+    sends, out, sigs, cnts, lit, err = _run(R, P, pb, C)
+    exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
+    for d in range(R):
+        assert np.array_equal(out[d], exp[d]), d
+    assert sigs == [[P // C] * C] * R and cnts == [[P // C] * C] * R
+    assert lit[1] == 0
+    assert err[0] == vr.VR_OK
