@@ -297,6 +297,22 @@ def run_rows(b: Bench, reps: int = 10):
     return rows
 
 
+def calib_copy(b: Bench, reps: int = 3):
+    """A plain elementwise kernel of known traffic: reads 1 GiB, writes 1 GiB.
+
+    Its FETCH_SIZE / WRITE_SIZE counters scale the same counters of our
+    kernels to bytes (the kernel is torch's bitwise_not on int32)."""
+    torch = b.torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        b.flush_cache()
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    log("calibration copy done (1 GiB read + 1 GiB write per launch)")
+
+
 # ---- the CPU oracle beside it ---------------------------------------------------------------------
 def cpu_baseline(xs, R: int, N: int, budget_s: float = 20.0):
     """Time the oracle's protocol simulation of the same AllReduce on one host core.
@@ -343,12 +359,16 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--reps", type=int, default=10, help="repetitions per other workload")
+    ap.add_argument("--calib", action="store_true",
+                    help="first run a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the R virtual ranks share one device, and no collectives cross "
               "GPUs in this build", file=sys.stderr)
         sys.exit(2)
     b = Bench()
+    if args.calib:
+        calib_copy(b)
     head = run_allreduce_headline(b, args.steps, args.warmup)
     kern = float(np.mean(head["kern_ms"]))
     achieved = head["bytes_alg"] / (kern * 1e-3) / 1e9
