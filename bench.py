@@ -37,7 +37,7 @@ METRIC = "achieved HBM GB/s (and % of peak) for R-rank AllReduce/AlltoAll/dispat
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "k_allreduce": "allreduce.hip", "k_alltoall": "alltoall.hip", "k_allgather": "allgather.hip",
-    "k_dispatch_put": "dispatch.hip", "k_ring": "ring.hip",
+    "k_dispatch": "dispatch.hip", "k_ring": "ring.hip",
 }
 
 
@@ -73,7 +73,7 @@ class Bench:
         self.torch, self.vr = torch, vr
         torch.cuda.set_device(0)
         self.stream = torch.cuda.current_stream()
-        self.flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        self.flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
 
     def slices(self, R: int, nbytes: int, arrays=None, fill=None):
         torch = self.torch
@@ -90,7 +90,10 @@ class Bench:
         return slab, views
 
     def flush_cache(self):
-        self.flush_buf.fill_(1)  # 1 GiB write evicts the 256 MiB Infinity Cache and the L2s
+        # Reading 1 GiB evicts the 256 MiB Infinity Cache and the L2s without
+        # leaving dirty lines behind (a write flush would leave up to 256 MiB
+        # of dirty lines to be written back inside the next timed kernel).
+        self.flush_buf.view(self.torch.int64).sum()
 
     def timed(self, fn, reps: int, flush: bool):
         """Per-repetition durations (ms) from events recorded on the launch stream."""
@@ -177,21 +180,36 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
 
 
 # ---- the other workloads ------------------------------------------------------------------------
-def run_rows(b: Bench, reps: int = 10):
-    import workloads as W
-    vr = b.vr
-    torch = b.torch
-    stream = b.stream.cuda_stream
+ROW_NAMES = ("allreduce_f32", "alltoall", "dispatch", "allgather", "ring")
+
+
+def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
     rows = {}
-
-    def comm_for(R, **kw):
-        return vr.vr_comm_create(R, **kw)
-
     # AllReduce fp32, R=4, 1 Mi elements (the worked-example shape)
+    if "allreduce_f32" in only:
+        run_allreduce_f32_row(b, reps, rows)
+    if "alltoall" in only:
+        run_alltoall_row(b, reps, rows)
+    if "dispatch" in only:
+        run_dispatch_row(b, reps, rows)
+    if "allgather" in only:
+        run_allgather_row(b, reps, rows)
+    if "ring" in only:
+        run_ring_row(b, reps, rows)
+    return rows
+
+
+def comm_for(vr, R, **kw):
+    return vr.vr_comm_create(R, **kw)
+
+
+def run_allreduce_f32_row(b, reps, rows):
+    import workloads as W
+    vr, stream = b.vr, b.stream.cuda_stream
     c = W.CONFIGS["c1"]
     R, N = c["ranks"], c["count"]
     xs = W.allreduce_f32_inputs(R, N, run="B", seed=c["seed"])
-    comm = comm_for(R, signal_count=2)
+    comm = comm_for(vr, R, signal_count=2)
     s1, sv = b.slices(R, N * 4, arrays=xs)
     r1, rv = b.slices(R, N * 4, fill=0)
     sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], N * 4)
@@ -205,11 +223,15 @@ def run_rows(b: Bench, reps: int = 10):
     vr.vr_comm_destroy(comm)
     del s1, r1
 
-    # AlltoAll R=8, 4 MiB blocks
+
+
+def run_alltoall_row(b, reps, rows):
+    import workloads as W
+    vr, stream = b.vr, b.stream.cuda_stream
     c = W.CONFIGS["c3"]
     R, B = c["ranks"], c["block_bytes"]
     sends = W.alltoall_inputs(R, B, seed=c["seed"])
-    comm = comm_for(R, signal_count=2)
+    comm = comm_for(vr, R, signal_count=2)
     s1, sv = b.slices(R, R * B, arrays=sends)
     r1, rv = b.slices(R, R * B, fill=0)
     sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], R * B)
@@ -223,13 +245,17 @@ def run_rows(b: Bench, reps: int = 10):
     vr.vr_comm_destroy(comm)
     del s1, r1
 
-    # MoE dispatch R=8, 4096 tokens x 512 B, 256 experts, top-8 Zipf(1.1)
+
+
+def run_dispatch_row(b, reps, rows):
+    import workloads as W
+    vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
     c = W.CONFIGS["c4"]
     R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
     topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
     rb = H * 2
     cap = R * T * min(K, E // R)
-    comm = comm_for(R, signal_count=4)
+    comm = comm_for(vr, R, signal_count=4)
     s1, xv = b.slices(R, T * rb, arrays=[x[r] for r in range(R)])
     r1, rv = b.slices(R, cap * rb, fill=0)
     xw = vr.vr_window_register(comm, [v.data_ptr() for v in xv], T * rb)
@@ -242,18 +268,22 @@ def run_rows(b: Bench, reps: int = 10):
     nrows = int((topk >= 0).sum())
     bytes_alg = R * T * rb + topk.nbytes + nrows * rb + nrows * 4 + R * (E // R) * 4
     rows["dispatch_r8_t4096_e256_k8"] = row_entry("dispatch R=8 T=4096 512B E=256 K=8", bytes_alg,
-                                                  b.timed(f, reps, True), "k_dispatch_put",
+                                                  b.timed(f, reps, True), "k_dispatch",
                                                   "dispatch_r8_t4096_e256_k8", {"rows": nrows})
     vr.vr_window_deregister(comm, xw)
     vr.vr_window_deregister(comm, rw)
     vr.vr_comm_destroy(comm)
     del s1, r1, tk, counts, src
 
-    # AllGather R=16, 64 MiB per rank
+
+
+def run_allgather_row(b, reps, rows):
+    import workloads as W
+    vr, stream = b.vr, b.stream.cuda_stream
     c = W.CONFIGS["c5a"]
     R, M = c["ranks"], c["bytes_per_rank"]
     sends = W.allgather_inputs(R, M, seed=c["seed"])
-    comm = comm_for(R, signal_count=2)
+    comm = comm_for(vr, R, signal_count=2)
     s1, sv = b.slices(R, M, arrays=sends)
     r1, rv = b.slices(R, R * M, fill=None)
     sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], M)
@@ -268,11 +298,15 @@ def run_rows(b: Bench, reps: int = 10):
     vr.vr_comm_destroy(comm)
     del s1, r1
 
-    # Ring exchange R=16, 65536 x 256 B per rank, 64 contexts, litmus on
+
+
+def run_ring_row(b, reps, rows):
+    import workloads as W
+    vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
     c = W.CONFIGS["c5b"]
     R, P, pb, C = c["ranks"], c["puts_per_rank"], c["put_bytes"], c["contexts"]
     sends = W.ring_inputs(R, P, pb, seed=c["seed"])
-    comm = comm_for(R, signal_count=C, counter_count=C, context_count=C)
+    comm = comm_for(vr, R, signal_count=C, counter_count=C, context_count=C)
     s1, sv = b.slices(R, P * pb, arrays=sends)
     r1, rv = b.slices(R, P * pb, fill=0)
     sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], P * pb)
@@ -294,7 +328,6 @@ def run_rows(b: Bench, reps: int = 10):
     vr.vr_window_deregister(comm, rw)
     vr.vr_comm_destroy(comm)
     del s1, r1
-    return rows
 
 
 def calib_copy(b: Bench, reps: int = 3):
@@ -357,6 +390,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true", help="skip the other workloads")
+    ap.add_argument("--rows", default=",".join(ROW_NAMES), help="comma-separated subset of " + ",".join(ROW_NAMES))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--reps", type=int, default=10, help="repetitions per other workload")
     ap.add_argument("--calib", action="store_true",
@@ -387,7 +421,7 @@ def main():
                      "kernel_ms_mean": round(kern, 5)},
     }
     if not args.no_rows:
-        out["rows"] = run_rows(b, args.reps)
+        out["rows"] = run_rows(b, args.reps, tuple(args.rows.split(",")))
     if not args.no_cpu:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(head["xs"], head["R"], head["N"])

@@ -32,7 +32,8 @@ __all__ = [
     "vr_allreduce", "vr_alltoall", "vr_allgather", "vr_dispatch", "vr_ring_exchange",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvrcomm.so")
+# The in-tree build; VRCOMM_LIB may name another build of the same library.
+LIB_PATH = os.environ.get("VRCOMM_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvrcomm.so")
 
 VR_OK = 0
 VR_ERR_INVALID_ARGUMENT = 1

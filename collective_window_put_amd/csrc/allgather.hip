@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void k_allgather(const AGArgs a) {
       wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
     return;
   }
-  const uint32_t s = b / a.tiles, tile = b % a.tiles;
+  const uint32_t s = b % R, tile = b / R;  // consecutive workgroups: different sources (even relay load)
   const uint64_t t0 = (uint64_t)tile * kTile;
   if (t0 < a.bytes) {
     const uint32_t n = static_cast<uint32_t>(std::min<uint64_t>(kTile, a.bytes - t0));

@@ -13,6 +13,8 @@
 // converts, and stores the tile into every rank's receive window (the puts of
 // the all-gather). The workgroup completing the chunk's relay applies one
 // SignalInc at every rank, so each rank's signal rises by R (one per owner).
+// Output stores are agent-coherent and streaming (sc1 nt): measured 2-3%
+// faster than sc1 alone for this write-once pattern.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -131,7 +133,7 @@ __device__ void reduce_tile(const ARArgs& a, uint64_t start, uint64_t end) {
         const v4u out = E::narrow(acc);
         const uint32_t off = static_cast<uint32_t>((i - start) * E::kSize);
         for (int d = 0; d < R; ++d)
-          store16_agent(rsrc(a.recv.p[d] + a.recv_off + start * E::kSize, nbytes), off, out);
+          store16_agent_stream(rsrc(a.recv.p[d] + a.recv_off + start * E::kSize, nbytes), off, out);
       } else if (i < end) {  // ragged tail of the whole vector: element by element
         for (uint64_t k = i; k < end; ++k) {
           const uint64_t sb = a.send_off + k * E::kSize;
@@ -165,7 +167,12 @@ __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
       wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
     return;
   }
-  const uint32_t c = b / a.tpc, j = b % a.tpc;
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs (b % 8);
+  // give XCD x the contiguous tile range [x, x+1) * nwork/8 -- for R = 8
+  // exactly owner x's chunk -- so each XCD streams one region and the owners'
+  // relay counters are hit in parallel rather than one at a time.
+  const uint32_t w = (nwork & 7u) == 0 ? (b & 7u) * (nwork >> 3) + (b >> 3) : b;
+  const uint32_t c = w / a.tpc, j = w % a.tpc;
   constexpr uint64_t tile = 256ull * kU * Elem<DT>::kPerVec;
   const uint64_t cbeg = (uint64_t)c * a.csz;
   const uint64_t cend = std::min<uint64_t>(a.count, cbeg + a.csz);

@@ -19,7 +19,8 @@
 namespace vr {
 namespace {
 
-constexpr uint32_t kTile = 16384;
+constexpr uint32_t kTile = 32768;
+constexpr int kU = kTile / (256 * 16);
 
 struct A2AArgs {
   WinTab send, recv;
@@ -45,14 +46,14 @@ __global__ __launch_bounds__(256) void k_alltoall(const A2AArgs a) {
       wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
     return;
   }
-  const uint32_t blk = b / a.tiles, tile = b % a.tiles;
+  const uint32_t blk = b % (R * R), tile = b / (R * R);
   const uint32_t s = blk / R, d = blk % R;
   const uint64_t t0 = (uint64_t)tile * kTile;
   if (t0 < a.block) {
     const uint32_t n = static_cast<uint32_t>(std::min<uint64_t>(kTile, a.block - t0));
     const char* src = a.send.p[s] + a.send_off + (uint64_t)d * a.block + t0;
     char* dst = a.recv.p[d] + a.recv_off + (uint64_t)s * a.block + t0;
-    copy_any<4>(dst, src, n, threadIdx.x, 256);
+    copy_any<kU>(dst, src, n, threadIdx.x, 256);
   }
   wg_stores_complete();
   if (threadIdx.x == 0 && relay_arrive(a.relay + blk, a.tiles))

@@ -6,21 +6,35 @@
 // one signal orders them cheaply. Layout of rank d's receive rows: by expert
 // (rank d owns experts [d*E/R, (d+1)*E/R)), then source rank, then token.
 //
-// Kernel 1 (count): workgroup (s, b) histograms the routing entries of its 64
-// tokens in LDS and stores the block histogram. The last block of source s
-// (relay) turns source s's block histograms into exclusive prefixes (the
-// stable position of each block's first row per expert), then puts the count
-// row C[s][.] into every rank's count window and applies a SignalInc at each
-// (count exchange). Block (s, 0) also records rank s's row signal as the base
-// its receiver will wait from.
-// Kernel 2 (put): workgroup (s, b) waits for rank s's count signal, derives
-// every expert's receive offset from the full count matrix
-//   off(s, e) = sum_{e' < e owned by the same rank} sum_s' C[s'][e]
-//             + sum_{s' < s} C[s'][e],
-// ranks its routing entries stably (token order) with wave ballots, and copies
-// each token row once per routed expert. The last block of source s applies
-// one SignalAdd(rows sent to d) at every rank d. The last R workgroups wait
-// until each rank's row signal has grown by the rows aimed at it.
+// One kernel, three kinds of workgroup, in grid order:
+// * count (s, b): histograms the routing entries of its 512 tokens in LDS, per
+//   64-token sub-block, and stores the sub-blocks' exclusive prefixes within
+//   the block plus the block's totals. The last block of source s (relay)
+//   sums the block totals into the count row C[s][.], puts it into every
+//   rank's count window and applies a SignalInc there (the count exchange).
+//   Block (s, 0) first records rank s's row signal as the base its receiver
+//   will wait from.
+// * put (s, b) of 64 tokens: ranks its routing entries within the block
+//   (wave ballots, token order), loads its token rows, waits for rank s's
+//   count signal, derives each expert's receive offset from the full count
+//   matrix
+//     off(s, e) = sum_{e' < e owned by the same rank} sum_s' C[s'][e]
+//               + sum_{s' < s} C[s'][e],
+//   adds the rows of earlier blocks and sub-blocks of source s, records each
+//   row's source, and copies each token row once per routed expert. The last
+//   block of source s applies one SignalAdd(rows sent to d) at every rank d.
+// * receiver d (the last R workgroups): waits until its row signal has grown
+//   by the rows aimed at it.
+// Count workgroups never wait, and every workgroup that waits comes later in
+// the grid than all the workgroups it waits for, so the waits always end.
+// Data published inside the kernel (prefixes, count rows, bases) is read with
+// agent-coherent loads after the announcing signal has been seen.
+//
+// Row copies use 16-byte lanes (two 512-byte rows per wave instruction) when
+// every rank's receive slice lies within one 4 GiB span, so that one buffer
+// resource addresses them all; otherwise 8-byte agent-coherent stores.
+// Measured on the 8 x 4096 x 512 B, E=256, K=8 shape: 16-byte lanes with 8
+// tokens per wave copy the rows in 29 us, 8-byte lanes in 55 us.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -31,208 +45,279 @@
 namespace vr {
 namespace {
 
-constexpr int kTokPerBlock = 64;   // tokens per workgroup
-constexpr int kTokPerWave = 16;    // 4 waves
-constexpr int kMaxE = 1024;
-constexpr int kMaxK = 64;
+constexpr int kThreads = 512;     // threads per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kTokPerWave = 8;    // tokens per wave in a put workgroup
+constexpr int kSub = kWaves * kTokPerWave;  // tokens per put workgroup (sub-block): 64
+constexpr int kCountBlock = 512;  // tokens per count workgroup
+constexpr int kSubs = kCountBlock / kSub;
+constexpr int kSubBits = 3;       // log2(kSubs): key bits above the expert's
+static_assert((1 << kSubBits) == kSubs, "kSubBits");
+constexpr int kRelayFan = 16;     // first-level relay counters per source (put blocks)
 
 struct DispArgs {
   WinTab x, recv;
   U64Tab target_counts;
   uint64_t x_off, recv_off, row_bytes, cap;
-  const int32_t* topk;  // [R][T][K]
-  int32_t* counts_out;  // [R][E/R]
-  int32_t* src_out;     // [R][cap]
-  int32_t* hblk;        // [R][NB][E]
-  int32_t* cwin;        // [R][R][E]: rank d's copy of every source's count row
-  uint64_t* base_rows;  // [R]
-  uint64_t* sig_counts; // &sig[0][id]
+  const int32_t* topk;   // [R][T][K]
+  int32_t* counts_out;   // [R][E/R]
+  int32_t* src_out;      // [R][cap]
+  int32_t* subpfx;       // [R][NB1*kSubs][E]: sub-block prefix within its count block
+  int32_t* blktot;       // [R][NB1][E]: rows per expert of each count block
+  int32_t* cwin;         // [R][R][E]: rank d's copy of every source's count row
+  uint64_t* base_rows;   // [R]
+  uint64_t* sig_counts;  // &sig[0][id]
   uint64_t* sig_rows;
   uint32_t sig_stride;
-  uint32_t* relay;      // [2R]: count kernel, put kernel
+  uint32_t* relay;       // [2R]: count kernel, put kernel
   uint32_t* err;
   uint64_t timeout_ns;
-  int R, T, K, E, NB, nbits;
-  int fast;             // rows and bases 8-byte aligned
+  char* span_base;       // lowest receive address, when the span path is on
+  uint32_t span_bytes;
+  uint32_t dspan[VR_MAX_RANKS];  // recv.p[d] + recv_off - span_base
+  int R, T, K, E, NB1, NB2, nbits;
+  int mode;              // 2: 16-byte lanes via the span; 1: 8-byte lanes; 0: bytes
 };
 
 __device__ inline int32_t load_topk(const DispArgs& a, int s, int t, int k) {
   return a.topk[((size_t)s * a.T + t) * a.K + k];
 }
 
-__global__ __launch_bounds__(256) void k_dispatch_count(const DispArgs a) {
-  __shared__ int32_t hist[kMaxE];
-  __shared__ int last;
-  const int s = blockIdx.x / a.NB, blk = blockIdx.x % a.NB;
+__device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int wg) {
+  const int R = a.R, E = a.E;
+  const int s = wg % R, blk = wg / R;  // interleaved: sources' relays hit in parallel
   const int tid = threadIdx.x;
-  for (int e = tid; e < a.E; e += 256) hist[e] = 0;
+  int32_t* hist = lds;  // [kSubs][E]
+  for (int i = tid; i < kSubs * E; i += kThreads) hist[i] = 0;
   if (blk == 0 && tid == 0)
     store8_agent(a.base_rows + s, load_relaxed_u64(a.sig_rows + (size_t)s * a.sig_stride));
   __syncthreads();
-  const int t0 = blk * kTokPerBlock;
-  const int ntok = max(0, min(a.T - t0, kTokPerBlock));
-  for (int i = tid; i < ntok * a.K; i += 256) {
-    const int e = load_topk(a, s, t0 + i / a.K, i % a.K);
-    if (e == -1) continue;
-    if (e < 0 || e >= a.E) {
-      atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
-      continue;
+  const int t0 = blk * kCountBlock;
+  const int ntok = max(0, min(a.T - t0, kCountBlock));
+  // entries with equal (sub-block, expert) in one wave instruction are added
+  // once, by their lowest lane (hot experts would otherwise serialize LDS adds)
+  const int lane = tid & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int iters = (ntok * a.K + kThreads - 1) / kThreads;
+  for (int it0 = 0; it0 < iters; it0 += 8) {  // 8 loads in flight per thread, then the adds
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = (it0 + u) * kThreads + tid;
+      ev[u] = (it0 + u < iters && i < ntok * a.K) ? load_topk(a, s, t0 + i / a.K, i % a.K) : -1;
     }
-    atomicAdd(&hist[e], 1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (it0 + u >= iters) break;
+      const int i = (it0 + u) * kThreads + tid;
+      const int tl = i / a.K;
+      const int e = ev[u];
+      if (e != -1 && (e < 0 || e >= E)) atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
+      if (e >= 0 && e < E) {
+        const int key = (tl / kSub) * E + e;
+        const uint64_t m = match_any(static_cast<uint32_t>(key), a.nbits + kSubBits);
+        if ((m & lt) == 0) atomicAdd(&hist[key], __popcll(m));
+      }
+    }
   }
   __syncthreads();
-  int32_t* hb = a.hblk + ((size_t)s * a.NB + blk) * a.E;
-  for (int e = tid; e < a.E; e += 256) store4_agent(reinterpret_cast<uint32_t*>(hb + e), hist[e]);
-  wg_stores_complete();
-  if (tid == 0) last = relay_arrive(a.relay + s, a.NB);
-  __syncthreads();
-  if (!last) return;
-  // last block of source s: exclusive prefix over blocks, count row to every rank
-  for (int e = tid; e < a.E; e += 256) {
+  for (int e = tid; e < E; e += kThreads) {
     int32_t run = 0;
-    for (int b = 0; b < a.NB; ++b) {
-      int32_t* p = a.hblk + ((size_t)s * a.NB + b) * a.E + e;
-      const int32_t v = *p;
-      store4_agent(reinterpret_cast<uint32_t*>(p), run);
-      run += v;
+    for (int q = 0; q < kSubs; ++q) {
+      store4_agent(reinterpret_cast<uint32_t*>(a.subpfx + ((size_t)s * a.NB1 * kSubs + blk * kSubs + q) * E + e), run);
+      run += hist[q * E + e];
     }
-    for (int d = 0; d < a.R; ++d)
-      store4_agent(reinterpret_cast<uint32_t*>(a.cwin + ((size_t)d * a.R + s) * a.E + e), run);
+    store4_agent(reinterpret_cast<uint32_t*>(a.blktot + ((size_t)s * a.NB1 + blk) * E + e), run);
   }
   wg_stores_complete();
-  if (tid < a.R) atomic_add_u64(a.sig_counts + (size_t)tid * a.sig_stride, 1ull);  // SignalInc at each rank
+  if (tid == 0) *last_flag = relay_arrive(a.relay + s, a.NB1, false);
+  __syncthreads();
+  if (!*last_flag) return;
+  // last block of source s: C[s][e] = sum of the block totals (16 independent
+  // loads in flight per expert), then the count row to every rank
+  for (int e = tid; e < E; e += kThreads) {
+    const int32_t* col = a.blktot + (size_t)s * a.NB1 * E + e;
+    int32_t run = 0;
+    for (int b0 = 0; b0 < a.NB1; b0 += 16) {
+      int32_t v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = b0 + q < a.NB1 ? load_coherent_i32(col + (size_t)(b0 + q) * E) : 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) run += v[q];
+    }
+    for (int d = 0; d < R; ++d)
+      store4_agent(reinterpret_cast<uint32_t*>(a.cwin + ((size_t)d * R + s) * E + e), run);
+  }
+  wg_stores_complete();
+  if (tid < R) atomic_add_u64(a.sig_counts + (size_t)tid * a.sig_stride, 1ull);  // SignalInc at each rank
 }
 
-__global__ __launch_bounds__(256) void k_dispatch_put(const DispArgs a) {
-  // dynamic LDS: tot[E] (rows of expert e over all sources), base[E] (receive
-  // row of this block's first row of expert e), hw[4][E] (per-wave counts, then
+__device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int wg) {
+  // LDS: tot[E] (rows of expert e over all sources), base[E] (receive row of
+  // this block's first row of expert e), hw[kWaves][E] (per-wave counts, then
   // exclusive per-wave prefixes), dpos/dexp[64*K] (destination row and expert
-  // of each routing entry of the block)
-  extern __shared__ int32_t lds[];
-  __shared__ int last;
-  const int R = a.R, E = a.E, epr = a.E / a.R;
+  // of each routing entry of the block), crow[E] (this source's count row)
+  const int R = a.R, E = a.E, epr = a.E / a.R, K = a.K;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int32_t* tot = lds;
   int32_t* base = tot + E;
   int32_t* hwf = base + E;
-  int32_t* dpos = hwf + 4 * E;
-  int32_t* dexp = dpos + kTokPerBlock * a.K;
-#define hw(w, e) hwf[(w) * E + (e)]
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nwork = R * a.NB;
-  if ((int)blockIdx.x >= nwork) {  // receiver d waits for the rows aimed at it
-    const int d = blockIdx.x - nwork;
-    if (tid == 0) {
-      uint64_t rows = 0;
-      for (int sp = 0; sp < R; ++sp)
-        for (int e = d * epr; e < (d + 1) * epr; ++e) rows += a.cwin[((size_t)d * R + sp) * E + e];
-      wait_reached(a.sig_rows + (size_t)d * a.sig_stride, a.base_rows[d] + rows, 64, a.timeout_ns, a.err,
-                   VR_ASYNC_TIMEOUT);
-    }
-    return;
-  }
-  const int s = blockIdx.x / a.NB, blk = blockIdx.x % a.NB;
-  // count exchange: rank s waits for every source's count row
-  if (tid == 0)
-    wait_reached(a.sig_counts + (size_t)s * a.sig_stride, a.target_counts.v[s], 64, a.timeout_ns, a.err,
-                 VR_ASYNC_TIMEOUT);
-  __syncthreads();
-  const int32_t* cw = a.cwin + (size_t)s * R * E;  // rank s's copy: cw[s'][e]
-  const int32_t* pb = a.hblk + ((size_t)s * a.NB + blk) * E;
-  for (int e = tid; e < E; e += 256) {
-    int32_t t = 0, pre = 0;
-    for (int sp = 0; sp < R; ++sp) {
-      const int32_t v = cw[(size_t)sp * E + e];
-      t += v;
-      if (sp < s) pre += v;
-    }
-    tot[e] = t;
-    base[e] = pre + pb[e];
-    for (int w = 0; w < 4; ++w) hw(w, e) = 0;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    int32_t seg = 0;
-    for (int q = (e / epr) * epr; q < e; ++q) seg += tot[q];
-    base[e] += seg;
-  }
-  if (blk == 0)
-    for (int j = tid; j < epr; j += 256)
-      store4_agent(reinterpret_cast<uint32_t*>(a.counts_out + (size_t)s * epr + j), tot[s * epr + j]);
-  // pass 1: per-wave counts; pass 2: stable positions
-  const int K = a.K;
-  const int tpr = 64 / K;  // tokens per round
-  const int tw0 = blk * kTokPerBlock + wave * kTokPerWave;
+  int32_t* dpos = hwf + kWaves * E;
+  int32_t* dexp = dpos + kSub * K;
+  int32_t* crow = dexp + kSub * K;
+  const int s = wg % R, b2 = wg / R;  // interleaved sources
+  const int b1 = b2 / kSubs;
+  const int tpr = 64 / K;  // tokens per ballot round
+  const int tw0 = b2 * kSub + wave * kTokPerWave;
   const int rounds = (kTokPerWave + tpr - 1) / tpr;
+  const int ntw = max(0, min(kTokPerWave, a.T - tw0));
+  const uint64_t rb = a.row_bytes;
+  // Loads that depend on no count are issued first: this wave's routing
+  // entries, one register per ballot round.
+  int lpr = 1;
+  const int nv = static_cast<int>(rb >> 4);
+  while (lpr < nv) lpr <<= 1;
+  const int rpi = a.mode == 2 ? 64 / lpr : 1;
+  const int l = lane & (lpr - 1), sub = lane / lpr;
+  const int groups = (kTokPerWave + rpi - 1) / rpi;
+  int ent[kTokPerWave];  // routing entry of this lane in each ballot round (-1: none)
+#pragma unroll
+  for (int rd = 0; rd < kTokPerWave; ++rd) {
+    const int tl = rd * tpr + lane / K;
+    ent[rd] = (rd < rounds && lane < tpr * K && tl < ntw) ? load_topk(a, s, tw0 + tl, lane % K) : -1;
+  }
+  // Ranking within the block needs no counts: per-wave counts, their
+  // exclusive prefix over the waves, then each entry's rank among the
+  // block's entries of its expert (token order). dpos holds that local rank.
+  for (int e = tid; e < E; e += kThreads)
+    for (int w = 0; w < kWaves; ++w) hwf[w * E + e] = 0;
   const uint64_t lt = (1ull << lane) - 1ull;
   __syncthreads();
   for (int pass = 0; pass < 2; ++pass) {
-    for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+    for (int rd = 0; rd < kTokPerWave; ++rd) {
+      if (rd >= rounds) break;
       const int tl = rd * tpr + lane / K;  // token index within the wave
       const int k = lane % K;
-      const int t = tw0 + tl;
-      const bool valid = lane < tpr * K && tl < kTokPerWave && t < a.T;
-      int e = valid ? load_topk(a, s, t, k) : -1;
+      const bool valid = lane < tpr * K && tl < ntw;
+      const int e = ent[rd];
       const bool ok = valid && e >= 0 && e < E;
       if (pass == 0 && valid && e != -1 && !ok) atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
-      int32_t pos = -1;
+      int32_t lpos = -1;
       if (ok) {
         const uint64_t m = match_any(static_cast<uint32_t>(e), a.nbits);
         const bool leader = (m & lt) == 0;
         const int cnt = __popcll(m);
-        if (pass == 1) pos = base[e] + hw(wave, e) + __popcll(m & lt);
-        if (leader) hw(wave, e) += cnt;
+        if (pass == 1) lpos = hwf[wave * E + e] + __popcll(m & lt);
+        if (leader) hwf[wave * E + e] += cnt;
       }
       if (pass == 1 && valid) {
         const int slot = (wave * kTokPerWave + tl) * K + k;
-        dpos[slot] = pos;
+        dpos[slot] = lpos;
         dexp[slot] = ok ? e : -1;
-        if (ok) {
-          const int d = e / epr;
-          if ((uint64_t)pos < a.cap)
-            store4_agent(reinterpret_cast<uint32_t*>(a.src_out + (size_t)d * a.cap + pos),
-                         static_cast<uint32_t>((s << 16) | t));
-          else
-            atomic_or_u32(a.err, VR_ASYNC_CAPACITY);
-        }
       }
     }
     __syncthreads();
     if (pass == 0)
-      for (int e = tid; e < E; e += 256) {
+      for (int e = tid; e < E; e += kThreads) {
         int32_t run = 0;
-        for (int w = 0; w < 4; ++w) {
-          const int32_t v = hw(w, e);
-          hw(w, e) = run;
-          run += v;
+        for (int w = 0; w < kWaves; ++w) {
+          const int32_t c = hwf[w * E + e];
+          hwf[w * E + e] = run;
+          run += c;
         }
       }
     __syncthreads();
   }
-  // copy: each wave moves its 16 tokens' rows, 512 bytes per wave instruction;
-  // all 16 rows' pieces are loaded before any is stored.
-  const uint64_t rb = a.row_bytes;
-  const int ntw = max(0, min(kTokPerWave, a.T - tw0));
-  if (a.fast) {
-    for (uint64_t c0 = 0; c0 < rb; c0 += 512) {
-      const uint64_t o = c0 + (uint64_t)lane * 8;
-      const bool in = o < rb;
-      uint64_t v[kTokPerWave];
+  // this wave's token rows (16-byte path), loaded while the counts are awaited
+  v4u v[kTokPerWave];
+  if (a.mode == 2) {
 #pragma unroll
-      for (int tl = 0; tl < kTokPerWave; ++tl)
-        v[tl] = (in && tl < ntw)
-                    ? __builtin_nontemporal_load(
-                          reinterpret_cast<const uint64_t*>(a.x.p[s] + a.x_off + (uint64_t)(tw0 + tl) * rb + o))
-                    : 0;
+    for (int g = 0; g < kTokPerWave; ++g) {
+      const int tl = g * rpi + sub;
+      v[g] = (g < groups && tl < ntw && l < nv)
+                 ? load16_stream(reinterpret_cast<const v4u*>(a.x.p[s] + a.x_off + (uint64_t)(tw0 + tl) * rb + l * 16))
+                 : v4u{0, 0, 0, 0};
+    }
+  }
+  // count exchange: rank s waits until every source's count row has arrived;
+  // the rows and prefixes are then read with agent-coherent loads.
+  if (tid == 0)
+    wait_reached(a.sig_counts + (size_t)s * a.sig_stride, a.target_counts.v[s], 64, a.timeout_ns, a.err,
+                 VR_ASYNC_TIMEOUT, false);
+  __syncthreads();
+  compiler_fence();
+  const int32_t* cw = a.cwin + (size_t)s * R * E;  // rank s's copy: cw[s'][e]
+  const int32_t* pb = a.blktot + (size_t)s * a.NB1 * E;  // block totals of source s
+  const int32_t* ps = a.subpfx + ((size_t)s * a.NB1 * kSubs + b2) * E;
+  for (int e = tid; e < E; e += kThreads) {
+    // count rows of every source, and the totals of this source's earlier
+    // blocks: independent loads issued in batches of 16, one round trip each
+    int32_t t = 0, pre = 0, own = 0;
+    int32_t before = load_coherent_i32(ps + e);  // earlier sub-blocks of this count block
+    for (int q0 = 0; q0 < R + b1; q0 += 16) {
+      int32_t v[16];
 #pragma unroll
-      for (int tl = 0; tl < kTokPerWave; ++tl) {
-        if (tl >= ntw) break;
+      for (int q = 0; q < 16; ++q) {
+        const int j = q0 + q;
+        v[q] = j < R ? load_coherent_i32(cw + (size_t)j * E + e)
+                     : (j < R + b1 ? load_coherent_i32(pb + (size_t)(j - R) * E + e) : 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int j = q0 + q;
+        if (j < R) {
+          t += v[q];
+          if (j < s) pre += v[q];
+          if (j == s) own = v[q];
+        } else if (j < R + b1) {
+          before += v[q];
+        }
+      }
+    }
+    tot[e] = t;
+    crow[e] = own;  // C[s][e], for the trailing signals
+    base[e] = pre + before;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    int32_t seg = 0;
+    for (int q = (e / epr) * epr; q < e; ++q) seg += tot[q];
+    base[e] += seg;
+  }
+  if (b2 == 0)
+    for (int j = tid; j < epr; j += kThreads)
+      store4_agent(reinterpret_cast<uint32_t*>(a.counts_out + (size_t)s * epr + j), tot[s * epr + j]);
+  __syncthreads();
+  // final receive rows; each row's source tag
+  for (int slot = tid; slot < kSub * K; slot += kThreads) {
+    const int tlb = slot / K;  // token within the block
+    const int e = dexp[slot];
+    if (tlb >= kSub || b2 * kSub + tlb >= a.T || e < 0) continue;
+    const int32_t pos = base[e] + dpos[slot];
+    dpos[slot] = pos;
+    const int d = e / epr;
+    if ((uint64_t)pos < a.cap)
+      store4_agent(reinterpret_cast<uint32_t*>(a.src_out + (size_t)d * a.cap + pos),
+                   static_cast<uint32_t>((s << 16) | (b2 * kSub + tlb)));
+    else
+      atomic_or_u32(a.err, VR_ASYNC_CAPACITY);
+  }
+  __syncthreads();
+  // copy: the wave's 8 token rows, each once per routed expert
+  if (a.mode == 2) {
+    const __amdgpu_buffer_rsrc_t rd = rsrc(a.span_base, a.span_bytes);
+#pragma unroll
+    for (int g = 0; g < kTokPerWave; ++g) {
+      if (g >= groups) break;
+      const int tl = g * rpi + sub;
+      if (tl < ntw && l < nv) {
         const int slot0 = (wave * kTokPerWave + tl) * K;
         for (int k = 0; k < K; ++k) {
           const int32_t pos = dpos[slot0 + k];
           if (pos < 0 || (uint64_t)pos >= a.cap) continue;
           const int d = dexp[slot0 + k] / epr;
-          if (in)
-            store8_agent(reinterpret_cast<uint64_t*>(a.recv.p[d] + a.recv_off + (uint64_t)pos * rb + o), v[tl]);
+          store16_agent(rd, a.dspan[d] + static_cast<uint32_t>(pos) * static_cast<uint32_t>(rb) + l * 16, v[g]);
         }
       }
     }
@@ -243,31 +328,92 @@ __global__ __launch_bounds__(256) void k_dispatch_put(const DispArgs a) {
       for (int k = 0; k < K; ++k) {
         const int32_t pos = dpos[slot0 + k];
         if (pos < 0 || (uint64_t)pos >= a.cap) continue;
-        const int d = dexp[slot0 + k] / epr;
-        copy_bytes(a.recv.p[d] + a.recv_off + (uint64_t)pos * rb, src, static_cast<uint32_t>(rb), lane, 64);
+        char* dst = a.recv.p[dexp[slot0 + k] / epr] + a.recv_off + (uint64_t)pos * rb;
+        if (a.mode == 1) {
+          for (uint64_t o = (uint64_t)lane * 8; o < rb; o += 512)
+            store8_agent(reinterpret_cast<uint64_t*>(dst + o),
+                         __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(src + o)));
+        } else {
+          copy_bytes(dst, src, static_cast<uint32_t>(rb), lane, 64);
+        }
       }
     }
   }
   wg_stores_complete();
-  if (tid == 0) last = relay_arrive(a.relay + R + s, a.NB);
+  if (tid == 0) {
+    // two-level relay: 16 first-level counters per source, then one per source
+    const int g = b2 % kRelayFan;
+    const int in_g = (a.NB2 - g + kRelayFan - 1) / kRelayFan;
+    bool lastp = relay_arrive(a.relay + R + s * kRelayFan + g, in_g, false);
+    if (lastp) lastp = relay_arrive(a.relay + R + R * kRelayFan + s, min(a.NB2, kRelayFan), false);
+    *last_flag = lastp;
+  }
   __syncthreads();
-  if (last && tid < R) {  // one trailing SignalAdd(rows from s) per destination
+  if (*last_flag && tid < R) {  // one trailing SignalAdd(rows from s) per destination
     const int d = tid;
     uint64_t rows = 0;
-    for (int e = d * epr; e < (d + 1) * epr; ++e) rows += cw[(size_t)s * E + e];
+    for (int e = d * epr; e < (d + 1) * epr; ++e) rows += crow[e];
     if (rows) atomic_add_u64(a.sig_rows + (size_t)d * a.sig_stride, rows);
   }
-#undef hw
 }
+
+// Receiver d: waits for the count exchange (which fixes how many rows are
+// aimed at d and the base recorded before any row signal moved), then for
+// the row signal to grow by that many rows.
+__device__ void receiver_block(const DispArgs& a, int32_t* lds, int d) {
+  const int R = a.R, E = a.E, epr = a.E / a.R;
+  const int tid = threadIdx.x;
+  if (tid == 0)
+    wait_reached(a.sig_counts + (size_t)d * a.sig_stride, a.target_counts.v[d], 64, a.timeout_ns, a.err,
+                 VR_ASYNC_TIMEOUT, false);
+  __syncthreads();
+  compiler_fence();
+  int32_t part = 0;
+  for (int i = tid; i < R * epr; i += kThreads)
+    part += load_coherent_i32(a.cwin + ((size_t)d * R + i / epr) * E + d * epr + i % epr);
+  lds[tid] = part;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) lds[tid] += lds[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const uint64_t base = load_relaxed_u64(a.base_rows + d);
+    wait_reached(a.sig_rows + (size_t)d * a.sig_stride, base + static_cast<uint64_t>(lds[0]), 64, a.timeout_ns,
+                 a.err, VR_ASYNC_TIMEOUT);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_dispatch(const DispArgs a) {
+  extern __shared__ int32_t lds[];
+  __shared__ int last;
+  const int ncount = a.R * a.NB1, nput = a.R * a.NB2;
+  const int b = blockIdx.x;
+  if (b < ncount) count_block(a, lds, &last, b);
+  else if (b < ncount + nput) put_block(a, lds, &last, b - ncount);
+  else receiver_block(a, lds, b - ncount - nput);
+}
+
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
+struct Layout {
+  size_t subpfx, blktot, cwin, base_rows, total;
+};
+Layout scratch_layout(int R, int T, int E) {
+  const size_t NB1 = std::max(1, (T + kCountBlock - 1) / kCountBlock);
+  Layout l;
+  l.subpfx = 0;
+  l.blktot = al256((size_t)R * NB1 * kSubs * E * 4);
+  l.cwin = l.blktot + al256((size_t)R * NB1 * E * 4);
+  l.base_rows = l.cwin + al256((size_t)R * R * E * 4);
+  l.total = l.base_rows + al256((size_t)R * 8);
+  return l;
+}
+
 }  // namespace
 
-size_t dispatch_scratch_bytes(int R, int T, int E) {
-  const size_t NB = std::max(1, (T + kTokPerBlock - 1) / kTokPerBlock);
-  return al256((size_t)R * NB * E * 4) + al256((size_t)R * R * E * 4) + al256((size_t)R * 8);
-}
+size_t dispatch_scratch_bytes(int R, int T, int E) { return scratch_layout(R, T, E).total; }
 
 vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t row_bytes, const int32_t* topk, int T,
                            int K, int E, const vrWindow* recv, size_t recv_off, size_t cap, int32_t* counts_out,
@@ -278,6 +424,7 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   for (int r = 0; r < VR_MAX_RANKS; ++r) {
     a.x.p[r] = x->base[r];
     a.recv.p[r] = recv->base[r];
+    a.dspan[r] = 0;
   }
   a.target_counts = target_counts;
   a.x_off = x_off;
@@ -287,10 +434,13 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.topk = topk;
   a.counts_out = counts_out;
   a.src_out = src_out;
-  a.NB = std::max(1, (T + kTokPerBlock - 1) / kTokPerBlock);
-  a.hblk = reinterpret_cast<int32_t*>(c->scratch);
-  a.cwin = reinterpret_cast<int32_t*>(c->scratch + al256((size_t)R * a.NB * E * 4));
-  a.base_rows = reinterpret_cast<uint64_t*>(c->scratch + al256((size_t)R * a.NB * E * 4) + al256((size_t)R * R * E * 4));
+  a.NB1 = std::max(1, (T + kCountBlock - 1) / kCountBlock);
+  a.NB2 = a.NB1 * kSubs;
+  const Layout l = scratch_layout(R, T, E);
+  a.subpfx = reinterpret_cast<int32_t*>(c->scratch + l.subpfx);
+  a.blktot = reinterpret_cast<int32_t*>(c->scratch + l.blktot);
+  a.cwin = reinterpret_cast<int32_t*>(c->scratch + l.cwin);
+  a.base_rows = reinterpret_cast<uint64_t*>(c->scratch + l.base_rows);
   a.sig_counts = c->sig + sig_counts;
   a.sig_rows = c->sig + sig_rows;
   a.sig_stride = c->req.signal_count;
@@ -304,11 +454,27 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   int nb = 1;
   while ((1 << nb) < E) ++nb;
   a.nbits = nb;
-  a.fast = (row_bytes % 8 == 0) && (x_off % 8 == 0) && (recv_off % 8 == 0);
-  hipLaunchKernelGGL(k_dispatch_count, dim3(R * a.NB), dim3(256), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return VR_ERR_HIP;
-  const size_t lds = sizeof(int32_t) * (6 * (size_t)E + 2 * (size_t)kTokPerBlock * K);
-  hipLaunchKernelGGL(k_dispatch_put, dim3(R * a.NB + (wait ? R : 0)), dim3(256), lds, st, a);
+  // copy path: one buffer resource over all receive slices when they fit a 4 GiB span
+  char* lo = recv->base[0] + recv_off;
+  char* hi = lo + cap * row_bytes;
+  for (int r = 1; r < R; ++r) {
+    lo = std::min(lo, recv->base[r] + recv_off);
+    hi = std::max(hi, recv->base[r] + recv_off + cap * row_bytes);
+  }
+  const bool al16 = row_bytes % 16 == 0 && x_off % 16 == 0 && recv_off % 16 == 0 && row_bytes <= 1024;
+  a.span_base = lo;
+  a.span_bytes = 0;
+  if (al16 && (uint64_t)(hi - lo) < (1ull << 32)) {
+    a.mode = 2;
+    a.span_bytes = static_cast<uint32_t>(hi - lo);
+    for (int r = 0; r < R; ++r) a.dspan[r] = static_cast<uint32_t>(recv->base[r] + recv_off - lo);
+  } else {
+    a.mode = (row_bytes % 8 == 0 && x_off % 8 == 0 && recv_off % 8 == 0) ? 1 : 0;
+  }
+  const size_t lds = sizeof(int32_t) *
+                    std::max<size_t>({(size_t)kSubs * E, (3 + kWaves) * (size_t)E + 2 * (size_t)kSub * K, (size_t)kThreads});
+  const int grid = R * a.NB1 + R * a.NB2 + (wait ? R : 0);
+  hipLaunchKernelGGL(k_dispatch, dim3(grid), dim3(kThreads), lds, st, a);
   return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;
 }
 

@@ -9,7 +9,8 @@
 //
 // Rank r sends puts_per_rank messages to rank (r+1) mod R, split into
 // `contexts` contiguous ranges. One wavefront owns each (rank, context) and
-// issues its messages in order, in rounds of up to 4 KiB: it loads the
+// issues its messages in order, in rounds of up to 16 KiB (at most 64
+// messages, one signalling lane each): it loads the
 // round's messages, stores them with agent-coherent stores, waits for its
 // stores, then applies one SignalInc per message at the receiver and one
 // CounterInc per message at itself. Every signal is therefore applied after
@@ -28,7 +29,7 @@
 namespace vr {
 namespace {
 
-constexpr uint32_t kRoundBytes = 4096;
+constexpr uint32_t kRoundBytes = 16384;
 
 struct RingArgs {
   WinTab send, recv;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(64) void k_ring(const RingArgs a) {
     for (uint64_t m = m0; m < m1; m += per_round) {
       const uint64_t nm = std::min<uint64_t>(per_round, m1 - m);
       const uint32_t bytes = static_cast<uint32_t>(nm * P);
-      copy16<4>(a.recv.p[peer] + m * P, a.send.p[r] + m * P, bytes, lane, 64);
+      copy16<16>(a.recv.p[peer] + m * P, a.send.p[r] + m * P, bytes, lane, 64);
       wait_vmem();  // this round's payloads are visible at agent scope
       if ((uint64_t)lane < nm) {
         atomic_add_u64(sig, 1ull);  // strong SignalInc of message m + lane

@@ -35,6 +35,7 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr uint32_t kRelaxed = __ATOMIC_RELAXED;
 constexpr int kLoadStream = 2;    // buffer/global cache policy: nt (streaming)
 constexpr int kStoreAgent = 16;   // cache policy: sc1 (coherent at agent scope)
+constexpr int kStoreAgentStream = 18;  // sc1 + nt: coherent at agent scope, streaming
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer descriptor, gfx9 family
 
 // Buffer resource over [base, base + nbytes); accesses outside are dropped by
@@ -47,6 +48,9 @@ __device__ inline v4u load16_stream(const v4u* p) { return __builtin_nontemporal
 
 __device__ inline void store16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, v4u v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreAgent);
+}
+__device__ inline void store16_agent_stream(__amdgpu_buffer_rsrc_t r, uint32_t off, v4u v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreAgentStream);
 }
 __device__ inline void store4_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -83,6 +87,13 @@ __device__ inline uint32_t load_relaxed_u32(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// Coherent 32-bit read at agent scope (sc1: never satisfied by a stale line of
+// an XCD-private L2). Used for small data published earlier in the same kernel
+// by other workgroups, read after the signal that announced it has been seen.
+__device__ inline int32_t load_coherent_i32(const int32_t* p) {
+  return static_cast<int32_t>(load_relaxed_u32(reinterpret_cast<const uint32_t*>(p)));
+}
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // Rolling comparison on `bits`-bit values (GIN page, signals and counters):
 // b has reached a when (b - a) mod 2^bits < 2^(bits-1).
@@ -95,9 +106,12 @@ __device__ inline bool rolling_le(uint64_t a, uint64_t b, int bits) {
 __device__ inline uint64_t now_ns() { return __builtin_amdgcn_s_memrealtime() * 10ull; }  // 100 MHz counter
 
 // Poll a 64-bit word until its low `bits` bits reach `least` (rolling order),
-// then acquire. On timeout sets the error bit and returns false.
+// then acquire (unless `acquire` is false: the caller only reads data that an
+// earlier kernel on the stream wrote, which the kernel boundary already made
+// visible). On timeout sets the error bit and returns false.
 __device__ inline bool wait_reached(const uint64_t* word, uint64_t least, int bits,
-                                    uint64_t timeout_ns, uint32_t* err, uint32_t err_bit) {
+                                    uint64_t timeout_ns, uint32_t* err, uint32_t err_bit,
+                                    bool acquire = true) {
   const uint64_t mask = bits >= 64 ? ~0ull : ((1ull << bits) - 1);
   const uint64_t t0 = now_ns();
   for (;;) {
@@ -109,19 +123,25 @@ __device__ inline bool wait_reached(const uint64_t* word, uint64_t least, int bi
     }
     __builtin_amdgcn_s_sleep(2);
   }
-  acquire_agent();
+  if (acquire) acquire_agent();
   return true;
 }
 
 // Relay of a multi-workgroup put: call from one thread after
 // wg_stores_complete(). Returns true in the workgroup that completes the set
-// of `parts`; that workgroup has acquired the other parts' publications.
-__device__ inline bool relay_arrive(uint32_t* counter, uint32_t parts) {
+// of `parts`; that workgroup has acquired the other parts' publications
+// (unless `acquire` is false: the caller then reads what the other parts
+// wrote only with agent-coherent loads, or not at all).
+// Measured on gfx950: returning atomics on one counter are cheap while every
+// arrival comes from the same XCD, and cost ~0.7 us each when consecutive
+// arrivals come from different XCDs, so callers keep a counter's parts on one
+// XCD or spread them over several counters.
+__device__ inline bool relay_arrive(uint32_t* counter, uint32_t parts, bool acquire = true) {
   if (parts <= 1) return true;
   uint32_t prev = atomic_add_u32(counter, 1u);
   if (prev + 1u != parts) return false;
   __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next use
-  acquire_agent();
+  if (acquire) acquire_agent();
   return true;
 }
 

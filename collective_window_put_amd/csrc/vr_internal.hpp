@@ -8,7 +8,7 @@
 #include <set>
 #include <vector>
 
-#include "../../include/vrcomm.h"
+#include "vrcomm.h"  // include/ is on the include path
 
 namespace vr {
 
@@ -16,8 +16,8 @@ namespace vr {
 // a single put enqueued back to back never share a counter.
 constexpr uint32_t kRelaySingle = 0;       // vr_put / vr_get: 1 counter
 constexpr uint32_t kRelayColl = 64;        // collectives: up to R*R counters
-constexpr uint32_t kRelayDispatch = 64 + VR_MAX_RANKS * VR_MAX_RANKS;  // 2 per source rank
-constexpr uint32_t kRelaySlots = kRelayDispatch + 2 * VR_MAX_RANKS;
+constexpr uint32_t kRelayDispatch = 64 + VR_MAX_RANKS * VR_MAX_RANKS;  // 18 per source rank
+constexpr uint32_t kRelaySlots = kRelayDispatch + 18 * VR_MAX_RANKS;
 
 constexpr uint64_t kDefaultTimeoutNs = 5ull * 1000 * 1000 * 1000;
 
