@@ -20,7 +20,9 @@ the order the pages describe the steps. Sources (cited by page and section):
 * GPUDirect Async survey -- 10100.com/article/158785524. Sections used: the
   motivating MoE token dispatch (opening), and section 4 on GIN's device
   API semantics (signal ordering, batch of puts with one trailing signal,
-  integer signal IDs, the ring-exchange example).
+  integer signal IDs, the ring-exchange example). The MoE combine (each
+  token's expert outputs brought back and mixed by its router weights) is
+  read as the dispatch's inverse; the pages describe only the dispatch.
 
 Modules:
   primitives   state model (windows, 64-bit signals, 56-bit counters) and
@@ -35,8 +37,10 @@ Modules:
 Every function is pinned by tests under ``tests/`` (``-m "not gpu"``)
 against the pages' worked examples, closed forms, library routines,
 brute force and invariants. Parity unpinned: none of the functions here
-is left without a pin; the dispatch result is pinned by brute force,
-a library stable sort and invariants only, since the pages give no
-worked example for it.
+is left without a pin; the dispatch result and its per-entry positions are
+pinned by brute force, a library stable sort and invariants only, and the
+combine by hand-worked binary32 cases (product rounding, k order), a closed
+form checked against torch's bf16 rounding, and the one-hot special case,
+since the pages give no worked example for either.
 """
 from . import primitives, definitions, protocol, ordering  # noqa: F401

@@ -186,6 +186,89 @@ def dispatch_rows_per_rank(topk_idx: np.ndarray, num_experts: int) -> np.ndarray
     return np.bincount(valid // epr, minlength=R).astype(np.int64)
 
 
+def dispatch_positions(topk_idx: np.ndarray, num_experts: int,
+                       capacity_rows: int | None = None) -> np.ndarray:
+    """Receive row of every routing entry: int32 ``[R, T, K]``.
+
+    Same layout as ``dispatch``: entry ``(s, t, k)`` with expert ``e`` lands
+    at rank ``e // (E/R)`` in the place the stable sort on ``(e, s, t)``
+    gives it (two entries of one token naming the same expert keep their k
+    order). -1 marks an entry that is not routed (``e == -1``) or whose row
+    fell past the capacity. This is the metadata the combine step needs to
+    find each token's rows again (reading: the pages stop at the dispatch;
+    the combine is its inverse).
+    """
+    topk_idx = np.asarray(topk_idx)
+    R, T, K = topk_idx.shape
+    epr = num_experts // R
+    entries = []
+    for s in range(R):
+        for t in range(T):
+            for k in range(K):
+                e = int(topk_idx[s, t, k])
+                if e == -1:
+                    continue
+                if not 0 <= e < num_experts:
+                    raise ValueError(f"expert id {e} out of range")
+                entries.append((e, s, t, k))
+    entries.sort()
+    pos = np.full((R, T, K), -1, dtype=np.int32)
+    filled = [0] * R
+    for (e, s, t, k) in entries:
+        d = e // epr
+        if capacity_rows is None or filled[d] < capacity_rows:
+            pos[s, t, k] = filled[d]
+        filled[d] += 1
+    return pos
+
+
+def combine(topk_idx: np.ndarray, weights: np.ndarray, pos: np.ndarray, y_rows,
+            num_experts: int, dtype: str = "bf16") -> np.ndarray:
+    """MoE combine: each token's expert rows brought back and mixed by its weights.
+
+    The inverse step of the dispatch (GPUDirect Async survey, opening
+    section, describes the dispatch; the combine that returns the expert
+    outputs to the token's rank is the plain reading of its other half).
+    For source rank s and token t, with y the expert-output rows of rank
+    ``d = topk[s,t,k] // (E/R)`` laid out like the dispatch's receive rows:
+
+        acc = +0.0
+        for k = 0 .. K-1 (in this order), if the entry has a row:
+            acc = acc + w[s,t,k] * y[d][pos[s,t,k]]
+
+    every product and every sum one IEEE binary32 operation rounded to
+    nearest even (no fused multiply-add); bf16 rows are widened exactly and
+    the result is rounded to bf16 (RNE, NaN -> 0x7FC0); fp32 rows stay fp32.
+    An entry has a row when its expert id is not -1 and its position is not
+    -1. Returns ``[R, T, H]`` (uint16 bf16 bits, or float32).
+    """
+    topk_idx = np.asarray(topk_idx)
+    R, T, K = topk_idx.shape
+    epr = num_experts // R
+    w = np.asarray(weights, dtype=np.float32)
+    pos = np.asarray(pos)
+    if dtype == "bf16":
+        ys = [bf16_bits_to_f32(np.asarray(y, dtype=np.uint16)) for y in y_rows]
+    elif dtype == "f32":
+        ys = [np.asarray(y, dtype=np.float32) for y in y_rows]
+    else:
+        raise ValueError(dtype)
+    H = ys[0].shape[1]
+    out = np.zeros((R, T, H), dtype=np.float32)
+    for s in range(R):
+        for t in range(T):
+            acc = np.zeros(H, dtype=np.float32)
+            for k in range(K):
+                e = int(topk_idx[s, t, k])
+                p = int(pos[s, t, k])
+                if e < 0 or p < 0:
+                    continue
+                prod = w[s, t, k] * ys[e // epr][p]  # float32 * float32 -> float32
+                acc = acc + prod
+            out[s, t] = acc
+    return f32_to_bf16_bits_rne(out) if dtype == "bf16" else out
+
+
 # -- Signal totals -------------------------------------------------------------
 def signal_increment(kind: str, nranks: int) -> int:
     """What one collective adds to every rank's completion signal.

@@ -24,6 +24,10 @@ The programs follow the pages:
   then one strong SignalAdd(rows) per destination.
 * Ring -- GPUDirect Async survey, section 4: each rank puts to its successor
   with a strong SignalInc and a CounterInc per put, then waits.
+* Combine -- the inverse of the dispatch (reading: the survey describes the
+  dispatch; its other half returns each expert row to the token's rank):
+  gets of every routed row, a k-ordered weighted sum, then a SignalInc to
+  every expert rank that its rows have been consumed.
 """
 from __future__ import annotations
 
@@ -407,6 +411,7 @@ class DispatchBuffers:
         self.recv_src = world.register_zeros(max(4, 4 * capacity_rows))
         self.counts = np.zeros((R, self.epr), dtype=np.int32)
         self.overflow = [False] * R
+        self.pos = np.full((R, T, K), -1, dtype=np.int32)  # receive row of each routing entry
 
 
 def dispatch_programs(world: World, b: DispatchBuffers, sig_counts: int, sig_rows: int):
@@ -461,6 +466,10 @@ def dispatch_programs(world: World, b: DispatchBuffers, sig_counts: int, sig_row
                 w.buf(b.stage_src, me)[so * 4:(so + len(toks)) * 4] = tags.view(np.uint8)
 
             yield Local(pack, f"pack e={e}")
+            for i, t in enumerate(toks):
+                for k in range(K):
+                    if b.topk[s, t, k] == e and off[e] + i < b.cap:
+                        b.pos[s, t, k] = off[e] + i
             keep = max(0, min(n, b.cap - int(off[e])))  # rows past the capacity are dropped
             if keep:
                 yield Put(d, b.recv, int(off[e]) * rb, b.stage, so * rb, keep * rb)
@@ -472,6 +481,69 @@ def dispatch_programs(world: World, b: DispatchBuffers, sig_counts: int, sig_row
             if rows_to[d]:
                 yield Signal(d, SignalAdd(sig_rows, rows_to[d], True))
         yield WaitSignal(sig_rows, base_r + my_rows)
+        yield Barrier()
+
+    return [prog(s) for s in range(R)]
+
+
+class CombineBuffers:
+    """Windows one combine needs: expert outputs, per-entry staging, results."""
+
+    def __init__(self, world: World, y_rows, topk_idx: np.ndarray, weights: np.ndarray,
+                 pos: np.ndarray, num_experts: int, dtype: str = "bf16"):
+        R, T, K = topk_idx.shape
+        self.R, self.T, self.K, self.E = R, T, K, num_experts
+        self.epr = num_experts // R
+        self.dtype = dtype
+        self.esize = 2 if dtype == "bf16" else 4
+        yb = [np.ascontiguousarray(y).view(np.uint8) for y in y_rows]
+        self.row_bytes = yb[0].shape[1]
+        cap = max(1, max(b.shape[0] for b in yb))  # symmetric window: every rank the same size
+        yb = [np.concatenate([b, np.zeros((cap - b.shape[0], self.row_bytes), np.uint8)]) for b in yb]
+        self.topk = np.asarray(topk_idx)
+        self.w = np.asarray(weights, dtype=np.float32)
+        self.pos = np.asarray(pos)
+        self.y = world.register([b.reshape(-1).copy() for b in yb])
+        self.stage = world.register_zeros(max(1, T * K * self.row_bytes))
+        self.out = world.register_zeros(max(1, T * self.row_bytes))
+
+
+def combine_programs(world: World, b: CombineBuffers, sig: int):
+    """Combine, step by step: every source rank gets each of its tokens' expert
+    rows from the rank that holds them into a local slot per (token, k), mixes
+    them in k order with the router weights, and then tells every expert rank
+    with a SignalInc that its rows have been read (each expert rank waits for
+    R of them before its rows may change)."""
+    R, T, K, epr, rb = b.R, b.T, b.K, b.epr, b.row_bytes
+
+    def prog(s):
+        base = yield ReadSignal(sig)
+        yield Barrier()
+        for t in range(T):
+            for k in range(K):
+                e, p = int(b.topk[s, t, k]), int(b.pos[s, t, k])
+                if e >= 0 and p >= 0:
+                    yield Get(e // epr, b.y, p * rb, b.stage, (t * K + k) * rb, rb)
+
+        def mix(w, me):
+            from .definitions import bf16_bits_to_f32, f32_to_bf16_bits_rne
+            st = w.buf(b.stage, me).reshape(T, K, rb)
+            out = np.zeros((T, rb // b.esize), dtype=np.float32)
+            for t in range(T):
+                acc = np.zeros(rb // b.esize, dtype=np.float32)
+                for k in range(K):
+                    if b.topk[me, t, k] < 0 or b.pos[me, t, k] < 0:
+                        continue
+                    y = bf16_bits_to_f32(st[t, k].view(np.uint16)) if b.dtype == "bf16" else st[t, k].view(np.float32)
+                    acc = acc + b.w[me, t, k] * y  # one rounded product, one rounded sum
+                out[t] = acc
+            res = f32_to_bf16_bits_rne(out) if b.dtype == "bf16" else out
+            w.buf(b.out, me)[:] = res.view(np.uint8).reshape(-1)
+
+        yield Local(mix, "mix")
+        for d in range(R):
+            yield Signal(d, SignalInc(sig))
+        yield WaitSignal(sig, base + R)
         yield Barrier()
 
     return [prog(s) for s in range(R)]

@@ -273,3 +273,148 @@ def test_dispatch_skips_unrouted_and_flags_capacity():
     assert src[0].tolist() == [(0 << 16) | 0, (0 << 16) | 1]  # third row dropped
     with pytest.raises(ValueError):
         D.dispatch(np.array([[[4]]], dtype=np.int32), np.zeros((1, 1, 1), np.uint16), 4)
+
+
+# -- dispatch positions and combine ------------------------------------------------
+def _positions_by_loops(topk, E, cap=None):
+    """Receive row of every entry by walking rank d's rows in the layout's own
+    nesting (expert, then source, then token, then k)."""
+    R, T, K = topk.shape
+    epr = E // R
+    pos = np.full((R, T, K), -1, dtype=np.int32)
+    for d in range(R):
+        row = 0
+        for e in range(d * epr, (d + 1) * epr):
+            for s in range(R):
+                for t in range(T):
+                    for k in range(K):
+                        if topk[s, t, k] == e:
+                            if cap is None or row < cap:
+                                pos[s, t, k] = row
+                            row += 1
+    return pos
+
+
+def test_dispatch_positions_brute_force_tiny():
+    R, T, K, E = 2, 2, 2, 4
+    pairs = list(itertools.permutations(range(E), K)) + [(-1, 1), (2, -1)]
+    for choice in itertools.product(pairs, repeat=R * T):
+        topk = np.array(choice, dtype=np.int32).reshape(R, T, K)
+        assert np.array_equal(D.dispatch_positions(topk, E), _positions_by_loops(topk, E))
+
+
+def test_dispatch_positions_point_at_the_dispatched_rows():
+    R, T, H, E, K = 4, 120, 4, 16, 3
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=21)
+    topk[np.random.default_rng(2).random(topk.shape) < 0.2] = -1
+    rows, src, _, _ = D.dispatch(topk, x, E)
+    pos = D.dispatch_positions(topk, E)
+    epr = E // R
+    xb = x.reshape(R, T, -1).view(np.uint8)
+    seen = [np.zeros(r.shape[0], dtype=int) for r in rows]
+    for s in range(R):
+        for t in range(T):
+            for k in range(K):
+                e, p = topk[s, t, k], pos[s, t, k]
+                if e < 0:
+                    assert p == -1
+                    continue
+                d = e // epr
+                assert src[d][p] == (s << 16) | t
+                assert np.array_equal(rows[d][p], xb[s, t])
+                seen[d][p] += 1
+    assert all(np.all(c == 1) for c in seen)  # every received row has exactly one entry
+
+
+def test_dispatch_positions_capacity():
+    topk = np.array([[[0, -1], [1, 0]], [[-1, -1], [0, 3]]], dtype=np.int32)  # R=2,T=2,K=2,E=4
+    pos = D.dispatch_positions(topk, 4, capacity_rows=2)
+    # rank 0's rows: e0 (s0,t0), e0 (s0,t1), e0 (s1,t1) dropped, e1 (s0,t1) dropped
+    assert pos.tolist() == [[[0, -1], [-1, 1]], [[-1, -1], [-1, 0]]]
+    assert np.array_equal(pos, _positions_by_loops(topk, 4, cap=2))
+
+
+def _f32(v):
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def _one_token_combine(ws, ys, dtype="f32"):
+    """Helper: R=1, T=1, K=len(ws), one expert per k, rows of one element."""
+    K = len(ws)
+    topk = np.arange(K, dtype=np.int32).reshape(1, 1, K)
+    pos = np.zeros((1, 1, K), dtype=np.int32)
+    pos[0, 0, :] = np.arange(K)
+    y = np.array(ys, dtype=np.float32).reshape(K, 1)
+    w = np.array(ws, dtype=np.float32).reshape(1, 1, K)
+    # one rank owns all K experts; row p of its y is entry k = p
+    return D.combine(topk, w, pos, [y], K, dtype)[0, 0, 0]
+
+
+def test_combine_hand_worked_rounding_each_product():
+    # k0: -1 * (1 + 2^-7); k1: (1 + 2^-20) * (1 + 2^-7) = 1 + 2^-7 + 2^-20 + 2^-27,
+    # rounded to binary32 before the add -> 1 + 2^-7 + 2^-20; the sum is 2^-20.
+    # A fused multiply-add would keep the 2^-27 and give 2^-20 + 2^-27.
+    got = _one_token_combine([1.0, 1.0 + 2.0 ** -20], [-(1.0 + 2.0 ** -7), 1.0 + 2.0 ** -7])
+    assert got == 2.0 ** -20
+
+
+def test_combine_hand_worked_k_order():
+    # 2^24 + 1 rounds (tie to even) back to 2^24, so k order gives 0;
+    # the reverse order would give 1.
+    assert _one_token_combine([1.0, 1.0, 1.0], [2.0 ** 24, 1.0, -(2.0 ** 24)]) == 0.0
+    assert _one_token_combine([1.0, 1.0, 1.0], [-(2.0 ** 24), 1.0, 2.0 ** 24]) == 1.0
+
+
+def test_combine_hand_worked_weights():
+    ws = [0.1, 0.2, 0.7]
+    ys = [3.0, -5.0, 0.25]
+    acc = 0.0
+    for w, y in zip(ws, ys):
+        acc = _f32(acc + _f32(_f32(w) * y))  # each product and sum exact in double, then rounded once
+    assert _one_token_combine(ws, ys) == np.float32(acc)
+
+
+def test_combine_round_trip_is_identity_for_one_hot_weights():
+    R, T, H, E, K = 4, 60, 8, 16, 4
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=22)
+    rows, _, _, _ = D.dispatch(topk, x, E)
+    pos = D.dispatch_positions(topk, E)
+    pick = np.random.default_rng(3).integers(0, K, (R, T))
+    w = np.zeros((R, T, K), dtype=np.float32)
+    w[np.arange(R)[:, None], np.arange(T)[None, :], pick] = 1.0
+    y = [r.view(np.uint16).reshape(r.shape[0], H) for r in rows]  # identity experts
+    out = D.combine(topk, w, pos, y, E)
+    assert np.array_equal(out, x)
+    # distinct expert outputs: a one-hot weight selects exactly the picked entry's row
+    y = W.expert_outputs([r.shape[0] for r in rows], H, seed=5)
+    out = D.combine(topk, w, pos, y, E)
+    epr = E // R
+    for s in range(R):
+        for t in range(T):
+            k = pick[s, t]
+            assert np.array_equal(out[s, t], y[topk[s, t, k] // epr][pos[s, t, k]])
+
+
+def test_combine_unit_weights_give_k_times_x_rounded_like_torch():
+    import torch
+    R, T, H, E, K = 2, 40, 16, 8, 3
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=23)
+    rows, _, _, _ = D.dispatch(topk, x, E)
+    pos = D.dispatch_positions(topk, E)
+    y = [r.view(np.uint16).reshape(r.shape[0], H) for r in rows]
+    out = D.combine(topk, np.ones((R, T, K), np.float32), pos, y, E)
+    # K * x is exact in fp32 for bf16 x; torch rounds it to bf16 independently
+    kx = torch.from_numpy(D.bf16_bits_to_f32(x) * np.float32(K)).to(torch.bfloat16)
+    assert np.array_equal(out, kx.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_combine_skips_entries_without_rows():
+    topk = np.array([[[0, -1], [1, 1]], [[-1, -1], [2, 3]]], dtype=np.int32)  # R=2,T=2,K=2,E=4
+    pos = D.dispatch_positions(topk, 4, capacity_rows=2)
+    y = [np.array([[1.0], [2.0]], np.float32), np.array([[4.0], [8.0]], np.float32)]
+    w = np.full((2, 2, 2), 0.5, np.float32)
+    out = D.combine(topk, w, pos, y, 4, "f32")
+    # rank 0 rows: e0 (0,0) -> row0, e1 (0,1,k0) -> row1, e1 (0,1,k1) dropped (capacity 2)
+    # rank 1 rows: e2 (1,1) -> row0, e3 (1,1) -> row1
+    assert out[:, :, 0].tolist() == [[0.5, 1.0], [0.0, 6.0]]
+    assert np.signbit(out[1, 0, 0]) == False  # noqa: E712 -- a token with no rows is +0.0

@@ -126,3 +126,54 @@ def test_strong_rule_treated_as_weak_is_caught(monkeypatch):
     orig = O._prereqs
     monkeypatch.setattr(O, "_prereqs", lambda n, strong: orig(n, False))
     _fails(TO.test_strong_signal_prefix_property_holds_in_every_state, 3)
+
+
+def test_combine_fused_multiply_add_is_caught(monkeypatch):
+    def fused(topk, weights, pos, y_rows, E, dtype="bf16"):
+        R, T, K = np.asarray(topk).shape
+        epr = E // R
+        ys = [np.asarray(y, np.float64) if dtype == "f32" else D.bf16_bits_to_f32(y).astype(np.float64)
+              for y in y_rows]
+        out = np.zeros((R, T, ys[0].shape[1]), np.float32)
+        for s in range(R):
+            for t in range(T):
+                acc = np.zeros(ys[0].shape[1], np.float32)
+                for k in range(K):
+                    e, p = int(topk[s, t, k]), int(pos[s, t, k])
+                    if e >= 0 and p >= 0:
+                        acc = (acc.astype(np.float64) + np.float64(weights[s, t, k]) * ys[e // epr][p]).astype(np.float32)
+                out[s, t] = acc
+        return D.f32_to_bf16_bits_rne(out) if dtype == "bf16" else out
+    monkeypatch.setattr(D, "combine", fused)
+    _fails(TD.test_combine_hand_worked_rounding_each_product)
+
+
+def test_combine_reversed_k_order_is_caught(monkeypatch):
+    orig = D.combine
+
+    def reversed_k(topk, weights, pos, y_rows, E, dtype="bf16"):
+        return orig(np.asarray(topk)[:, :, ::-1], np.asarray(weights)[:, :, ::-1], np.asarray(pos)[:, :, ::-1],
+                    y_rows, E, dtype)
+    monkeypatch.setattr(D, "combine", reversed_k)
+    _fails(TD.test_combine_hand_worked_k_order)
+
+
+def test_combine_weights_of_wrong_entry_is_caught(monkeypatch):
+    orig = D.combine
+
+    def shifted(topk, weights, pos, y_rows, E, dtype="bf16"):
+        return orig(topk, np.roll(np.asarray(weights), 1, axis=2), pos, y_rows, E, dtype)
+    monkeypatch.setattr(D, "combine", shifted)
+    _fails(TD.test_combine_round_trip_is_identity_for_one_hot_weights)
+
+
+def test_positions_ignoring_source_order_is_caught(monkeypatch):
+    orig = D.dispatch_positions
+
+    def token_first(topk, E, capacity_rows=None):
+        # rows of one expert ordered by token before source: a plausible slip
+        t = np.asarray(topk)
+        return orig(t.transpose(1, 0, 2).copy(), E, capacity_rows).transpose(1, 0, 2) if t.shape[0] == t.shape[1] \
+            else orig(t[::-1].copy(), E, capacity_rows)[::-1]
+    monkeypatch.setattr(D, "dispatch_positions", token_first)
+    _fails(TD.test_dispatch_positions_point_at_the_dispatched_rows)

@@ -237,3 +237,46 @@ def test_deadlock_is_detected_when_a_put_is_missing():
 
     with pytest.raises(Deadlock):
         pr.run(w, [prog(q) for q in range(R)], seed=0)
+
+
+def test_dispatch_protocol_positions_match_definition():
+    for (R, T, H, E, K, seed, cap) in [(4, 37, 8, 16, 3, 0, None), (2, 40, 2, 4, 2, 5, 30)]:
+        topk, x, w, b, cap = _run_dispatch(R, T, H, E, K, seed, cap)
+        assert np.array_equal(b.pos, D.dispatch_positions(topk, E, cap))
+
+
+def _run_combine(R, T, H, E, K, seed, dtype="bf16", every=False):
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    topk[np.random.default_rng(seed).random(topk.shape) < 0.15] = -1
+    weights = W.router_weights(topk, E)
+    pos = D.dispatch_positions(topk, E)
+    y = W.expert_outputs(D.dispatch_rows_per_rank(topk, E), H, seed=seed + 7, dtype=dtype)
+    want = D.combine(topk, weights, pos, y, E, dtype)
+    bufs = []
+
+    def setup():
+        w = World(R)
+        b = pr.CombineBuffers(w, y, topk, weights, pos, E, dtype)
+        bufs.append(b)
+        return w, pr.combine_programs(w, b, 3)
+
+    worlds = pr.distinct_final_states(setup) if every else [pr.run(*setup(), seed=seed)]
+    n = 0
+    for w in worlds:
+        b = bufs[-1]
+        for s in range(R):
+            got = w.buf(b.out, s).view(np.uint16 if dtype == "bf16" else np.float32).reshape(T, H)
+            assert np.array_equal(got, want[s])
+            assert w.sig[s][3] == R  # one SignalInc from every source once its reads are done
+        n += 1
+    return n
+
+
+@pytest.mark.parametrize("R,T,H,E,K,seed,dtype", [(4, 30, 8, 16, 3, 0, "bf16"), (3, 20, 4, 6, 2, 1, "f32"),
+                                                  (8, 16, 4, 64, 8, 2, "bf16")])
+def test_combine_protocol_matches_definition(R, T, H, E, K, seed, dtype):
+    _run_combine(R, T, H, E, K, seed, dtype)
+
+
+def test_combine_every_interleaving_two_ranks():
+    assert _run_combine(2, 2, 2, 4, 2, 9, every=True) == 1

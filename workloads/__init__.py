@@ -123,3 +123,27 @@ def dispatch_inputs(nranks: int, tokens: int, hidden: int, experts: int, topk: i
         idx[r] = np.take_along_axis(part, order, axis=1).astype(np.int32)
         xs[r] = f32_to_bf16_bits_torch(g.standard_normal((tokens, hidden), dtype=np.float32))
     return idx, xs
+
+
+def router_weights(topk_idx: np.ndarray, experts: int, zipf_s: float = 1.1) -> np.ndarray:
+    """Router weight of every routing entry, float32 [R][T][K].
+
+    The probability of the chosen expert under the routing distribution,
+    renormalised over the token's K chosen experts (the usual top-k gate);
+    entries equal to -1 get weight 0.
+    """
+    p = zipf_expert_probs(experts, zipf_s)
+    idx = np.asarray(topk_idx)
+    w = np.where(idx >= 0, p[np.clip(idx, 0, experts - 1)], 0.0)
+    tot = w.sum(axis=2, keepdims=True)
+    return np.divide(w, tot, out=np.zeros_like(w), where=tot > 0).astype(np.float32)
+
+
+def expert_outputs(rows_per_rank, hidden: int, seed: int = 106, dtype: str = "bf16") -> list[np.ndarray]:
+    """Synthetic expert-output rows: rank d holds rows_per_rank[d] rows of
+    ``hidden`` normal(0, 1) values, as bf16 bit patterns (uint16) or float32."""
+    out = []
+    for n, g in zip(rows_per_rank, rank_rngs(seed, len(rows_per_rank))):
+        v = g.standard_normal((int(n), hidden), dtype=np.float32)
+        out.append(f32_to_bf16_bits_torch(v) if dtype == "bf16" else v)
+    return out
