@@ -37,7 +37,7 @@ METRIC = "achieved HBM GB/s (and % of peak) for R-rank AllReduce/AlltoAll/dispat
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "k_allreduce": "allreduce.hip", "k_alltoall": "alltoall.hip", "k_allgather": "allgather.hip",
-    "k_dispatch": "dispatch.hip", "k_ring": "ring.hip",
+    "k_dispatch": "dispatch.hip", "k_combine": "combine.hip", "k_ring": "ring.hip",
 }
 
 
@@ -180,7 +180,7 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
 
 
 # ---- the other workloads ------------------------------------------------------------------------
-ROW_NAMES = ("allreduce_f32", "alltoall", "dispatch", "allgather", "ring")
+ROW_NAMES = ("allreduce_f32", "alltoall", "dispatch", "combine", "allgather", "ring")
 
 
 def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
@@ -192,6 +192,8 @@ def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
         run_alltoall_row(b, reps, rows)
     if "dispatch" in only:
         run_dispatch_row(b, reps, rows)
+    if "combine" in only:
+        run_combine_row(b, reps, rows)
     if "allgather" in only:
         run_allgather_row(b, reps, rows)
     if "ring" in only:
@@ -263,7 +265,7 @@ def run_dispatch_row(b, reps, rows):
     tk = torch.from_numpy(topk).cuda()
     counts = torch.zeros(R, E // R, dtype=torch.int32, device="cuda")
     src = torch.zeros(R, cap, dtype=torch.int32, device="cuda")
-    f = lambda: vr.vr_dispatch(comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, 0, 1, stream=stream)  # noqa
+    f = lambda: vr.vr_dispatch(comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, None, 0, 1, stream=stream)  # noqa
     f()
     nrows = int((topk >= 0).sum())
     bytes_alg = R * T * rb + topk.nbytes + nrows * rb + nrows * 4 + R * (E // R) * 4
@@ -275,6 +277,46 @@ def run_dispatch_row(b, reps, rows):
     vr.vr_comm_destroy(comm)
     del s1, r1, tk, counts, src
 
+
+
+def run_combine_row(b, reps, rows):
+    import workloads as W
+    vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
+    c = W.CONFIGS["c4"]
+    R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
+    topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
+    weights = W.router_weights(topk, E, c["zipf_s"])
+    rb = H * 2
+    cap = R * T * min(K, E // R)
+    comm = comm_for(vr, R, signal_count=4)
+    s1, xv = b.slices(R, T * rb, arrays=[x[r] for r in range(R)])
+    r1, rv = b.slices(R, cap * rb, fill=0)
+    o1, ov = b.slices(R, T * rb, fill=0)
+    xw = vr.vr_window_register(comm, [v.data_ptr() for v in xv], T * rb)
+    yw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], cap * rb)
+    ow = vr.vr_window_register(comm, [v.data_ptr() for v in ov], T * rb)
+    tk = torch.from_numpy(topk).cuda()
+    wt = torch.from_numpy(weights).cuda()
+    counts = torch.zeros(R, E // R, dtype=torch.int32, device="cuda")
+    src = torch.zeros(R, cap, dtype=torch.int32, device="cuda")
+    pos = torch.zeros(R, T, K, dtype=torch.int32, device="cuda")
+    # the dispatched token rows stand in for the expert outputs
+    vr.vr_dispatch(comm, xw, 0, rb, tk, T, K, E, yw, 0, cap, counts, src, pos, 0, 1, stream=stream)
+    f = lambda: vr.vr_combine(comm, yw, 0, cap, rb, vr.VR_DT_BF16, tk, wt, pos, T, K, E, ow, 0, 2,  # noqa: E731
+                              stream=stream)
+    f()
+    nrows = int((topk >= 0).sum())
+    bytes_alg = nrows * rb + R * T * rb + 3 * topk.nbytes
+    rows["combine_r8_t4096_e256_k8"] = row_entry("combine R=8 T=4096 512B E=256 K=8", bytes_alg,
+                                                 b.timed(f, reps, True), "k_combine",
+                                                 "combine_r8_t4096_e256_k8", {"rows": nrows})
+    code, bits = vr.vr_comm_get_async_error(comm)
+    if code != vr.VR_OK:
+        raise RuntimeError(f"device error in the combine: {vr.vr_error_string(code)} bits={bits:#x}")
+    for w in (xw, yw, ow):
+        vr.vr_window_deregister(comm, w)
+    vr.vr_comm_destroy(comm)
+    del s1, r1, o1, tk, wt, counts, src, pos
 
 
 def run_allgather_row(b, reps, rows):

@@ -29,7 +29,7 @@ __all__ = [
     "vr_comm_get_async_error", "vr_comm_query", "vr_window_register", "vr_window_deregister",
     "vr_put", "vr_get", "vr_signal", "vr_signal_wait", "vr_signal_read", "vr_signal_reset",
     "vr_signal_expected", "vr_counter_wait", "vr_counter_read", "vr_counter_reset",
-    "vr_allreduce", "vr_alltoall", "vr_allgather", "vr_dispatch", "vr_ring_exchange",
+    "vr_allreduce", "vr_alltoall", "vr_allgather", "vr_dispatch", "vr_combine", "vr_ring_exchange",
 ]
 
 # The in-tree build; VRCOMM_LIB may name another build of the same library.
@@ -122,7 +122,9 @@ SYMBOLS = {
     "vr_alltoall": (_R, [_P, _P, c_size_t, _P, c_size_t, c_size_t, c_uint32, c_uint32, _P]),
     "vr_allgather": (_R, [_P, _P, c_size_t, _P, c_size_t, c_size_t, c_uint32, c_uint32, _P]),
     "vr_dispatch": (_R, [_P, _P, c_size_t, c_size_t, _P, c_int, c_int, c_int, _P, c_size_t, c_size_t, _P, _P,
-                         c_uint32, c_uint32, c_uint32, _P]),
+                         _P, c_uint32, c_uint32, c_uint32, _P]),
+    "vr_combine": (_R, [_P, _P, c_size_t, c_size_t, c_size_t, c_int, _P, _P, _P, c_int, c_int, c_int, _P,
+                        c_size_t, c_uint32, c_uint32, _P]),
     "vr_ring_exchange": (_R, [_P, _P, _P, c_size_t, c_size_t, c_int, c_uint32, c_uint32, _P, c_uint32, _P]),
 }
 
@@ -297,10 +299,17 @@ def vr_allgather(comm, send, send_off, recv, recv_off, bytes_per_rank, sig=0, fl
 
 
 def vr_dispatch(comm, x, x_off, row_bytes, topk_idx, T, K, num_experts, recv, recv_off, capacity_rows,
-                recv_expert_counts, recv_src, sig_counts, sig_rows, flags=0, stream=None):
+                recv_expert_counts, recv_src, send_pos, sig_counts, sig_rows, flags=0, stream=None):
     _check(lib().vr_dispatch(comm, x, x_off, row_bytes, _ptr(topk_idx), T, K, num_experts, recv, recv_off,
-                             capacity_rows, _ptr(recv_expert_counts), _ptr(recv_src), sig_counts, sig_rows, flags,
-                             _stream(stream)), "vr_dispatch")
+                             capacity_rows, _ptr(recv_expert_counts), _ptr(recv_src), _ptr(send_pos), sig_counts,
+                             sig_rows, flags, _stream(stream)), "vr_dispatch")
+
+
+def vr_combine(comm, y, y_off, y_capacity_rows, row_bytes, dtype, topk_idx, weights, send_pos, T, K, num_experts,
+               out, out_off, sig, flags=0, stream=None):
+    _check(lib().vr_combine(comm, y, y_off, y_capacity_rows, row_bytes, dtype, _ptr(topk_idx), _ptr(weights),
+                            _ptr(send_pos), T, K, num_experts, out, out_off, sig, flags, _stream(stream)),
+           "vr_combine")
 
 
 def vr_ring_exchange(comm, send, recv, put_bytes, puts_per_rank, contexts, sig_base=0, cnt_base=0, litmus=None,

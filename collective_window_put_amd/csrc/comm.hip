@@ -552,7 +552,8 @@ vrResult_t vr_allgather(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t
 
 vrResult_t vr_dispatch(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes, const int32_t* topk,
                        int T, int K, int E, vrWindow_t recv, size_t recv_off, size_t cap, int32_t* counts_out,
-                       int32_t* src_out, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags, void* stream) {
+                       int32_t* src_out, int32_t* send_pos, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags,
+                       void* stream) {
   if (!live(c) || !has_win(c, x) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
   if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
@@ -572,12 +573,37 @@ vrResult_t vr_dispatch(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes,
     if (check_signal_mode(c, d, sig_rows, VR_SIGNAL_ADD) != VR_OK) return VR_ERR_INVALID_USAGE;
   r = ensure_scratch(c, dispatch_scratch_bytes(R, T, E));
   if (r != VR_OK) return r;
-  r = launch_dispatch(c, x, x_off, row_bytes, topk, T, K, E, recv, recv_off, cap, counts_out, src_out, sig_counts,
-                      sig_rows, tc, wait, S(stream));
+  r = launch_dispatch(c, x, x_off, row_bytes, topk, T, K, E, recv, recv_off, cap, counts_out, src_out, send_pos,
+                      sig_counts, sig_rows, tc, wait, S(stream));
   if (r == VR_OK) {
     commit_inc(c, sig_counts, R);
     for (int d = 0; d < R; ++d) note_signal(c, d, sig_rows, VR_SIGNAL_ADD, 0, false);
   }
+  return r;
+}
+
+vrResult_t vr_combine(vrComm_t c, vrWindow_t y, size_t y_off, size_t cap, size_t row_bytes, int dtype,
+                      const int32_t* topk, const float* weights, const int32_t* send_pos, int T, int K, int E,
+                      vrWindow_t out, size_t out_off, uint32_t sig, uint32_t flags, void* stream) {
+  if (!live(c) || !has_win(c, y) || !has_win(c, out)) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
+  const int R = c->nranks;
+  if (dtype != VR_DT_F32 && dtype != VR_DT_BF16) return VR_ERR_INVALID_ARGUMENT;
+  const size_t es = dtype == VR_DT_F32 ? 4 : 2;
+  if (T < 0 || T >= 65536 || K < 1 || K > 64 || E < R || E % R || E > 1024) return VR_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!topk || !weights || !send_pos)) return VR_ERR_INVALID_ARGUMENT;
+  if (row_bytes == 0 || row_bytes > (size_t(1) << 30) || row_bytes % es || y_off % es || out_off % es)
+    return VR_ERR_INVALID_ARGUMENT;
+  if (cap > (size_t(1) << 31)) return VR_ERR_INVALID_ARGUMENT;
+  if (!span_ok(y, y_off, row_bytes * cap) || !span_ok(out, out_off, row_bytes * T)) return VR_ERR_INVALID_ARGUMENT;
+  if (any_overlap(y, y_off, row_bytes * cap, out, out_off, row_bytes * T, R)) return VR_ERR_INVALID_ARGUMENT;
+  const bool wait = !(flags & VR_COLL_NO_WAIT);
+  U64Tab t;
+  vrResult_t r = inc_targets(c, sig, R, wait, &t);
+  if (r != VR_OK) return r;
+  r = launch_combine(c, y, y_off, cap, row_bytes, dtype, topk, weights, send_pos, T, K, E, out, out_off, sig, t,
+                     wait, S(stream));
+  if (r == VR_OK) commit_inc(c, sig, R);
   return r;
 }
 

@@ -62,6 +62,7 @@ struct DispArgs {
   const int32_t* topk;   // [R][T][K]
   int32_t* counts_out;   // [R][E/R]
   int32_t* src_out;      // [R][cap]
+  int32_t* pos_out;      // [R][T][K] receive row of each routing entry, or nullptr
   int32_t* subpfx;       // [R][NB1*kSubs][E]: sub-block prefix within its count block
   int32_t* blktot;       // [R][NB1][E]: rows per expert of each count block
   int32_t* cwin;         // [R][R][E]: rank d's copy of every source's count row
@@ -292,16 +293,25 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
   // final receive rows; each row's source tag
   for (int slot = tid; slot < kSub * K; slot += kThreads) {
     const int tlb = slot / K;  // token within the block
+    if (tlb >= kSub || b2 * kSub + tlb >= a.T) continue;
     const int e = dexp[slot];
-    if (tlb >= kSub || b2 * kSub + tlb >= a.T || e < 0) continue;
+    uint32_t* po = a.pos_out ? reinterpret_cast<uint32_t*>(a.pos_out + ((size_t)s * a.T + b2 * kSub) * K + slot)
+                             : nullptr;
+    if (e < 0) {
+      if (po) store4_agent(po, 0xFFFFFFFFu);
+      continue;
+    }
     const int32_t pos = base[e] + dpos[slot];
     dpos[slot] = pos;
     const int d = e / epr;
-    if ((uint64_t)pos < a.cap)
+    if ((uint64_t)pos < a.cap) {
       store4_agent(reinterpret_cast<uint32_t*>(a.src_out + (size_t)d * a.cap + pos),
                    static_cast<uint32_t>((s << 16) | (b2 * kSub + tlb)));
-    else
+      if (po) store4_agent(po, static_cast<uint32_t>(pos));
+    } else {
       atomic_or_u32(a.err, VR_ASYNC_CAPACITY);
+      if (po) store4_agent(po, 0xFFFFFFFFu);
+    }
   }
   __syncthreads();
   // copy: the wave's 8 token rows, each once per routed expert
@@ -417,8 +427,8 @@ size_t dispatch_scratch_bytes(int R, int T, int E) { return scratch_layout(R, T,
 
 vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t row_bytes, const int32_t* topk, int T,
                            int K, int E, const vrWindow* recv, size_t recv_off, size_t cap, int32_t* counts_out,
-                           int32_t* src_out, uint32_t sig_counts, uint32_t sig_rows, const U64Tab& target_counts,
-                           bool wait, hipStream_t st) {
+                           int32_t* src_out, int32_t* pos_out, uint32_t sig_counts, uint32_t sig_rows,
+                           const U64Tab& target_counts, bool wait, hipStream_t st) {
   DispArgs a;
   const int R = c->nranks;
   for (int r = 0; r < VR_MAX_RANKS; ++r) {
@@ -434,6 +444,7 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.topk = topk;
   a.counts_out = counts_out;
   a.src_out = src_out;
+  a.pos_out = pos_out;
   a.NB1 = std::max(1, (T + kCountBlock - 1) / kCountBlock);
   a.NB2 = a.NB1 * kSubs;
   const Layout l = scratch_layout(R, T, E);

@@ -46,6 +46,22 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t nbytes)
 
 __device__ inline v4u load16_stream(const v4u* p) { return __builtin_nontemporal_load(p); }
 
+// Loads through a pointer the compiler cannot place (read from LDS, say)
+// would be emitted as flat loads, which also count against lgkmcnt and so
+// serialize behind every LDS wait; these name the global address space.
+typedef __attribute__((address_space(1))) const v4u g_v4u;
+typedef __attribute__((address_space(1))) const uint16_t g_u16;
+typedef __attribute__((address_space(1))) const float g_f32;
+__device__ inline v4u load16_stream_global(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<g_v4u*>(reinterpret_cast<uintptr_t>(p)));
+}
+__device__ inline uint16_t load2_global(const void* p) {
+  return *reinterpret_cast<g_u16*>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ inline float load4f_global(const void* p) {
+  return *reinterpret_cast<g_f32*>(reinterpret_cast<uintptr_t>(p));
+}
+
 __device__ inline void store16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, v4u v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreAgent);
 }

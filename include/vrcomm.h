@@ -263,6 +263,10 @@ vrResult_t vr_allgather(vrComm_t comm, vrWindow_t send, size_t send_off, vrWindo
  *   recv, recv_off  rank d's receive rows (window), capacity recv_capacity_rows
  *   recv_expert_counts  device int32 [R][E/R]: rows received per local expert
  *   recv_src        device int32 [R][recv_capacity_rows]: (s << 16) | t per row
+ *   send_pos        device int32 [R][T][K] or NULL: the receive row of every
+ *                   routing entry at rank expert/(E/R), -1 for entries that are
+ *                   not routed or whose row fell past the capacity (the
+ *                   metadata vr_combine uses to find the rows again)
  * Layout of rank d's rows: by expert, then source rank, then token (a stable
  * sort of the routing entries on (expert, source, token)).
  * Method: (1) each rank counts its tokens per expert and puts its count row
@@ -277,8 +281,38 @@ vrResult_t vr_allgather(vrComm_t comm, vrWindow_t send, size_t send_off, vrWindo
 vrResult_t vr_dispatch(vrComm_t comm, vrWindow_t x, size_t x_off, size_t row_bytes,
                        const int32_t* topk_idx, int T, int K, int num_experts, vrWindow_t recv,
                        size_t recv_off, size_t recv_capacity_rows, int32_t* recv_expert_counts,
-                       int32_t* recv_src, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags,
-                       void* stream);
+                       int32_t* recv_src, int32_t* send_pos, uint32_t sig_counts, uint32_t sig_rows,
+                       uint32_t flags, void* stream);
+
+/* MoE combine, the inverse of vr_dispatch (reading: the GDA survey's opening
+ * section describes the dispatch; its other half brings every expert output
+ * back to the token's rank and mixes the K of them with the router weights).
+ *   y, y_off        rank d's expert-output rows (window), y_capacity_rows of
+ *                   row_bytes each, in the dispatch's receive layout: the row
+ *                   for routing entry (s, t, k) is at send_pos[s][t][k]
+ *   dtype           VR_DT_BF16 (rows of bf16) or VR_DT_F32
+ *   topk_idx        device int32 [R][T][K], the routing given to vr_dispatch
+ *   weights         device float [R][T][K], router weights
+ *   send_pos        device int32 [R][T][K], as vr_dispatch wrote it
+ *   out, out_off    rank s's T combined rows (window), row_bytes each
+ * For each source s and token t: acc = +0.0, then for k = 0..K-1 in order,
+ * for entries with a row (expert id and position not -1),
+ * acc = acc + weights[s][t][k] * y[d][send_pos[s][t][k]] with d = expert / (E/R),
+ * every product and sum rounded to binary32 (no fused multiply-add); bf16
+ * rows are widened exactly and the result rounded to bf16 (RNE, NaN ->
+ * 0x7FC0). Each row is read once with a get (GIN page, one-sided transfers);
+ * once source s has read all its rows it applies a SignalInc on `sig` at
+ * every rank d, so each rank's signal rises by R, and unless VR_COLL_NO_WAIT
+ * each rank waits in-kernel for that (its rows may then be overwritten).
+ * Device checks: an expert id outside [-1, E) sets VR_ASYNC_BAD_EXPERT, a
+ * position outside [-1, y_capacity_rows) sets VR_ASYNC_CAPACITY; either entry
+ * is skipped. row_bytes and both offsets must be multiples of the element
+ * size; T < 65536, K in 1..64, num_experts a multiple of R up to 1024; the y
+ * and out ranges must not overlap (VR_ERR_INVALID_ARGUMENT). */
+vrResult_t vr_combine(vrComm_t comm, vrWindow_t y, size_t y_off, size_t y_capacity_rows,
+                      size_t row_bytes, int dtype, const int32_t* topk_idx, const float* weights,
+                      const int32_t* send_pos, int T, int K, int num_experts, vrWindow_t out,
+                      size_t out_off, uint32_t sig, uint32_t flags, void* stream);
 
 /* Ring exchange (GDA survey, section 4, the ring-exchange example): rank r
  * puts puts_per_rank messages of put_bytes each to rank (r+1) mod R, message

@@ -72,7 +72,8 @@ def test_argument_errors_without_gpu(lib):
     assert e.value.code == vr.VR_ERR_INVALID_ARGUMENT
     # handles that were never created are rejected, not dereferenced
     for fn, args in ((vr.vr_comm_destroy, (0x1234,)), (vr.vr_comm_query, (0,)),
-                     (vr.vr_signal_read, (0x10, 0, 0)), (vr.vr_window_deregister, (0x10, 0x20))):
+                     (vr.vr_signal_read, (0x10, 0, 0)), (vr.vr_window_deregister, (0x10, 0x20)),
+                     (vr.vr_combine, (0x10, 0x20, 0, 1, 16, vr.VR_DT_BF16, None, None, None, 1, 1, 8, 0x30, 0, 0, 0, 0))):
         with pytest.raises(vr.VrError) as e:
             fn(*args)
         assert e.value.code == vr.VR_ERR_INVALID_ARGUMENT

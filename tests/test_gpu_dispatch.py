@@ -26,12 +26,13 @@ def _run(topk, x, E, cap=None, repeats=1, x_off=0, recv_off=0):
         tk = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).cuda()
         counts = torch.full((R, E // R), -7, dtype=torch.int32, device="cuda")
         src = torch.full((R, cap), -1, dtype=torch.int32, device="cuda")
+        pos = torch.full((R, T, K), -5, dtype=torch.int32, device="cuda")
         for _ in range(repeats):
-            vr.vr_dispatch(job.comm, xw, x_off, rb, tk, T, K, E, rw, recv_off, cap, counts, src, SIG_COUNTS,
+            vr.vr_dispatch(job.comm, xw, x_off, rb, tk, T, K, E, rw, recv_off, cap, counts, src, pos, SIG_COUNTS,
                            SIG_ROWS)
         out = job.host(rv)
         res = dict(rows=[o[recv_off:].reshape(cap, rb) for o in out], src=src.cpu().numpy(),
-                   counts=counts.cpu().numpy(), sig_counts=[job.sig(d, SIG_COUNTS) for d in range(R)],
+                   counts=counts.cpu().numpy(), pos=pos.cpu().numpy(), sig_counts=[job.sig(d, SIG_COUNTS) for d in range(R)],
                    sig_rows=[job.sig(d, SIG_ROWS) for d in range(R)], err=job.async_error(), cap=cap)
     return res
 
@@ -48,6 +49,8 @@ def _check(res, topk, x, E, repeats=1):
     assert res["sig_counts"] == [repeats * R] * R
     per = D.dispatch_rows_per_rank(topk, E)
     assert res["sig_rows"] == [int(repeats * v) for v in per]
+    assert np.array_equal(res["pos"], D.dispatch_positions(np.where((topk >= -1) & (topk < E), topk, -1), E,
+                                                           res["cap"]))
     return over
 
 
