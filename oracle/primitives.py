@@ -24,6 +24,7 @@ import numpy as np
 SIGNAL_BITS = 64
 COUNTER_BITS = 56
 WINDOW_ALIGNMENT = 4096  # Symmetric-memory page, window registration: required alignment
+WIN_STRICT_ORDERING = 0x02  # window flag a VA signal's window must carry (GIN page, VA signals)
 
 
 class InvalidArgument(ValueError):
@@ -69,6 +70,25 @@ class SignalAdd:
 
 
 @dataclass(frozen=True)
+class VASignalInc:
+    """Remote action on a VA signal: add 1 to the 64-bit word at byte ``offset``
+    of the peer's slice of window ``win`` (GIN page, VA signals: a signal that
+    lives at a (window, offset) pair instead of a preallocated signal slot)."""
+    win: int
+    offset: int
+    strong: bool = True
+
+
+@dataclass(frozen=True)
+class VASignalAdd:
+    """Remote action on a VA signal: add ``value`` to the word at (win, offset)."""
+    win: int
+    offset: int
+    value: int
+    strong: bool = True
+
+
+@dataclass(frozen=True)
 class CounterInc:
     """Local action: add 1 to ``cnt[rank][id]`` once the source has been consumed."""
     id: int
@@ -90,10 +110,17 @@ class World:
         # GIN page, strong and weak signals: SignalInc must not be mixed with
         # other modifications of the same signal unless it is reset in between.
         self._sig_mode = [[None] * signal_count for _ in range(nranks)]
+        self.win_flags: dict[int, int] = {}
+        # GIN page, VA signals: once a word serves as a signal, every access to
+        # it must be a signal operation. (win, rank, offset) -> "inc" / "add"
+        self._va_words: dict[tuple[int, int, int], str | None] = {}
 
     # -- windows -------------------------------------------------------------
-    def register(self, buffers) -> int:
-        """Register one buffer per rank as a symmetric window; returns a handle."""
+    def register(self, buffers, flags: int = 0) -> int:
+        """Register one buffer per rank as a symmetric window; returns a handle.
+
+        ``flags``: ``WIN_STRICT_ORDERING`` marks a window that may hold VA
+        signals (GIN page, VA signals)."""
         bufs = [np.asarray(b) for b in buffers]
         if len(bufs) != self.nranks:
             raise InvalidArgument("one buffer per rank is required")
@@ -108,6 +135,7 @@ class World:
         h = self._next_win
         self._next_win += 1
         self.windows[h] = views
+        self.win_flags[h] = flags
         return h
 
     def register_zeros(self, nbytes: int) -> int:
@@ -117,6 +145,8 @@ class World:
         if win not in self.windows:
             raise InvalidArgument("unknown window")
         del self.windows[win]
+        del self.win_flags[win]
+        self._va_words = {k: v for k, v in self._va_words.items() if k[0] != win}
 
     def buf(self, win: int, rank: int) -> np.ndarray:
         self._check_rank(rank)
@@ -154,7 +184,50 @@ class World:
             if isinstance(action, SignalAdd) and not 0 <= action.value < (1 << 64):
                 raise InvalidArgument("SignalAdd value must fit in 64 bits")
             return
+        if isinstance(action, (VASignalInc, VASignalAdd)):
+            self._check_va(peer, action.win, action.offset)
+            if isinstance(action, VASignalAdd) and not 0 <= action.value < (1 << 64):
+                raise InvalidArgument("SignalAdd value must fit in 64 bits")
+            return
         raise InvalidArgument(f"not a remote action: {action!r}")
+
+    # -- VA signals ----------------------------------------------------------
+    def _check_va(self, rank: int, win: int, offset: int) -> None:
+        """A VA signal word: 8 bytes, 8-byte aligned, inside a strict-ordering window."""
+        self._span(win, rank, offset, 8)
+        if offset % 8:
+            raise InvalidArgument("a VA signal word must be 8-byte aligned")
+        if not self.win_flags[win] & WIN_STRICT_ORDERING:
+            raise InvalidUsage("VA signals need a window registered with strict ordering")
+
+    def _va_value(self, rank: int, win: int, offset: int) -> int:
+        return int(self.buf(win, rank)[offset:offset + 8].view("<u8")[0])
+
+    def _set_va_value(self, rank: int, win: int, offset: int, v: int) -> None:
+        self.buf(win, rank)[offset:offset + 8] = np.array([v], dtype="<u8").view(np.uint8)
+
+    def _check_plain_access(self, win: int, rank: int, off: int, n: int) -> None:
+        """Plain data movement must not touch a word in use as a VA signal."""
+        for (w, r, o) in self._va_words:
+            if w == win and r == rank and n > 0 and o < off + n and off < o + 8:
+                raise InvalidUsage("a VA signal word may only be accessed by signal operations")
+
+    def read_va_signal(self, rank: int, win: int, offset: int, bits: int = SIGNAL_BITS) -> int:
+        self._check_va(rank, win, offset)
+        if not 1 <= bits <= SIGNAL_BITS:
+            raise InvalidArgument("bits out of range")
+        self._va_words.setdefault((win, rank, offset), None)
+        return self._va_value(rank, win, offset) & ((1 << bits) - 1)
+
+    def va_signal_reached(self, rank: int, win: int, offset: int, least: int, bits: int = SIGNAL_BITS) -> bool:
+        m = (1 << bits) - 1
+        return rolling_le(least & m, self.read_va_signal(rank, win, offset, bits), bits)
+
+    def reset_va_signal(self, rank: int, win: int, offset: int) -> None:
+        """Store 0 in the word; it stays a signal, its Inc/Add mode ends."""
+        self._check_va(rank, win, offset)
+        self._set_va_value(rank, win, offset, 0)
+        self._va_words[(win, rank, offset)] = None
 
     def _validate_local(self, rank: int, action) -> None:
         if action is None:
@@ -169,6 +242,17 @@ class World:
         if action is None:
             return
         self._validate_remote(peer, action)
+        if isinstance(action, (VASignalInc, VASignalAdd)):
+            key = (action.win, peer, action.offset)
+            mode = "inc" if isinstance(action, VASignalInc) else "add"
+            cur = self._va_words.get(key)
+            if cur is not None and cur != mode:
+                raise InvalidUsage("SignalInc mixed with SignalAdd on one signal without a reset")
+            self._va_words[key] = mode
+            inc = 1 if mode == "inc" else action.value
+            v = self._va_value(peer, action.win, action.offset)
+            self._set_va_value(peer, action.win, action.offset, (v + inc) % (1 << SIGNAL_BITS))
+            return
         mode = "inc" if isinstance(action, SignalInc) else "add"
         cur = self._sig_mode[peer][action.id]
         if cur is not None and cur != mode:
@@ -199,6 +283,8 @@ class World:
         self._check_rank(peer)
         s = self._span(src, rank, soff, nbytes)
         d = self._span(dst, peer, doff, nbytes)
+        self._check_plain_access(src, rank, soff, nbytes)
+        self._check_plain_access(dst, peer, doff, nbytes)
         self._validate_remote(peer, remote)
         self._validate_local(rank, local)
         data = s.copy()
@@ -218,6 +304,8 @@ class World:
         self._check_rank(peer)
         s = self._span(remote_win, peer, roff, nbytes)
         d = self._span(local_win, rank, loff, nbytes)
+        self._check_plain_access(remote_win, peer, roff, nbytes)
+        self._check_plain_access(local_win, rank, loff, nbytes)
         self._validate_local(rank, local)
         data = s.copy()
         d[...] = data

@@ -104,6 +104,21 @@ class ResetSignal:
 
 
 @dataclass
+class ReadVASignal:
+    win: int
+    offset: int
+    bits: int = SIGNAL_BITS
+
+
+@dataclass
+class WaitVASignal:
+    win: int
+    offset: int
+    least: int
+    bits: int = SIGNAL_BITS
+
+
+@dataclass
 class Barrier:
     """Every unfinished rank must arrive before any of them continues."""
 
@@ -148,6 +163,8 @@ class Sim:
             return w.signal_reached(r, op.id, op.least, op.bits)
         if isinstance(op, WaitCounter):
             return w.counter_reached(r, op.id, op.least, op.bits)
+        if isinstance(op, WaitVASignal):
+            return w.va_signal_reached(r, op.win, op.offset, op.least, op.bits)
         if isinstance(op, Barrier):
             live = [q for q in range(len(self.pending)) if self.pending[q] is not None]
             return all(isinstance(self.pending[q], Barrier) for q in live)
@@ -172,7 +189,10 @@ class Sim:
         elif isinstance(op, ReadCounter):
             result = w.read_counter(r, op.id, op.bits)
             self.reads[r].append(result)
-        elif isinstance(op, (WaitSignal, WaitCounter)):
+        elif isinstance(op, ReadVASignal):
+            result = w.read_va_signal(r, op.win, op.offset, op.bits)
+            self.reads[r].append(result)
+        elif isinstance(op, (WaitSignal, WaitCounter, WaitVASignal)):
             pass
         elif isinstance(op, ResetSignal):
             w.reset_signal(r, op.id)

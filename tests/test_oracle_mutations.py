@@ -177,3 +177,28 @@ def test_positions_ignoring_source_order_is_caught(monkeypatch):
             else orig(t[::-1].copy(), E, capacity_rows)[::-1]
     monkeypatch.setattr(D, "dispatch_positions", token_first)
     _fails(TD.test_dispatch_positions_point_at_the_dispatched_rows)
+
+
+def test_va_signal_big_endian_word_is_caught(monkeypatch):
+    from oracle.primitives import World
+
+    def get_be(self, rank, win, offset):
+        return int(self.buf(win, rank)[offset:offset + 8].view(">u8")[0])
+
+    def set_be(self, rank, win, offset, v):
+        self.buf(win, rank)[offset:offset + 8] = np.array([v], dtype=">u8").view(np.uint8)
+    monkeypatch.setattr(World, "_va_value", get_be)
+    monkeypatch.setattr(World, "_set_va_value", set_be)
+    _fails(TP.test_va_signal_word_is_little_endian_uint64_and_wraps)
+
+
+def test_va_word_overlap_off_by_one_is_caught(monkeypatch):
+    from oracle.primitives import World, InvalidUsage
+
+    def loose(self, win, rank, off, n):
+        for (w, r, o) in self._va_words:
+            if w == win and r == rank and n > 0 and o < off + n - 1 and off < o + 7:
+                raise InvalidUsage("overlap")
+    monkeypatch.setattr(World, "_check_plain_access", loose)
+    with pytest.raises(pytest.fail.Exception):
+        TP.test_plain_access_to_a_va_signal_word_is_refused()

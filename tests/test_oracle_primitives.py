@@ -140,3 +140,103 @@ def test_argument_errors():
         w.register([np.zeros(4, np.uint8), np.zeros(8, np.uint8)])
     # a failed put changes nothing
     assert w.sig == [[0, 0], [0, 0]] and w.cnt == [[0], [0]]
+
+
+# -- VA signals (GIN page, VA signals) ------------------------------------------------
+from oracle.primitives import VASignalAdd, VASignalInc, WIN_STRICT_ORDERING, InvalidUsage  # noqa: E402
+
+
+def _va_world(R=2, nbytes=64, flags=WIN_STRICT_ORDERING):
+    w = World(R)
+    win = w.register([np.zeros(nbytes, np.uint8) for _ in range(R)], flags=flags)
+    data = w.register_zeros(nbytes)
+    return w, win, data
+
+
+def test_va_signal_counts_like_an_id_signal():
+    # the same sequence of actions on an id signal and on a VA word gives the same values
+    w, win, data = _va_world()
+    seq = [VASignalInc(win, 16), VASignalInc(win, 16), VASignalInc(win, 16)]
+    for a in seq:
+        w.signal(0, 1, a)
+        w.signal(0, 1, SignalInc(3))
+        assert w.read_va_signal(1, win, 16) == w.read_signal(1, 3)
+    w2, win2, _ = _va_world()
+    for v in (5, 0, (1 << 64) - 1, 7):
+        w2.signal(1, 0, VASignalAdd(win2, 8, v))
+        w2.signal(1, 0, SignalAdd(2, v))
+        assert w2.read_va_signal(0, win2, 8) == w2.read_signal(0, 2)
+
+
+def test_va_signal_word_is_little_endian_uint64_and_wraps():
+    w, win, _ = _va_world()
+    w.signal(0, 0, VASignalAdd(win, 24, 0x0102030405060708))
+    assert w.buf(win, 0)[24:32].tolist() == [8, 7, 6, 5, 4, 3, 2, 1]
+    assert w.buf(win, 0)[:24].tolist() == [0] * 24 and w.buf(win, 1).tolist() == [0] * 64
+    w.reset_va_signal(0, win, 24)
+    w.signal(0, 0, VASignalAdd(win, 24, (1 << 64) - 3))
+    w.signal(0, 0, VASignalAdd(win, 24, 5))
+    assert w.read_va_signal(0, win, 24) == 2
+    assert w.va_signal_reached(0, win, 24, (1 << 64) - 1)  # rolling compare across the wrap
+    assert w.read_va_signal(0, win, 24, bits=1) == 0
+
+
+def test_va_signal_rules():
+    w, win, data = _va_world()
+    with pytest.raises(InvalidUsage):
+        w2, plain2, _ = _va_world(flags=0)
+        w2.signal(0, 1, VASignalInc(plain2, 0))
+    with pytest.raises(InvalidArgument):
+        w.signal(0, 1, VASignalInc(win, 4))  # not 8-byte aligned
+    with pytest.raises(InvalidArgument):
+        w.signal(0, 1, VASignalInc(win, 64))  # past the window
+    w.signal(0, 1, VASignalInc(win, 32))
+    with pytest.raises(InvalidUsage):
+        w.signal(0, 1, VASignalAdd(win, 32, 2))  # Inc and Add mixed without a reset
+    w.reset_va_signal(1, win, 32)
+    w.signal(0, 1, VASignalAdd(win, 32, 2))
+    assert w.read_va_signal(1, win, 32) == 2
+
+
+def test_plain_access_to_a_va_signal_word_is_refused():
+    w, win, data = _va_world()
+    w.signal(0, 1, VASignalInc(win, 32))
+    with pytest.raises(InvalidUsage):
+        w.put(0, 1, win, 28, data, 0, 8)       # overlaps the word's first bytes
+    with pytest.raises(InvalidUsage):
+        w.get(0, 1, win, 36, data, 0, 4)       # reads its last bytes
+    with pytest.raises(InvalidUsage):
+        w.put(0, 1, win, 25, data, 0, 8)       # only the word's first byte
+    with pytest.raises(InvalidUsage):
+        w.get(0, 1, win, 39, data, 0, 1)       # only its last byte
+    w.put(0, 1, win, 24, data, 0, 8)           # the 8 bytes before it are plain data
+    w.put(0, 1, win, 40, data, 0, 24)          # and so is everything after it
+    w.put(0, 0, win, 32, data, 0, 8)           # the same offset on another rank is not a signal
+    assert w.read_va_signal(1, win, 32) == 1
+
+
+def test_va_signal_put_then_wait_every_interleaving():
+    from oracle import protocol as pr
+    payload = np.arange(16, dtype=np.uint8)
+
+    def setup():
+        w = World(2)
+        win = w.register([np.zeros(16, np.uint8)] * 2, flags=WIN_STRICT_ORDERING)
+        src = w.register([payload.copy(), payload.copy() + 100])
+        dst = w.register_zeros(16)
+        seen = []
+
+        def prog(r):
+            if r == 0:
+                yield pr.Put(1, dst, 0, src, 0, 16, VASignalInc(win, 8))
+            else:
+                yield pr.WaitVASignal(win, 8, 1)
+                seen.append(w.buf(dst, 1).copy())
+        setup.seen = seen
+        return w, [prog(0), prog(1)]
+
+    n = 0
+    for w in pr.all_runs(setup):
+        n += 1
+    assert n >= 1
+    assert all(np.array_equal(s, payload) for s in setup.seen)
