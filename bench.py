@@ -354,7 +354,7 @@ def run_ring_row(b, reps, rows):
     sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], P * pb)
     rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], P * pb)
     lit = torch.zeros(2, dtype=torch.int64, device="cuda")
-    f = lambda: vr.vr_ring_exchange(comm, sw, rw, pb, P, C, 0, 0, lit, stream=stream)  # noqa: E731
+    f = lambda: vr.vr_ring_exchange(comm, sw, rw, pb, P, C, 0, 0, litmus=lit, stream=stream)  # noqa: E731
     f()
     t = b.timed(f, reps, True)
     med = float(np.median(t))

@@ -51,6 +51,7 @@ VR_WIN_COLL_SYMMETRIC = 0x1
 VR_WIN_STRICT_ORDERING = 0x2
 VR_WIN_REQUIRED_ALIGNMENT = 4096
 VR_ACTION_NONE, VR_SIGNAL_INC, VR_SIGNAL_ADD, VR_COUNTER_INC = 0, 1, 2, 3
+VR_VA_SIGNAL_INC, VR_VA_SIGNAL_ADD = 4, 5
 VR_DT_F32, VR_DT_BF16 = 0, 1
 VR_OP_SUM = 0
 VR_COLL_NO_WAIT = 0x1
@@ -75,7 +76,7 @@ class vrCommRequirements(Structure):
 
 class vrRemoteAction(Structure):
     _fields_ = [("kind", c_uint32), ("id", c_uint32), ("value", c_uint64), ("strong", c_uint32),
-                ("reserved", c_uint32)]
+                ("reserved", c_uint32), ("window", c_void_p), ("offset", c_uint64)]
 
 
 class vrLocalAction(Structure):
@@ -83,11 +84,19 @@ class vrLocalAction(Structure):
 
 
 def SignalInc(sig_id: int, strong: bool = True) -> vrRemoteAction:
-    return vrRemoteAction(VR_SIGNAL_INC, sig_id, 0, int(strong), 0)
+    return vrRemoteAction(VR_SIGNAL_INC, sig_id, 0, int(strong), 0, None, 0)
 
 
 def SignalAdd(sig_id: int, value: int, strong: bool = True) -> vrRemoteAction:
-    return vrRemoteAction(VR_SIGNAL_ADD, sig_id, value, int(strong), 0)
+    return vrRemoteAction(VR_SIGNAL_ADD, sig_id, value, int(strong), 0, None, 0)
+
+
+def VASignalInc(window, offset: int, strong: bool = True) -> vrRemoteAction:
+    return vrRemoteAction(VR_VA_SIGNAL_INC, 0, 0, int(strong), 0, window, offset)
+
+
+def VASignalAdd(window, offset: int, value: int, strong: bool = True) -> vrRemoteAction:
+    return vrRemoteAction(VR_VA_SIGNAL_ADD, 0, value, int(strong), 0, window, offset)
 
 
 def CounterInc(cnt_id: int) -> vrLocalAction:
@@ -125,7 +134,11 @@ SYMBOLS = {
                          _P, c_uint32, c_uint32, c_uint32, _P]),
     "vr_combine": (_R, [_P, _P, c_size_t, c_size_t, c_size_t, c_int, _P, _P, _P, c_int, c_int, c_int, _P,
                         c_size_t, c_uint32, c_uint32, _P]),
-    "vr_ring_exchange": (_R, [_P, _P, _P, c_size_t, c_size_t, c_int, c_uint32, c_uint32, _P, c_uint32, _P]),
+    "vr_ring_exchange": (_R, [_P, _P, _P, c_size_t, c_size_t, c_int, c_uint32, c_uint32, _P, c_size_t, _P,
+                              c_uint32, _P]),
+    "vr_va_signal_wait": (_R, [_P, _P, c_int, c_size_t, c_uint64, c_int, c_uint64, _P]),
+    "vr_va_signal_read": (_R, [_P, _P, c_int, c_size_t, c_int, POINTER(c_uint64)]),
+    "vr_va_signal_reset": (_R, [_P, _P, c_int, c_size_t, _P]),
 }
 
 _lib = None
@@ -263,6 +276,21 @@ def vr_signal_reset(comm, rank, sig_id, stream=None):
     _check(lib().vr_signal_reset(comm, rank, sig_id, _stream(stream)), "vr_signal_reset")
 
 
+def vr_va_signal_wait(comm, window, rank, offset, least, bits=64, timeout_ns=0, stream=None):
+    _check(lib().vr_va_signal_wait(comm, window, rank, offset, least, bits, timeout_ns, _stream(stream)),
+           "vr_va_signal_wait")
+
+
+def vr_va_signal_read(comm, window, rank, offset, bits=64) -> int:
+    out = c_uint64()
+    _check(lib().vr_va_signal_read(comm, window, rank, offset, bits, ctypes.byref(out)), "vr_va_signal_read")
+    return out.value
+
+
+def vr_va_signal_reset(comm, window, rank, offset, stream=None):
+    _check(lib().vr_va_signal_reset(comm, window, rank, offset, _stream(stream)), "vr_va_signal_reset")
+
+
 def vr_signal_expected(comm, rank, sig_id) -> int:
     out = c_uint64()
     _check(lib().vr_signal_expected(comm, rank, sig_id, ctypes.byref(out)), "vr_signal_expected")
@@ -312,7 +340,8 @@ def vr_combine(comm, y, y_off, y_capacity_rows, row_bytes, dtype, topk_idx, weig
            "vr_combine")
 
 
-def vr_ring_exchange(comm, send, recv, put_bytes, puts_per_rank, contexts, sig_base=0, cnt_base=0, litmus=None,
-                     flags=0, stream=None):
+def vr_ring_exchange(comm, send, recv, put_bytes, puts_per_rank, contexts, sig_base=0, cnt_base=0, sig_window=None,
+                     sig_window_off=0, litmus=None, flags=0, stream=None):
     _check(lib().vr_ring_exchange(comm, send, recv, put_bytes, puts_per_rank, contexts, sig_base, cnt_base,
-                                  _ptr(litmus) or None, flags, _stream(stream)), "vr_ring_exchange")
+                                  sig_window, sig_window_off, _ptr(litmus) or None, flags, _stream(stream)),
+           "vr_ring_exchange")

@@ -65,6 +65,26 @@ vrResult_t hip_ok(hipError_t e) { return e == hipSuccess ? VR_OK : VR_ERR_HIP; }
 
 size_t sidx(const vrComm* c, int rank, uint32_t id) { return (size_t)rank * c->req.signal_count + id; }
 
+// Whether [off, off + n) of rank's slice (any rank when rank < 0) touches a
+// word in use as a VA signal: such words are accessed by signal operations
+// only (GIN page, VA signals).
+bool va_touch(const vrWindow* w, int rank, size_t off, size_t n) {
+  if (!n || w->va_words.empty()) return false;
+  for (const auto& kv : w->va_words) {
+    const uint64_t o = kv.first.second;
+    if ((rank < 0 || kv.first.first == rank) && o < off + n && off < o + 8) return true;
+  }
+  return false;
+}
+// A VA signal word: 8-byte aligned, inside the window, which carries strict ordering.
+vrResult_t check_va_word(vrComm* c, const vrWindow* w, size_t off) {
+  if (!has_win(c, const_cast<vrWindow*>(w))) return VR_ERR_INVALID_ARGUMENT;
+  if (off % 8 || !span_ok(w, off, 8)) return VR_ERR_INVALID_ARGUMENT;
+  if (!(w->flags & VR_WIN_STRICT_ORDERING)) return VR_ERR_INVALID_USAGE;
+  return VR_OK;
+}
+bool is_va(uint32_t kind) { return kind == VR_VA_SIGNAL_INC || kind == VR_VA_SIGNAL_ADD; }
+
 // Checks that a signal action may be applied (Inc/Add not mixed since the
 // last reset: GIN page, strong and weak signals).
 vrResult_t check_signal_mode(const vrComm* c, int peer, uint32_t id, uint32_t kind) {
@@ -82,9 +102,27 @@ void note_signal(vrComm* c, int peer, uint32_t id, uint32_t kind, uint64_t amoun
 vrResult_t check_remote(vrComm* c, int peer, const vrRemoteAction& a) {
   if (a.reserved) return VR_ERR_INVALID_ARGUMENT;
   if (a.kind == VR_ACTION_NONE) return VR_OK;
+  if (is_va(a.kind)) {
+    vrResult_t r = check_va_word(c, a.window, a.offset);
+    if (r != VR_OK) return r;
+    const auto it = a.window->va_words.find({peer, a.offset});
+    const uint8_t want = a.kind == VR_VA_SIGNAL_INC ? 1 : 2;
+    return (it != a.window->va_words.end() && it->second && it->second != want) ? VR_ERR_INVALID_USAGE : VR_OK;
+  }
   if (a.kind != VR_SIGNAL_INC && a.kind != VR_SIGNAL_ADD) return VR_ERR_INVALID_ARGUMENT;
   if (a.id >= c->req.signal_count) return VR_ERR_INVALID_ARGUMENT;
   return check_signal_mode(c, peer, a.id, a.kind);
+}
+// The word a remote action adds to, and how much.
+uint64_t* remote_word(vrComm* c, int peer, const vrRemoteAction& a, uint64_t* add) {
+  *add = (a.kind == VR_SIGNAL_INC || a.kind == VR_VA_SIGNAL_INC) ? 1 : a.value;
+  if (is_va(a.kind)) return reinterpret_cast<uint64_t*>(a.window->base[peer] + a.offset);
+  return c->sig + sidx(c, peer, a.id);
+}
+// Host bookkeeping once a remote action has been enqueued.
+void note_remote(vrComm* c, int peer, const vrRemoteAction& a, uint64_t add) {
+  if (is_va(a.kind)) a.window->va_words[{peer, a.offset}] = a.kind == VR_VA_SIGNAL_INC ? 1 : 2;
+  else note_signal(c, peer, a.id, a.kind, add, true);
 }
 vrResult_t check_local(vrComm* c, const vrLocalAction& a) {
   if (a.kind == VR_ACTION_NONE) return VR_OK;
@@ -366,15 +404,18 @@ vrResult_t vr_put(vrComm_t c, int ctx, int rank, int peer, vrWindow_t dst, size_
   vrResult_t r = check_remote(c, peer, remote);
   if (r != VR_OK) return r;
   if ((r = check_local(c, local)) != VR_OK) return r;
+  if (va_touch(dst, peer, dst_off, bytes) || va_touch(src, rank, src_off, bytes)) return VR_ERR_INVALID_USAGE;
+  if (is_va(remote.kind) && ((remote.window == dst && overlap(dst->base[peer] + dst_off, bytes,
+                                                               dst->base[peer] + remote.offset, 8)) ||
+                             (remote.window == src && overlap(src->base[rank] + src_off, bytes,
+                                                               src->base[peer] + remote.offset, 8))))
+    return VR_ERR_INVALID_USAGE;  // the put would move the signal word's own bytes
   uint64_t* sig = nullptr;
   uint64_t add = 0;
-  if (remote.kind != VR_ACTION_NONE) {
-    sig = c->sig + sidx(c, peer, remote.id);
-    add = remote.kind == VR_SIGNAL_INC ? 1 : remote.value;
-  }
+  if (remote.kind != VR_ACTION_NONE) sig = remote_word(c, peer, remote, &add);
   uint64_t* cnt = local.kind == VR_COUNTER_INC ? c->cnt + (size_t)rank * c->req.counter_count + local.id : nullptr;
   r = enqueue_copy(c, dst->base[peer] + dst_off, src->base[rank] + src_off, bytes, sig, add, cnt, S(stream));
-  if (r == VR_OK && sig) note_signal(c, peer, remote.id, remote.kind, add, true);
+  if (r == VR_OK && sig) note_remote(c, peer, remote, add);
   return r;
 }
 
@@ -386,6 +427,8 @@ vrResult_t vr_get(vrComm_t c, int ctx, int rank, int peer, vrWindow_t remote, si
   if (!span_ok(remote, remote_off, bytes) || !span_ok(localw, local_off, bytes)) return VR_ERR_INVALID_ARGUMENT;
   vrResult_t r = check_local(c, local);
   if (r != VR_OK) return r;
+  if (va_touch(remote, peer, remote_off, bytes) || va_touch(localw, rank, local_off, bytes))
+    return VR_ERR_INVALID_USAGE;
   uint64_t* cnt = local.kind == VR_COUNTER_INC ? c->cnt + (size_t)rank * c->req.counter_count + local.id : nullptr;
   return enqueue_copy(c, localw->base[rank] + local_off, remote->base[peer] + remote_off, bytes, nullptr, 0,
                       cnt, S(stream));
@@ -397,10 +440,11 @@ vrResult_t vr_signal(vrComm_t c, int ctx, int rank, int peer, vrRemoteAction rem
   if (remote.kind == VR_ACTION_NONE) return VR_ERR_INVALID_ARGUMENT;
   vrResult_t r = check_remote(c, peer, remote);
   if (r != VR_OK) return r;
-  const uint64_t add = remote.kind == VR_SIGNAL_INC ? 1 : remote.value;
-  hipLaunchKernelGGL(k_signal, dim3(1), dim3(64), 0, S(stream), c->sig + sidx(c, peer, remote.id), add);
+  uint64_t add = 0;
+  uint64_t* word = remote_word(c, peer, remote, &add);
+  hipLaunchKernelGGL(k_signal, dim3(1), dim3(64), 0, S(stream), word, add);
   r = hip_ok(hipGetLastError());
-  if (r == VR_OK) note_signal(c, peer, remote.id, remote.kind, add, true);
+  if (r == VR_OK) note_remote(c, peer, remote, add);
   return r;
 }
 
@@ -416,6 +460,22 @@ vrResult_t vr_signal_wait(vrComm_t c, int rank, uint32_t id, uint64_t least, int
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count) return VR_ERR_INVALID_ARGUMENT;
   if (bits < 1 || bits > VR_SIGNAL_BITS) return VR_ERR_INVALID_ARGUMENT;
   return wait_word(c, c->sig + sidx(c, rank, id), least, bits, timeout_ns, stream);
+}
+
+static vrResult_t va_prepare(vrComm* c, vrWindow* w, int rank, size_t off) {
+  if (!live(c) || !rank_ok(c, rank)) return VR_ERR_INVALID_ARGUMENT;
+  vrResult_t r = check_va_word(c, w, off);
+  if (r != VR_OK) return r;
+  w->va_words.emplace(std::make_pair(rank, (uint64_t)off), 0);  // a signal from now on
+  return VR_OK;
+}
+
+vrResult_t vr_va_signal_wait(vrComm_t c, vrWindow_t w, int rank, size_t off, uint64_t least, int bits,
+                             uint64_t timeout_ns, void* stream) {
+  if (bits < 1 || bits > VR_SIGNAL_BITS) return VR_ERR_INVALID_ARGUMENT;
+  vrResult_t r = va_prepare(c, w, rank, off);
+  if (r != VR_OK) return r;
+  return wait_word(c, reinterpret_cast<uint64_t*>(w->base[rank] + off), least, bits, timeout_ns, stream);
 }
 
 vrResult_t vr_counter_wait(vrComm_t c, int rank, uint32_t id, uint64_t least, int bits, uint64_t timeout_ns,
@@ -436,6 +496,22 @@ vrResult_t vr_signal_read(vrComm_t c, int rank, uint32_t id, int bits, uint64_t*
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count || !out) return VR_ERR_INVALID_ARGUMENT;
   if (bits < 1 || bits > VR_SIGNAL_BITS) return VR_ERR_INVALID_ARGUMENT;
   return read_word(c->sig + sidx(c, rank, id), bits, out);
+}
+
+vrResult_t vr_va_signal_read(vrComm_t c, vrWindow_t w, int rank, size_t off, int bits, uint64_t* out) {
+  if (!out || bits < 1 || bits > VR_SIGNAL_BITS) return VR_ERR_INVALID_ARGUMENT;
+  vrResult_t r = va_prepare(c, w, rank, off);
+  if (r != VR_OK) return r;
+  return read_word(reinterpret_cast<uint64_t*>(w->base[rank] + off), bits, out);
+}
+
+vrResult_t vr_va_signal_reset(vrComm_t c, vrWindow_t w, int rank, size_t off, void* stream) {
+  vrResult_t r = va_prepare(c, w, rank, off);
+  if (r != VR_OK) return r;
+  hipLaunchKernelGGL(k_store0, dim3(1), dim3(64), 0, S(stream), reinterpret_cast<uint64_t*>(w->base[rank] + off));
+  r = hip_ok(hipGetLastError());
+  if (r == VR_OK) w->va_words[{rank, (uint64_t)off}] = 0;
+  return r;
 }
 
 vrResult_t vr_counter_read(vrComm_t c, int rank, uint32_t id, int bits, uint64_t* out) {
@@ -506,6 +582,7 @@ vrResult_t vr_allreduce(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t
   const size_t n = count * es;
   if (!span_ok(send, send_off, n) || !span_ok(recv, recv_off, n)) return VR_ERR_INVALID_ARGUMENT;
   if (any_overlap(send, send_off, n, recv, recv_off, n, c->nranks)) return VR_ERR_INVALID_ARGUMENT;
+  if (va_touch(send, -1, send_off, n) || va_touch(recv, -1, recv_off, n)) return VR_ERR_INVALID_USAGE;
   const bool wait = !(flags & VR_COLL_NO_WAIT);
   U64Tab t;
   vrResult_t r = inc_targets(c, sig, c->nranks, wait, &t);
@@ -524,6 +601,7 @@ vrResult_t vr_alltoall(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t 
   const size_t n = block * R;
   if (!span_ok(send, send_off, n) || !span_ok(recv, recv_off, n)) return VR_ERR_INVALID_ARGUMENT;
   if (any_overlap(send, send_off, n, recv, recv_off, n, R)) return VR_ERR_INVALID_ARGUMENT;
+  if (va_touch(send, -1, send_off, n) || va_touch(recv, -1, recv_off, n)) return VR_ERR_INVALID_USAGE;
   const bool wait = !(flags & VR_COLL_NO_WAIT);
   U64Tab t;
   vrResult_t r = inc_targets(c, sig, R, wait, &t);
@@ -541,6 +619,8 @@ vrResult_t vr_allgather(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t
   if (bytes > (size_t(1) << 40)) return VR_ERR_INVALID_ARGUMENT;
   if (!span_ok(send, send_off, bytes) || !span_ok(recv, recv_off, bytes * R)) return VR_ERR_INVALID_ARGUMENT;
   if (any_overlap(send, send_off, bytes, recv, recv_off, bytes * R, R)) return VR_ERR_INVALID_ARGUMENT;
+  if (va_touch(send, -1, send_off, bytes) || va_touch(recv, -1, recv_off, bytes * R))
+    return VR_ERR_INVALID_USAGE;
   const bool wait = !(flags & VR_COLL_NO_WAIT);
   U64Tab t;
   vrResult_t r = inc_targets(c, sig, R, wait, &t);
@@ -563,6 +643,8 @@ vrResult_t vr_dispatch(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes,
   if (row_bytes == 0 || row_bytes > (size_t(1) << 30) || cap > (size_t(1) << 31)) return VR_ERR_INVALID_ARGUMENT;
   if (!span_ok(x, x_off, row_bytes * T) || !span_ok(recv, recv_off, row_bytes * cap)) return VR_ERR_INVALID_ARGUMENT;
   if (any_overlap(x, x_off, row_bytes * T, recv, recv_off, row_bytes * cap, R)) return VR_ERR_INVALID_ARGUMENT;
+  if (va_touch(x, -1, x_off, row_bytes * T) || va_touch(recv, -1, recv_off, row_bytes * cap))
+    return VR_ERR_INVALID_USAGE;
   if (sig_counts >= c->req.signal_count || sig_rows >= c->req.signal_count || sig_counts == sig_rows)
     return VR_ERR_INVALID_ARGUMENT;
   const bool wait = !(flags & VR_COLL_NO_WAIT);
@@ -597,6 +679,8 @@ vrResult_t vr_combine(vrComm_t c, vrWindow_t y, size_t y_off, size_t cap, size_t
   if (cap > (size_t(1) << 31)) return VR_ERR_INVALID_ARGUMENT;
   if (!span_ok(y, y_off, row_bytes * cap) || !span_ok(out, out_off, row_bytes * T)) return VR_ERR_INVALID_ARGUMENT;
   if (any_overlap(y, y_off, row_bytes * cap, out, out_off, row_bytes * T, R)) return VR_ERR_INVALID_ARGUMENT;
+  if (va_touch(y, -1, y_off, row_bytes * cap) || va_touch(out, -1, out_off, row_bytes * T))
+    return VR_ERR_INVALID_USAGE;
   const bool wait = !(flags & VR_COLL_NO_WAIT);
   U64Tab t;
   vrResult_t r = inc_targets(c, sig, R, wait, &t);
@@ -608,34 +692,55 @@ vrResult_t vr_combine(vrComm_t c, vrWindow_t y, size_t y_off, size_t cap, size_t
 }
 
 vrResult_t vr_ring_exchange(vrComm_t c, vrWindow_t send, vrWindow_t recv, size_t put_bytes, size_t puts_per_rank,
-                            int contexts, uint32_t sig_base, uint32_t cnt_base, uint64_t* litmus, uint32_t flags,
-                            void* stream) {
+                            int contexts, uint32_t sig_base, uint32_t cnt_base, vrWindow_t sig_window,
+                            size_t sig_window_off, uint64_t* litmus, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
   if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (contexts < 1 || (uint32_t)contexts > c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
   if (put_bytes == 0 || put_bytes % 16 || put_bytes > 65536) return VR_ERR_INVALID_ARGUMENT;
-  if (puts_per_rank == 0 || puts_per_rank % contexts || puts_per_rank > (size_t(1) << 32)) return VR_ERR_INVALID_ARGUMENT;
-  if ((uint64_t)sig_base + contexts > c->req.signal_count || (uint64_t)cnt_base + contexts > c->req.counter_count)
+  if (puts_per_rank == 0 || puts_per_rank % contexts || puts_per_rank > (size_t(1) << 32))
     return VR_ERR_INVALID_ARGUMENT;
+  if ((uint64_t)cnt_base + contexts > c->req.counter_count) return VR_ERR_INVALID_ARGUMENT;
+  const bool va = sig_window != nullptr;
+  if (!va && (uint64_t)sig_base + contexts > c->req.signal_count) return VR_ERR_INVALID_ARGUMENT;
   const size_t n = put_bytes * puts_per_rank;
   if (!span_ok(send, 0, n) || !span_ok(recv, 0, n)) return VR_ERR_INVALID_ARGUMENT;
   if (any_overlap(send, 0, n, recv, 0, n, R)) return VR_ERR_INVALID_ARGUMENT;
+  if (va_touch(send, -1, 0, n) || va_touch(recv, -1, 0, n)) return VR_ERR_INVALID_USAGE;
   const uint64_t per_ctx = puts_per_rank / contexts;
-  std::vector<uint64_t> target((size_t)R * contexts);
-  for (int d = 0; d < R; ++d)
-    for (int k = 0; k < contexts; ++k) {
-      const size_t i = sidx(c, d, sig_base + k);
-      if (check_signal_mode(c, d, sig_base + k, VR_SIGNAL_INC) != VR_OK) return VR_ERR_INVALID_USAGE;
-      if (!c->expect_known[i]) return VR_ERR_INVALID_USAGE;
-      target[(size_t)d * contexts + k] = c->expect[i] + per_ctx;
+  uint64_t* ctx0[VR_MAX_RANKS];
+  if (va) {
+    // one VA signal word per context, consecutive, in every rank's slice
+    vrResult_t r = check_va_word(c, sig_window, sig_window_off);
+    if (r != VR_OK) return r;
+    if (!span_ok(sig_window, sig_window_off, (size_t)8 * contexts)) return VR_ERR_INVALID_ARGUMENT;
+    if ((sig_window == send && any_overlap(send, 0, n, sig_window, sig_window_off, (size_t)8 * contexts, R)) ||
+        (sig_window == recv && any_overlap(recv, 0, n, sig_window, sig_window_off, (size_t)8 * contexts, R)))
+      return VR_ERR_INVALID_USAGE;  // the messages would move the signal words' own bytes
+    for (int d = 0; d < R; ++d) {
+      for (int k = 0; k < contexts; ++k) {
+        const auto it = sig_window->va_words.find({d, sig_window_off + 8ull * k});
+        if (it != sig_window->va_words.end() && it->second == 2) return VR_ERR_INVALID_USAGE;
+      }
+      ctx0[d] = reinterpret_cast<uint64_t*>(sig_window->base[d] + sig_window_off);
     }
+  } else {
+    for (int d = 0; d < R; ++d) {
+      for (int k = 0; k < contexts; ++k)
+        if (check_signal_mode(c, d, sig_base + k, VR_SIGNAL_INC) != VR_OK) return VR_ERR_INVALID_USAGE;
+      ctx0[d] = c->sig + sidx(c, d, sig_base);
+    }
+  }
   const bool wait = !(flags & VR_COLL_NO_WAIT);
-  vrResult_t r = launch_ring(c, send, recv, put_bytes, puts_per_rank, contexts, sig_base, cnt_base,
-                             wait ? target : std::vector<uint64_t>(), litmus, S(stream));
+  vrResult_t r = launch_ring(c, send, recv, put_bytes, puts_per_rank, contexts, ctx0, cnt_base, wait, litmus,
+                             S(stream));
   if (r == VR_OK)
     for (int d = 0; d < R; ++d)
-      for (int k = 0; k < contexts; ++k) note_signal(c, d, sig_base + k, VR_SIGNAL_INC, per_ctx, true);
+      for (int k = 0; k < contexts; ++k) {
+        if (va) sig_window->va_words[{d, sig_window_off + 8ull * k}] = 1;
+        else note_signal(c, d, sig_base + k, VR_SIGNAL_INC, per_ctx, true);
+      }
   return r;
 }
 

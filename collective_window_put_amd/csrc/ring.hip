@@ -34,9 +34,9 @@ constexpr uint32_t kRoundBytes = 16384;
 struct RingArgs {
   WinTab send, recv;
   uint64_t put_bytes, per_ctx;
-  uint64_t* sig;        // &sig[0][sig_base]
+  uint64_t* sigp[VR_MAX_RANKS];  // rank d's signal of context 0; context k at sigp[d] + k
   uint64_t* cnt;        // &cnt[0][cnt_base]
-  uint32_t sig_stride, cnt_stride;
+  uint32_t cnt_stride;
   uint64_t* bases;      // [R][C] signal values before this exchange
   uint64_t* litmus;     // [2] checks, violations; or null
   uint32_t* err;
@@ -48,7 +48,7 @@ __global__ void k_ring_snapshot(const RingArgs a) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < a.R * a.C) {
     const int d = i / a.C, k = i % a.C;
-    store8_agent(a.bases + i, load_relaxed_u64(a.sig + (size_t)d * a.sig_stride + k));
+    store8_agent(a.bases + i, load_relaxed_u64(a.sigp[d] + k));
   }
 }
 
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(64) void k_ring(const RingArgs a) {
     // one lane applies each message's signal, so a round holds at most 64 messages
     const uint64_t per_round = std::min<uint64_t>(64, std::max<uint64_t>(1, kRoundBytes / P));
     const uint64_t m0 = (uint64_t)k * a.per_ctx, m1 = m0 + a.per_ctx;
-    uint64_t* sig = a.sig + (size_t)peer * a.sig_stride + k;
+    uint64_t* sig = a.sigp[peer] + k;
     uint64_t* cnt = a.cnt + (size_t)r * a.cnt_stride + k;
     for (uint64_t m = m0; m < m1; m += per_round) {
       const uint64_t nm = std::min<uint64_t>(per_round, m1 - m);
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64) void k_ring(const RingArgs a) {
   if (i >= a.waiters) return;
   const int d = i / C, k = i % C, sender = (d + R - 1) % R;
   const uint64_t base = a.bases[(size_t)d * C + k];
-  const uint64_t* sig = a.sig + (size_t)d * a.sig_stride + k;
+  const uint64_t* sig = a.sigp[d] + k;
   const uint64_t m0 = (uint64_t)k * a.per_ctx;
   const uint64_t t0 = now_ns();
   uint64_t seen = 0;
@@ -128,8 +128,8 @@ __global__ __launch_bounds__(64) void k_ring(const RingArgs a) {
 }  // namespace
 
 vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, size_t put_bytes, size_t puts_per_rank,
-                       int contexts, uint32_t sig_base, uint32_t cnt_base, const std::vector<uint64_t>& target,
-                       uint64_t* litmus, hipStream_t st) {
+                       int contexts, uint64_t* const* sig_ctx0, uint32_t cnt_base, bool wait, uint64_t* litmus,
+                       hipStream_t st) {
   const int R = c->nranks;
   vrResult_t r = ensure_scratch(c, sizeof(uint64_t) * R * contexts);
   if (r != VR_OK) return r;
@@ -140,9 +140,8 @@ vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, si
   }
   a.put_bytes = put_bytes;
   a.per_ctx = puts_per_rank / contexts;
-  a.sig = c->sig + sig_base;
+  for (int q = 0; q < VR_MAX_RANKS; ++q) a.sigp[q] = q < R ? sig_ctx0[q] : nullptr;
   a.cnt = c->cnt + cnt_base;
-  a.sig_stride = c->req.signal_count;
   a.cnt_stride = c->req.counter_count;
   a.bases = reinterpret_cast<uint64_t*>(c->scratch);
   a.litmus = litmus;
@@ -150,7 +149,7 @@ vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, si
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;
   a.C = contexts;
-  a.waiters = target.empty() ? 0 : R * contexts;
+  a.waiters = wait ? R * contexts : 0;
   if (a.waiters) {
     const int n = R * contexts;
     hipLaunchKernelGGL(k_ring_snapshot, dim3((n + 255) / 256), dim3(256), 0, st, a);

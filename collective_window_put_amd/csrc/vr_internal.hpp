@@ -5,7 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
 #include <set>
+#include <utility>
 #include <vector>
 
 #include "vrcomm.h"  // include/ is on the include path
@@ -36,6 +38,8 @@ struct vrWindow {
   uint32_t flags;
   int nranks;
   char* base[VR_MAX_RANKS];
+  // words in use as VA signals: (rank, offset) -> 0 (no Inc/Add yet), 1 Inc, 2 Add
+  std::map<std::pair<int, uint64_t>, uint8_t> va_words;
 };
 
 struct vrComm {
@@ -83,8 +87,8 @@ vrResult_t launch_combine(vrComm* c, const vrWindow* y, size_t y_off, size_t cap
                           hipStream_t st);
 size_t dispatch_scratch_bytes(int R, int T, int E);
 vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, size_t put_bytes,
-                       size_t puts_per_rank, int contexts, uint32_t sig_base, uint32_t cnt_base,
-                       const std::vector<uint64_t>& target, uint64_t* litmus, hipStream_t st);
+                       size_t puts_per_rank, int contexts, uint64_t* const* sig_ctx0, uint32_t cnt_base,
+                       bool wait, uint64_t* litmus, hipStream_t st);
 
 // helpers in comm.hip
 vrResult_t ensure_scratch(vrComm* c, size_t bytes);

@@ -90,24 +90,38 @@ typedef struct {
 /* Remote action, applied at the peer after the put's payload has landed
  * (GIN page, one-sided transfers and signals and counters).
  *   kind  VR_ACTION_NONE, VR_SIGNAL_INC (add 1) or VR_SIGNAL_ADD (add value)
- *   id    signal id at the peer
+ *         on signal `id`; or VR_VA_SIGNAL_INC / VR_VA_SIGNAL_ADD on the VA
+ *         signal at (window, offset) (GIN page, VA signals)
+ *   id    signal id at the peer (id signals)
  *   strong nonzero: the signal also covers every earlier put of the same
  *         context to the same peer (GIN page, strong and weak signals). This
  *         library always publishes a signal after all earlier stores of the
  *         issuing context, so weak signals get the strong guarantee too.
- * A signal id must not receive both SignalInc and SignalAdd without a reset
- * in between (GIN page, strong and weak signals); the library rejects such a
+ *   window, offset  VA signals: the signal is the little-endian uint64 at
+ *         byte `offset` (a multiple of 8) of the peer's slice of `window`,
+ *         which must be registered with VR_WIN_STRICT_ORDERING
+ *         (VR_ERR_INVALID_USAGE otherwise). Once a word has served as a VA
+ *         signal (action, wait, read or reset), puts, gets and collectives
+ *         whose data ranges touch it are refused with VR_ERR_INVALID_USAGE:
+ *         the word is accessed by signal operations only. NULL / 0 for id
+ *         signals.
+ * A signal must not receive both SignalInc and SignalAdd without a reset in
+ * between (GIN page, strong and weak signals); the library rejects such a
  * call with VR_ERR_INVALID_USAGE. */
-#define VR_ACTION_NONE   0u
-#define VR_SIGNAL_INC    1u
-#define VR_SIGNAL_ADD    2u
-#define VR_COUNTER_INC   3u
+#define VR_ACTION_NONE     0u
+#define VR_SIGNAL_INC      1u
+#define VR_SIGNAL_ADD      2u
+#define VR_COUNTER_INC     3u
+#define VR_VA_SIGNAL_INC   4u
+#define VR_VA_SIGNAL_ADD   5u
 typedef struct {
   uint32_t kind;
   uint32_t id;
   uint64_t value;
   uint32_t strong;
   uint32_t reserved;  /* must be 0 */
+  vrWindow_t window;  /* VA signals only */
+  uint64_t offset;    /* VA signals only */
 } vrRemoteAction;
 
 /* Local action, applied at the issuing rank once the source bytes have been
@@ -191,6 +205,17 @@ vrResult_t vr_signal(vrComm_t comm, int ctx, int rank, int peer, vrRemoteAction 
  * long and set VR_ASYNC_TIMEOUT (0 = 5 s). bits in 1..64. */
 vrResult_t vr_signal_wait(vrComm_t comm, int rank, uint32_t id, uint64_t least, int bits,
                           uint64_t timeout_ns, void* stream);
+
+/* VA signals (GIN page, VA signals): wait on, read or reset the uint64 word
+ * at byte `offset` (a multiple of 8) of rank's slice of `win`, a window
+ * registered with VR_WIN_STRICT_ORDERING (VR_ERR_INVALID_USAGE otherwise).
+ * Semantics as vr_signal_wait / vr_signal_read / vr_signal_reset; the word
+ * counts as a signal from then on (see vrRemoteAction). */
+vrResult_t vr_va_signal_wait(vrComm_t comm, vrWindow_t win, int rank, size_t offset, uint64_t least,
+                             int bits, uint64_t timeout_ns, void* stream);
+vrResult_t vr_va_signal_read(vrComm_t comm, vrWindow_t win, int rank, size_t offset, int bits,
+                             uint64_t* out);
+vrResult_t vr_va_signal_reset(vrComm_t comm, vrWindow_t win, int rank, size_t offset, void* stream);
 
 /* Read the low `bits` bits of a signal now (synchronous device read; the
  * caller synchronizes the stream that modified it). */
@@ -319,8 +344,10 @@ vrResult_t vr_combine(vrComm_t comm, vrWindow_t y, size_t y_off, size_t y_capaci
  * k from send offset k*put_bytes to recv offset k*put_bytes. Messages are
  * split into `contexts` contiguous ranges, each issued in order by one
  * wavefront; every message carries a strong SignalInc on signal
- * sig_base + ctx at the receiver and a CounterInc on counter cnt_base + ctx
- * at the sender. Receivers wait in-kernel until each context signal has
+ * sig_base + ctx at the receiver (or, when sig_window is not NULL, on the
+ * VA signal at sig_window_off + 8*ctx of the receiver's slice of
+ * sig_window, a VR_WIN_STRICT_ORDERING window; sig_base is then unused) and
+ * a CounterInc on counter cnt_base + ctx at the sender. Receivers wait in-kernel until each context signal has
  * grown by puts_per_rank / contexts. litmus (device uint64[2] or NULL): when
  * given, the waiting wavefronts repeatedly read a context signal v and check
  * that messages v-1 and an earlier one are visible, counting checks in
@@ -328,7 +355,8 @@ vrResult_t vr_combine(vrComm_t comm, vrWindow_t y, size_t y_off, size_t y_capaci
  * puts_per_rank must be a multiple of contexts; put_bytes a multiple of 16. */
 vrResult_t vr_ring_exchange(vrComm_t comm, vrWindow_t send, vrWindow_t recv, size_t put_bytes,
                             size_t puts_per_rank, int contexts, uint32_t sig_base,
-                            uint32_t cnt_base, uint64_t* litmus, uint32_t flags, void* stream);
+                            uint32_t cnt_base, vrWindow_t sig_window, size_t sig_window_off,
+                            uint64_t* litmus, uint32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

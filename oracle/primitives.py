@@ -127,6 +127,10 @@ class World:
         sizes = {b.nbytes for b in bufs}
         if len(sizes) != 1:
             raise InvalidArgument("a symmetric window has the same size on every rank")
+        for i in range(len(bufs)):
+            for j in range(i):
+                if np.shares_memory(bufs[i], bufs[j]):
+                    raise InvalidArgument("the ranks' buffers of a window must not overlap")
         views = []
         for b in bufs:
             if not b.flags.c_contiguous:

@@ -27,7 +27,7 @@ class Job:
         self._wins = []
         self._slabs = []
 
-    def window(self, nbytes: int, fill: int | None = 0, arrays=None):
+    def window(self, nbytes: int, fill: int | None = 0, arrays=None, flags: int = 0):
         """Register a window of nbytes per rank; returns (handle, [per-rank uint8 tensors])."""
         torch = self.torch
         stride = (nbytes + ALIGN - 1) // ALIGN * ALIGN
@@ -39,7 +39,7 @@ class Job:
                 v.copy_(torch.from_numpy(np.ascontiguousarray(a).reshape(-1).view(np.uint8)))
         elif fill is not None:
             slab.fill_(fill)
-        h = vr.vr_window_register(self.comm, [v.data_ptr() for v in views], nbytes)
+        h = vr.vr_window_register(self.comm, [v.data_ptr() for v in views], nbytes, flags)
         self._wins.append(h)
         self._slabs.append(slab)
         return h, views

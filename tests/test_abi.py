@@ -82,7 +82,7 @@ def test_argument_errors_without_gpu(lib):
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(vr.vrRemoteAction) == 24
+    assert ctypes.sizeof(vr.vrRemoteAction) == 40
     assert ctypes.sizeof(vr.vrLocalAction) == 8
     assert ctypes.sizeof(vr.vrCommRequirements) == 12
 

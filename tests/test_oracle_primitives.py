@@ -221,7 +221,7 @@ def test_va_signal_put_then_wait_every_interleaving():
 
     def setup():
         w = World(2)
-        win = w.register([np.zeros(16, np.uint8)] * 2, flags=WIN_STRICT_ORDERING)
+        win = w.register([np.zeros(16, np.uint8) for _ in range(2)], flags=WIN_STRICT_ORDERING)
         src = w.register([payload.copy(), payload.copy() + 100])
         dst = w.register_zeros(16)
         seen = []
