@@ -8,13 +8,17 @@
 // has been consumed.
 //
 // Rank r sends puts_per_rank messages to rank (r+1) mod R, split into
-// `contexts` contiguous ranges. One wavefront owns each (rank, context) and
-// issues its messages in order, in rounds of up to 16 KiB (at most 64
-// messages, one signalling lane each): it loads the
-// round's messages, stores them with agent-coherent stores, waits for its
-// stores, then applies one SignalInc per message at the receiver and one
-// CounterInc per message at itself. Every signal is therefore applied after
-// the payloads of all earlier messages of its context are visible (strong).
+// `contexts` contiguous ranges. One workgroup owns each (rank, context) and
+// issues its messages in order, in rounds of up to 64 KiB (at most 256
+// messages, one signalling thread each): it loads the round's messages,
+// stores them with agent-coherent stores, waits for every wave's stores,
+// then applies one SignalInc per message at the receiver and one CounterInc
+// per message at itself. Every signal is therefore applied after the
+// payloads of all earlier messages of its context are visible (strong).
+// Measured on 16 ranks x 65536 puts of 256 B, 64 contexts: rounds of 16 KiB
+// by one wave took 225 us, 64 KiB rounds by one wave 119 us, 64 KiB rounds
+// by a 256-thread workgroup 98 us (32 KiB: 155 us; 128 KiB: 97 us): the time
+// follows the number of serial rounds per issuer and the loads in flight.
 // One waiting wavefront per receiving (rank, context) polls the signal until
 // it has grown by the context's message count; with the litmus on, each time
 // it sees a new value v it acquires and checks that message v-1 and one
@@ -29,7 +33,9 @@
 namespace vr {
 namespace {
 
-constexpr uint32_t kRoundBytes = 16384;
+constexpr int kThreads = 256;          // one workgroup issues each (rank, context)
+constexpr uint32_t kRoundBytes = 65536;  // bytes per round
+constexpr uint32_t kSigPerThread = 1;    // signals (and counter increments) each thread applies per round
 
 struct RingArgs {
   WinTab send, recv;
@@ -64,30 +70,33 @@ __device__ bool message_present(const RingArgs& a, int d, int sender, uint64_t m
   return ballot(!same) == 0;
 }
 
-__global__ __launch_bounds__(64) void k_ring(const RingArgs a) {
+__global__ __launch_bounds__(kThreads) void k_ring(const RingArgs a) {
   const int R = a.R, C = a.C;
   const int w = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   if (w < R * C) {  // producer: rank r, context k
     const int r = w / C, k = w % C, peer = (r + 1) % R;
     const uint64_t P = a.put_bytes;
-    // one lane applies each message's signal, so a round holds at most 64 messages
-    const uint64_t per_round = std::min<uint64_t>(64, std::max<uint64_t>(1, kRoundBytes / P));
+    // thread t applies the signals of messages t, t + kThreads, ...
+    const uint64_t per_round =
+        std::min<uint64_t>(kThreads * kSigPerThread, std::max<uint64_t>(1, kRoundBytes / P));
     const uint64_t m0 = (uint64_t)k * a.per_ctx, m1 = m0 + a.per_ctx;
     uint64_t* sig = a.sigp[peer] + k;
     uint64_t* cnt = a.cnt + (size_t)r * a.cnt_stride + k;
     for (uint64_t m = m0; m < m1; m += per_round) {
       const uint64_t nm = std::min<uint64_t>(per_round, m1 - m);
       const uint32_t bytes = static_cast<uint32_t>(nm * P);
-      copy16<16>(a.recv.p[peer] + m * P, a.send.p[r] + m * P, bytes, lane, 64);
-      wait_vmem();  // this round's payloads are visible at agent scope
-      if ((uint64_t)lane < nm) {
-        atomic_add_u64(sig, 1ull);  // strong SignalInc of message m + lane
+      copy16<16>(a.recv.p[peer] + m * P, a.send.p[r] + m * P, bytes, tid, kThreads);
+      wg_stores_complete();  // this round's payloads, from every wave, are visible at agent scope
+      for (uint64_t j = tid; j < nm; j += kThreads) {
+        atomic_add_u64(sig, 1ull);  // strong SignalInc of message m + j
         atomic_add_u64(cnt, 1ull);  // CounterInc: its source has been read
       }
     }
     return;
   }
+  if (tid >= 64) return;  // one wave waits for each receiving (rank, context)
+  const int lane = tid;
   // receiver d, context k: wait (and check prefixes when the litmus is on)
   const int i = w - R * C;
   if (i >= a.waiters) return;
@@ -155,7 +164,7 @@ vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, si
     hipLaunchKernelGGL(k_ring_snapshot, dim3((n + 255) / 256), dim3(256), 0, st, a);
     if (hipGetLastError() != hipSuccess) return VR_ERR_HIP;
   }
-  hipLaunchKernelGGL(k_ring, dim3(R * contexts + a.waiters), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(k_ring, dim3(R * contexts + a.waiters), dim3(kThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;
 }
 

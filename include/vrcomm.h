@@ -343,7 +343,7 @@ vrResult_t vr_combine(vrComm_t comm, vrWindow_t y, size_t y_off, size_t y_capaci
  * puts puts_per_rank messages of put_bytes each to rank (r+1) mod R, message
  * k from send offset k*put_bytes to recv offset k*put_bytes. Messages are
  * split into `contexts` contiguous ranges, each issued in order by one
- * wavefront; every message carries a strong SignalInc on signal
+ * workgroup; every message carries a strong SignalInc on signal
  * sig_base + ctx at the receiver (or, when sig_window is not NULL, on the
  * VA signal at sig_window_off + 8*ctx of the receiver's slice of
  * sig_window, a VR_WIN_STRICT_ORDERING window; sig_base is then unused) and
