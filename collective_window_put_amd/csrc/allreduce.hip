@@ -180,7 +180,19 @@ __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
   const uint64_t end = std::min<uint64_t>(cend, start + tile);
   if (start < end) reduce_tile<DT, RT, ALIGNED>(a, start, end);
   wg_stores_complete();
-  if (threadIdx.x == 0 && relay_arrive(a.relay + c, a.tpc))
+  if (threadIdx.x != 0) return;
+  bool last;
+  if ((nwork & 7u) == 0) {
+    // two-level relay: first the tiles of chunk c on this XCD (arrivals from
+    // one XCD only), then the XCDs that hold part of chunk c (one for R = 8)
+    const uint32_t x = b & 7u, per = nwork >> 3;
+    const uint32_t lo = std::max(x * per, c * a.tpc), hi = std::min((x + 1) * per, (c + 1) * a.tpc);
+    const uint32_t nx = ((c + 1) * a.tpc - 1) / per - (c * a.tpc) / per + 1;
+    last = relay_arrive(a.relay + R + c * 8 + x, hi - lo, false) && relay_arrive(a.relay + c, nx, false);
+  } else {
+    last = relay_arrive(a.relay + c, a.tpc, false);
+  }
+  if (last)
     for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
 }
 
@@ -224,7 +236,7 @@ vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, co
   a.tpc = static_cast<uint32_t>(tpc);
   a.sig = c->sig + sig;
   a.sig_stride = c->req.signal_count;
-  a.relay = c->relay + kRelayColl;
+  a.relay = c->relay + kRelayColl;  // [R] per chunk, then [R][8] per (chunk, XCD)
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;
