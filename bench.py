@@ -38,6 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "k_allreduce": "allreduce.hip", "k_alltoall": "alltoall.hip", "k_allgather": "allgather.hip",
     "k_dispatch": "dispatch.hip", "k_combine": "combine.hip", "k_ring": "ring.hip",
+    "k_alltoall_sessions": "sessions.hip",
 }
 
 
@@ -48,8 +49,11 @@ def log(msg: str) -> None:
 def source_hash(kernel: str) -> str:
     """Hash of a kernel's source and the shared device header (to age traffic figures)."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "vr_device.hpp"):
-        with open(os.path.join(ROOT, "collective_window_put_amd", "csrc", f), "rb") as fh:
+    files = [os.path.join("collective_window_put_amd", "csrc", f) for f in (KERNEL_SOURCES[kernel], "vr_device.hpp")]
+    if kernel == "k_alltoall_sessions":
+        files.append(os.path.join("include", "vrcomm_device.hpp"))
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -180,7 +184,7 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
 
 
 # ---- the other workloads ------------------------------------------------------------------------
-ROW_NAMES = ("allreduce_f32", "alltoall", "dispatch", "combine", "allgather", "ring")
+ROW_NAMES = ("allreduce_f32", "alltoall", "alltoall_sessions", "dispatch", "combine", "allgather", "ring")
 
 
 def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
@@ -190,6 +194,8 @@ def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
         run_allreduce_f32_row(b, reps, rows)
     if "alltoall" in only:
         run_alltoall_row(b, reps, rows)
+    if "alltoall_sessions" in only:
+        run_alltoall_row(b, reps, rows, sessions=True)
     if "dispatch" in only:
         run_dispatch_row(b, reps, rows)
     if "combine" in only:
@@ -227,21 +233,26 @@ def run_allreduce_f32_row(b, reps, rows):
 
 
 
-def run_alltoall_row(b, reps, rows):
+def run_alltoall_row(b, reps, rows, sessions=False):
     import workloads as W
     vr, stream = b.vr, b.stream.cuda_stream
     c = W.CONFIGS["c3"]
     R, B = c["ranks"], c["block_bytes"]
     sends = W.alltoall_inputs(R, B, seed=c["seed"])
-    comm = comm_for(vr, R, signal_count=2)
+    comm = comm_for(vr, R, signal_count=2, barrier_count=1)
     s1, sv = b.slices(R, R * B, arrays=sends)
     r1, rv = b.slices(R, R * B, fill=0)
     sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], R * B)
     rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], R * B)
-    f = lambda: vr.vr_alltoall(comm, sw, 0, rw, 0, B, sig=0, stream=stream)  # noqa: E731
+    if sessions:  # the same exchange inside entry and exit barrier-session syncs
+        f = lambda: vr.vr_alltoall_sessions(comm, sw, 0, rw, 0, B, sig=0, barrier_index=0,  # noqa: E731
+                                            stream=stream)
+        name, kernel, label = "alltoall_sessions_r8_4MiB", "k_alltoall_sessions", "AlltoAll+sessions R=8 B=4MiB"
+    else:
+        f = lambda: vr.vr_alltoall(comm, sw, 0, rw, 0, B, sig=0, stream=stream)  # noqa: E731
+        name, kernel, label = "alltoall_r8_4MiB", "k_alltoall", "AlltoAll R=8 B=4MiB"
     f()
-    rows["alltoall_r8_4MiB"] = row_entry("AlltoAll R=8 B=4MiB", 2 * R * R * B, b.timed(f, reps, True),
-                                         "k_alltoall", "alltoall_r8_4MiB")
+    rows[name] = row_entry(label, 2 * R * R * B, b.timed(f, reps, True), kernel, name)
     vr.vr_window_deregister(comm, sw)
     vr.vr_window_deregister(comm, rw)
     vr.vr_comm_destroy(comm)

@@ -55,6 +55,7 @@ VR_VA_SIGNAL_INC, VR_VA_SIGNAL_ADD = 4, 5
 VR_DT_F32, VR_DT_BF16 = 0, 1
 VR_OP_SUM = 0
 VR_COLL_NO_WAIT = 0x1
+VR_FENCE_NONE, VR_FENCE_PUT, VR_FENCE_GET = 0x0, 0x1, 0x2
 VR_ASYNC_TIMEOUT, VR_ASYNC_CAPACITY, VR_ASYNC_BAD_EXPERT, VR_ASYNC_LITMUS = 0x1, 0x2, 0x4, 0x8
 
 
@@ -71,7 +72,18 @@ class VrLibraryMissing(ImportError):
 
 
 class vrCommRequirements(Structure):
-    _fields_ = [("signal_count", c_uint32), ("counter_count", c_uint32), ("context_count", c_uint32)]
+    _fields_ = [("signal_count", c_uint32), ("counter_count", c_uint32), ("context_count", c_uint32),
+                ("barrier_count", c_uint32)]
+
+
+class vrDevComm(Structure):
+    _fields_ = [("nranks", c_int), ("signal_count", c_uint32), ("counter_count", c_uint32),
+                ("barrier_count", c_uint32), ("signals", c_void_p), ("counters", c_void_p),
+                ("barriers", c_void_p), ("error", c_void_p)]
+
+
+class vrDevWindow(Structure):
+    _fields_ = [("base", c_void_p * 64), ("bytes", c_uint64)]
 
 
 class vrRemoteAction(Structure):
@@ -137,6 +149,12 @@ SYMBOLS = {
     "vr_ring_exchange": (_R, [_P, _P, _P, c_size_t, c_size_t, c_int, c_uint32, c_uint32, _P, c_size_t, _P,
                               c_uint32, _P]),
     "vr_va_signal_wait": (_R, [_P, _P, c_int, c_size_t, c_uint64, c_int, c_uint64, _P]),
+    "vr_comm_device_view": (_R, [_P, POINTER(vrDevComm)]),
+    "vr_window_device_view": (_R, [_P, _P, POINTER(vrDevWindow)]),
+    "vr_barrier_expected": (_R, [_P, c_uint32, POINTER(c_uint64)]),
+    "vr_barrier_advance": (_R, [_P, c_uint32, c_uint64]),
+    "vr_barrier": (_R, [_P, c_uint32, c_uint32, c_uint64, _P]),
+    "vr_alltoall_sessions": (_R, [_P, _P, c_size_t, _P, c_size_t, c_size_t, c_uint32, c_uint32, c_uint32, _P]),
     "vr_va_signal_read": (_R, [_P, _P, c_int, c_size_t, c_int, POINTER(c_uint64)]),
     "vr_va_signal_reset": (_R, [_P, _P, c_int, c_size_t, _P]),
 }
@@ -207,14 +225,14 @@ def vr_version() -> int:
 
 
 def vr_comm_workspace_bytes(nranks: int, signal_count: int = 16, counter_count: int = 16,
-                            context_count: int = 1) -> int:
-    q = vrCommRequirements(signal_count, counter_count, context_count)
+                            context_count: int = 1, barrier_count: int = 0) -> int:
+    q = vrCommRequirements(signal_count, counter_count, context_count, barrier_count)
     return lib().vr_comm_workspace_bytes(nranks, ctypes.byref(q))
 
 
 def vr_comm_create(nranks: int, signal_count: int = 16, counter_count: int = 16, context_count: int = 1,
-                   workspace=None, workspace_bytes: int = 0) -> int:
-    q = vrCommRequirements(signal_count, counter_count, context_count)
+                   workspace=None, workspace_bytes: int = 0, barrier_count: int = 0) -> int:
+    q = vrCommRequirements(signal_count, counter_count, context_count, barrier_count)
     out = c_void_p()
     _check(lib().vr_comm_create(nranks, ctypes.byref(q), _ptr(workspace) or None, workspace_bytes,
                                 ctypes.byref(out)), "vr_comm_create")
@@ -231,10 +249,37 @@ def vr_comm_get_async_error(comm: int) -> tuple[int, int]:
     return code.value, bits.value
 
 
-def vr_comm_query(comm: int) -> tuple[int, tuple[int, int, int]]:
+def vr_comm_query(comm: int) -> tuple[int, tuple[int, int, int, int]]:
     n, q = c_int(), vrCommRequirements()
     _check(lib().vr_comm_query(comm, ctypes.byref(n), ctypes.byref(q)), "vr_comm_query")
-    return n.value, (q.signal_count, q.counter_count, q.context_count)
+    return n.value, (q.signal_count, q.counter_count, q.context_count, q.barrier_count)
+
+
+def vr_comm_device_view(comm: int) -> vrDevComm:
+    out = vrDevComm()
+    _check(lib().vr_comm_device_view(comm, ctypes.byref(out)), "vr_comm_device_view")
+    return out
+
+
+def vr_window_device_view(comm: int, window) -> vrDevWindow:
+    out = vrDevWindow()
+    _check(lib().vr_window_device_view(comm, window, ctypes.byref(out)), "vr_window_device_view")
+    return out
+
+
+def vr_barrier_expected(comm: int, index: int) -> int:
+    out = c_uint64()
+    _check(lib().vr_barrier_expected(comm, index, ctypes.byref(out)), "vr_barrier_expected")
+    return out.value
+
+
+def vr_barrier_advance(comm: int, index: int, arrivals: int) -> None:
+    _check(lib().vr_barrier_advance(comm, index, arrivals), "vr_barrier_advance")
+
+
+def vr_barrier(comm: int, index: int, fence: int = VR_FENCE_PUT | VR_FENCE_GET, timeout_ns: int = 0,
+               stream=None) -> None:
+    _check(lib().vr_barrier(comm, index, fence, timeout_ns, _stream(stream)), "vr_barrier")
 
 
 def vr_window_register(comm: int, bases, nbytes: int, flags: int = VR_WIN_DEFAULT) -> int:
@@ -319,6 +364,12 @@ def vr_allreduce(comm, send, send_off, recv, recv_off, count, dtype, op=VR_OP_SU
 def vr_alltoall(comm, send, send_off, recv, recv_off, block_bytes, sig=0, flags=0, stream=None):
     _check(lib().vr_alltoall(comm, send, send_off, recv, recv_off, block_bytes, sig, flags, _stream(stream)),
            "vr_alltoall")
+
+
+def vr_alltoall_sessions(comm, send, send_off, recv, recv_off, block_bytes, sig=0, barrier_index=0, flags=0,
+                         stream=None):
+    _check(lib().vr_alltoall_sessions(comm, send, send_off, recv, recv_off, block_bytes, sig, barrier_index, flags,
+                                      _stream(stream)), "vr_alltoall_sessions")
 
 
 def vr_allgather(comm, send, send_off, recv, recv_off, bytes_per_rank, sig=0, flags=0, stream=None):

@@ -33,11 +33,12 @@ bool valid_req(int nranks, const vrCommRequirements* req) {
   if (req->signal_count < 1 || req->signal_count > 65536) return false;
   if (req->counter_count > 65536) return false;
   if (req->context_count < 1 || req->context_count > 1024) return false;
+  if (req->barrier_count > 65536) return false;
   return true;
 }
 
 struct Layout {
-  size_t sig, cnt, err, relay, total;
+  size_t sig, cnt, err, relay, bar, total;
 };
 Layout layout(int R, const vrCommRequirements& q) {
   Layout l;
@@ -45,7 +46,8 @@ Layout layout(int R, const vrCommRequirements& q) {
   l.cnt = align_up(l.sig + sizeof(uint64_t) * R * q.signal_count, 256);
   l.err = align_up(l.cnt + sizeof(uint64_t) * R * std::max<uint32_t>(q.counter_count, 1), 256);
   l.relay = align_up(l.err + 256, 256);
-  l.total = align_up(l.relay + sizeof(uint32_t) * kRelaySlots, 256);
+  l.bar = align_up(l.relay + sizeof(uint32_t) * kRelaySlots, 256);
+  l.total = align_up(l.bar + sizeof(uint64_t) * std::max<uint32_t>(q.barrier_count, 1), 256);
   return l;
 }
 
@@ -226,6 +228,25 @@ vrResult_t enqueue_copy(vrComm* c, char* dst, const char* src, size_t bytes, uin
 
 // ---- internal helpers used by the collectives ---------------------------------------
 namespace vr {
+vrDevComm device_view(const vrComm* c) {
+  vrDevComm v;
+  v.nranks = c->nranks;
+  v.signal_count = c->req.signal_count;
+  v.counter_count = c->req.counter_count;
+  v.barrier_count = c->req.barrier_count;
+  v.signals = c->sig;
+  v.counters = c->cnt;
+  v.barriers = c->bar;
+  v.error = c->err;
+  return v;
+}
+vrDevWindow device_view(const vrWindow* w) {
+  vrDevWindow v;
+  for (int r = 0; r < VR_MAX_RANKS; ++r) v.base[r] = w->base[r];
+  v.bytes = w->bytes;
+  return v;
+}
+
 vrResult_t ensure_scratch(vrComm* c, size_t bytes) {
   if (bytes <= c->scratch_bytes) return VR_OK;
   // the previous scratch may still be in use by enqueued work
@@ -307,6 +328,8 @@ vrResult_t vr_comm_create(int nranks, const vrCommRequirements* req, void* works
   c->cnt = reinterpret_cast<uint64_t*>(c->ws + l.cnt);
   c->err = reinterpret_cast<uint32_t*>(c->ws + l.err);
   c->relay = reinterpret_cast<uint32_t*>(c->ws + l.relay);
+  c->bar = reinterpret_cast<uint64_t*>(c->ws + l.bar);
+  c->bar_expect.assign(req->barrier_count, 0);
   c->scratch = nullptr;
   c->scratch_bytes = 0;
   const size_t ns = (size_t)nranks * req->signal_count;
@@ -514,6 +537,39 @@ vrResult_t vr_va_signal_reset(vrComm_t c, vrWindow_t w, int rank, size_t off, vo
   return r;
 }
 
+vrResult_t vr_comm_device_view(vrComm_t c, vrDevComm* out) {
+  if (!live(c) || !out) return VR_ERR_INVALID_ARGUMENT;
+  *out = device_view(c);
+  return VR_OK;
+}
+
+vrResult_t vr_window_device_view(vrComm_t c, vrWindow_t w, vrDevWindow* out) {
+  if (!live(c) || !has_win(c, w) || !out) return VR_ERR_INVALID_ARGUMENT;
+  *out = device_view(w);
+  return VR_OK;
+}
+
+vrResult_t vr_barrier_expected(vrComm_t c, uint32_t index, uint64_t* out) {
+  if (!live(c) || index >= c->req.barrier_count || !out) return VR_ERR_INVALID_ARGUMENT;
+  *out = c->bar_expect[index];
+  return VR_OK;
+}
+
+vrResult_t vr_barrier_advance(vrComm_t c, uint32_t index, uint64_t arrivals) {
+  if (!live(c) || index >= c->req.barrier_count) return VR_ERR_INVALID_ARGUMENT;
+  c->bar_expect[index] += arrivals;
+  return VR_OK;
+}
+
+vrResult_t vr_barrier(vrComm_t c, uint32_t index, uint32_t fence, uint64_t timeout_ns, void* stream) {
+  if (!live(c) || index >= c->req.barrier_count) return VR_ERR_INVALID_ARGUMENT;
+  if (fence & ~(VR_FENCE_PUT | VR_FENCE_GET)) return VR_ERR_INVALID_ARGUMENT;
+  const uint64_t target = c->bar_expect[index] + c->nranks;
+  vrResult_t r = launch_barrier(c, index, target, fence, timeout_ns ? timeout_ns : kDefaultTimeoutNs, S(stream));
+  if (r == VR_OK) c->bar_expect[index] = target;
+  return r;
+}
+
 vrResult_t vr_counter_read(vrComm_t c, int rank, uint32_t id, int bits, uint64_t* out) {
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.counter_count || !out) return VR_ERR_INVALID_ARGUMENT;
   if (bits < 1 || bits > VR_COUNTER_BITS) return VR_ERR_INVALID_ARGUMENT;
@@ -608,6 +664,29 @@ vrResult_t vr_alltoall(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t 
   if (r != VR_OK) return r;
   r = launch_alltoall(c, send, send_off, recv, recv_off, block, sig, t, wait, S(stream));
   if (r == VR_OK) commit_inc(c, sig, R);
+  return r;
+}
+
+vrResult_t vr_alltoall_sessions(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
+                                size_t block, uint32_t sig, uint32_t index, uint32_t flags, void* stream) {
+  if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (flags || index >= c->req.barrier_count) return VR_ERR_INVALID_ARGUMENT;
+  const int R = c->nranks;
+  if (block > (size_t(1) << 40)) return VR_ERR_INVALID_ARGUMENT;
+  const size_t n = block * R;
+  if (!span_ok(send, send_off, n) || !span_ok(recv, recv_off, n)) return VR_ERR_INVALID_ARGUMENT;
+  if (any_overlap(send, send_off, n, recv, recv_off, n, R)) return VR_ERR_INVALID_ARGUMENT;
+  if (va_touch(send, -1, send_off, n) || va_touch(recv, -1, recv_off, n)) return VR_ERR_INVALID_USAGE;
+  U64Tab t;
+  vrResult_t r = inc_targets(c, sig, R, true, &t);
+  if (r != VR_OK) return r;
+  const uint64_t base = c->bar_expect[index];
+  r = launch_alltoall_sessions(c, device_view(send), send_off, device_view(recv), recv_off, block, sig, t, index,
+                               base, S(stream));
+  if (r == VR_OK) {
+    commit_inc(c, sig, R);
+    c->bar_expect[index] = base + 2ull * R;
+  }
   return r;
 }
 

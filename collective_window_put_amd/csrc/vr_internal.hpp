@@ -54,6 +54,7 @@ struct vrComm {
   uint64_t* cnt;    // [R][counter_count]
   uint32_t* err;    // error bits
   uint32_t* relay;  // [kRelaySlots]
+  uint64_t* bar;    // [barrier_count] barrier-session slots
   // growable scratch for dispatch (histograms, count exchange)
   char* scratch;
   size_t scratch_bytes;
@@ -61,6 +62,7 @@ struct vrComm {
   std::vector<uint64_t> expect;      // [R][S]
   std::vector<uint8_t> expect_known; // 0 when a device-computed amount was added
   std::vector<uint8_t> sig_mode;     // 0 none, 1 SignalInc, 2 SignalAdd (since the last reset)
+  std::vector<uint64_t> bar_expect;  // [barrier_count] slot values once enqueued work has run
   std::set<vrWindow*> windows;
 };
 
@@ -90,7 +92,15 @@ vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, si
                        size_t puts_per_rank, int contexts, uint64_t* const* sig_ctx0, uint32_t cnt_base,
                        bool wait, uint64_t* litmus, hipStream_t st);
 
+vrResult_t launch_barrier(vrComm* c, uint32_t index, uint64_t target, uint32_t fence, uint64_t timeout_ns,
+                          hipStream_t st);
+vrResult_t launch_alltoall_sessions(vrComm* c, const vrDevWindow& send, size_t send_off, const vrDevWindow& recv,
+                                    size_t recv_off, size_t block, uint32_t sig, const U64Tab& target, uint32_t index,
+                                    uint64_t bar_base, hipStream_t st);
+
 // helpers in comm.hip
 vrResult_t ensure_scratch(vrComm* c, size_t bytes);
+vrDevComm device_view(const vrComm* c);
+vrDevWindow device_view(const vrWindow* w);
 
 }  // namespace vr

@@ -80,12 +80,38 @@ typedef struct vrWindow* vrWindow_t;
  * counter_count  counters per rank, 0..65536
  * context_count  ordering contexts per rank, 1..1024 (GIN page, ncclGin:
  *                several contexts spread traffic; a context orders the puts
- *                of the one issuer that owns it). */
+ *                of the one issuer that owns it)
+ * barrier_count  barrier-session slots shared by the ranks, 0..65536 (GIN
+ *                page, ncclGinBarrierSession: one slot per cooperating group
+ *                that syncs). */
 typedef struct {
   uint32_t signal_count;
   uint32_t counter_count;
   uint32_t context_count;
+  uint32_t barrier_count;
 } vrCommRequirements;
+
+/* Fence levels of a barrier-session sync (GIN page, sync and fence levels):
+ * bit flags, combined with |. */
+#define VR_FENCE_NONE  0x0u  /* pure synchronization */
+#define VR_FENCE_PUT   0x1u  /* puts other members issued before the sync, aimed at the caller, are visible */
+#define VR_FENCE_GET   0x2u  /* gets the caller issued before the sync have landed */
+
+/* Device views for kernels written against include/vrcomm_device.hpp: plain
+ * structs passed by value. Pointers are device addresses owned by the
+ * communicator or the window and valid until it is destroyed / deregistered. */
+typedef struct {
+  int nranks;
+  uint32_t signal_count, counter_count, barrier_count;
+  uint64_t* signals;   /* [nranks][signal_count] */
+  uint64_t* counters;  /* [nranks][counter_count] */
+  uint64_t* barriers;  /* [barrier_count] */
+  uint32_t* error;     /* VR_ASYNC_* bits */
+} vrDevComm;
+typedef struct {
+  char* base[VR_MAX_RANKS];  /* rank r's slice (NULL past nranks) */
+  uint64_t bytes;
+} vrDevWindow;
 
 /* Remote action, applied at the peer after the put's payload has landed
  * (GIN page, one-sided transfers and signals and counters).
@@ -217,6 +243,24 @@ vrResult_t vr_va_signal_read(vrComm_t comm, vrWindow_t win, int rank, size_t off
                              uint64_t* out);
 vrResult_t vr_va_signal_reset(vrComm_t comm, vrWindow_t win, int rank, size_t offset, void* stream);
 
+/* ---- barrier sessions and device views ---------------------------------------------- */
+/* Fill the device views of a communicator and of one of its windows. */
+vrResult_t vr_comm_device_view(vrComm_t comm, vrDevComm* out);
+vrResult_t vr_window_device_view(vrComm_t comm, vrWindow_t win, vrDevWindow* out);
+
+/* The value barrier slot `index` will hold once every operation enqueued so
+ * far has run (every sync of a session adds its member count). A kernel that
+ * syncs k times on the slot with m members targets base + m, ..., base + k*m;
+ * vr_barrier_advance records those arrivals on the host. */
+vrResult_t vr_barrier_expected(vrComm_t comm, uint32_t index, uint64_t* out);
+vrResult_t vr_barrier_advance(vrComm_t comm, uint32_t index, uint64_t arrivals);
+
+/* One sync of the R ranks on barrier slot `index` (GIN page,
+ * ncclGinBarrierSession::sync), enqueued on the stream: one workgroup per
+ * rank arrives, with the drains `fence` asks for, and waits for the others.
+ * timeout_ns as vr_signal_wait. */
+vrResult_t vr_barrier(vrComm_t comm, uint32_t index, uint32_t fence, uint64_t timeout_ns, void* stream);
+
 /* Read the low `bits` bits of a signal now (synchronous device read; the
  * caller synchronizes the stream that modified it). */
 vrResult_t vr_signal_read(vrComm_t comm, int rank, uint32_t id, int bits, uint64_t* out);
@@ -270,6 +314,16 @@ vrResult_t vr_allreduce(vrComm_t comm, vrWindow_t send, size_t send_off, vrWindo
 vrResult_t vr_alltoall(vrComm_t comm, vrWindow_t send, size_t send_off, vrWindow_t recv,
                        size_t recv_off, size_t block_bytes, uint32_t sig, uint32_t flags,
                        void* stream);
+
+/* The pure-GIN AlltoAll kernel's structure (GIN page, the AlltoAll example),
+ * written with include/vrcomm_device.hpp: every rank enters through a
+ * barrier-session sync on slot `barrier_index` (VR_FENCE_NONE), puts its
+ * blocks with a weak SignalInc on `sig` at each destination, waits until its
+ * own signal has risen by R, and leaves through a second sync. Same result
+ * and signal totals as vr_alltoall; the slot advances by 2R. */
+vrResult_t vr_alltoall_sessions(vrComm_t comm, vrWindow_t send, size_t send_off, vrWindow_t recv,
+                                size_t recv_off, size_t block_bytes, uint32_t sig, uint32_t barrier_index,
+                                uint32_t flags, void* stream);
 
 /* AllGather: rank s's bytes_per_rank bytes at send_off land in every rank's
  * recv slice at recv_off + s*bytes_per_rank, one put + SignalInc per (s, d)

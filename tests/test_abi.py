@@ -3,6 +3,7 @@ and rejects bad arguments before touching a GPU (runs without a GPU)."""
 import ctypes
 import os
 import re
+import shutil
 import subprocess
 
 import pytest
@@ -84,7 +85,9 @@ def test_argument_errors_without_gpu(lib):
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(vr.vrRemoteAction) == 40
     assert ctypes.sizeof(vr.vrLocalAction) == 8
-    assert ctypes.sizeof(vr.vrCommRequirements) == 12
+    assert ctypes.sizeof(vr.vrCommRequirements) == 16
+    assert ctypes.sizeof(vr.vrDevComm) == 48
+    assert ctypes.sizeof(vr.vrDevWindow) == 64 * 8 + 8
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -92,3 +95,31 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(vr, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(vr.VrLibraryMissing):
         vr.vr_version()
+
+
+USER_KERNEL = r"""
+#include "vrcomm_device.hpp"
+// a user kernel: each workgroup r puts its block to rank (r+1) % R, signals it,
+// then all ranks meet at a barrier session with a Put fence
+__global__ void ring_once(vrDevComm c, vrDevWindow w, uint64_t block, uint64_t bar_base) {
+  const int r = blockIdx.x, peer = (r + 1) % c.nranks;
+  vrdev::put_wg(w, peer, block, w, r, 0, block);
+  vrdev::publish_wg();
+  if (threadIdx.x == 0) vrdev::signal_add(vrdev::signal_word(c, peer, 0), 1);
+  vrdev::barrier_sync_wg(vrdev::barrier_word(c, 0), bar_base + c.nranks, VR_FENCE_PUT, 0, c.error);
+  if (threadIdx.x == 0) vrdev::wait_word(vrdev::signal_word(c, r, 0), 1, 64, 0, c.error);
+}
+"""
+
+
+def test_device_header_compiles_in_a_user_kernel(tmp_path):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    src = tmp_path / "user.hip"
+    src.write_text(USER_KERNEL)
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    r = subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", inc, "-Xclang", "-target-feature",
+                        "-Xclang", "-packed-fp32-ops", "-c", str(src), "-o", str(tmp_path / "user.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
