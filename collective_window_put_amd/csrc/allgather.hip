@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void k_allgather(const AGArgs a) {
     }
   }
   wg_stores_complete();
-  if (threadIdx.x == 0 && relay_arrive(a.relay + s, a.tiles))
+  if (threadIdx.x == 0 && relay_arrive(a.relay + s, a.tiles, false))
     for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
 }
 

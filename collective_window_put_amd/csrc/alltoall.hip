@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void k_alltoall(const A2AArgs a) {
     copy_any<kU>(dst, src, n, threadIdx.x, 256);
   }
   wg_stores_complete();
-  if (threadIdx.x == 0 && relay_arrive(a.relay + blk, a.tiles))
+  if (threadIdx.x == 0 && relay_arrive(a.relay + blk, a.tiles, false))
     atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);  // SignalInc at d
 }
 

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void k_put(PutArgs a) {
     memmove_wg(a.dst, a.src, a.bytes, a.dir);
   }
   wg_stores_complete();
-  if (threadIdx.x == 0 && relay_arrive(a.relay, a.parts)) {
+  if (threadIdx.x == 0 && relay_arrive(a.relay, a.parts, false)) {
     if (a.sig) atomic_add_u64(a.sig, a.add);
     if (a.cnt) atomic_add_u64(a.cnt, 1ull);
   }
