@@ -184,7 +184,8 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
 
 
 # ---- the other workloads ------------------------------------------------------------------------
-ROW_NAMES = ("allreduce_f32", "alltoall", "alltoall_sessions", "dispatch", "combine", "allgather", "ring")
+ROW_NAMES = ("allreduce_f32", "alltoall", "alltoall_sessions", "alltoall_ce", "dispatch", "combine", "allgather",
+             "allgather_ce", "ring")
 
 
 def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
@@ -196,12 +197,16 @@ def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
         run_alltoall_row(b, reps, rows)
     if "alltoall_sessions" in only:
         run_alltoall_row(b, reps, rows, sessions=True)
+    if "alltoall_ce" in only:
+        run_alltoall_row(b, reps, rows, copy_engine=True)
     if "dispatch" in only:
         run_dispatch_row(b, reps, rows)
     if "combine" in only:
         run_combine_row(b, reps, rows)
     if "allgather" in only:
         run_allgather_row(b, reps, rows)
+    if "allgather_ce" in only:
+        run_allgather_row(b, reps, rows, copy_engine=True)
     if "ring" in only:
         run_ring_row(b, reps, rows)
     return rows
@@ -233,7 +238,7 @@ def run_allreduce_f32_row(b, reps, rows):
 
 
 
-def run_alltoall_row(b, reps, rows, sessions=False):
+def run_alltoall_row(b, reps, rows, sessions=False, copy_engine=False):
     import workloads as W
     vr, stream = b.vr, b.stream.cuda_stream
     c = W.CONFIGS["c3"]
@@ -248,6 +253,10 @@ def run_alltoall_row(b, reps, rows, sessions=False):
         f = lambda: vr.vr_alltoall_sessions(comm, sw, 0, rw, 0, B, sig=0, barrier_index=0,  # noqa: E731
                                             stream=stream)
         name, kernel, label = "alltoall_sessions_r8_4MiB", "k_alltoall_sessions", "AlltoAll+sessions R=8 B=4MiB"
+    elif copy_engine:  # the same exchange by the copy engines (SDMA), no compute units for the bytes
+        f = lambda: vr.vr_alltoall(comm, sw, 0, rw, 0, B, sig=0, flags=vr.VR_COLL_COPY_ENGINE,  # noqa: E731
+                                   stream=stream)
+        name, kernel, label = "alltoall_copy_engine_r8_4MiB", "sdma", "AlltoAll copy engine R=8 B=4MiB"
     else:
         f = lambda: vr.vr_alltoall(comm, sw, 0, rw, 0, B, sig=0, stream=stream)  # noqa: E731
         name, kernel, label = "alltoall_r8_4MiB", "k_alltoall", "AlltoAll R=8 B=4MiB"
@@ -330,7 +339,7 @@ def run_combine_row(b, reps, rows):
     del s1, r1, o1, tk, wt, counts, src, pos
 
 
-def run_allgather_row(b, reps, rows):
+def run_allgather_row(b, reps, rows, copy_engine=False):
     import workloads as W
     vr, stream = b.vr, b.stream.cuda_stream
     c = W.CONFIGS["c5a"]
@@ -341,11 +350,15 @@ def run_allgather_row(b, reps, rows):
     r1, rv = b.slices(R, R * M, fill=None)
     sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], M)
     rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], R * M)
-    f = lambda: vr.vr_allgather(comm, sw, 0, rw, 0, M, sig=0, stream=stream)  # noqa: E731
+    if copy_engine:  # the bytes moved by the copy engines (SDMA)
+        f = lambda: vr.vr_allgather(comm, sw, 0, rw, 0, M, sig=0, flags=vr.VR_COLL_COPY_ENGINE,  # noqa: E731
+                                    stream=stream)
+        name, kernel, label, n = "allgather_copy_engine_r16_64MiB", "sdma", "AllGather copy engine R=16 M=64MiB", 2
+    else:
+        f = lambda: vr.vr_allgather(comm, sw, 0, rw, 0, M, sig=0, stream=stream)  # noqa: E731
+        name, kernel, label, n = "allgather_r16_64MiB", "k_allgather", "AllGather R=16 M=64MiB", max(3, reps // 2)
     f()
-    rows["allgather_r16_64MiB"] = row_entry("AllGather R=16 M=64MiB", R * M + R * R * M,
-                                            b.timed(f, max(3, reps // 2), True), "k_allgather",
-                                            "allgather_r16_64MiB")
+    rows[name] = row_entry(label, R * M + R * R * M, b.timed(f, n, True), kernel, name)
     vr.vr_window_deregister(comm, sw)
     vr.vr_window_deregister(comm, rw)
     vr.vr_comm_destroy(comm)

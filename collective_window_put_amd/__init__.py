@@ -55,6 +55,8 @@ VR_VA_SIGNAL_INC, VR_VA_SIGNAL_ADD = 4, 5
 VR_DT_F32, VR_DT_BF16 = 0, 1
 VR_OP_SUM = 0
 VR_COLL_NO_WAIT = 0x1
+VR_COLL_COPY_ENGINE = 0x4
+VR_CE_STREAMS = 8
 VR_FENCE_NONE, VR_FENCE_PUT, VR_FENCE_GET = 0x0, 0x1, 0x2
 VR_ASYNC_TIMEOUT, VR_ASYNC_CAPACITY, VR_ASYNC_BAD_EXPERT, VR_ASYNC_LITMUS = 0x1, 0x2, 0x4, 0x8
 

@@ -197,6 +197,18 @@ __global__ void k_signal(uint64_t* sig, uint64_t add) {
   if (threadIdx.x == 0) atomic_add_u64(sig, add);
 }
 
+// After copy-engine puts (all complete in stream order): thread (s, d) applies
+// the SignalInc of put (s, d) at d; then, in workgroup d + 1, receiver d waits.
+__global__ void k_ce_complete(uint64_t* sig, uint32_t stride, int R, vr::U64Tab target, int wait,
+                              uint64_t timeout_ns, uint32_t* err) {
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < R * R; i += blockDim.x) atomic_add_u64(sig + (size_t)(i % R) * stride, 1ull);
+    return;
+  }
+  const int d = blockIdx.x - 1;
+  if (wait && threadIdx.x == 0) wait_reached(sig + (size_t)d * stride, target.v[d], 64, timeout_ns, err, VR_ASYNC_TIMEOUT);
+}
+
 __global__ void k_wait(const uint64_t* word, uint64_t least, int bits, uint64_t timeout_ns, uint32_t* err) {
   if (threadIdx.x == 0) wait_reached(word, least, bits, timeout_ns, err, VR_ASYNC_TIMEOUT);
 }
@@ -228,6 +240,46 @@ vrResult_t enqueue_copy(vrComm* c, char* dst, const char* src, size_t bytes, uin
 
 // ---- internal helpers used by the collectives ---------------------------------------
 namespace vr {
+// Copy-engine puts: ops spread over the internal streams, forked from and
+// joined back into st (default-priority streams).
+struct CeCopy {
+  char* dst;
+  const char* src;
+  size_t bytes;
+};
+vrResult_t ce_puts(vrComm* c, const std::vector<CeCopy>& ops, hipStream_t st) {
+  if (c->ce_streams.empty()) {
+    for (int i = 0; i < VR_CE_STREAMS; ++i) {
+      hipStream_t s;
+      if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return VR_ERR_HIP;
+      c->ce_streams.push_back(s);
+    }
+    for (int i = 0; i <= VR_CE_STREAMS; ++i) {
+      hipEvent_t e;
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return VR_ERR_HIP;
+      c->ce_events.push_back(e);
+    }
+  }
+  const int n = std::min<int>(VR_CE_STREAMS, std::max<int>(1, (int)ops.size()));
+  if (hipEventRecord(c->ce_events[0], st) != hipSuccess) return VR_ERR_HIP;
+  for (int i = 0; i < n; ++i)
+    if (hipStreamWaitEvent(c->ce_streams[i], c->ce_events[0], 0) != hipSuccess) return VR_ERR_HIP;
+  for (size_t k = 0; k < ops.size(); ++k)
+    if (ops[k].bytes && hipMemcpyAsync(ops[k].dst, ops[k].src, ops[k].bytes, hipMemcpyDeviceToDeviceNoCU,
+                                       c->ce_streams[k % n]) != hipSuccess)
+      return VR_ERR_HIP;
+  for (int i = 0; i < n; ++i) {
+    if (hipEventRecord(c->ce_events[1 + i], c->ce_streams[i]) != hipSuccess) return VR_ERR_HIP;
+    if (hipStreamWaitEvent(st, c->ce_events[1 + i], 0) != hipSuccess) return VR_ERR_HIP;
+  }
+  return VR_OK;
+}
+vrResult_t ce_complete(vrComm* c, uint32_t sig, const U64Tab& target, bool wait, hipStream_t st) {
+  hipLaunchKernelGGL(k_ce_complete, dim3(1 + c->nranks), dim3(256), 0, st, c->sig + sig, c->req.signal_count,
+                     c->nranks, target, wait ? 1 : 0, kDefaultTimeoutNs, c->err);
+  return hip_ok(hipGetLastError());
+}
+
 vrDevComm device_view(const vrComm* c) {
   vrDevComm v;
   v.nranks = c->nranks;
@@ -350,6 +402,8 @@ vrResult_t vr_comm_destroy(vrComm_t c) {
   (void)hipDeviceSynchronize();
   if (c->owns_ws) (void)hipFree(c->ws);
   if (c->scratch) (void)hipFree(c->scratch);
+  for (hipStream_t s : c->ce_streams) (void)hipStreamDestroy(s);
+  for (hipEvent_t e : c->ce_events) (void)hipEventDestroy(e);
   {
     std::lock_guard<std::mutex> g(g_mu);
     g_comms.erase(c);
@@ -651,7 +705,7 @@ vrResult_t vr_allreduce(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t
 vrResult_t vr_alltoall(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
                        size_t block, uint32_t sig, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
-  if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~(VR_COLL_NO_WAIT | VR_COLL_COPY_ENGINE)) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (block > (size_t(1) << 40)) return VR_ERR_INVALID_ARGUMENT;
   const size_t n = block * R;
@@ -662,7 +716,17 @@ vrResult_t vr_alltoall(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t 
   U64Tab t;
   vrResult_t r = inc_targets(c, sig, R, wait, &t);
   if (r != VR_OK) return r;
-  r = launch_alltoall(c, send, send_off, recv, recv_off, block, sig, t, wait, S(stream));
+  if (flags & VR_COLL_COPY_ENGINE) {
+    std::vector<CeCopy> ops;
+    for (int s = 0; s < R; ++s)  // destination-major, so consecutive copies target different ranks
+      for (int d = 0; d < R; ++d)
+        ops.push_back({recv->base[(d + s) % R] + recv_off + (size_t)s * block,
+                       send->base[s] + send_off + (size_t)((d + s) % R) * block, block});
+    r = ce_puts(c, ops, S(stream));
+    if (r == VR_OK) r = ce_complete(c, sig, t, wait, S(stream));
+  } else {
+    r = launch_alltoall(c, send, send_off, recv, recv_off, block, sig, t, wait, S(stream));
+  }
   if (r == VR_OK) commit_inc(c, sig, R);
   return r;
 }
@@ -693,7 +757,7 @@ vrResult_t vr_alltoall_sessions(vrComm_t c, vrWindow_t send, size_t send_off, vr
 vrResult_t vr_allgather(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
                         size_t bytes, uint32_t sig, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
-  if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~(VR_COLL_NO_WAIT | VR_COLL_COPY_ENGINE)) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (bytes > (size_t(1) << 40)) return VR_ERR_INVALID_ARGUMENT;
   if (!span_ok(send, send_off, bytes) || !span_ok(recv, recv_off, bytes * R)) return VR_ERR_INVALID_ARGUMENT;
@@ -704,7 +768,16 @@ vrResult_t vr_allgather(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t
   U64Tab t;
   vrResult_t r = inc_targets(c, sig, R, wait, &t);
   if (r != VR_OK) return r;
-  r = launch_allgather(c, send, send_off, recv, recv_off, bytes, sig, t, wait, S(stream));
+  if (flags & VR_COLL_COPY_ENGINE) {
+    std::vector<CeCopy> ops;
+    for (int s = 0; s < R; ++s)
+      for (int d = 0; d < R; ++d)
+        ops.push_back({recv->base[(d + s) % R] + recv_off + (size_t)s * bytes, send->base[s] + send_off, bytes});
+    r = ce_puts(c, ops, S(stream));
+    if (r == VR_OK) r = ce_complete(c, sig, t, wait, S(stream));
+  } else {
+    r = launch_allgather(c, send, send_off, recv, recv_off, bytes, sig, t, wait, S(stream));
+  }
   if (r == VR_OK) commit_inc(c, sig, R);
   return r;
 }

@@ -63,6 +63,9 @@ struct vrComm {
   std::vector<uint8_t> expect_known; // 0 when a device-computed amount was added
   std::vector<uint8_t> sig_mode;     // 0 none, 1 SignalInc, 2 SignalAdd (since the last reset)
   std::vector<uint64_t> bar_expect;  // [barrier_count] slot values once enqueued work has run
+  // copy-engine path: internal streams and fork/join events, created on first use
+  std::vector<hipStream_t> ce_streams;
+  std::vector<hipEvent_t> ce_events;  // [0] fork, [1 + i] join of stream i
   std::set<vrWindow*> windows;
 };
 

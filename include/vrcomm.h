@@ -287,7 +287,15 @@ vrResult_t vr_counter_reset(vrComm_t comm, int rank, uint32_t id, void* stream);
 #define VR_DT_BF16  1
 #define VR_OP_SUM   0
 /* flags */
-#define VR_COLL_NO_WAIT  0x1u  /* skip the in-kernel receiver waits (signals are still applied) */
+#define VR_COLL_NO_WAIT      0x1u  /* skip the in-kernel receiver waits (signals are still applied) */
+/* vr_alltoall and vr_allgather: move the bytes with the copy engines (SDMA)
+ * instead of compute units (Symmetric page, AllGather with the copy engine),
+ * one copy per (s, d) spread over VR_CE_STREAMS internal streams that fork
+ * from and join back into the caller's stream; then one kernel applies the
+ * SignalIncs (each rank's signal rises by R) and, unless VR_COLL_NO_WAIT,
+ * the receivers' waits. Offsets and sizes need no alignment. */
+#define VR_COLL_COPY_ENGINE  0x4u
+#define VR_CE_STREAMS        8
 
 /* Sum-AllReduce over `count` elements at send_off of every rank's send slice;
  * every rank's recv slice receives the sum at recv_off.

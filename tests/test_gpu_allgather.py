@@ -13,14 +13,14 @@ from gpu_util import Job, say
 pytestmark = pytest.mark.gpu
 
 
-def _run(sends, M, send_off=0, recv_off=0, sig=1):
+def _run(sends, M, send_off=0, recv_off=0, sig=1, flags=0):
     R = len(sends)
     with Job(R) as job:
         sw, sv = job.window(send_off + M, fill=0)
         rw, rv = job.window(recv_off + R * M, fill=0x5A)
         for r in range(R):
             sv[r][send_off:].copy_(job.torch.from_numpy(sends[r]))
-        vr.vr_allgather(job.comm, sw, send_off, rw, recv_off, M, sig=sig)
+        vr.vr_allgather(job.comm, sw, send_off, rw, recv_off, M, sig=sig, flags=flags)
         out = job.host(rv)
         sigs = [job.sig(d, sig) for d in range(R)]
         job.assert_no_async_error()
@@ -79,3 +79,16 @@ def test_allgather_config_c5a_full_size():
             del got
         assert [job.sig(d, 0) for d in range(R)] == [R] * R
         job.assert_no_async_error()
+
+
+@pytest.mark.parametrize("R,M,send_off,recv_off", [(2, 1, 0, 0), (3, 16385, 7, 3), (8, 1 << 20, 0, 0),
+                                                   (16, 32768 + 16, 16, 4096)])
+def test_allgather_copy_engine_vs_oracle(R, M, send_off, recv_off):
+    say(f"allgather copy engine R={R} M={M}")
+    sends = W.allgather_inputs(R, M, seed=R * 5 + M)
+    out, sigs = _run(sends, M, send_off, recv_off, flags=vr.VR_COLL_COPY_ENGINE)
+    exp = D.allgather(sends)
+    for d in range(R):
+        assert np.array_equal(out[d][recv_off:], exp[d]), d
+        assert np.all(out[d][:recv_off] == 0x5A)
+    assert sigs == [R] * R

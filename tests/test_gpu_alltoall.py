@@ -13,14 +13,14 @@ from gpu_util import Job, say
 pytestmark = pytest.mark.gpu
 
 
-def _run(R, B, sends, send_off=0, recv_off=0, repeats=1, sig=3):
+def _run(R, B, sends, send_off=0, recv_off=0, repeats=1, sig=3, flags=0):
     with Job(R) as job:
         sw, sv = job.window(send_off + R * B, fill=0)
         rw, rv = job.window(recv_off + R * B, fill=0xAB)
         for r in range(R):
             sv[r][send_off:].copy_(job.torch.from_numpy(sends[r]))
         for rep in range(repeats):
-            vr.vr_alltoall(job.comm, sw, send_off, rw, recv_off, B, sig=sig)
+            vr.vr_alltoall(job.comm, sw, send_off, rw, recv_off, B, sig=sig, flags=flags)
         out = job.host(rv)
         sigs = [job.sig(d, sig) for d in range(R)]
         job.assert_no_async_error()
@@ -83,3 +83,16 @@ def test_alltoall_full_size_config():
     for d in range(R):
         assert np.array_equal(out[d], exp[d]), d
     assert sigs == [R] * R
+
+
+@pytest.mark.parametrize("R,B,send_off,recv_off", [(2, 1, 0, 0), (4, 4096, 0, 0), (5, 16385, 3, 7),
+                                                   (8, 65536 + 48, 16, 0), (16, 1000, 0, 5)])
+def test_alltoall_copy_engine_vs_oracle(R, B, send_off, recv_off):
+    say(f"alltoall copy engine R={R} B={B} offsets {send_off},{recv_off}")
+    sends = W.alltoall_inputs(R, B, seed=R * 11 + B)
+    out, sigs = _run(R, B, sends, send_off, recv_off, repeats=2, flags=vr.VR_COLL_COPY_ENGINE)
+    exp = D.alltoall(sends, B)
+    for d in range(R):
+        assert np.array_equal(out[d][recv_off:], exp[d]), d
+        assert np.all(out[d][:recv_off] == 0xAB)
+    assert sigs == [2 * R] * R
