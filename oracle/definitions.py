@@ -280,3 +280,105 @@ def signal_increment(kind: str, nranks: int) -> int:
     if kind in ("allreduce", "alltoall", "allgather", "dispatch_counts"):
         return nranks
     raise ValueError(kind)
+
+
+# -- dispatch with one row per (token, destination rank) --------------------------
+def dispatch_dedup(topk_idx: np.ndarray, x_rows: np.ndarray, num_experts: int,
+                   capacity_rows: int | None = None):
+    """The dispatch in the per-rank layout: each token lands once on every rank
+    that owns at least one of its experts.
+
+    Reading (the pages describe the per-expert dispatch; this is the layout
+    that sends a token once per destination rank instead of once per
+    expert): rank d's rows are ordered by source rank, then token index, one
+    row per token of any source routed to d. Each row carries the tag
+    ``(s << 16) | t`` and the token's K entries as seen by d: the local
+    expert index ``e - d*E/R`` where ``e`` belongs to d, else -1.
+
+    Returns ``(rows, src, experts, counts, overflow)`` per destination rank:
+    ``rows[d]`` [n_d, row_bytes] uint8, ``src[d]`` int32 tags, ``experts[d]``
+    int32 [n_d, K], ``counts[d]`` int32 rows per local expert (one per routing
+    entry naming it, as in ``dispatch``), ``overflow[d]``.
+    """
+    topk_idx = np.asarray(topk_idx)
+    R, T, K = topk_idx.shape
+    if num_experts % R:
+        raise ValueError("num_experts must be a multiple of the rank count")
+    epr = num_experts // R
+    x_rows = np.asarray(x_rows)
+    row_bytes = x_rows[0].reshape(T, -1).view(np.uint8).shape[1] if T else 0
+    xb = [x_rows[s].reshape(T, -1).view(np.uint8) for s in range(R)]
+    for e in topk_idx.reshape(-1):
+        if e != -1 and not 0 <= e < num_experts:
+            raise ValueError(f"expert id {e} out of range")
+    rows, src, experts, counts, overflow = [], [], [], [], []
+    for d in range(R):
+        mine = []  # (s, t), source-major then token
+        c = np.zeros(epr, dtype=np.int32)
+        for s in range(R):
+            for t in range(T):
+                local = [int(e) - d * epr if e >= 0 and e // epr == d else -1 for e in topk_idx[s, t]]
+                if any(v >= 0 for v in local):
+                    mine.append((s, t, local))
+                    for v in local:
+                        if v >= 0:
+                            c[v] += 1
+        counts.append(c)
+        overflow.append(capacity_rows is not None and len(mine) > capacity_rows)
+        if capacity_rows is not None:
+            mine = mine[:capacity_rows]
+        rows.append(np.stack([xb[s][t] for (s, t, _) in mine]) if mine
+                    else np.zeros((0, row_bytes), dtype=np.uint8))
+        src.append(np.array([(s << 16) | t for (s, t, _) in mine], dtype=np.int32))
+        experts.append(np.array([loc for (_, _, loc) in mine], dtype=np.int32).reshape(len(mine), K))
+    return rows, src, experts, counts, overflow
+
+
+def dispatch_dedup_positions(topk_idx: np.ndarray, num_experts: int,
+                             capacity_rows: int | None = None) -> np.ndarray:
+    """Row of token (s, t) at each destination rank d, int32 ``[R, T, R]``;
+    -1 where the token is not routed to d or its row fell past the capacity."""
+    topk_idx = np.asarray(topk_idx)
+    R, T, K = topk_idx.shape
+    epr = num_experts // R
+    pos = np.full((R, T, R), -1, dtype=np.int32)
+    for d in range(R):
+        n = 0
+        for s in range(R):
+            for t in range(T):
+                if any(e >= 0 and e // epr == d for e in topk_idx[s, t]):
+                    if capacity_rows is None or n < capacity_rows:
+                        pos[s, t, d] = n
+                    n += 1
+    return pos
+
+
+def combine_dedup(pos: np.ndarray, y_rows, dtype: str = "bf16") -> np.ndarray:
+    """Combine in the per-rank layout: each destination rank returns one row
+    per token (its experts' outputs already mixed there), and the token's
+    rank sums them in rank order.
+
+    For source s and token t: ``acc = +0.0``, then for d = 0 .. R-1 with
+    ``pos[s,t,d] != -1``, ``acc = acc + y[d][pos[s,t,d]]`` (binary32, nearest
+    even); bf16 rows widened exactly and the sum rounded to bf16 (RNE).
+    Returns ``[R, T, H]``.
+    """
+    pos = np.asarray(pos)
+    R, T, _ = pos.shape
+    if dtype == "bf16":
+        ys = [bf16_bits_to_f32(np.asarray(y, dtype=np.uint16)) for y in y_rows]
+    elif dtype == "f32":
+        ys = [np.asarray(y, dtype=np.float32) for y in y_rows]
+    else:
+        raise ValueError(dtype)
+    H = ys[0].shape[1]
+    out = np.zeros((R, T, H), dtype=np.float32)
+    for s in range(R):
+        for t in range(T):
+            acc = np.zeros(H, dtype=np.float32)
+            for d in range(R):
+                p = int(pos[s, t, d])
+                if p >= 0:
+                    acc = acc + ys[d][p]
+            out[s, t] = acc
+    return f32_to_bf16_bits_rne(out) if dtype == "bf16" else out

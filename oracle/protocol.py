@@ -567,3 +567,126 @@ def combine_programs(world: World, b: CombineBuffers, sig: int):
         yield Barrier()
 
     return [prog(s) for s in range(R)]
+
+
+class DedupBuffers:
+    """Windows one per-rank (dedup) dispatch needs on the oracle's world."""
+
+    def __init__(self, world: World, x_bits: np.ndarray, topk_idx: np.ndarray,
+                 num_experts: int, capacity_rows: int):
+        R, T, K = topk_idx.shape
+        self.R, self.T, self.K, self.E = R, T, K, num_experts
+        self.epr = num_experts // R
+        self.cap = capacity_rows
+        xb = [np.ascontiguousarray(x_bits[s]).reshape(T, -1).view(np.uint8) for s in range(R)]
+        self.row_bytes = xb[0].shape[1] if T else 0
+        self.topk = np.asarray(topk_idx)
+        self.x = world.register([b.reshape(-1).copy() for b in xb])
+        self.cnt_send = world.register_zeros(4 * R)
+        self.cnt_all = world.register_zeros(4 * R * R)
+        self.stage = world.register_zeros(max(1, T * R * self.row_bytes))
+        self.stage_meta = world.register_zeros(max(4, 4 * T * R * (1 + K)))
+        self.recv = world.register_zeros(max(1, capacity_rows * self.row_bytes))
+        self.recv_meta = world.register_zeros(max(4, 4 * capacity_rows * (1 + K)))  # tag, then K local ids
+        self.pos = np.full((R, T, R), -1, dtype=np.int32)
+        self.overflow = [False] * R
+
+
+def dispatch_dedup_programs(world: World, b: DedupBuffers, sig_counts: int, sig_rows: int):
+    """Per-rank dispatch, step by step: count the tokens bound for each rank
+    and exchange the counts (SignalInc), take the offsets from the count
+    matrix, then put each destination's packed rows with their tags and local
+    expert lists, closed by one SignalAdd(rows) per destination."""
+    R, T, K, epr, rb = b.R, b.T, b.K, b.epr, b.row_bytes
+
+    def dests(s, t):
+        return sorted({int(e) // epr for e in b.topk[s, t] if e >= 0})
+
+    def prog(s):
+        base_c = yield ReadSignal(sig_counts)
+        base_r = yield ReadSignal(sig_rows)
+        yield Barrier()
+
+        def histogram(w, me):
+            c = np.zeros(R, dtype=np.int32)
+            for t in range(T):
+                for d in dests(me, t):
+                    c[d] += 1
+            w.buf(b.cnt_send, me)[:] = c.view(np.uint8)
+
+        yield Local(histogram, "histogram")
+        for d in range(R):
+            yield Put(d, b.cnt_all, s * R * 4, b.cnt_send, 0, R * 4, SignalInc(sig_counts))
+        yield WaitSignal(sig_counts, base_c + R)
+        C = world.buf(b.cnt_all, s).view(np.int32).reshape(R, R).astype(np.int64)
+        off = C[:s].sum(axis=0)  # rows of earlier sources at each destination
+        my_rows = int(C[:, s].sum())
+        b.overflow[s] = my_rows > b.cap
+        so = 0
+        for d in range(R):
+            toks = [t for t in range(T) if d in dests(s, t)]
+            n = len(toks)
+            if n == 0:
+                continue
+
+            def pack(w, me, toks=toks, so=so, d=d):
+                w.buf(b.stage, me)[so * rb:(so + len(toks)) * rb] = w.buf(b.x, me).reshape(T, rb)[toks].reshape(-1)
+                meta = np.array([[(me << 16) | t] + [int(e) - d * epr if e >= 0 and e // epr == d else -1
+                                                     for e in b.topk[me, t]] for t in toks], dtype=np.int32)
+                w.buf(b.stage_meta, me)[so * 4 * (1 + K):(so + len(toks)) * 4 * (1 + K)] = meta.view(np.uint8).reshape(-1)
+
+            yield Local(pack, f"pack d={d}")
+            keep = max(0, min(n, b.cap - int(off[d])))
+            for i, t in enumerate(toks):
+                if off[d] + i < b.cap:
+                    b.pos[s, t, d] = off[d] + i
+            if keep:
+                yield Put(d, b.recv, int(off[d]) * rb, b.stage, so * rb, keep * rb)
+                yield Put(d, b.recv_meta, int(off[d]) * 4 * (1 + K), b.stage_meta, so * 4 * (1 + K),
+                          keep * 4 * (1 + K))
+            yield Signal(d, SignalAdd(sig_rows, n, True))
+            so += n
+        yield WaitSignal(sig_rows, base_r + my_rows)
+        yield Barrier()
+
+    return [prog(s) for s in range(R)]
+
+
+def combine_dedup_programs(world: World, y_win: int, out_win: int, pos: np.ndarray, row_bytes: int,
+                           dtype: str, sig: int):
+    """Per-rank combine, step by step: every source gets its tokens' rows from
+    each destination rank they reached, sums them in rank order, then
+    SignalIncs every rank that its rows have been read."""
+    R, T, _ = pos.shape
+    esize = 2 if dtype == "bf16" else 4
+    stage = world.register_zeros(max(1, T * R * row_bytes))
+
+    def prog(s):
+        base = yield ReadSignal(sig)
+        yield Barrier()
+        for t in range(T):
+            for d in range(R):
+                if pos[s, t, d] >= 0:
+                    yield Get(d, y_win, int(pos[s, t, d]) * row_bytes, stage, (t * R + d) * row_bytes, row_bytes)
+
+        def mix(w, me):
+            from .definitions import bf16_bits_to_f32, f32_to_bf16_bits_rne
+            st = w.buf(stage, me).reshape(T, R, row_bytes)
+            out = np.zeros((T, row_bytes // esize), dtype=np.float32)
+            for t in range(T):
+                acc = np.zeros(row_bytes // esize, dtype=np.float32)
+                for d in range(R):
+                    if pos[me, t, d] >= 0:
+                        acc = acc + (bf16_bits_to_f32(st[t, d].view(np.uint16)) if dtype == "bf16"
+                                     else st[t, d].view(np.float32))
+                out[t] = acc
+            res = f32_to_bf16_bits_rne(out) if dtype == "bf16" else out
+            w.buf(out_win, me)[:T * row_bytes] = res.view(np.uint8).reshape(-1)
+
+        yield Local(mix, "mix")
+        for d in range(R):
+            yield Signal(d, SignalInc(sig))
+        yield WaitSignal(sig, base + R)
+        yield Barrier()
+
+    return [prog(s) for s in range(R)]

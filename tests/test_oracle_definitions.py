@@ -418,3 +418,87 @@ def test_combine_skips_entries_without_rows():
     # rank 1 rows: e2 (1,1) -> row0, e3 (1,1) -> row1
     assert out[:, :, 0].tolist() == [[0.5, 1.0], [0.0, 6.0]]
     assert np.signbit(out[1, 0, 0]) == False  # noqa: E712 -- a token with no rows is +0.0
+
+
+# -- per-rank (dedup) dispatch and its combine -----------------------------------------
+def _dedup_case(R, T, H, E, K, seed, drop=0.0):
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    if drop:
+        topk[np.random.default_rng(seed).random(topk.shape) < drop] = -1
+    return topk, x
+
+
+@pytest.mark.parametrize("R,T,H,E,K,seed,drop", [(2, 30, 4, 4, 2, 1, 0.0), (4, 80, 2, 16, 3, 2, 0.25),
+                                                  (3, 50, 3, 6, 2, 3, 0.1), (8, 40, 2, 64, 8, 4, 0.0)])
+def test_dedup_dispatch_against_the_per_expert_dispatch(R, T, H, E, K, seed, drop):
+    topk, x = _dedup_case(R, T, H, E, K, seed, drop)
+    epr = E // R
+    rows, src, experts, counts, over = D.dispatch_dedup(topk, x, E)
+    prow, psrc, pcounts, _ = D.dispatch(topk, x, E)
+    xb = x.reshape(R, T, -1).view(np.uint8)
+    for d in range(R):
+        # library form: the unique (s, t) of d's per-expert rows, in (s, t) order
+        st = np.unique(psrc[d]) if len(psrc[d]) else np.zeros(0, np.int32)
+        assert np.array_equal(src[d], st.astype(np.int32))
+        assert np.array_equal(rows[d], xb[src[d] >> 16, src[d] & 0xFFFF])
+        # the experts lists hold exactly the per-expert layout's (s, t, e) entries of d
+        got = sorted((int(tag) >> 16, int(tag) & 0xFFFF, d * epr + int(v))
+                     for tag, loc in zip(src[d], experts[d]) for v in loc if v >= 0)
+        want = []
+        off = 0
+        for j in range(epr):
+            for tag in psrc[d][off:off + pcounts[d][j]]:
+                want.append((int(tag) >> 16, int(tag) & 0xFFFF, d * epr + j))
+            off += pcounts[d][j]
+        assert got == sorted(want)
+        assert np.array_equal(counts[d], pcounts[d])
+        assert not over[d]
+    # per token: the ranks it reaches, each once
+    for s in range(R):
+        for t in range(T):
+            dests = {int(e) // epr for e in topk[s, t] if e >= 0}
+            seen = {d for d in range(R) if ((s << 16) | t) in set(src[d].tolist())}
+            assert seen == dests
+
+
+def test_dedup_positions_point_at_the_rows_and_capacity():
+    R, T, H, E, K = 4, 60, 2, 16, 4
+    topk, x = _dedup_case(R, T, H, E, K, 5, 0.2)
+    rows, src, _, _, _ = D.dispatch_dedup(topk, x, E)
+    pos = D.dispatch_dedup_positions(topk, E)
+    for s in range(R):
+        for t in range(T):
+            for d in range(R):
+                p = pos[s, t, d]
+                if p >= 0:
+                    assert src[d][p] == (s << 16) | t
+                else:
+                    assert ((s << 16) | t) not in set(src[d].tolist())
+    cap = 7
+    pc = D.dispatch_dedup_positions(topk, E, capacity_rows=cap)
+    assert np.array_equal(pc, np.where(pos < cap, pos, -1))
+    rows_c, src_c, _, _, over_c = D.dispatch_dedup(topk, x, E, capacity_rows=cap)
+    assert all(len(v) <= cap for v in src_c) and any(over_c)
+
+
+def test_combine_dedup_unit_rows_give_the_destination_count_times_x():
+    import torch
+    R, T, H, E, K = 4, 50, 16, 16, 3
+    topk, x = _dedup_case(R, T, H, E, K, 6, 0.15)
+    rows, _, _, _, _ = D.dispatch_dedup(topk, x, E)
+    pos = D.dispatch_dedup_positions(topk, E)
+    y = [r.view(np.uint16).reshape(r.shape[0], H) for r in rows]  # identity experts
+    out = D.combine_dedup(pos, y)
+    n = (pos >= 0).sum(axis=2).astype(np.float32)[:, :, None]
+    want = torch.from_numpy(D.bf16_bits_to_f32(x) * n).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out, want)
+
+
+def test_combine_dedup_hand_worked_rank_order():
+    # three destinations; 2^24 + 1 ties to even, so rank order 0, 1, 2 gives 0
+    pos = np.array([[[0, 0, 0]], [[-1, -1, -1]], [[-1, -1, -1]]], dtype=np.int32)  # R=3, T=1
+    y = [np.array([[2.0 ** 24]], np.float32), np.array([[1.0]], np.float32), np.array([[-(2.0 ** 24)]], np.float32)]
+    out = D.combine_dedup(pos, y, "f32")
+    assert out[0, 0, 0] == 0.0 and out[1, 0, 0] == 0.0 and not np.signbit(out[1, 0, 0])
+    y2 = [y[2], y[1], y[0]]
+    assert D.combine_dedup(pos, y2, "f32")[0, 0, 0] == 1.0

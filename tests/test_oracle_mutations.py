@@ -202,3 +202,25 @@ def test_va_word_overlap_off_by_one_is_caught(monkeypatch):
     monkeypatch.setattr(World, "_check_plain_access", loose)
     with pytest.raises(pytest.fail.Exception):
         TP.test_plain_access_to_a_va_signal_word_is_refused()
+
+
+def test_dedup_token_major_order_is_caught(monkeypatch):
+    orig = D.dispatch_dedup
+
+    def token_major(topk, x, E, capacity_rows=None):
+        rows, src, experts, counts, over = orig(topk, x, E, capacity_rows)
+        for d in range(len(rows)):  # order by token, then source: a plausible slip
+            order = np.lexsort((src[d] >> 16, src[d] & 0xFFFF))
+            rows[d], src[d], experts[d] = rows[d][order], src[d][order], experts[d][order]
+        return rows, src, experts, counts, over
+    monkeypatch.setattr(D, "dispatch_dedup", token_major)
+    _fails(TD.test_dedup_dispatch_against_the_per_expert_dispatch, 4, 80, 2, 16, 3, 2, 0.25)
+
+
+def test_combine_dedup_reversed_rank_order_is_caught(monkeypatch):
+    orig = D.combine_dedup
+
+    def reversed_ranks(pos, y_rows, dtype="bf16"):
+        return orig(np.asarray(pos)[:, :, ::-1], list(y_rows)[::-1], dtype)
+    monkeypatch.setattr(D, "combine_dedup", reversed_ranks)
+    _fails(TD.test_combine_dedup_hand_worked_rank_order)

@@ -280,3 +280,56 @@ def test_combine_protocol_matches_definition(R, T, H, E, K, seed, dtype):
 
 def test_combine_every_interleaving_two_ranks():
     assert _run_combine(2, 2, 2, 4, 2, 9, every=True) == 1
+
+
+@pytest.mark.parametrize("R,T,H,E,K,seed,cap", [(4, 30, 4, 16, 3, 0, None), (2, 25, 2, 4, 2, 1, 12),
+                                                 (3, 20, 2, 6, 2, 2, None)])
+def test_dedup_dispatch_and_combine_protocols_match_definitions(R, T, H, E, K, seed, cap):
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    topk[np.random.default_rng(seed).random(topk.shape) < 0.2] = -1
+    cap = cap if cap is not None else R * T
+    w = World(R)
+    b = pr.DedupBuffers(w, x, topk, E, cap)
+    pr.run(w, pr.dispatch_dedup_programs(w, b, 0, 1), seed=seed)
+    rows, src, experts, counts, over = D.dispatch_dedup(topk, x, E, cap)
+    for d in range(R):
+        n, rb = rows[d].shape
+        assert np.array_equal(w.buf(b.recv, d)[:n * rb], rows[d].reshape(-1))
+        meta = w.buf(b.recv_meta, d)[:n * 4 * (1 + K)].view(np.int32).reshape(n, 1 + K)
+        assert np.array_equal(meta[:, 0], src[d]) and np.array_equal(meta[:, 1:], experts[d])
+        assert w.sig[d][0] == R
+        assert w.sig[d][1] == sum(1 for s in range(R) for t in range(T)
+                                  if any(e >= 0 and e // (E // R) == d for e in topk[s, t]))
+        assert b.overflow[d] == over[d]
+    assert np.array_equal(b.pos, D.dispatch_dedup_positions(topk, E, cap))
+    # combine the dispatched rows back (identity experts) through the protocol
+    y_win = b.recv
+    out_win = w.register_zeros(max(1, T * b.row_bytes))
+    pr.run(w, pr.combine_dedup_programs(w, y_win, out_win, b.pos, b.row_bytes, "bf16", 2), seed=seed)
+    y = [w.buf(b.recv, d).reshape(cap, b.row_bytes).view(np.uint16) for d in range(R)]
+    want = D.combine_dedup(b.pos, y)
+    for s in range(R):
+        assert np.array_equal(w.buf(out_win, s)[:T * b.row_bytes].view(np.uint16).reshape(T, -1), want[s])
+        assert w.sig[s][2] == R
+
+
+def test_dedup_dispatch_every_interleaving_two_ranks():
+    R, T, H, E, K = 2, 3, 1, 4, 2
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=8)
+    rows, src, experts, _, _ = D.dispatch_dedup(topk, x, E)
+    bufs = []
+
+    def setup():
+        w = World(R)
+        b = pr.DedupBuffers(w, x, topk, E, R * T)
+        bufs.append(b)
+        return w, pr.dispatch_dedup_programs(w, b, 0, 1)
+
+    n = 0
+    for w in pr.distinct_final_states(setup):
+        b = bufs[-1]
+        for d in range(R):
+            k, rb = rows[d].shape
+            assert np.array_equal(w.buf(b.recv, d)[:k * rb], rows[d].reshape(-1))
+        n += 1
+    assert n == 1
