@@ -38,7 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "k_allreduce": "allreduce.hip", "k_alltoall": "alltoall.hip", "k_allgather": "allgather.hip",
     "k_dispatch": "dispatch.hip", "k_combine": "combine.hip", "k_ring": "ring.hip",
-    "k_alltoall_sessions": "sessions.hip",
+    "k_alltoall_sessions": "sessions.hip", "k_dispatch_dedup": "dispatch.hip", "k_combine_dedup": "combine.hip",
 }
 
 
@@ -184,8 +184,8 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
 
 
 # ---- the other workloads ------------------------------------------------------------------------
-ROW_NAMES = ("allreduce_f32", "alltoall", "alltoall_sessions", "alltoall_ce", "dispatch", "combine", "allgather",
-             "allgather_ce", "ring")
+ROW_NAMES = ("allreduce_f32", "alltoall", "alltoall_sessions", "alltoall_ce", "dispatch", "combine", "dedup",
+             "allgather", "allgather_ce", "ring")
 
 
 def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
@@ -203,6 +203,8 @@ def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
         run_dispatch_row(b, reps, rows)
     if "combine" in only:
         run_combine_row(b, reps, rows)
+    if "dedup" in only:
+        run_dedup_rows(b, reps, rows)
     if "allgather" in only:
         run_allgather_row(b, reps, rows)
     if "allgather_ce" in only:
@@ -337,6 +339,53 @@ def run_combine_row(b, reps, rows):
         vr.vr_window_deregister(comm, w)
     vr.vr_comm_destroy(comm)
     del s1, r1, o1, tk, wt, counts, src, pos
+
+
+def run_dedup_rows(b, reps, rows):
+    """The per-rank (dedup) dispatch and its combine on the dispatch workload."""
+    import workloads as W
+    vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
+    c = W.CONFIGS["c4"]
+    R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
+    topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
+    rb = H * 2
+    cap = R * T
+    comm = comm_for(vr, R, signal_count=4)
+    s1, xv = b.slices(R, T * rb, arrays=[x[r] for r in range(R)])
+    r1, rv = b.slices(R, cap * rb, fill=0)
+    o1, ov = b.slices(R, T * rb, fill=0)
+    xw = vr.vr_window_register(comm, [v.data_ptr() for v in xv], T * rb)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], cap * rb)
+    ow = vr.vr_window_register(comm, [v.data_ptr() for v in ov], T * rb)
+    tk = torch.from_numpy(topk).cuda()
+    counts = torch.zeros(R, E // R, dtype=torch.int32, device="cuda")
+    src = torch.zeros(R, cap, dtype=torch.int32, device="cuda")
+    experts = torch.zeros(R, cap, K, dtype=torch.int32, device="cuda")
+    pos = torch.zeros(R, T, R, dtype=torch.int32, device="cuda")
+    fd = lambda: vr.vr_dispatch_dedup(comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, experts,  # noqa: E731
+                                      pos, 0, 1, stream=stream)
+    fd()
+    epr = E // R
+    nrows = int(sum(len({int(e) // epr for e in topk[s, t] if e >= 0}) for s in range(R) for t in range(T)))
+    bytes_d = R * T * rb + topk.nbytes + nrows * (rb + 4 + 4 * K) + R * epr * 4 + pos.numel() * 4
+    rows["dispatch_dedup_r8_t4096_e256_k8"] = row_entry("dedup dispatch R=8 T=4096 512B E=256 K=8", bytes_d,
+                                                        b.timed(fd, reps, True), "k_dispatch_dedup",
+                                                        "dispatch_dedup_r8_t4096_e256_k8", {"rows": nrows})
+    # combine: the dispatched rows stand in for each rank's mixed expert outputs
+    fc = lambda: vr.vr_combine_dedup(comm, rw, 0, cap, rb, vr.VR_DT_BF16, pos, T, ow, 0, 2,  # noqa: E731
+                                     stream=stream)
+    fc()
+    bytes_c = nrows * rb + R * T * rb + pos.numel() * 4
+    rows["combine_dedup_r8_t4096_e256_k8"] = row_entry("dedup combine R=8 T=4096 512B E=256 K=8", bytes_c,
+                                                       b.timed(fc, reps, True), "k_combine_dedup",
+                                                       "combine_dedup_r8_t4096_e256_k8", {"rows": nrows})
+    code, bits = vr.vr_comm_get_async_error(comm)
+    if code != vr.VR_OK:
+        raise RuntimeError(f"device error in the dedup rows: {vr.vr_error_string(code)} bits={bits:#x}")
+    for w in (xw, rw, ow):
+        vr.vr_window_deregister(comm, w)
+    vr.vr_comm_destroy(comm)
+    del s1, r1, o1, tk, counts, src, experts, pos
 
 
 def run_allgather_row(b, reps, rows, copy_engine=False):

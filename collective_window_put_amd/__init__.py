@@ -148,6 +148,10 @@ SYMBOLS = {
                          _P, c_uint32, c_uint32, c_uint32, _P]),
     "vr_combine": (_R, [_P, _P, c_size_t, c_size_t, c_size_t, c_int, _P, _P, _P, c_int, c_int, c_int, _P,
                         c_size_t, c_uint32, c_uint32, _P]),
+    "vr_dispatch_dedup": (_R, [_P, _P, c_size_t, c_size_t, _P, c_int, c_int, c_int, _P, c_size_t, c_size_t, _P, _P,
+                               _P, _P, c_uint32, c_uint32, c_uint32, _P]),
+    "vr_combine_dedup": (_R, [_P, _P, c_size_t, c_size_t, c_size_t, c_int, _P, c_int, _P, c_size_t, c_uint32,
+                              c_uint32, _P]),
     "vr_ring_exchange": (_R, [_P, _P, _P, c_size_t, c_size_t, c_int, c_uint32, c_uint32, _P, c_size_t, _P,
                               c_uint32, _P]),
     "vr_va_signal_wait": (_R, [_P, _P, c_int, c_size_t, c_uint64, c_int, c_uint64, _P]),
@@ -384,6 +388,20 @@ def vr_dispatch(comm, x, x_off, row_bytes, topk_idx, T, K, num_experts, recv, re
     _check(lib().vr_dispatch(comm, x, x_off, row_bytes, _ptr(topk_idx), T, K, num_experts, recv, recv_off,
                              capacity_rows, _ptr(recv_expert_counts), _ptr(recv_src), _ptr(send_pos), sig_counts,
                              sig_rows, flags, _stream(stream)), "vr_dispatch")
+
+
+def vr_dispatch_dedup(comm, x, x_off, row_bytes, topk_idx, T, K, num_experts, recv, recv_off, capacity_rows,
+                      recv_expert_counts, recv_src, recv_experts, send_pos, sig_counts, sig_rows, flags=0,
+                      stream=None):
+    _check(lib().vr_dispatch_dedup(comm, x, x_off, row_bytes, _ptr(topk_idx), T, K, num_experts, recv, recv_off,
+                                   capacity_rows, _ptr(recv_expert_counts), _ptr(recv_src), _ptr(recv_experts),
+                                   _ptr(send_pos), sig_counts, sig_rows, flags, _stream(stream)), "vr_dispatch_dedup")
+
+
+def vr_combine_dedup(comm, y, y_off, y_capacity_rows, row_bytes, dtype, send_pos, T, out, out_off, sig, flags=0,
+                     stream=None):
+    _check(lib().vr_combine_dedup(comm, y, y_off, y_capacity_rows, row_bytes, dtype, _ptr(send_pos), T, out,
+                                  out_off, sig, flags, _stream(stream)), "vr_combine_dedup")
 
 
 def vr_combine(comm, y, y_off, y_capacity_rows, row_bytes, dtype, topk_idx, weights, send_pos, T, K, num_experts,

@@ -48,6 +48,7 @@ struct CombArgs {
   uint32_t* err;
   uint64_t timeout_ns;
   int R, T, K, E, nblk;
+  int dedup;  // entries are destination ranks (k = d), weight 1, no topk or weights
 };
 
 template <int DT> struct CElem;
@@ -171,9 +172,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(const CombArgs a) {
   // entries of this workgroup's tokens: one per thread, coalesced
   for (int i = tid; i < ntok * K; i += kThreads) {
     const size_t g = ((size_t)s * a.T + t0) * K + i;
-    const int e = a.topk[g];
+    const int e = a.dedup ? i % K : a.topk[g];
     const int p = a.pos[g];
-    const float w = a.weights[g];
+    const float w = a.dedup ? 1.0f : a.weights[g];
     const char* addr = nullptr;
     if (e != -1 && (e < 0 || e >= a.E)) {
       atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
@@ -245,8 +246,8 @@ void launch_dt(const CombArgs& a, bool vec, int grid, hipStream_t st) {
 
 vrResult_t launch_combine(vrComm* c, const vrWindow* y, size_t y_off, size_t cap, size_t row_bytes, int dtype,
                           const int32_t* topk, const float* weights, const int32_t* pos, int T, int K, int E,
-                          const vrWindow* out, size_t out_off, uint32_t sig, const U64Tab& target, bool wait,
-                          hipStream_t st) {
+                          bool dedup, const vrWindow* out, size_t out_off, uint32_t sig, const U64Tab& target,
+                          bool wait, hipStream_t st) {
   CombArgs a;
   const int R = c->nranks;
   for (int r = 0; r < VR_MAX_RANKS; ++r) {
@@ -270,6 +271,7 @@ vrResult_t launch_combine(vrComm* c, const vrWindow* y, size_t y_off, size_t cap
   a.T = T;
   a.K = K;
   a.E = E;
+  a.dedup = dedup ? 1 : 0;
   a.nblk = std::max(1, (T + kTok - 1) / kTok);
   const bool vec = row_bytes % 16 == 0 && y_off % 16 == 0 && out_off % 16 == 0;
   const int grid = R * a.nblk + (wait ? R : 0);

@@ -782,14 +782,15 @@ vrResult_t vr_allgather(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t
   return r;
 }
 
-vrResult_t vr_dispatch(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes, const int32_t* topk,
-                       int T, int K, int E, vrWindow_t recv, size_t recv_off, size_t cap, int32_t* counts_out,
-                       int32_t* src_out, int32_t* send_pos, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags,
-                       void* stream) {
+static vrResult_t dispatch_common(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes, const int32_t* topk,
+                                  int T, int K, int E, vrWindow_t recv, size_t recv_off, size_t cap,
+                                  int32_t* counts_out, int32_t* src_out, int32_t* experts_out, int32_t* send_pos,
+                                  bool dedup, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, x) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
   if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if ((!topk && T > 0) || !counts_out || (!src_out && cap > 0)) return VR_ERR_INVALID_ARGUMENT;
+  if (dedup && !experts_out && cap > 0) return VR_ERR_INVALID_ARGUMENT;
   if (T < 0 || T >= 65536 || K < 1 || K > 64 || E < R || E % R || E > 1024)
     return VR_ERR_INVALID_ARGUMENT;
   if (row_bytes == 0 || row_bytes > (size_t(1) << 30) || cap > (size_t(1) << 31)) return VR_ERR_INVALID_ARGUMENT;
@@ -805,10 +806,10 @@ vrResult_t vr_dispatch(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes,
   if (r != VR_OK) return r;
   for (int d = 0; d < R; ++d)
     if (check_signal_mode(c, d, sig_rows, VR_SIGNAL_ADD) != VR_OK) return VR_ERR_INVALID_USAGE;
-  r = ensure_scratch(c, dispatch_scratch_bytes(R, T, E));
+  r = ensure_scratch(c, dispatch_scratch_bytes(R, T, dedup ? R : E, dedup ? E : 0));
   if (r != VR_OK) return r;
   r = launch_dispatch(c, x, x_off, row_bytes, topk, T, K, E, recv, recv_off, cap, counts_out, src_out, send_pos,
-                      sig_counts, sig_rows, tc, wait, S(stream));
+                      experts_out, dedup, sig_counts, sig_rows, tc, wait, S(stream));
   if (r == VR_OK) {
     commit_inc(c, sig_counts, R);
     for (int d = 0; d < R; ++d) note_signal(c, d, sig_rows, VR_SIGNAL_ADD, 0, false);
@@ -816,16 +817,33 @@ vrResult_t vr_dispatch(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes,
   return r;
 }
 
-vrResult_t vr_combine(vrComm_t c, vrWindow_t y, size_t y_off, size_t cap, size_t row_bytes, int dtype,
-                      const int32_t* topk, const float* weights, const int32_t* send_pos, int T, int K, int E,
-                      vrWindow_t out, size_t out_off, uint32_t sig, uint32_t flags, void* stream) {
+vrResult_t vr_dispatch(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes, const int32_t* topk,
+                       int T, int K, int E, vrWindow_t recv, size_t recv_off, size_t cap, int32_t* counts_out,
+                       int32_t* src_out, int32_t* send_pos, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags,
+                       void* stream) {
+  return dispatch_common(c, x, x_off, row_bytes, topk, T, K, E, recv, recv_off, cap, counts_out, src_out, nullptr,
+                         send_pos, false, sig_counts, sig_rows, flags, stream);
+}
+
+vrResult_t vr_dispatch_dedup(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes, const int32_t* topk,
+                             int T, int K, int E, vrWindow_t recv, size_t recv_off, size_t cap,
+                             int32_t* counts_out, int32_t* src_out, int32_t* experts_out, int32_t* send_pos,
+                             uint32_t sig_counts, uint32_t sig_rows, uint32_t flags, void* stream) {
+  return dispatch_common(c, x, x_off, row_bytes, topk, T, K, E, recv, recv_off, cap, counts_out, src_out,
+                         experts_out, send_pos, true, sig_counts, sig_rows, flags, stream);
+}
+
+static vrResult_t combine_common(vrComm_t c, vrWindow_t y, size_t y_off, size_t cap, size_t row_bytes, int dtype,
+                                 const int32_t* topk, const float* weights, const int32_t* send_pos, int T, int K,
+                                 int E, bool dedup, vrWindow_t out, size_t out_off, uint32_t sig, uint32_t flags,
+                                 void* stream) {
   if (!live(c) || !has_win(c, y) || !has_win(c, out)) return VR_ERR_INVALID_ARGUMENT;
   if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (dtype != VR_DT_F32 && dtype != VR_DT_BF16) return VR_ERR_INVALID_ARGUMENT;
   const size_t es = dtype == VR_DT_F32 ? 4 : 2;
   if (T < 0 || T >= 65536 || K < 1 || K > 64 || E < R || E % R || E > 1024) return VR_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!topk || !weights || !send_pos)) return VR_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!send_pos || (!dedup && (!topk || !weights)))) return VR_ERR_INVALID_ARGUMENT;
   if (row_bytes == 0 || row_bytes > (size_t(1) << 30) || row_bytes % es || y_off % es || out_off % es)
     return VR_ERR_INVALID_ARGUMENT;
   if (cap > (size_t(1) << 31)) return VR_ERR_INVALID_ARGUMENT;
@@ -837,10 +855,26 @@ vrResult_t vr_combine(vrComm_t c, vrWindow_t y, size_t y_off, size_t cap, size_t
   U64Tab t;
   vrResult_t r = inc_targets(c, sig, R, wait, &t);
   if (r != VR_OK) return r;
-  r = launch_combine(c, y, y_off, cap, row_bytes, dtype, topk, weights, send_pos, T, K, E, out, out_off, sig, t,
-                     wait, S(stream));
+  r = launch_combine(c, y, y_off, cap, row_bytes, dtype, topk, weights, send_pos, T, K, E, dedup, out, out_off, sig,
+                     t, wait, S(stream));
   if (r == VR_OK) commit_inc(c, sig, R);
   return r;
+}
+
+vrResult_t vr_combine(vrComm_t c, vrWindow_t y, size_t y_off, size_t cap, size_t row_bytes, int dtype,
+                      const int32_t* topk, const float* weights, const int32_t* send_pos, int T, int K, int E,
+                      vrWindow_t out, size_t out_off, uint32_t sig, uint32_t flags, void* stream) {
+  return combine_common(c, y, y_off, cap, row_bytes, dtype, topk, weights, send_pos, T, K, E, false, out, out_off,
+                        sig, flags, stream);
+}
+
+vrResult_t vr_combine_dedup(vrComm_t c, vrWindow_t y, size_t y_off, size_t cap, size_t row_bytes, int dtype,
+                            const int32_t* send_pos, int T, vrWindow_t out, size_t out_off, uint32_t sig,
+                            uint32_t flags, void* stream) {
+  if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
+  const int R = c->nranks;  // a row per destination rank: K = E = R entries per token
+  return combine_common(c, y, y_off, cap, row_bytes, dtype, nullptr, nullptr, send_pos, T, R, R, true, out, out_off,
+                        sig, flags, stream);
 }
 
 vrResult_t vr_ring_exchange(vrComm_t c, vrWindow_t send, vrWindow_t recv, size_t put_bytes, size_t puts_per_rank,

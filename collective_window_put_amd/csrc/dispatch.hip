@@ -62,7 +62,14 @@ struct DispArgs {
   const int32_t* topk;   // [R][T][K]
   int32_t* counts_out;   // [R][E/R]
   int32_t* src_out;      // [R][cap]
-  int32_t* pos_out;      // [R][T][K] receive row of each routing entry, or nullptr
+  int32_t* pos_out;      // [R][T][K] receive row of each routing entry ([R][T][R] per rank when dedup), or nullptr
+  int32_t* experts_out;  // dedup: [R][cap][K] local expert of each entry of a received row
+  int32_t* ecounts_out;  // dedup: [R][Eo/R] rows per local expert
+  int32_t* eblk;         // dedup: [R][NB1][Eo] entries per expert of each count block
+  int32_t* ecw;          // dedup: [R][Eo] entries per expert of each source
+  int Eo, epro;          // dedup: keys are destination ranks (E = R); Eo experts, epro per rank
+  int wave_tokens;       // 64 % K == 0: a wave's 64 entries hold whole tokens
+  int nbits_o;           // dedup: bits of an expert id
   int32_t* subpfx;       // [R][NB1*kSubs][E]: sub-block prefix within its count block
   int32_t* blktot;       // [R][NB1][E]: rows per expert of each count block
   int32_t* cwin;         // [R][R][E]: rank d's copy of every source's count row
@@ -84,12 +91,49 @@ __device__ inline int32_t load_topk(const DispArgs& a, int s, int t, int k) {
   return a.topk[((size_t)s * a.T + t) * a.K + k];
 }
 
+// The key entry (s, t, k) is laid out by: its expert, or, in the per-rank
+// (dedup) layout, the rank owning its expert when no earlier entry of the
+// token names the same rank (-1 otherwise: the token is already bound for
+// that rank). Ids outside [-1, E) map to an out-of-range key, which the
+// callers flag and skip.
+template <bool DEDUP>
+__device__ inline int32_t entry_key(const DispArgs& a, int s, int t, int k) {
+  const int32_t e = load_topk(a, s, t, k);
+  if (!DEDUP || e == -1) return e;
+  if (e < 0 || e >= a.Eo) return a.E;
+  const int32_t d = e / a.epro;
+  for (int q = 0; q < k; ++q) {
+    const int32_t f = load_topk(a, s, t, q);
+    if (f >= 0 && f < a.Eo && f / a.epro == d) return -1;
+  }
+  return d;
+}
+
+// Dedup key of an entry whose token's entries sit in neighbouring lanes of
+// this wave (`group` names the token within the wave): the destination rank
+// if no lower lane of the same token names that rank, -1 for such a later
+// entry and for unrouted ones; ids outside [-1, E) map to the out-of-range
+// key a.E, which the callers flag and skip. All lanes of the wave call it.
+__device__ inline int32_t dedup_rep(const DispArgs& a, int32_t e, int group, bool active) {
+  const int32_t d = (e >= 0 && e < a.Eo) ? e / a.epro : (e == -1 ? -1 : a.E);
+  const bool cand = active && d >= 0 && d < a.E;
+  const uint32_t key = cand ? static_cast<uint32_t>(group * 128 + d) : 0xFFFFu;
+  const uint64_t m = match_any(key, 16);
+  const uint64_t lt = (1ull << lane_id()) - 1ull;
+  if (!active) return -1;
+  return cand ? ((m & lt) == 0 ? d : -1) : d;
+}
+
+template <bool DEDUP>
 __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int wg) {
   const int R = a.R, E = a.E;
   const int s = wg % R, blk = wg / R;  // interleaved: sources' relays hit in parallel
   const int tid = threadIdx.x;
   int32_t* hist = lds;  // [kSubs][E]
+  int32_t* hist_o = hist + kSubs * E;  // dedup: [Eo] entries per expert (for the per-expert counts)
   for (int i = tid; i < kSubs * E; i += kThreads) hist[i] = 0;
+  if (DEDUP)
+    for (int i = tid; i < a.Eo; i += kThreads) hist_o[i] = 0;
   if (blk == 0 && tid == 0)
     store8_agent(a.base_rows + s, load_relaxed_u64(a.sig_rows + (size_t)s * a.sig_stride));
   __syncthreads();
@@ -105,14 +149,25 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = (it0 + u) * kThreads + tid;
-      ev[u] = (it0 + u < iters && i < ntok * a.K) ? load_topk(a, s, t0 + i / a.K, i % a.K) : -1;
+      const bool in = it0 + u < iters && i < ntok * a.K;
+      // dedup with whole tokens per wave: the raw id now, the key below; otherwise the key now
+      ev[u] = in ? ((DEDUP && a.wave_tokens) ? load_topk(a, s, t0 + i / a.K, i % a.K)
+                                             : entry_key<DEDUP>(a, s, t0 + i / a.K, i % a.K))
+                 : -1;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (it0 + u >= iters) break;
       const int i = (it0 + u) * kThreads + tid;
       const int tl = i / a.K;
-      const int e = ev[u];
+      int e = ev[u];
+      if (DEDUP) {  // every entry counts toward its expert, whichever entry of the token carries the row
+        const int32_t f = a.wave_tokens ? e : (i < ntok * a.K ? load_topk(a, s, t0 + i / a.K, i % a.K) : -1);
+        const bool fv = f >= 0 && f < a.Eo;
+        const uint64_t mo = match_any(fv ? static_cast<uint32_t>(f) : 0xFFFFFFFFu, a.nbits_o + 1);
+        if (fv && (mo & lt) == 0) atomicAdd(&hist_o[f], __popcll(mo));
+        if (a.wave_tokens) e = dedup_rep(a, e, (i / a.K) & 63, i < ntok * a.K);
+      }
       if (e != -1 && (e < 0 || e >= E)) atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
       if (e >= 0 && e < E) {
         const int key = (tl / kSub) * E + e;
@@ -130,6 +185,9 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
     }
     store4_agent(reinterpret_cast<uint32_t*>(a.blktot + ((size_t)s * a.NB1 + blk) * E + e), run);
   }
+  if (DEDUP)
+    for (int e = tid; e < a.Eo; e += kThreads)
+      store4_agent(reinterpret_cast<uint32_t*>(a.eblk + ((size_t)s * a.NB1 + blk) * a.Eo + e), hist_o[e]);
   wg_stores_complete();
   if (tid == 0) *last_flag = relay_arrive(a.relay + s, a.NB1, false);
   __syncthreads();
@@ -149,10 +207,18 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
     for (int d = 0; d < R; ++d)
       store4_agent(reinterpret_cast<uint32_t*>(a.cwin + ((size_t)d * R + s) * E + e), run);
   }
+  if (DEDUP)  // source s's entries per expert, over its count blocks
+    for (int e = tid; e < a.Eo; e += kThreads) {
+      const int32_t* col = a.eblk + (size_t)s * a.NB1 * a.Eo + e;
+      int32_t run = 0;
+      for (int b0 = 0; b0 < a.NB1; ++b0) run += load_coherent_i32(col + (size_t)b0 * a.Eo);
+      store4_agent(reinterpret_cast<uint32_t*>(a.ecw + (size_t)s * a.Eo + e), run);
+    }
   wg_stores_complete();
   if (tid < R) atomic_add_u64(a.sig_counts + (size_t)tid * a.sig_stride, 1ull);  // SignalInc at each rank
 }
 
+template <bool DEDUP>
 __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int wg) {
   // LDS: tot[E] (rows of expert e over all sources), base[E] (receive row of
   // this block's first row of expert e), hw[kWaves][E] (per-wave counts, then
@@ -166,6 +232,7 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
   int32_t* dpos = hwf + kWaves * E;
   int32_t* dexp = dpos + kSub * K;
   int32_t* crow = dexp + kSub * K;
+  int32_t* dorig = crow + E;  // dedup: [kSub*K] each entry's expert id
   const int s = wg % R, b2 = wg / R;  // interleaved sources
   const int b1 = b2 / kSubs;
   const int tpr = 64 / K;  // tokens per ballot round
@@ -201,7 +268,8 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
       const int tl = rd * tpr + lane / K;  // token index within the wave
       const int k = lane % K;
       const bool valid = lane < tpr * K && tl < ntw;
-      const int e = ent[rd];
+      // a round holds whole tokens, so the dedup key comes from the neighbouring lanes
+      const int e = DEDUP ? dedup_rep(a, ent[rd], lane / K, valid) : ent[rd];
       const bool ok = valid && e >= 0 && e < E;
       if (pass == 0 && valid && e != -1 && !ok) atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
       int32_t lpos = -1;
@@ -216,6 +284,7 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
         const int slot = (wave * kTokPerWave + tl) * K + k;
         dpos[slot] = lpos;
         dexp[slot] = ok ? e : -1;
+        if (DEDUP) dorig[slot] = ent[rd];
       }
     }
     __syncthreads();
@@ -289,14 +358,30 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
   if (b2 == 0)
     for (int j = tid; j < epr; j += kThreads)
       store4_agent(reinterpret_cast<uint32_t*>(a.counts_out + (size_t)s * epr + j), tot[s * epr + j]);
+  if (DEDUP && b2 == 0)  // rank s's entries per local expert, over every source
+    for (int j = tid; j < a.epro; j += kThreads) {
+      int32_t run = 0;
+      for (int q = 0; q < R; ++q) run += load_coherent_i32(a.ecw + (size_t)q * a.Eo + s * a.epro + j);
+      store4_agent(reinterpret_cast<uint32_t*>(a.ecounts_out + (size_t)s * a.epro + j), static_cast<uint32_t>(run));
+    }
+  if (DEDUP && a.pos_out) {  // every (token, rank) starts as "not sent"; the token's key entries fill theirs
+    for (int i = tid; i < kSub * R; i += kThreads)
+      if (b2 * kSub + i / R < a.T)
+        store4_agent(reinterpret_cast<uint32_t*>(a.pos_out + ((size_t)s * a.T + b2 * kSub) * R + i), 0xFFFFFFFFu);
+    wg_stores_complete();
+  }
   __syncthreads();
   // final receive rows; each row's source tag
   for (int slot = tid; slot < kSub * K; slot += kThreads) {
     const int tlb = slot / K;  // token within the block
     if (tlb >= kSub || b2 * kSub + tlb >= a.T) continue;
     const int e = dexp[slot];
-    uint32_t* po = a.pos_out ? reinterpret_cast<uint32_t*>(a.pos_out + ((size_t)s * a.T + b2 * kSub) * K + slot)
-                             : nullptr;
+    const int tg = b2 * kSub + tlb;
+    uint32_t* po = nullptr;
+    if (a.pos_out)
+      po = reinterpret_cast<uint32_t*>(DEDUP ? a.pos_out + ((size_t)s * a.T + tg) * R + (e >= 0 ? e : 0)
+                                                : a.pos_out + ((size_t)s * a.T + b2 * kSub) * K + slot);
+    if (DEDUP && e < 0) continue;  // not a key entry: the position slot belongs to another entry
     if (e < 0) {
       if (po) store4_agent(po, 0xFFFFFFFFu);
       continue;
@@ -304,7 +389,15 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     const int32_t pos = base[e] + dpos[slot];
     dpos[slot] = pos;
     const int d = e / epr;
-    if ((uint64_t)pos < a.cap) {
+    const bool kept = (uint64_t)pos < a.cap;
+    if (DEDUP && kept)  // the row's entries as rank d sees them
+      for (int k = 0; k < K; ++k) {
+        const int32_t f = dorig[tlb * K + k];
+        const bool mine = f >= 0 && f < a.Eo && f / a.epro == d;
+        store4_agent(reinterpret_cast<uint32_t*>(a.experts_out + ((size_t)d * a.cap + pos) * K + k),
+                     static_cast<uint32_t>(mine ? f - d * a.epro : -1));
+      }
+    if (kept) {
       store4_agent(reinterpret_cast<uint32_t*>(a.src_out + (size_t)d * a.cap + pos),
                    static_cast<uint32_t>((s << 16) | (b2 * kSub + tlb)));
       if (po) store4_agent(po, static_cast<uint32_t>(pos));
@@ -394,13 +487,14 @@ __device__ void receiver_block(const DispArgs& a, int32_t* lds, int d) {
   }
 }
 
+template <bool DEDUP>
 __global__ __launch_bounds__(kThreads) void k_dispatch(const DispArgs a) {
   extern __shared__ int32_t lds[];
   __shared__ int last;
   const int ncount = a.R * a.NB1, nput = a.R * a.NB2;
   const int b = blockIdx.x;
-  if (b < ncount) count_block(a, lds, &last, b);
-  else if (b < ncount + nput) put_block(a, lds, &last, b - ncount);
+  if (b < ncount) count_block<DEDUP>(a, lds, &last, b);
+  else if (b < ncount + nput) put_block<DEDUP>(a, lds, &last, b - ncount);
   else receiver_block(a, lds, b - ncount - nput);
 }
 
@@ -408,29 +502,40 @@ __global__ __launch_bounds__(kThreads) void k_dispatch(const DispArgs a) {
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct Layout {
-  size_t subpfx, blktot, cwin, base_rows, total;
+  size_t subpfx, blktot, cwin, base_rows, rows, eblk, ecw, total;
 };
-Layout scratch_layout(int R, int T, int E) {
+Layout scratch_layout(int R, int T, int E, int Eo) {
   const size_t NB1 = std::max(1, (T + kCountBlock - 1) / kCountBlock);
   Layout l;
   l.subpfx = 0;
   l.blktot = al256((size_t)R * NB1 * kSubs * E * 4);
   l.cwin = l.blktot + al256((size_t)R * NB1 * E * 4);
   l.base_rows = l.cwin + al256((size_t)R * R * E * 4);
-  l.total = l.base_rows + al256((size_t)R * 8);
+  l.rows = l.base_rows + al256((size_t)R * 8);  // dedup: rows per destination rank
+  l.eblk = l.rows + al256((size_t)R * 4);
+  l.ecw = l.eblk + al256((size_t)R * NB1 * Eo * 4);
+  l.total = l.ecw + al256((size_t)R * Eo * 4);
   return l;
 }
 
 }  // namespace
 
-size_t dispatch_scratch_bytes(int R, int T, int E) { return scratch_layout(R, T, E).total; }
+size_t dispatch_scratch_bytes(int R, int T, int E, int Eo) { return scratch_layout(R, T, E, Eo).total; }
 
 vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t row_bytes, const int32_t* topk, int T,
                            int K, int E, const vrWindow* recv, size_t recv_off, size_t cap, int32_t* counts_out,
-                           int32_t* src_out, int32_t* pos_out, uint32_t sig_counts, uint32_t sig_rows,
-                           const U64Tab& target_counts, bool wait, hipStream_t st) {
+                           int32_t* src_out, int32_t* pos_out, int32_t* experts_out, bool dedup, uint32_t sig_counts,
+                           uint32_t sig_rows, const U64Tab& target_counts, bool wait, hipStream_t st) {
   DispArgs a;
   const int R = c->nranks;
+  // dedup: the layout's keys are the destination ranks (E = R, one per rank)
+  a.Eo = E;
+  a.epro = E / R;
+  a.experts_out = experts_out;
+  a.ecounts_out = dedup ? counts_out : nullptr;
+  a.wave_tokens = 64 % K == 0;
+  const int Eo = E;
+  if (dedup) E = R;
   for (int r = 0; r < VR_MAX_RANKS; ++r) {
     a.x.p[r] = x->base[r];
     a.recv.p[r] = recv->base[r];
@@ -447,7 +552,13 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.pos_out = pos_out;
   a.NB1 = std::max(1, (T + kCountBlock - 1) / kCountBlock);
   a.NB2 = a.NB1 * kSubs;
-  const Layout l = scratch_layout(R, T, E);
+  const Layout l = scratch_layout(R, T, E, dedup ? Eo : 0);
+  if (dedup) a.counts_out = reinterpret_cast<int32_t*>(c->scratch + l.rows);
+  a.eblk = reinterpret_cast<int32_t*>(c->scratch + l.eblk);
+  a.ecw = reinterpret_cast<int32_t*>(c->scratch + l.ecw);
+  int nbo = 1;
+  while ((1 << nbo) < Eo) ++nbo;
+  a.nbits_o = nbo;
   a.subpfx = reinterpret_cast<int32_t*>(c->scratch + l.subpfx);
   a.blktot = reinterpret_cast<int32_t*>(c->scratch + l.blktot);
   a.cwin = reinterpret_cast<int32_t*>(c->scratch + l.cwin);
@@ -482,10 +593,13 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   } else {
     a.mode = (row_bytes % 8 == 0 && x_off % 8 == 0 && recv_off % 8 == 0) ? 1 : 0;
   }
-  const size_t lds = sizeof(int32_t) *
-                    std::max<size_t>({(size_t)kSubs * E, (3 + kWaves) * (size_t)E + 2 * (size_t)kSub * K, (size_t)kThreads});
+  const size_t lds = sizeof(int32_t) * std::max<size_t>({(size_t)kSubs * E + (dedup ? (size_t)Eo : 0),
+                                                         (3 + kWaves) * (size_t)E + 2 * (size_t)kSub * K +
+                                                             (dedup ? (size_t)kSub * K : 0),
+                                                         (size_t)kThreads});
   const int grid = R * a.NB1 + R * a.NB2 + (wait ? R : 0);
-  hipLaunchKernelGGL(k_dispatch, dim3(grid), dim3(kThreads), lds, st, a);
+  if (dedup) hipLaunchKernelGGL(k_dispatch<true>, dim3(grid), dim3(kThreads), lds, st, a);
+  else hipLaunchKernelGGL(k_dispatch<false>, dim3(grid), dim3(kThreads), lds, st, a);
   return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;
 }
 

@@ -371,6 +371,35 @@ vrResult_t vr_dispatch(vrComm_t comm, vrWindow_t x, size_t x_off, size_t row_byt
                        int32_t* recv_src, int32_t* send_pos, uint32_t sig_counts, uint32_t sig_rows,
                        uint32_t flags, void* stream);
 
+/* MoE dispatch in the per-rank (dedup) layout (reading: the GDA survey's
+ * dispatch, sending each token once to every rank that owns at least one of
+ * its experts instead of once per expert). Rank d's rows are ordered by
+ * source rank, then token; row i carries recv_src[d][i] = (s << 16) | t and
+ * recv_experts[d][i][k] (device int32 [R][cap][K]) = the local expert index
+ * of the token's entry k when that expert lives on d, else -1.
+ * recv_expert_counts[d][j] counts the routing entries naming local expert j
+ * (as vr_dispatch). send_pos (device int32 [R][T][R] or NULL): the row of
+ * token (s, t) at each rank d, -1 where it is not sent (or fell past the
+ * capacity). Count exchange, signals (sig_counts rises by R, sig_rows by the
+ * rows aimed at each rank), checks and limits as vr_dispatch. */
+vrResult_t vr_dispatch_dedup(vrComm_t comm, vrWindow_t x, size_t x_off, size_t row_bytes,
+                             const int32_t* topk_idx, int T, int K, int num_experts, vrWindow_t recv,
+                             size_t recv_off, size_t recv_capacity_rows, int32_t* recv_expert_counts,
+                             int32_t* recv_src, int32_t* recv_experts, int32_t* send_pos, uint32_t sig_counts,
+                             uint32_t sig_rows, uint32_t flags, void* stream);
+
+/* Combine in the per-rank layout: every rank d holds one row per token it
+ * received (its experts' outputs for that token, already mixed there), at
+ * the row vr_dispatch_dedup placed it (send_pos, [R][T][R]). For each source s
+ * and token t: acc = +0.0, then for d = 0..R-1 with send_pos[s][t][d] != -1,
+ * acc = acc + y[d][send_pos[s][t][d]] (binary32 additions in rank order);
+ * bf16 rows widened exactly, the result rounded to bf16 (RNE). Gets,
+ * completion signal (each rank's `sig` rises by R), waits and checks as
+ * vr_combine. */
+vrResult_t vr_combine_dedup(vrComm_t comm, vrWindow_t y, size_t y_off, size_t y_capacity_rows,
+                            size_t row_bytes, int dtype, const int32_t* send_pos, int T, vrWindow_t out,
+                            size_t out_off, uint32_t sig, uint32_t flags, void* stream);
+
 /* MoE combine, the inverse of vr_dispatch (reading: the GDA survey's opening
  * section describes the dispatch; its other half brings every expert output
  * back to the token's rank and mixes the K of them with the router weights).
