@@ -461,6 +461,20 @@ def calib_copy(b: Bench, reps: int = 3):
     log("calibration copy done (1 GiB read + 1 GiB write per launch)")
 
 
+def copy_ceiling(b: Bench, reps: int = 5):
+    """Context for the roofline: a plain device copy of 1 GiB (torch copy_),
+    back to back, events on the stream; GB/s over the 2 GiB moved."""
+    torch = b.torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t = b.timed(lambda: dst.copy_(src), reps, False)
+    med = float(np.median(t))
+    del src, dst
+    return {"GBps": round(2 * n / (med * 1e-3) / 1e9, 1), "how": f"torch copy_ of 1 GiB on the device, median of {reps}"}
+
+
 # ---- the CPU oracle beside it ---------------------------------------------------------------------
 def cpu_baseline(xs, R: int, N: int, budget_s: float = 20.0):
     """Time the oracle's protocol simulation of the same AllReduce on one host core.
@@ -497,6 +511,64 @@ def cpu_baseline(xs, R: int, N: int, budget_s: float = 20.0):
             "sample": f"protocol simulation of the bf16 AllReduce, R={R}, first {n} of {N} elements per rank "
                       f"({dt:.2f} s on one pinned host core, numpy single-threaded)",
             "seconds": round(dt, 3), "host_cpu_count": os.cpu_count()}
+
+
+def cpu_rows():
+    """The oracle's plain definition of every other workload, timed on one host
+    core on a bounded sample of its inputs (the sample is named; GB/s over the
+    sample's algorithmic bytes; the best of a few runs for the short ones).
+    Inputs are generated before the clock starts."""
+    import workloads as W
+    from oracle import definitions as D
+    out = {}
+
+    def clock(name, fn, nbytes, sample, runs=1):
+        best = None
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            fn()
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        out[name] = {"GBps": round(nbytes / best / 1e9, 3), "seconds": round(best, 4), "sample": sample}
+
+    c = W.CONFIGS["c1"]
+    xs = W.allreduce_f32_inputs(c["ranks"], c["count"], run="B", seed=c["seed"])
+    clock("allreduce_f32_r4_1Mi", lambda: D.allreduce(xs, "f32"), 2 * c["ranks"] * c["count"] * 4, "whole workload",
+          runs=5)
+    c = W.CONFIGS["c3"]
+    R, B = c["ranks"], c["block_bytes"]
+    sends = W.alltoall_inputs(R, B, seed=c["seed"])
+    clock("alltoall_r8_4MiB", lambda: D.alltoall(sends, B), 2 * R * R * B, "whole workload", runs=3)
+    del sends
+    c = W.CONFIGS["c4"]
+    R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
+    topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
+    n = int((topk >= 0).sum())
+    clock("dispatch_r8_t4096_e256_k8", lambda: D.dispatch(topk, x, E),
+          R * T * H * 2 + topk.nbytes + n * (H * 2 + 4), "whole workload")
+    epr = E // R
+    nd = int(sum(len({int(e) // epr for e in topk[s, t] if e >= 0}) for s in range(R) for t in range(T)))
+    clock("dispatch_dedup_r8_t4096_e256_k8", lambda: D.dispatch_dedup(topk, x, E),
+          R * T * H * 2 + topk.nbytes + nd * (H * 2 + 4 + 4 * K), "whole workload")
+    Ts = 1024
+    ts, xs_ = topk[:, :Ts].copy(), x[:, :Ts].copy()
+    pos = D.dispatch_positions(ts, E)
+    y = W.expert_outputs(D.dispatch_rows_per_rank(ts, E), H, seed=7)
+    wts = W.router_weights(ts, E)
+    ns = int((ts >= 0).sum())
+    clock("combine_r8_t4096_e256_k8", lambda: D.combine(ts, wts, pos, y, E),
+          ns * H * 2 + R * Ts * H * 2 + 3 * ts.nbytes, f"{Ts} of {T} tokens per rank")
+    c = W.CONFIGS["c5a"]
+    R, M = c["ranks"], c["bytes_per_rank"] // 4
+    sends = W.allgather_inputs(R, M, seed=c["seed"])
+    clock("allgather_r16_64MiB", lambda: D.allgather(sends), R * M + R * R * M, "16 MiB per rank (of 64 MiB)")
+    del sends
+    c = W.CONFIGS["c5b"]
+    R, P, pb = c["ranks"], c["puts_per_rank"], c["put_bytes"]
+    sends = W.ring_inputs(R, P, pb, seed=c["seed"])
+    zero = [np.zeros(P * pb, np.uint8)] * R
+    clock("ring_r16_1Mi_x_256B", lambda: D.ring(sends, zero, P, pb), 2 * R * P * pb, "whole workload", runs=3)
+    return out
 
 
 def main():
@@ -537,9 +609,12 @@ def main():
     }
     if not args.no_rows:
         out["rows"] = run_rows(b, args.reps, tuple(args.rows.split(",")))
+        out["copy_ceiling"] = copy_ceiling(b)
     if not args.no_cpu:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(head["xs"], head["R"], head["N"])
+        if not args.no_rows:
+            out["cpu_baseline"]["rows"] = cpu_rows()
     print(json.dumps(out), flush=True)
 
 
