@@ -7,20 +7,22 @@
 // (rank d owns experts [d*E/R, (d+1)*E/R)), then source rank, then token.
 //
 // One kernel, three kinds of workgroup, in grid order:
-// * count (s, b): histograms the routing entries of its 512 tokens in LDS, per
+// * count (s, b): histograms the routing entries of its 256 tokens in LDS, per
 //   64-token sub-block, and stores the sub-blocks' exclusive prefixes within
 //   the block plus the block's totals. The last block of source s (relay)
-//   sums the block totals into the count row C[s][.], puts it into every
-//   rank's count window and applies a SignalInc there (the count exchange).
-//   Block (s, 0) first records rank s's row signal as the base its receiver
-//   will wait from.
+//   sums the block totals into the count row C[s][.] (turning each block's
+//   total into the prefix of the earlier blocks' on the way), puts the row
+//   into every rank's count window and applies a SignalInc there (the count
+//   exchange). Block (s, 0) first records rank s's row signal as the base its
+//   receiver will wait from.
 // * put (s, b) of 64 tokens: ranks its routing entries within the block
 //   (wave ballots, token order), loads its token rows, waits for rank s's
 //   count signal, derives each expert's receive offset from the full count
 //   matrix
 //     off(s, e) = sum_{e' < e owned by the same rank} sum_s' C[s'][e]
 //               + sum_{s' < s} C[s'][e],
-//   adds the rows of earlier blocks and sub-blocks of source s, records each
+//   adds the rows of earlier blocks and sub-blocks of source s (two loads:
+//   both prefixes are stored), records each
 //   row's source, and copies each token row once per routed expert. The last
 //   block of source s applies one SignalAdd(rows sent to d) at every rank d.
 // * receiver d (the last R workgroups): waits until its row signal has grown
@@ -49,9 +51,9 @@ constexpr int kThreads = 512;     // threads per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kTokPerWave = 8;    // tokens per wave in a put workgroup
 constexpr int kSub = kWaves * kTokPerWave;  // tokens per put workgroup (sub-block): 64
-constexpr int kCountBlock = 512;  // tokens per count workgroup
+constexpr int kCountBlock = 256;  // tokens per count workgroup
 constexpr int kSubs = kCountBlock / kSub;
-constexpr int kSubBits = 3;       // log2(kSubs): key bits above the expert's
+constexpr int kSubBits = 2;       // log2(kSubs): key bits above the expert's
 static_assert((1 << kSubBits) == kSubs, "kSubBits");
 constexpr int kRelayFan = 16;     // first-level relay counters per source (put blocks)
 
@@ -193,16 +195,21 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
   __syncthreads();
   if (!*last_flag) return;
   // last block of source s: C[s][e] = sum of the block totals (16 independent
-  // loads in flight per expert), then the count row to every rank
+  // loads in flight per expert), each block's total replaced in place by the
+  // exclusive prefix of the earlier blocks' totals; then the count row to
+  // every rank
   for (int e = tid; e < E; e += kThreads) {
-    const int32_t* col = a.blktot + (size_t)s * a.NB1 * E + e;
+    int32_t* col = a.blktot + (size_t)s * a.NB1 * E + e;
     int32_t run = 0;
     for (int b0 = 0; b0 < a.NB1; b0 += 16) {
       int32_t v[16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) v[q] = b0 + q < a.NB1 ? load_coherent_i32(col + (size_t)(b0 + q) * E) : 0;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) run += v[q];
+      for (int q = 0; q < 16; ++q) {
+        if (b0 + q < a.NB1) store4_agent(reinterpret_cast<uint32_t*>(col + (size_t)(b0 + q) * E), run);
+        run += v[q];
+      }
     }
     for (int d = 0; d < R; ++d)
       store4_agent(reinterpret_cast<uint32_t*>(a.cwin + ((size_t)d * R + s) * E + e), run);
@@ -318,21 +325,18 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
   __syncthreads();
   compiler_fence();
   const int32_t* cw = a.cwin + (size_t)s * R * E;  // rank s's copy: cw[s'][e]
-  const int32_t* pb = a.blktot + (size_t)s * a.NB1 * E;  // block totals of source s
+  const int32_t* pb = a.blktot + ((size_t)s * a.NB1 + b1) * E;  // rows of source s's earlier count blocks
   const int32_t* ps = a.subpfx + ((size_t)s * a.NB1 * kSubs + b2) * E;
   for (int e = tid; e < E; e += kThreads) {
-    // count rows of every source, and the totals of this source's earlier
-    // blocks: independent loads issued in batches of 16, one round trip each
+    // count rows of every source, the prefix over this source's earlier count
+    // blocks and over the earlier sub-blocks of this one: independent loads
+    // issued in batches of 16, one round trip each
     int32_t t = 0, pre = 0, own = 0;
-    int32_t before = load_coherent_i32(ps + e);  // earlier sub-blocks of this count block
-    for (int q0 = 0; q0 < R + b1; q0 += 16) {
+    int32_t before = load_coherent_i32(ps + e) + load_coherent_i32(pb + e);
+    for (int q0 = 0; q0 < R; q0 += 16) {
       int32_t v[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int j = q0 + q;
-        v[q] = j < R ? load_coherent_i32(cw + (size_t)j * E + e)
-                     : (j < R + b1 ? load_coherent_i32(pb + (size_t)(j - R) * E + e) : 0);
-      }
+      for (int q = 0; q < 16; ++q) v[q] = q0 + q < R ? load_coherent_i32(cw + (size_t)(q0 + q) * E + e) : 0;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int j = q0 + q;
@@ -340,8 +344,6 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
           t += v[q];
           if (j < s) pre += v[q];
           if (j == s) own = v[q];
-        } else if (j < R + b1) {
-          before += v[q];
         }
       }
     }
