@@ -111,15 +111,21 @@ struct Mixer {
   // returns the mask of entries that have a row
   __device__ __forceinline__ uint32_t load(int it, v4u (&v)[kBatch]) const {
     const int tl = token(it), k0 = (it % nb) * kBatch;
-    // entries without a row load this token's own output slot instead (always
-    // in bounds) and are dropped by a select in mix(), so no branches
-    const char* own = out + (uint64_t)(t0 + tl) * rb;
+    // entries without a row load another row of the batch instead (a cache
+    // hit), or the token's own output slot when the batch has none (always in
+    // bounds); mix() drops them by a select, so the loads need no branches
+    const char* p[kBatch];
+    const char* fill = out + (uint64_t)(t0 + tl) * rb;
+#pragma unroll
+    for (int q = kBatch - 1; q >= 0; --q) {
+      p[q] = k0 + q < K ? src[tl * K + k0 + q] : nullptr;
+      fill = p[q] ? p[q] : fill;
+    }
     uint32_t m = 0;
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const char* p = k0 + q < K ? src[tl * K + k0 + q] : nullptr;
-      m |= p ? 1u << q : 0u;
-      v[q] = load16_stream_global((p ? p : own) + col * 16);
+      m |= p[q] ? 1u << q : 0u;
+      v[q] = load16_stream_global((p[q] ? p[q] : fill) + col * 16);
     }
     return m;
   }
