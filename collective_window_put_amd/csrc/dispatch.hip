@@ -72,6 +72,7 @@ struct DispArgs {
   int Eo, epro;          // dedup: keys are destination ranks (E = R); Eo experts, epro per rank
   int wave_tokens;       // 64 % K == 0: a wave's 64 entries hold whole tokens
   int nbits_o;           // dedup: bits of an expert id
+  int xo_vec;            // dedup: K % 4 == 0 and experts_out 16-byte aligned: 16-byte stores
   int32_t* subpfx;       // [R][NB1*kSubs][E]: sub-block prefix within its count block
   int32_t* blktot;       // [R][NB1][E]: rows per expert of each count block
   int32_t* cwin;         // [R][R][E]: rank d's copy of every source's count row
@@ -366,12 +367,6 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
       for (int q = 0; q < R; ++q) run += load_coherent_i32(a.ecw + (size_t)q * a.Eo + s * a.epro + j);
       store4_agent(reinterpret_cast<uint32_t*>(a.ecounts_out + (size_t)s * a.epro + j), static_cast<uint32_t>(run));
     }
-  if (DEDUP && a.pos_out) {  // every (token, rank) starts as "not sent"; the token's key entries fill theirs
-    for (int i = tid; i < kSub * R; i += kThreads)
-      if (b2 * kSub + i / R < a.T)
-        store4_agent(reinterpret_cast<uint32_t*>(a.pos_out + ((size_t)s * a.T + b2 * kSub) * R + i), 0xFFFFFFFFu);
-    wg_stores_complete();
-  }
   __syncthreads();
   // final receive rows; each row's source tag
   for (int slot = tid; slot < kSub * K; slot += kThreads) {
@@ -379,11 +374,9 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     if (tlb >= kSub || b2 * kSub + tlb >= a.T) continue;
     const int e = dexp[slot];
     const int tg = b2 * kSub + tlb;
-    uint32_t* po = nullptr;
-    if (a.pos_out)
-      po = reinterpret_cast<uint32_t*>(DEDUP ? a.pos_out + ((size_t)s * a.T + tg) * R + (e >= 0 ? e : 0)
-                                                : a.pos_out + ((size_t)s * a.T + b2 * kSub) * K + slot);
-    if (DEDUP && e < 0) continue;  // not a key entry: the position slot belongs to another entry
+    uint32_t* po = nullptr;  // dedup positions are written below, one per (token, rank)
+    if (a.pos_out && !DEDUP) po = reinterpret_cast<uint32_t*>(a.pos_out + ((size_t)s * a.T + b2 * kSub) * K + slot);
+    if (DEDUP && e < 0) continue;  // not a key entry
     if (e < 0) {
       if (po) store4_agent(po, 0xFFFFFFFFu);
       continue;
@@ -392,13 +385,20 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     dpos[slot] = pos;
     const int d = e / epr;
     const bool kept = (uint64_t)pos < a.cap;
-    if (DEDUP && kept)  // the row's entries as rank d sees them
-      for (int k = 0; k < K; ++k) {
+    if (DEDUP && kept) {  // the row's entries as rank d sees them (an output: plain stores)
+      int32_t* xo = a.experts_out + ((size_t)d * a.cap + pos) * K;
+      auto local = [&](int k) {
         const int32_t f = dorig[tlb * K + k];
-        const bool mine = f >= 0 && f < a.Eo && f / a.epro == d;
-        store4_agent(reinterpret_cast<uint32_t*>(a.experts_out + ((size_t)d * a.cap + pos) * K + k),
-                     static_cast<uint32_t>(mine ? f - d * a.epro : -1));
+        return (f >= 0 && f < a.Eo && f / a.epro == d) ? f - d * a.epro : -1;
+      };
+      if (a.xo_vec) {
+        for (int k = 0; k < K; k += 4)
+          *reinterpret_cast<v4u*>(xo + k) = v4u{static_cast<uint32_t>(local(k)), static_cast<uint32_t>(local(k + 1)),
+                                                static_cast<uint32_t>(local(k + 2)), static_cast<uint32_t>(local(k + 3))};
+      } else {
+        for (int k = 0; k < K; ++k) xo[k] = local(k);
       }
+    }
     if (kept) {
       store4_agent(reinterpret_cast<uint32_t*>(a.src_out + (size_t)d * a.cap + pos),
                    static_cast<uint32_t>((s << 16) | (b2 * kSub + tlb)));
@@ -409,6 +409,15 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     }
   }
   __syncthreads();
+  if (DEDUP && a.pos_out)  // each token's row at every rank, -1 where it is not sent (contiguous per token)
+    for (int i = tid; i < kSub * R; i += kThreads) {
+      const int tlb = i / R, d = i % R;
+      if (b2 * kSub + tlb >= a.T) continue;
+      int32_t pos = -1;
+      for (int k = 0; k < K; ++k)
+        if (dexp[tlb * K + k] == d) pos = dpos[tlb * K + k];
+      a.pos_out[((size_t)s * a.T + b2 * kSub) * R + i] = (uint64_t)pos < a.cap ? pos : -1;
+    }
   // copy: the wave's 8 token rows, each once per routed expert
   if (a.mode == 2) {
     const __amdgpu_buffer_rsrc_t rd = rsrc(a.span_base, a.span_bytes);
@@ -536,6 +545,7 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.experts_out = experts_out;
   a.ecounts_out = dedup ? counts_out : nullptr;
   a.wave_tokens = 64 % K == 0;
+  a.xo_vec = K % 4 == 0 && (reinterpret_cast<uintptr_t>(experts_out) & 15) == 0;
   const int Eo = E;
   if (dedup) E = R;
   for (int r = 0; r < VR_MAX_RANKS; ++r) {
