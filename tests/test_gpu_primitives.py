@@ -145,3 +145,53 @@ def test_usage_errors():
         with pytest.raises(vr.VrError):  # past the end of the allocation
             vr.vr_window_register(job.comm, [p, p + (1 << 45)], 1 << 45)
         job.assert_no_async_error()
+
+
+def test_caller_workspace_and_two_communicators_on_two_streams():
+    # each communicator owns its signal, counter and relay words (here one in
+    # a caller-provided workspace), so two of them can run AlltoAlls on two
+    # streams at once without sharing any word
+    import torch
+    from oracle import definitions as D
+    import workloads as W
+    say("two communicators, two streams, caller workspace")
+    R, B = 4, 1 << 16
+    need = vr.vr_comm_workspace_bytes(R, signal_count=2, counter_count=1)
+    ws = torch.zeros(need + 256, dtype=torch.uint8, device="cuda")
+    off = (-ws.data_ptr()) % 256
+    comms = [vr.vr_comm_create(R, 2, 1, 1, workspace=ws.data_ptr() + off, workspace_bytes=need),
+             vr.vr_comm_create(R, 2, 1, 1)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    sends = [W.alltoall_inputs(R, B, seed=41), W.alltoall_inputs(R, B, seed=42)]
+    slabs, wins = [], []
+    try:
+        for i, comm in enumerate(comms):
+            a = vr.VR_WIN_REQUIRED_ALIGNMENT
+            slab = torch.zeros(2 * R * R * B + a, dtype=torch.uint8, device="cuda")
+            sh = (-slab.data_ptr()) % a
+            sv = [slab[sh + r * R * B: sh + (r + 1) * R * B] for r in range(R)]
+            rv = [slab[sh + (R + r) * R * B: sh + (R + r + 1) * R * B] for r in range(R)]
+            for v, x in zip(sv, sends[i]):
+                v.copy_(torch.from_numpy(x))
+            sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], R * B)
+            rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], R * B)
+            slabs.append((slab, rv))
+            wins.append((sw, rw))
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for i, comm in enumerate(comms):
+                vr.vr_alltoall(comm, wins[i][0], 0, wins[i][1], 0, B, sig=1, stream=streams[i])
+        torch.cuda.synchronize()
+        for i, comm in enumerate(comms):
+            want = D.alltoall(sends[i], B)
+            got = [v.cpu().numpy() for v in slabs[i][1]]
+            assert all(np.array_equal(got[d], want[d]) for d in range(R)), i
+            assert [vr.vr_signal_read(comm, d, 1) for d in range(R)] == [3 * R] * R
+            assert vr.vr_comm_get_async_error(comm)[0] == vr.VR_OK
+    finally:
+        torch.cuda.synchronize()
+        for comm, (sw, rw) in zip(comms, wins):
+            vr.vr_window_deregister(comm, sw)
+            vr.vr_window_deregister(comm, rw)
+        for comm in comms:
+            vr.vr_comm_destroy(comm)
