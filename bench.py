@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
     "k_allreduce": "allreduce.hip", "k_alltoall": "alltoall.hip", "k_allgather": "allgather.hip",
     "k_dispatch": "dispatch.hip", "k_combine": "combine.hip", "k_ring": "ring.hip",
     "k_alltoall_sessions": "sessions.hip", "k_dispatch_dedup": "dispatch.hip", "k_combine_dedup": "combine.hip",
+    "k_ring_weak": "ring.hip",
 }
 
 
@@ -188,7 +189,7 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
 
 # ---- the other workloads ------------------------------------------------------------------------
 ROW_NAMES = ("allreduce_f32", "alltoall", "alltoall_sessions", "alltoall_ce", "dispatch", "combine", "dedup",
-             "allgather", "allgather_ce", "ring")
+             "allgather", "allgather_ce", "ring", "ring_weak")
 
 
 def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
@@ -214,6 +215,8 @@ def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
         run_allgather_row(b, reps, rows, copy_engine=True)
     if "ring" in only:
         run_ring_row(b, reps, rows)
+    if "ring_weak" in only:
+        run_ring_row(b, reps, rows, weak=True)
     return rows
 
 
@@ -418,7 +421,7 @@ def run_allgather_row(b, reps, rows, copy_engine=False):
 
 
 
-def run_ring_row(b, reps, rows):
+def run_ring_row(b, reps, rows, weak=False):
     import workloads as W
     vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
     c = W.CONFIGS["c5b"]
@@ -430,15 +433,18 @@ def run_ring_row(b, reps, rows):
     sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], P * pb)
     rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], P * pb)
     lit = torch.zeros(2, dtype=torch.int64, device="cuda")
-    f = lambda: vr.vr_ring_exchange(comm, sw, rw, pb, P, C, 0, 0, litmus=lit, stream=stream)  # noqa: E731
+    flags = vr.VR_RING_WEAK if weak else 0
+    f = lambda: vr.vr_ring_exchange(comm, sw, rw, pb, P, C, 0, 0, litmus=lit, flags=flags, stream=stream)  # noqa: E731
     f()
     t = b.timed(f, reps, True)
     med = float(np.median(t))
     lh = lit.cpu().numpy()
-    rows["ring_r16_1Mi_x_256B"] = row_entry("ring R=16 2^20 puts x 256B", 2 * R * P * pb, t, "k_ring",
-                                            "ring_r16_1Mi_x_256B",
-                                            {"Mputs_per_s": round(R * P / (med * 1e-3) / 1e6, 1),
-                                             "litmus_checks": int(lh[0]), "litmus_violations": int(lh[1])})
+    # weak: litmus[1] counts observations the weak rule allows (a later message seen first)
+    extra = {"Mputs_per_s": round(R * P / (med * 1e-3) / 1e6, 1), "litmus_checks": int(lh[0]),
+             ("litmus_reorders_observed" if weak else "litmus_violations"): int(lh[1])}
+    name = "ring_weak_r16_1Mi_x_256B" if weak else "ring_r16_1Mi_x_256B"
+    rows[name] = row_entry(f"ring{' (weak signals)' if weak else ''} R=16 2^20 puts x 256B", 2 * R * P * pb, t,
+                           "k_ring_weak" if weak else "k_ring", name, extra)
     code, bits = vr.vr_comm_get_async_error(comm)
     if code != vr.VR_OK:
         raise RuntimeError(f"device error in the ring exchange: {vr.vr_error_string(code)} bits={bits:#x}")

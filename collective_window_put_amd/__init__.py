@@ -57,6 +57,7 @@ VR_OP_SUM = 0
 VR_COLL_NO_WAIT = 0x1
 VR_COLL_COPY_ENGINE = 0x4
 VR_CE_STREAMS = 8
+VR_RING_WEAK = 0x8
 VR_FENCE_NONE, VR_FENCE_PUT, VR_FENCE_GET = 0x0, 0x1, 0x2
 VR_ASYNC_TIMEOUT, VR_ASYNC_CAPACITY, VR_ASYNC_BAD_EXPERT, VR_ASYNC_LITMUS = 0x1, 0x2, 0x4, 0x8
 

@@ -881,7 +881,7 @@ vrResult_t vr_ring_exchange(vrComm_t c, vrWindow_t send, vrWindow_t recv, size_t
                             int contexts, uint32_t sig_base, uint32_t cnt_base, vrWindow_t sig_window,
                             size_t sig_window_off, uint64_t* litmus, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
-  if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
+  if (flags & ~(VR_COLL_NO_WAIT | VR_RING_WEAK)) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (contexts < 1 || (uint32_t)contexts > c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
   if (put_bytes == 0 || put_bytes % 16 || put_bytes > 65536) return VR_ERR_INVALID_ARGUMENT;
@@ -919,8 +919,8 @@ vrResult_t vr_ring_exchange(vrComm_t c, vrWindow_t send, vrWindow_t recv, size_t
     }
   }
   const bool wait = !(flags & VR_COLL_NO_WAIT);
-  vrResult_t r = launch_ring(c, send, recv, put_bytes, puts_per_rank, contexts, ctx0, cnt_base, wait, litmus,
-                             S(stream));
+  vrResult_t r = launch_ring(c, send, recv, put_bytes, puts_per_rank, contexts, ctx0, cnt_base, wait,
+                             (flags & VR_RING_WEAK) != 0, litmus, S(stream));
   if (r == VR_OK)
     for (int d = 0; d < R; ++d)
       for (int k = 0; k < contexts; ++k) {

@@ -23,6 +23,15 @@
 // it has grown by the context's message count; with the litmus on, each time
 // it sees a new value v it acquires and checks that message v-1 and one
 // earlier message of the context are present, counting violations.
+//
+// Weak signals (GIN page, strong and weak signals: a weak signal is ordered
+// after its own put only) need no workgroup-wide completion: each wavefront
+// takes every fourth 16 KiB chunk of the context's messages, stores it, waits
+// for its own stores and applies the chunk's signals, never meeting the other
+// waves. A reader that sees v may then miss one of the first v messages (a
+// later chunk's wave finished first); the litmus counts those observations,
+// and only a missing message once the signal reads the full count is an
+// error.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -34,7 +43,8 @@ namespace vr {
 namespace {
 
 constexpr int kThreads = 256;          // one workgroup issues each (rank, context)
-constexpr uint32_t kRoundBytes = 65536;  // bytes per round
+constexpr int kWaves = kThreads / 64;
+constexpr uint32_t kRoundBytes = 65536;  // bytes per round (per chunk with weak signals: a quarter)
 constexpr uint32_t kSigPerThread = 1;    // signals (and counter increments) each thread applies per round
 
 struct RingArgs {
@@ -70,6 +80,7 @@ __device__ bool message_present(const RingArgs& a, int d, int sender, uint64_t m
   return ballot(!same) == 0;
 }
 
+template <bool WEAK>
 __global__ __launch_bounds__(kThreads) void k_ring(const RingArgs a) {
   const int R = a.R, C = a.C;
   const int w = blockIdx.x;
@@ -83,6 +94,20 @@ __global__ __launch_bounds__(kThreads) void k_ring(const RingArgs a) {
     const uint64_t m0 = (uint64_t)k * a.per_ctx, m1 = m0 + a.per_ctx;
     uint64_t* sig = a.sigp[peer] + k;
     uint64_t* cnt = a.cnt + (size_t)r * a.cnt_stride + k;
+    if (WEAK) {  // wave v: chunks v, v + 4, ... of the context; lane j signals message j of a chunk
+      const uint32_t lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addresses
+      const uint64_t per_chunk = std::min<uint64_t>(64, std::max<uint64_t>(1, kRoundBytes / kWaves / P));
+      for (uint64_t m = m0 + wave * per_chunk; m < m1; m += kWaves * per_chunk) {
+        const uint64_t nm = std::min<uint64_t>(per_chunk, m1 - m);
+        copy16<16>(a.recv.p[peer] + m * P, a.send.p[r] + m * P, static_cast<uint32_t>(nm * P), lane, 64);
+        wait_vmem();  // this wave's stores (and loads) of the chunk have completed
+        if (lane < nm) {
+          atomic_add_u64(sig, 1ull);  // weak SignalInc of message m + lane
+          atomic_add_u64(cnt, 1ull);  // CounterInc: its source has been read
+        }
+      }
+      return;
+    }
     for (uint64_t m = m0; m < m1; m += per_round) {
       const uint64_t nm = std::min<uint64_t>(per_round, m1 - m);
       const uint32_t bytes = static_cast<uint32_t>(nm * P);
@@ -119,7 +144,8 @@ __global__ __launch_bounds__(kThreads) void k_ring(const RingArgs a) {
         atomic_add_u64(a.litmus, 2ull);
         if (!ok) {
           atomic_add_u64(a.litmus + 1, 1ull);
-          atomic_or_u32(a.err, VR_ASYNC_LITMUS);
+          // strong: every observation must see its prefix; weak: only the full count
+          if (!WEAK || n == a.per_ctx) atomic_or_u32(a.err, VR_ASYNC_LITMUS);
         }
       }
       seen = n;
@@ -137,8 +163,8 @@ __global__ __launch_bounds__(kThreads) void k_ring(const RingArgs a) {
 }  // namespace
 
 vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, size_t put_bytes, size_t puts_per_rank,
-                       int contexts, uint64_t* const* sig_ctx0, uint32_t cnt_base, bool wait, uint64_t* litmus,
-                       hipStream_t st) {
+                       int contexts, uint64_t* const* sig_ctx0, uint32_t cnt_base, bool wait, bool weak,
+                       uint64_t* litmus, hipStream_t st) {
   const int R = c->nranks;
   vrResult_t r = ensure_scratch(c, sizeof(uint64_t) * R * contexts);
   if (r != VR_OK) return r;
@@ -164,7 +190,8 @@ vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, si
     hipLaunchKernelGGL(k_ring_snapshot, dim3((n + 255) / 256), dim3(256), 0, st, a);
     if (hipGetLastError() != hipSuccess) return VR_ERR_HIP;
   }
-  hipLaunchKernelGGL(k_ring, dim3(R * contexts + a.waiters), dim3(kThreads), 0, st, a);
+  if (weak) hipLaunchKernelGGL(k_ring<true>, dim3(R * contexts + a.waiters), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(k_ring<false>, dim3(R * contexts + a.waiters), dim3(kThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;
 }
 

@@ -94,7 +94,7 @@ vrResult_t launch_combine(vrComm* c, const vrWindow* y, size_t y_off, size_t cap
 size_t dispatch_scratch_bytes(int R, int T, int E, int Eo);
 vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, size_t put_bytes,
                        size_t puts_per_rank, int contexts, uint64_t* const* sig_ctx0, uint32_t cnt_base,
-                       bool wait, uint64_t* litmus, hipStream_t st);
+                       bool wait, bool weak, uint64_t* litmus, hipStream_t st);
 
 vrResult_t launch_barrier(vrComm* c, uint32_t index, uint64_t target, uint32_t fence, uint64_t timeout_ns,
                           hipStream_t st);

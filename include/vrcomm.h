@@ -296,6 +296,8 @@ vrResult_t vr_counter_reset(vrComm_t comm, int rank, uint32_t id, void* stream);
  * the receivers' waits. Offsets and sizes need no alignment. */
 #define VR_COLL_COPY_ENGINE  0x4u
 #define VR_CE_STREAMS        8
+/* vr_ring_exchange only: weak SignalIncs (see there) */
+#define VR_RING_WEAK         0x8u
 
 /* Sum-AllReduce over `count` elements at send_off of every rank's send slice;
  * every rank's recv slice receives the sum at recv_off.
@@ -443,6 +445,13 @@ vrResult_t vr_combine(vrComm_t comm, vrWindow_t y, size_t y_off, size_t y_capaci
  * given, the waiting wavefronts repeatedly read a context signal v and check
  * that messages v-1 and an earlier one are visible, counting checks in
  * litmus[0] and violations in litmus[1] (and VR_ASYNC_LITMUS).
+ * flags: VR_COLL_NO_WAIT, and VR_RING_WEAK: the SignalIncs are weak (GIN
+ * page, strong and weak signals: each is ordered after its own put only),
+ * so the library publishes per wavefront instead of per workgroup; a
+ * reader that sees v may then find one of the first v messages missing.
+ * litmus[1] counts such observations, which the weak rule allows; only a
+ * missing message once the signal reads the context's full count sets
+ * VR_ASYNC_LITMUS.
  * puts_per_rank must be a multiple of contexts; put_bytes a multiple of 16. */
 vrResult_t vr_ring_exchange(vrComm_t comm, vrWindow_t send, vrWindow_t recv, size_t put_bytes,
                             size_t puts_per_rank, int contexts, uint32_t sig_base,

@@ -10,7 +10,7 @@ from gpu_util import Job, say
 pytestmark = pytest.mark.gpu
 
 
-def _run(R, P, pb, C, litmus=True, repeats=1):
+def _run(R, P, pb, C, litmus=True, repeats=1, flags=0):
     import torch
     sends = W.ring_inputs(R, P, pb, seed=R + P)
     with Job(R, signal_count=C + 2, counter_count=C + 1, context_count=C) as job:
@@ -18,7 +18,7 @@ def _run(R, P, pb, C, litmus=True, repeats=1):
         rw, rv = job.window(P * pb, fill=0)
         lit = torch.zeros(2, dtype=torch.int64, device="cuda") if litmus else None
         for _ in range(repeats):
-            vr.vr_ring_exchange(job.comm, sw, rw, pb, P, C, sig_base=1, cnt_base=1, litmus=lit)
+            vr.vr_ring_exchange(job.comm, sw, rw, pb, P, C, sig_base=1, cnt_base=1, litmus=lit, flags=flags)
         out = job.host(rv)
         sigs = [[job.sig(d, 1 + k) for k in range(C)] for d in range(R)]
         cnts = [[job.cnt(d, 1 + k) for k in range(C)] for d in range(R)]
@@ -60,3 +60,33 @@ def test_ring_config_c5b_full_size():
     assert sigs == [[P // C] * C] * R and cnts == [[P // C] * C] * R
     assert lit[1] == 0
     assert err[0] == vr.VR_OK
+
+
+@pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 2), (3, 96, 256, 4), (4, 1000, 48, 10), (16, 4096, 256, 64),
+                                      (5, 64, 8192, 2), (3, 12, 32768, 3), (2, 520, 16, 1)])
+def test_ring_weak_vs_oracle(R, P, pb, C):
+    """Weak SignalIncs: same bytes, signals and counters; the litmus may see
+    reorders (allowed), never a missing message at the full count."""
+    say(f"ring weak R={R} P={P} pb={pb} C={C}")
+    sends, out, sigs, cnts, lit, err = _run(R, P, pb, C, flags=vr.VR_RING_WEAK)
+    exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
+    for d in range(R):
+        assert np.array_equal(out[d], exp[d]), d
+    assert sigs == [[P // C] * C] * R
+    assert cnts == [[P // C] * C] * R
+    assert lit[0] > 0 and 0 <= lit[1] <= lit[0]
+    assert err[0] == vr.VR_OK, (vr.vr_error_string(err[0]), hex(err[1]))
+    print(f"weak ring: {lit[0]} checks, {lit[1]} observed reorders")
+
+
+def test_ring_weak_config_c5b_full_size():
+    c = W.CONFIGS["c5b"]
+    say("ring weak c5b full")
+    R, P, pb, C = c["ranks"], c["puts_per_rank"], c["put_bytes"], c["contexts"]
+    sends, out, sigs, cnts, lit, err = _run(R, P, pb, C, flags=vr.VR_RING_WEAK)
+    exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
+    for d in range(R):
+        assert np.array_equal(out[d], exp[d]), d
+    assert sigs == [[P // C] * C] * R and cnts == [[P // C] * C] * R
+    assert err[0] == vr.VR_OK
+    print(f"weak ring c5b: {lit[0]} checks, {lit[1]} observed reorders")
