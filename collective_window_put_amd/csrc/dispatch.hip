@@ -71,6 +71,7 @@ struct DispArgs {
   int32_t* ecw;          // dedup: [R][Eo] entries per expert of each source
   int Eo, epro;          // dedup: keys are destination ranks (E = R); Eo experts, epro per rank
   int wave_tokens;       // 64 % K == 0: a wave's 64 entries hold whole tokens
+  int gbits;             // bits naming a token within a wave: 2^gbits >= ceil(64 / K)
   int nbits_o;           // dedup: bits of an expert id
   int xo_vec;            // dedup: K % 4 == 0 and experts_out 16-byte aligned: 16-byte stores
   int32_t* subpfx;       // [R][NB1*kSubs][E]: sub-block prefix within its count block
@@ -113,15 +114,17 @@ __device__ inline int32_t entry_key(const DispArgs& a, int s, int t, int k) {
 }
 
 // Dedup key of an entry whose token's entries sit in neighbouring lanes of
-// this wave (`group` names the token within the wave): the destination rank
-// if no lower lane of the same token names that rank, -1 for such a later
-// entry and for unrouted ones; ids outside [-1, E) map to the out-of-range
-// key a.E, which the callers flag and skip. All lanes of the wave call it.
+// this wave (`group` < 2^gbits names the token within the wave): the
+// destination rank if no lower lane of the same token names that rank, -1
+// for such a later entry and for unrouted ones; ids outside [-1, E) map to
+// the out-of-range key a.E, which the callers flag and skip. All lanes of
+// the wave call it.
 __device__ inline int32_t dedup_rep(const DispArgs& a, int32_t e, int group, bool active) {
   const int32_t d = (e >= 0 && e < a.Eo) ? e / a.epro : (e == -1 ? -1 : a.E);
   const bool cand = active && d >= 0 && d < a.E;
-  const uint32_t key = cand ? static_cast<uint32_t>(group * 128 + d) : 0xFFFFu;
-  const uint64_t m = match_any(key, 16);
+  // (token, rank) in gbits + 7 bits (ranks < 128); non-candidates share the value above them all
+  const uint32_t key = cand ? static_cast<uint32_t>((group << 7) | d) : (1u << (a.gbits + 7));
+  const uint64_t m = match_any(key, a.gbits + 8);
   const uint64_t lt = (1ull << lane_id()) - 1ull;
   if (!active) return -1;
   return cand ? ((m & lt) == 0 ? d : -1) : d;
@@ -169,7 +172,7 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
         const bool fv = f >= 0 && f < a.Eo;
         const uint64_t mo = match_any(fv ? static_cast<uint32_t>(f) : 0xFFFFFFFFu, a.nbits_o + 1);
         if (fv && (mo & lt) == 0) atomicAdd(&hist_o[f], __popcll(mo));
-        if (a.wave_tokens) e = dedup_rep(a, e, (i / a.K) & 63, i < ntok * a.K);
+        if (a.wave_tokens) e = dedup_rep(a, e, (i / a.K) & ((64 / a.K) - 1), i < ntok * a.K);
       }
       if (e != -1 && (e < 0 || e >= E)) atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
       if (e >= 0 && e < E) {
@@ -215,11 +218,17 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
     for (int d = 0; d < R; ++d)
       store4_agent(reinterpret_cast<uint32_t*>(a.cwin + ((size_t)d * R + s) * E + e), run);
   }
-  if (DEDUP)  // source s's entries per expert, over its count blocks
+  if (DEDUP)  // source s's entries per expert, over its count blocks (16 loads in flight)
     for (int e = tid; e < a.Eo; e += kThreads) {
       const int32_t* col = a.eblk + (size_t)s * a.NB1 * a.Eo + e;
       int32_t run = 0;
-      for (int b0 = 0; b0 < a.NB1; ++b0) run += load_coherent_i32(col + (size_t)b0 * a.Eo);
+      for (int b0 = 0; b0 < a.NB1; b0 += 16) {
+        int32_t v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = b0 + q < a.NB1 ? load_coherent_i32(col + (size_t)(b0 + q) * a.Eo) : 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) run += v[q];
+      }
       store4_agent(reinterpret_cast<uint32_t*>(a.ecw + (size_t)s * a.Eo + e), run);
     }
   wg_stores_complete();
@@ -364,7 +373,14 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
   if (DEDUP && b2 == 0)  // rank s's entries per local expert, over every source
     for (int j = tid; j < a.epro; j += kThreads) {
       int32_t run = 0;
-      for (int q = 0; q < R; ++q) run += load_coherent_i32(a.ecw + (size_t)q * a.Eo + s * a.epro + j);
+      for (int q0 = 0; q0 < R; q0 += 16) {  // 16 loads in flight
+        int32_t v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          v[q] = q0 + q < R ? load_coherent_i32(a.ecw + (size_t)(q0 + q) * a.Eo + s * a.epro + j) : 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) run += v[q];
+      }
       store4_agent(reinterpret_cast<uint32_t*>(a.ecounts_out + (size_t)s * a.epro + j), static_cast<uint32_t>(run));
     }
   __syncthreads();
@@ -545,6 +561,8 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.experts_out = experts_out;
   a.ecounts_out = dedup ? counts_out : nullptr;
   a.wave_tokens = 64 % K == 0;
+  a.gbits = 0;  // tokens within a wave: lane / K < ceil(64 / K)
+  while ((1 << a.gbits) < (64 + K - 1) / K) ++a.gbits;
   a.xo_vec = K % 4 == 0 && (reinterpret_cast<uintptr_t>(experts_out) & 15) == 0;
   const int Eo = E;
   if (dedup) E = R;
