@@ -39,7 +39,7 @@ KERNEL_SOURCES = {
     "k_allreduce": "allreduce.hip", "k_alltoall": "alltoall.hip", "k_allgather": "allgather.hip",
     "k_dispatch": "dispatch.hip", "k_combine": "combine.hip", "k_ring": "ring.hip",
     "k_alltoall_sessions": "sessions.hip", "k_dispatch_dedup": "dispatch.hip", "k_combine_dedup": "combine.hip",
-    "k_ring_weak": "ring.hip",
+    "k_ring_weak": "ring.hip", "k_put": "comm.hip",
 }
 
 
@@ -188,12 +188,14 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
 
 
 # ---- the other workloads ------------------------------------------------------------------------
-ROW_NAMES = ("allreduce_f32", "alltoall", "alltoall_sessions", "alltoall_ce", "dispatch", "combine", "dedup",
+ROW_NAMES = ("put_get", "allreduce_f32", "alltoall", "alltoall_sessions", "alltoall_ce", "dispatch", "combine", "dedup",
              "allgather", "allgather_ce", "ring", "ring_weak")
 
 
 def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
     rows = {}
+    if "put_get" in only:
+        run_put_get_rows(b, reps, rows)
     # AllReduce fp32, R=4, 1 Mi elements (the worked-example shape)
     if "allreduce_f32" in only:
         run_allreduce_f32_row(b, reps, rows)
@@ -419,6 +421,30 @@ def run_allgather_row(b, reps, rows, copy_engine=False):
     vr.vr_comm_destroy(comm)
     del s1, r1
 
+
+
+def run_put_get_rows(b, reps, rows):
+    """One-sided put and get of 1 GiB between two ranks (a multi-workgroup coop):
+    put with a SignalInc and a CounterInc, get with a CounterInc."""
+    vr, stream = b.vr, b.stream.cuda_stream
+    R, n = 2, 1 << 30
+    comm = comm_for(vr, R, signal_count=2, counter_count=2)
+    s1, sv = b.slices(R, n, fill=7)
+    r1, rv = b.slices(R, n, fill=0)
+    sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], n)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], n)
+    fp = lambda: vr.vr_put(comm, 0, 0, 1, rw, 0, sw, 0, n, vr.SignalInc(0), vr.CounterInc(0), stream=stream)  # noqa
+    fg = lambda: vr.vr_get(comm, 0, 1, 0, sw, 0, rw, 0, n, vr.CounterInc(1), stream=stream)  # noqa: E731
+    for name, label, f in (("put_1GiB", "put 1 GiB", fp), ("get_1GiB", "get 1 GiB", fg)):
+        f()
+        rows[name] = row_entry(label, 2 * n, b.timed(f, max(3, reps // 2), True), "k_put", name)
+    code, bits = vr.vr_comm_get_async_error(comm)
+    if code != vr.VR_OK:
+        raise RuntimeError(f"device error in put/get: {vr.vr_error_string(code)} bits={bits:#x}")
+    vr.vr_window_deregister(comm, sw)
+    vr.vr_window_deregister(comm, rw)
+    vr.vr_comm_destroy(comm)
+    del s1, r1
 
 
 def run_ring_row(b, reps, rows, weak=False):

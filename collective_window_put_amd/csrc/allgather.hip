@@ -29,7 +29,8 @@ struct AGArgs {
   uint64_t* sig;
   uint32_t sig_stride;
   uint32_t tiles;      // tiles per source
-  uint32_t* relay;     // [R]
+  uint32_t* relay;     // [R] counters, rstride words apart
+  uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
   int R;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256) void k_allgather(const AGArgs a) {
     }
   }
   wg_stores_complete();
-  if (threadIdx.x == 0 && relay_arrive(a.relay + s, a.tiles, false))
+  if (threadIdx.x == 0 && relay_arrive(a.relay + s * a.rstride, a.tiles, false))
     for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
 }
 
@@ -96,6 +97,7 @@ vrResult_t launch_allgather(vrComm* c, const vrWindow* send, size_t send_off, co
   if (tiles * R > 0x7FFFFFFFull) return VR_ERR_INVALID_ARGUMENT;
   a.tiles = static_cast<uint32_t>(tiles);
   a.relay = c->relay + kRelayColl;
+  a.rstride = relay_stride(R);
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;

@@ -36,7 +36,8 @@ struct ARArgs {
   uint32_t tpc;     // tiles per chunk
   uint64_t* sig;
   uint32_t sig_stride;
-  uint32_t* relay;  // [R]
+  uint32_t* relay;  // [R] per chunk, then [R][8] per (chunk, XCD); rstride words apart
+  uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
   int R;
@@ -188,9 +189,10 @@ __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
     const uint32_t x = b & 7u, per = nwork >> 3;
     const uint32_t lo = std::max(x * per, c * a.tpc), hi = std::min((x + 1) * per, (c + 1) * a.tpc);
     const uint32_t nx = ((c + 1) * a.tpc - 1) / per - (c * a.tpc) / per + 1;
-    last = relay_arrive(a.relay + R + c * 8 + x, hi - lo, false) && relay_arrive(a.relay + c, nx, false);
+    last = relay_arrive(a.relay + (R + c * 8 + x) * a.rstride, hi - lo, false) &&
+           relay_arrive(a.relay + c * a.rstride, nx, false);
   } else {
-    last = relay_arrive(a.relay + c, a.tpc, false);
+    last = relay_arrive(a.relay + c * a.rstride, a.tpc, false);
   }
   if (last)
     for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
@@ -237,6 +239,7 @@ vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, co
   a.sig = c->sig + sig;
   a.sig_stride = c->req.signal_count;
   a.relay = c->relay + kRelayColl;  // [R] per chunk, then [R][8] per (chunk, XCD)
+  a.rstride = relay_stride(9 * R);
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;

@@ -29,7 +29,8 @@ struct A2AArgs {
   uint64_t* sig;         // &sig[0][id]
   uint32_t sig_stride;   // signals per rank
   uint32_t tiles;        // tiles per block
-  uint32_t* relay;       // [R*R]
+  uint32_t* relay;       // [R*R] counters, rstride words apart
+  uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
   int R;
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void k_alltoall(const A2AArgs a) {
     copy_any<kU>(dst, src, n, threadIdx.x, 256);
   }
   wg_stores_complete();
-  if (threadIdx.x == 0 && relay_arrive(a.relay + blk, a.tiles, false))
+  if (threadIdx.x == 0 && relay_arrive(a.relay + blk * a.rstride, a.tiles, false))
     atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);  // SignalInc at d
 }
 
@@ -80,6 +81,7 @@ vrResult_t launch_alltoall(vrComm* c, const vrWindow* send, size_t send_off, con
   if (tiles * R * R > 0x7FFFFFFFull) return VR_ERR_INVALID_ARGUMENT;
   a.tiles = static_cast<uint32_t>(tiles);
   a.relay = c->relay + kRelayColl;
+  a.rstride = relay_stride(R * R);
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;

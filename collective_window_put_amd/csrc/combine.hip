@@ -44,7 +44,8 @@ struct CombArgs {
   const int32_t* pos;    // [R][T][K]
   uint64_t* sig;
   uint32_t sig_stride;
-  uint32_t* relay;       // [R]
+  uint32_t* relay;       // [R] counters, rstride words apart
+  uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
   int R, T, K, E, nblk;
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const CombArgs a) {
     }
   }
   wg_stores_complete();
-  if (tid == 0) last = relay_arrive(a.relay + s, a.nblk, false);
+  if (tid == 0) last = relay_arrive(a.relay + s * a.rstride, a.nblk, false);
   __syncthreads();
   if (last && tid < R) atomic_add_u64(a.sig + (size_t)tid * a.sig_stride, 1ull);  // SignalInc at each rank
 }
@@ -271,6 +272,7 @@ vrResult_t launch_combine(vrComm* c, const vrWindow* y, size_t y_off, size_t cap
   a.sig = c->sig + sig;
   a.sig_stride = c->req.signal_count;
   a.relay = c->relay + kRelayColl;
+  a.rstride = relay_stride(R);
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;

@@ -187,7 +187,18 @@ __global__ __launch_bounds__(256) void k_put(PutArgs a) {
     memmove_wg(a.dst, a.src, a.bytes, a.dir);
   }
   wg_stores_complete();
-  if (threadIdx.x == 0 && relay_arrive(a.relay, a.parts, false)) {
+  if (threadIdx.x != 0) return;
+  // two-level relay for many tiles: the tiles of one XCD (workgroup b runs on
+  // XCD b mod 8), then the XCDs; each counter on its own 256-byte span
+  bool last;
+  if (a.parts >= 16) {
+    const uint32_t x = blockIdx.x & 7u;
+    last = relay_arrive(a.relay + (1 + x) * kRelaySpread, (a.parts - x + 7) / 8, false) &&
+           relay_arrive(a.relay, 8, false);
+  } else {
+    last = relay_arrive(a.relay, a.parts, false);
+  }
+  if (last) {
     if (a.sig) atomic_add_u64(a.sig, a.add);
     if (a.cnt) atomic_add_u64(a.cnt, 1ull);
   }

@@ -81,7 +81,8 @@ struct DispArgs {
   uint64_t* sig_counts;  // &sig[0][id]
   uint64_t* sig_rows;
   uint32_t sig_stride;
-  uint32_t* relay;       // [2R]: count kernel, put kernel
+  uint32_t* relay;       // [18R]: count blocks [R], put blocks [16R] then [R]; rstride words apart
+  uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
   char* span_base;       // lowest receive address, when the span path is on
@@ -145,10 +146,9 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
   __syncthreads();
   const int t0 = blk * kCountBlock;
   const int ntok = max(0, min(a.T - t0, kCountBlock));
-  // entries with equal (sub-block, expert) in one wave instruction are added
-  // once, by their lowest lane (hot experts would otherwise serialize LDS adds)
+  // plain LDS atomics (measured faster than first grouping equal keys of a
+  // wave instruction with ballots)
   const int lane = tid & 63;
-  const uint64_t lt = (1ull << lane) - 1ull;
   const int iters = (ntok * a.K + kThreads - 1) / kThreads;
   for (int it0 = 0; it0 < iters; it0 += 8) {  // 8 loads in flight per thread, then the adds
     int ev[8];
@@ -170,15 +170,13 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
       if (DEDUP) {  // every entry counts toward its expert, whichever entry of the token carries the row
         const int32_t f = a.wave_tokens ? e : (i < ntok * a.K ? load_topk(a, s, t0 + i / a.K, i % a.K) : -1);
         const bool fv = f >= 0 && f < a.Eo;
-        const uint64_t mo = match_any(fv ? static_cast<uint32_t>(f) : 0xFFFFFFFFu, a.nbits_o + 1);
-        if (fv && (mo & lt) == 0) atomicAdd(&hist_o[f], __popcll(mo));
+        if (fv) atomicAdd(&hist_o[f], 1);
         if (a.wave_tokens) e = dedup_rep(a, e, (i / a.K) & ((64 / a.K) - 1), i < ntok * a.K);
       }
       if (e != -1 && (e < 0 || e >= E)) atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
       if (e >= 0 && e < E) {
         const int key = (tl / kSub) * E + e;
-        const uint64_t m = match_any(static_cast<uint32_t>(key), a.nbits + kSubBits);
-        if ((m & lt) == 0) atomicAdd(&hist[key], __popcll(m));
+        atomicAdd(&hist[key], 1);
       }
     }
   }
@@ -195,7 +193,7 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
     for (int e = tid; e < a.Eo; e += kThreads)
       store4_agent(reinterpret_cast<uint32_t*>(a.eblk + ((size_t)s * a.NB1 + blk) * a.Eo + e), hist_o[e]);
   wg_stores_complete();
-  if (tid == 0) *last_flag = relay_arrive(a.relay + s, a.NB1, false);
+  if (tid == 0) *last_flag = relay_arrive(a.relay + s * a.rstride, a.NB1, false);
   __syncthreads();
   if (!*last_flag) return;
   // last block of source s: C[s][e] = sum of the block totals (16 independent
@@ -290,11 +288,12 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
       const bool ok = valid && e >= 0 && e < E;
       if (pass == 0 && valid && e != -1 && !ok) atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
       int32_t lpos = -1;
-      if (ok) {
+      if (ok && pass == 0) atomicAdd(&hwf[wave * E + e], 1);  // counts only
+      if (ok && pass == 1) {  // rank among the wave's entries of expert e, in lane (token) order
         const uint64_t m = match_any(static_cast<uint32_t>(e), a.nbits);
         const bool leader = (m & lt) == 0;
         const int cnt = __popcll(m);
-        if (pass == 1) lpos = hwf[wave * E + e] + __popcll(m & lt);
+        lpos = hwf[wave * E + e] + __popcll(m & lt);
         if (leader) hwf[wave * E + e] += cnt;
       }
       if (pass == 1 && valid) {
@@ -474,8 +473,8 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     // two-level relay: 16 first-level counters per source, then one per source
     const int g = b2 % kRelayFan;
     const int in_g = (a.NB2 - g + kRelayFan - 1) / kRelayFan;
-    bool lastp = relay_arrive(a.relay + R + s * kRelayFan + g, in_g, false);
-    if (lastp) lastp = relay_arrive(a.relay + R + R * kRelayFan + s, min(a.NB2, kRelayFan), false);
+    bool lastp = relay_arrive(a.relay + (R + s * kRelayFan + g) * a.rstride, in_g, false);
+    if (lastp) lastp = relay_arrive(a.relay + (R + R * kRelayFan + s) * a.rstride, min(a.NB2, kRelayFan), false);
     *last_flag = lastp;
   }
   __syncthreads();
@@ -597,6 +596,7 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.sig_rows = c->sig + sig_rows;
   a.sig_stride = c->req.signal_count;
   a.relay = c->relay + kRelayDispatch;
+  a.rstride = relay_stride((2 + kRelayFan) * R, kRelayDispatchWords);
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;

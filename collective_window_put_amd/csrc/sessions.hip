@@ -41,7 +41,8 @@ struct SessArgs {
   uint64_t send_off, recv_off, block;
   uint64_t bar_base;
   uint32_t sig, index, tiles;
-  uint32_t* relay;  // [R*R]
+  uint32_t* relay;  // [R*R] counters, rstride words apart
+  uint32_t rstride;
 };
 
 __global__ __launch_bounds__(256) void k_alltoall_sessions(const SessArgs a) {
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(256) void k_alltoall_sessions(const SessArgs a) {
     vrdev::put_wg(a.recv, d, a.recv_off + (uint64_t)s * a.block + t0, a.send, s,
                   a.send_off + (uint64_t)d * a.block + t0, std::min<uint64_t>(kTile, a.block - t0));
   vrdev::publish_wg();
-  if (threadIdx.x == 0 && relay_arrive(a.relay + blk, a.tiles, false))
+  if (threadIdx.x == 0 && relay_arrive(a.relay + blk * a.rstride, a.tiles, false))
     vrdev::signal_add(vrdev::signal_word(a.comm, d, a.sig), 1);  // weak SignalInc at d
 }
 
@@ -102,6 +103,7 @@ vrResult_t launch_alltoall_sessions(vrComm* c, const vrDevWindow& send, size_t s
   if (tiles * R * R + 2 * R > 0x7FFFFFFFull) return VR_ERR_INVALID_ARGUMENT;
   a.tiles = static_cast<uint32_t>(tiles);
   a.relay = c->relay + kRelayColl;
+  a.rstride = relay_stride(R * R);
   const uint32_t grid = R + a.tiles * R * R + R;
   hipLaunchKernelGGL(k_alltoall_sessions, dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;

@@ -15,11 +15,24 @@
 namespace vr {
 
 // Relay counters: one region per kind of operation, so that a collective and
-// a single put enqueued back to back never share a counter.
-constexpr uint32_t kRelaySingle = 0;       // vr_put / vr_get: 1 counter
-constexpr uint32_t kRelayColl = 64;        // collectives: up to R*R counters
-constexpr uint32_t kRelayDispatch = 64 + VR_MAX_RANKS * VR_MAX_RANKS;  // 18 per source rank
-constexpr uint32_t kRelaySlots = kRelayDispatch + 18 * VR_MAX_RANKS;
+// a single put enqueued back to back never share a counter. Counters that
+// many workgroups hit sit kRelaySpread words (256 bytes) apart: measured on
+// gfx950, returning atomics on one 256-byte span serialize at ~12 ns each,
+// while separate spans proceed in parallel.
+constexpr uint32_t kRelaySpread = 64;
+constexpr uint32_t kRelaySingle = 0;  // vr_put / vr_get: 8 per-XCD counters and a total, spread
+constexpr uint32_t kRelayColl = 9 * kRelaySpread;  // collectives: up to R*R counters
+constexpr uint32_t kRelayCollWords = VR_MAX_RANKS * VR_MAX_RANKS;
+constexpr uint32_t kRelayDispatch = kRelayColl + kRelayCollWords;  // 18 counters per source rank
+constexpr uint32_t kRelayDispatchWords = 18 * VR_MAX_RANKS * 8;
+constexpr uint32_t kRelaySlots = kRelayDispatch + kRelayDispatchWords;
+// Stride between n counters in a region of `words`: as wide as the region
+// allows, up to kRelaySpread.
+inline uint32_t relay_stride(uint32_t n, uint32_t words = kRelayCollWords) {
+  uint32_t st = kRelaySpread;
+  while (st > 1 && (uint64_t)st * n > words) st >>= 1;
+  return st;
+}
 
 constexpr uint64_t kDefaultTimeoutNs = 5ull * 1000 * 1000 * 1000;
 
