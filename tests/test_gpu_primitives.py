@@ -40,7 +40,7 @@ def test_put_get_brute_force_small_ranges():
         job.assert_no_async_error()
 
 
-@pytest.mark.parametrize("n", [1, 100, 16384, 16385, 5 * 16384 + 33, 1 << 22])
+@pytest.mark.parametrize("n", [1, 100, 16384, 16385, 5 * 16384 + 33, 21 * 16384 + 5, 1 << 22])
 def test_put_multi_workgroup_with_signal(n):
     say(f"put {n} bytes")
     rng = np.random.default_rng(n)
@@ -54,6 +54,26 @@ def test_put_multi_workgroup_with_signal(n):
         assert np.all(out[1] == 0) and np.all(out[2] == 0)
         assert job.sig(0, 3) == 1000 and job.cnt(2, 2) == 1
         assert vr.vr_signal_expected(job.comm, 0, 3) == 1000
+        job.assert_no_async_error()
+
+
+def test_large_puts_back_to_back_each_signal_once():
+    """Puts of 16 tiles or more count their tiles per XCD, then the XCDs: every
+    counter must be back at zero for the next put (sizes 22, 16 and 300 tiles)."""
+    say("large puts back to back")
+    rng = np.random.default_rng(5)
+    sizes = [21 * 16384 + 5, 16 * 16384, 300 * 16384 - 7]
+    n = max(sizes)
+    with Job(2, signal_count=2, counter_count=2) as job:
+        src = [rng.integers(0, 256, n, dtype=np.uint8) for _ in range(2)]
+        sw, _ = job.window(n, arrays=src)
+        dw, dv = job.window(n, fill=0)
+        for m in sizes:
+            vr.vr_put(job.comm, 0, 0, 1, dw, 0, sw, 0, m, vr.SignalInc(1), vr.CounterInc(0))
+            vr.vr_get(job.comm, 0, 0, 1, sw, 0, dw, 0, m, vr.CounterInc(1))
+        out = job.host(dv)
+        assert np.array_equal(out[1], src[0]) and np.array_equal(out[0], src[1])
+        assert job.sig(1, 1) == 3 and job.cnt(0, 0) == 3 and job.cnt(0, 1) == 3
         job.assert_no_async_error()
 
 
