@@ -361,9 +361,24 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     base[e] = pre + before;
   }
   __syncthreads();
+  // seg[e]: rows of the experts before e on the same rank. When the rank's
+  // experts tile the waves (epr a power of two up to 64), a shuffle scan
+  // within each group of epr lanes; otherwise a loop over LDS.
+  const bool scan = epr <= 64 && (epr & (epr - 1)) == 0;
   for (int e = tid; e < E; e += kThreads) {
     int32_t seg = 0;
-    for (int q = (e / epr) * epr; q < e; ++q) seg += tot[q];
+    if (scan) {
+      const int32_t v = tot[e];
+      const int pos = e & (epr - 1);  // = lane mod epr: kThreads is a multiple of 64
+      int32_t x = v;
+      for (int d = 1; d < epr; d <<= 1) {
+        const int32_t y = __shfl_up(x, d, 64);
+        if (pos >= d) x += y;
+      }
+      seg = x - v;
+    } else {
+      for (int q = (e / epr) * epr; q < e; ++q) seg += tot[q];
+    }
     base[e] += seg;
   }
   if (b2 == 0)

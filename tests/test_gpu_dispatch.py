@@ -57,7 +57,8 @@ def _check(res, topk, x, E, repeats=1):
 @pytest.mark.parametrize("R,T,H,E,K,seed", [(2, 5, 4, 4, 2, 0), (4, 37, 8, 16, 3, 1), (3, 130, 12, 6, 2, 2),
                                              (8, 64, 256, 256, 8, 3), (8, 200, 32, 64, 8, 4), (5, 1, 8, 10, 1, 5),
                                              (4, 65, 3, 8, 4, 6), (2, 300, 256, 8, 8, 7),
-                                             (4, 1100, 8, 1024, 64, 8), (8, 1537, 64, 32, 4, 9)])
+                                             (4, 1100, 8, 1024, 64, 8), (8, 1537, 64, 32, 4, 9),
+                                             (3, 50, 8, 9, 2, 10), (2, 70, 8, 128, 4, 11)])
 def test_dispatch_small_vs_oracle(R, T, H, E, K, seed):
     say(f"dispatch R={R} T={T} H={H} E={E} K={K}")
     topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
