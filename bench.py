@@ -645,6 +645,8 @@ def main():
     if not args.no_rows:
         out["rows"] = run_rows(b, args.reps, tuple(args.rows.split(",")))
         out["copy_ceiling"] = copy_ceiling(b)
+        if "put_1GiB" in out["rows"]:  # the library's own dwordx4 copy: a 1 GiB one-sided put
+            out["copy_ceiling"]["library_put_1GiB_GBps"] = out["rows"]["put_1GiB"]["GBps"]
     if not args.no_cpu:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(head["xs"], head["R"], head["N"])
