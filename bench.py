@@ -13,9 +13,12 @@ starts. The metric is achieved HBM GB/s over the algorithmic bytes
 Printed: one JSON line with the metric, the roofline of the AllReduce kernel
 (its algorithmic bytes over its event-timed duration, against the 8 TB/s
 HBM3E peak), the CPU oracle timed on a bounded sample, and -- unless
---no-rows -- the other workloads (AllReduce fp32 R=4, AlltoAll, dispatch,
-AllGather, ring exchange) each measured the same way, with the 256 MiB
-Infinity Cache flushed before every timed repetition.
+--no-rows -- the other workloads (1 GiB put and get, AllReduce fp32 R=4,
+AlltoAll by compute units, in barrier sessions and by the copy engines,
+dispatch, combine, their per-rank-dedup forms, AllGather by compute units
+and by the copy engines, ring exchange with strong and weak signals) each
+measured the same way, with the 256 MiB Infinity Cache flushed before every
+timed repetition.
 """
 from __future__ import annotations
 
