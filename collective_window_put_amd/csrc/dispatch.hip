@@ -81,7 +81,7 @@ struct DispArgs {
   uint64_t* sig_counts;  // &sig[0][id]
   uint64_t* sig_rows;
   uint32_t sig_stride;
-  uint32_t* relay;       // [18R]: count blocks [R], put blocks [16R] then [R]; rstride words apart
+  uint32_t* relay;       // [19R + 2] counters (see launch_dispatch), rstride words apart
   uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
@@ -131,16 +131,87 @@ __device__ inline int32_t dedup_rep(const DispArgs& a, int32_t e, int group, boo
   return cand ? ((m & lt) == 0 ? d : -1) : d;
 }
 
+// Last count block of source s: C[s][e] = sum of the block totals (16
+// independent loads in flight per expert), each block's total replaced in
+// place by the exclusive prefix of the earlier blocks' totals; then the count
+// row to every rank and a SignalInc there (the count exchange).
+__device__ void count_exchange(const DispArgs& a, int s) {
+  const int R = a.R, E = a.E;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kThreads) {
+    int32_t* col = a.blktot + (size_t)s * a.NB1 * E + e;
+    int32_t run = 0;
+    for (int b0 = 0; b0 < a.NB1; b0 += 16) {
+      int32_t v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = b0 + q < a.NB1 ? load_coherent_i32(col + (size_t)(b0 + q) * E) : 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (b0 + q < a.NB1) store4_agent(reinterpret_cast<uint32_t*>(col + (size_t)(b0 + q) * E), run);
+        run += v[q];
+      }
+    }
+    for (int d = 0; d < R; ++d)
+      store4_agent(reinterpret_cast<uint32_t*>(a.cwin + ((size_t)d * R + s) * E + e), run);
+  }
+  wg_stores_complete();
+  if (tid < R) atomic_add_u64(a.sig_counts + (size_t)tid * a.sig_stride, 1ull);  // SignalInc at each rank
+}
+
+// Dedup layout, off the count exchange's critical path: the entries of
+// count block (s, blk) per expert (any entry of a token counts, whichever
+// entry carries its row), then -- in the block completing source s's second
+// relay -- source s's entries per expert over its count blocks, announced on
+// a counter that the put blocks writing the per-expert counts wait for.
+__device__ void expert_counts(const DispArgs& a, int32_t* lds, int* last_flag, int s, int blk) {
+  const int tid = threadIdx.x;
+  int32_t* hist_o = lds;  // [Eo]
+  __syncthreads();  // the key histogram is no longer needed
+  for (int i = tid; i < a.Eo; i += kThreads) hist_o[i] = 0;
+  __syncthreads();
+  const int t0 = blk * kCountBlock;
+  const int n = max(0, min(a.T - t0, kCountBlock)) * a.K;
+  for (int i0 = 0; i0 < n; i0 += 8 * kThreads) {  // 8 loads in flight per thread
+    int32_t f[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      f[u] = i < n ? a.topk[((size_t)s * a.T + t0) * a.K + i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (f[u] >= 0 && f[u] < a.Eo) atomicAdd(&hist_o[f[u]], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < a.Eo; e += kThreads)
+    store4_agent(reinterpret_cast<uint32_t*>(a.eblk + ((size_t)s * a.NB1 + blk) * a.Eo + e), hist_o[e]);
+  wg_stores_complete();
+  if (tid == 0) *last_flag = relay_arrive(a.relay + (18 * a.R + s) * a.rstride, a.NB1, false);
+  __syncthreads();
+  if (!*last_flag) return;
+  for (int e = tid; e < a.Eo; e += kThreads) {  // 16 loads in flight
+    const int32_t* col = a.eblk + (size_t)s * a.NB1 * a.Eo + e;
+    int32_t run = 0;
+    for (int b0 = 0; b0 < a.NB1; b0 += 16) {
+      int32_t v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = b0 + q < a.NB1 ? load_coherent_i32(col + (size_t)(b0 + q) * a.Eo) : 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) run += v[q];
+    }
+    store4_agent(reinterpret_cast<uint32_t*>(a.ecw + (size_t)s * a.Eo + e), run);
+  }
+  wg_stores_complete();
+  if (tid == 0) atomic_add_u32(a.relay + (19 * a.R) * a.rstride, 1u);  // source s's expert counts are out
+}
+
 template <bool DEDUP>
 __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int wg) {
   const int R = a.R, E = a.E;
   const int s = wg % R, blk = wg / R;  // interleaved: sources' relays hit in parallel
   const int tid = threadIdx.x;
   int32_t* hist = lds;  // [kSubs][E]
-  int32_t* hist_o = hist + kSubs * E;  // dedup: [Eo] entries per expert (for the per-expert counts)
   for (int i = tid; i < kSubs * E; i += kThreads) hist[i] = 0;
-  if (DEDUP)
-    for (int i = tid; i < a.Eo; i += kThreads) hist_o[i] = 0;
   if (blk == 0 && tid == 0)
     store8_agent(a.base_rows + s, load_relaxed_u64(a.sig_rows + (size_t)s * a.sig_stride));
   __syncthreads();
@@ -167,12 +238,7 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
       const int i = (it0 + u) * kThreads + tid;
       const int tl = i / a.K;
       int e = ev[u];
-      if (DEDUP) {  // every entry counts toward its expert, whichever entry of the token carries the row
-        const int32_t f = a.wave_tokens ? e : (i < ntok * a.K ? load_topk(a, s, t0 + i / a.K, i % a.K) : -1);
-        const bool fv = f >= 0 && f < a.Eo;
-        if (fv) atomicAdd(&hist_o[f], 1);
-        if (a.wave_tokens) e = dedup_rep(a, e, (i / a.K) & ((64 / a.K) - 1), i < ntok * a.K);
-      }
+      if (DEDUP && a.wave_tokens) e = dedup_rep(a, e, (i / a.K) & ((64 / a.K) - 1), i < ntok * a.K);
       if (e != -1 && (e < 0 || e >= E)) atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
       if (e >= 0 && e < E) {
         const int key = (tl / kSub) * E + e;
@@ -189,48 +255,51 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
     }
     store4_agent(reinterpret_cast<uint32_t*>(a.blktot + ((size_t)s * a.NB1 + blk) * E + e), run);
   }
-  if (DEDUP)
-    for (int e = tid; e < a.Eo; e += kThreads)
-      store4_agent(reinterpret_cast<uint32_t*>(a.eblk + ((size_t)s * a.NB1 + blk) * a.Eo + e), hist_o[e]);
   wg_stores_complete();
   if (tid == 0) *last_flag = relay_arrive(a.relay + s * a.rstride, a.NB1, false);
   __syncthreads();
-  if (!*last_flag) return;
-  // last block of source s: C[s][e] = sum of the block totals (16 independent
-  // loads in flight per expert), each block's total replaced in place by the
-  // exclusive prefix of the earlier blocks' totals; then the count row to
-  // every rank
-  for (int e = tid; e < E; e += kThreads) {
-    int32_t* col = a.blktot + (size_t)s * a.NB1 * E + e;
-    int32_t run = 0;
-    for (int b0 = 0; b0 < a.NB1; b0 += 16) {
-      int32_t v[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) v[q] = b0 + q < a.NB1 ? load_coherent_i32(col + (size_t)(b0 + q) * E) : 0;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (b0 + q < a.NB1) store4_agent(reinterpret_cast<uint32_t*>(col + (size_t)(b0 + q) * E), run);
-        run += v[q];
+  if (*last_flag) count_exchange(a, s);
+  if (DEDUP) expert_counts(a, lds, last_flag, s, blk);
+}
+
+// Dedup layout, put block (s, 0): rank s's entries per local expert over
+// every source, once every source's counts are out; the last of the R
+// readers resets the announcement counter for the next launch.
+__device__ void put_expert_counts(const DispArgs& a, int s) {
+  const int R = a.R, tid = threadIdx.x;
+  __shared__ int ok;
+  uint32_t* ready = a.relay + (19 * R) * a.rstride;
+  uint32_t* readers = a.relay + (19 * R + 1) * a.rstride;
+  if (tid == 0) {
+    const uint64_t t0 = now_ns();
+    ok = 1;
+    while (load_relaxed_u32(ready) < static_cast<uint32_t>(R)) {
+      if (now_ns() - t0 > a.timeout_ns) {
+        atomic_or_u32(a.err, VR_ASYNC_TIMEOUT);
+        ok = 0;
+        break;
       }
+      __builtin_amdgcn_s_sleep(2);
     }
-    for (int d = 0; d < R; ++d)
-      store4_agent(reinterpret_cast<uint32_t*>(a.cwin + ((size_t)d * R + s) * E + e), run);
   }
-  if (DEDUP)  // source s's entries per expert, over its count blocks (16 loads in flight)
-    for (int e = tid; e < a.Eo; e += kThreads) {
-      const int32_t* col = a.eblk + (size_t)s * a.NB1 * a.Eo + e;
+  __syncthreads();
+  if (ok)
+    for (int j = tid; j < a.epro; j += kThreads) {
       int32_t run = 0;
-      for (int b0 = 0; b0 < a.NB1; b0 += 16) {
+      for (int q0 = 0; q0 < R; q0 += 16) {  // 16 loads in flight
         int32_t v[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) v[q] = b0 + q < a.NB1 ? load_coherent_i32(col + (size_t)(b0 + q) * a.Eo) : 0;
+        for (int q = 0; q < 16; ++q)
+          v[q] = q0 + q < R ? load_coherent_i32(a.ecw + (size_t)(q0 + q) * a.Eo + s * a.epro + j) : 0;
 #pragma unroll
         for (int q = 0; q < 16; ++q) run += v[q];
       }
-      store4_agent(reinterpret_cast<uint32_t*>(a.ecw + (size_t)s * a.Eo + e), run);
+      store4_agent(reinterpret_cast<uint32_t*>(a.ecounts_out + (size_t)s * a.epro + j), static_cast<uint32_t>(run));
     }
-  wg_stores_complete();
-  if (tid < R) atomic_add_u64(a.sig_counts + (size_t)tid * a.sig_stride, 1ull);  // SignalInc at each rank
+  wait_vmem();  // this thread's loads of the counts are done
+  __syncthreads();
+  if (tid == 0 && relay_arrive(readers, R, false))
+    __hip_atomic_store(ready, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool DEDUP>
@@ -384,19 +453,6 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
   if (b2 == 0)
     for (int j = tid; j < epr; j += kThreads)
       store4_agent(reinterpret_cast<uint32_t*>(a.counts_out + (size_t)s * epr + j), tot[s * epr + j]);
-  if (DEDUP && b2 == 0)  // rank s's entries per local expert, over every source
-    for (int j = tid; j < a.epro; j += kThreads) {
-      int32_t run = 0;
-      for (int q0 = 0; q0 < R; q0 += 16) {  // 16 loads in flight
-        int32_t v[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          v[q] = q0 + q < R ? load_coherent_i32(a.ecw + (size_t)(q0 + q) * a.Eo + s * a.epro + j) : 0;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) run += v[q];
-      }
-      store4_agent(reinterpret_cast<uint32_t*>(a.ecounts_out + (size_t)s * a.epro + j), static_cast<uint32_t>(run));
-    }
   __syncthreads();
   // final receive rows; each row's source tag
   for (int slot = tid; slot < kSub * K; slot += kThreads) {
@@ -483,6 +539,7 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
       }
     }
   }
+  if (DEDUP && b2 == 0) put_expert_counts(a, s);
   wg_stores_complete();
   if (tid == 0) {
     // two-level relay: 16 first-level counters per source, then one per source
@@ -611,7 +668,9 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.sig_rows = c->sig + sig_rows;
   a.sig_stride = c->req.signal_count;
   a.relay = c->relay + kRelayDispatch;
-  a.rstride = relay_stride((2 + kRelayFan) * R, kRelayDispatchWords);
+  // counters: [R) count blocks, [R, 17R) and [17R, 18R) put blocks, [18R, 19R)
+  // dedup expert counts, then the dedup counts' announcement and its readers
+  a.rstride = relay_stride(19 * R + 2, kRelayDispatchWords);
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;
