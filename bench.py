@@ -13,7 +13,8 @@ starts. The metric is achieved HBM GB/s over the algorithmic bytes
 Printed: one JSON line with the metric, the roofline of the AllReduce kernel
 (its algorithmic bytes over its event-timed duration, against the 8 TB/s
 HBM3E peak), the CPU oracle timed on a bounded sample, and -- unless
---no-rows -- the other workloads (1 GiB put and get, AllReduce fp32 R=4,
+--no-rows -- the other workloads (1 GiB put and get, a 256 B signal
+ping-pong, AllReduce fp32 R=4,
 AlltoAll by compute units, in barrier sessions and by the copy engines,
 dispatch, combine, their per-rank-dedup forms, AllGather by compute units
 and by the copy engines, ring exchange with strong and weak signals) each
@@ -42,7 +43,7 @@ KERNEL_SOURCES = {
     "k_allreduce": "allreduce.hip", "k_alltoall": "alltoall.hip", "k_allgather": "allgather.hip",
     "k_dispatch": "dispatch.hip", "k_combine": "combine.hip", "k_ring": "ring.hip",
     "k_alltoall_sessions": "sessions.hip", "k_dispatch_dedup": "dispatch.hip", "k_combine_dedup": "combine.hip",
-    "k_ring_weak": "ring.hip", "k_put": "comm.hip",
+    "k_ring_weak": "ring.hip", "k_put": "comm.hip", "k_pingpong": "pingpong.hip",
 }
 
 
@@ -191,7 +192,7 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
 
 
 # ---- the other workloads ------------------------------------------------------------------------
-ROW_NAMES = ("put_get", "allreduce_f32", "alltoall", "alltoall_sessions", "alltoall_ce", "dispatch", "combine", "dedup",
+ROW_NAMES = ("put_get", "pingpong", "allreduce_f32", "alltoall", "alltoall_sessions", "alltoall_ce", "dispatch", "combine", "dedup",
              "allgather", "allgather_ce", "ring", "ring_weak")
 
 
@@ -199,6 +200,8 @@ def run_rows(b: Bench, reps: int = 10, only=ROW_NAMES):
     rows = {}
     if "put_get" in only:
         run_put_get_rows(b, reps, rows)
+    if "pingpong" in only:
+        run_pingpong_rows(b, reps, rows)
     # AllReduce fp32, R=4, 1 Mi elements (the worked-example shape)
     if "allreduce_f32" in only:
         run_allreduce_f32_row(b, reps, rows)
@@ -448,6 +451,31 @@ def run_put_get_rows(b, reps, rows):
     vr.vr_window_deregister(comm, rw)
     vr.vr_comm_destroy(comm)
     del s1, r1
+
+
+def run_pingpong_rows(b, reps, rows):
+    """The control path of a small put: 2000 round trips of 256 B between two
+    workgroups inside one kernel (put + SignalInc + wait each way), with the
+    second rank on another XCD and on the same XCD."""
+    vr, stream = b.vr, b.stream.cuda_stream
+    R, n, iters = 2, 256, 2000
+    comm = comm_for(vr, R, signal_count=2)
+    s1, sv = b.slices(R, 4096, fill=3)
+    w = vr.vr_window_register(comm, [v.data_ptr() for v in sv], 4096)
+    for name, label, flags in (("pingpong_cross_xcd_256B", "ping-pong 256 B, other XCD", 0),
+                               ("pingpong_same_xcd_256B", "ping-pong 256 B, same XCD", vr.VR_PINGPONG_SAME_XCD)):
+        f = lambda: vr.vr_signal_pingpong(comm, w, 0, n, iters, sig=0, flags=flags, stream=stream)  # noqa: E731
+        f()
+        t = b.timed(f, max(3, reps // 2), False)
+        med = float(np.median(t))
+        rows[name] = row_entry(label, 4 * n * iters, t, "k_pingpong", name,
+                               {"round_trips": iters, "us_per_round_trip": round(med * 1e3 / iters, 3)})
+    code, bits = vr.vr_comm_get_async_error(comm)
+    if code != vr.VR_OK:
+        raise RuntimeError(f"device error in the ping-pong: {vr.vr_error_string(code)} bits={bits:#x}")
+    vr.vr_window_deregister(comm, w)
+    vr.vr_comm_destroy(comm)
+    del s1
 
 
 def run_ring_row(b, reps, rows, weak=False):

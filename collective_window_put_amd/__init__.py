@@ -30,6 +30,7 @@ __all__ = [
     "vr_put", "vr_get", "vr_signal", "vr_signal_wait", "vr_signal_read", "vr_signal_reset",
     "vr_signal_expected", "vr_counter_wait", "vr_counter_read", "vr_counter_reset",
     "vr_allreduce", "vr_alltoall", "vr_allgather", "vr_dispatch", "vr_combine", "vr_ring_exchange",
+    "vr_signal_pingpong",
 ]
 
 # The in-tree build; VRCOMM_LIB may name another build of the same library.
@@ -58,6 +59,7 @@ VR_COLL_NO_WAIT = 0x1
 VR_COLL_COPY_ENGINE = 0x4
 VR_CE_STREAMS = 8
 VR_RING_WEAK = 0x8
+VR_PINGPONG_SAME_XCD = 0x10
 VR_FENCE_NONE, VR_FENCE_PUT, VR_FENCE_GET = 0x0, 0x1, 0x2
 VR_ASYNC_TIMEOUT, VR_ASYNC_CAPACITY, VR_ASYNC_BAD_EXPERT, VR_ASYNC_LITMUS = 0x1, 0x2, 0x4, 0x8
 
@@ -155,6 +157,7 @@ SYMBOLS = {
                               c_uint32, _P]),
     "vr_ring_exchange": (_R, [_P, _P, _P, c_size_t, c_size_t, c_int, c_uint32, c_uint32, _P, c_size_t, _P,
                               c_uint32, _P]),
+    "vr_signal_pingpong": (_R, [_P, _P, c_size_t, c_size_t, c_uint32, c_uint32, c_uint32, _P]),
     "vr_va_signal_wait": (_R, [_P, _P, c_int, c_size_t, c_uint64, c_int, c_uint64, _P]),
     "vr_comm_device_view": (_R, [_P, POINTER(vrDevComm)]),
     "vr_window_device_view": (_R, [_P, _P, POINTER(vrDevWindow)]),
@@ -410,6 +413,10 @@ def vr_combine(comm, y, y_off, y_capacity_rows, row_bytes, dtype, topk_idx, weig
     _check(lib().vr_combine(comm, y, y_off, y_capacity_rows, row_bytes, dtype, _ptr(topk_idx), _ptr(weights),
                             _ptr(send_pos), T, K, num_experts, out, out_off, sig, flags, _stream(stream)),
            "vr_combine")
+
+
+def vr_signal_pingpong(comm, win, off, nbytes, iters, sig=0, flags=0, stream=None):
+    _check(lib().vr_signal_pingpong(comm, win, off, nbytes, iters, sig, flags, _stream(stream)), "vr_signal_pingpong")
 
 
 def vr_ring_exchange(comm, send, recv, put_bytes, puts_per_rank, contexts, sig_base=0, cnt_base=0, sig_window=None,

@@ -298,6 +298,8 @@ vrResult_t vr_counter_reset(vrComm_t comm, int rank, uint32_t id, void* stream);
 #define VR_CE_STREAMS        8
 /* vr_ring_exchange only: weak SignalIncs (see there) */
 #define VR_RING_WEAK         0x8u
+/* vr_signal_pingpong only: rank 1's workgroup on rank 0's XCD */
+#define VR_PINGPONG_SAME_XCD 0x10u
 
 /* Sum-AllReduce over `count` elements at send_off of every rank's send slice;
  * every rank's recv slice receives the sum at recv_off.
@@ -453,6 +455,24 @@ vrResult_t vr_combine(vrComm_t comm, vrWindow_t y, size_t y_off, size_t y_capaci
  * missing message once the signal reads the context's full count sets
  * VR_ASYNC_LITMUS.
  * puts_per_rank must be a multiple of contexts; put_bytes a multiple of 16. */
+/* Signal ping-pong (GIN page, one-sided transfers: put with a SignalInc, and
+ * the signal methods: wait; GDA survey, opening section: for messages of a few
+ * hundred bytes the control path sets the time): ranks 0 and 1 make `iters`
+ * round trips inside one kernel, written with the device API of
+ * vrcomm_device.hpp. Round i: rank 0 puts bytes [off, off+bytes) of its slice
+ * of `win` to the same range of rank 1's slice with a SignalInc on `sig` at
+ * rank 1; rank 1 waits for that, then puts [off, off+bytes) of its slice to
+ * [off+bytes, off+2*bytes) of rank 0's slice with a SignalInc on `sig` at
+ * rank 0, which waits for it. Each of the two signals rises by iters; other
+ * ranks are untouched. flags: VR_PINGPONG_SAME_XCD runs rank 1 on rank 0's
+ * XCD (otherwise on the next one). Needs nranks >= 2, iters >= 1,
+ * bytes <= 1 MiB (0 allowed: signals only), [off, off+2*bytes) inside the
+ * window and clear of VA signal words, and both signals' values known to the
+ * host (VR_ERR_INVALID_USAGE otherwise). A wait that times out sets
+ * VR_ASYNC_TIMEOUT and ends the exchange. */
+vrResult_t vr_signal_pingpong(vrComm_t comm, vrWindow_t win, size_t off, size_t bytes, uint32_t iters,
+                              uint32_t sig, uint32_t flags, void* stream);
+
 vrResult_t vr_ring_exchange(vrComm_t comm, vrWindow_t send, vrWindow_t recv, size_t put_bytes,
                             size_t puts_per_rank, int contexts, uint32_t sig_base,
                             uint32_t cnt_base, vrWindow_t sig_window, size_t sig_window_off,

@@ -120,6 +120,24 @@ def ring(sends, recv_before, puts_per_rank: int, put_bytes: int) -> list[np.ndar
     return out
 
 
+def signal_pingpong(slices, off: int, nbytes: int) -> list[np.ndarray]:
+    """Windows after any number (at least one) of ping-pong round trips
+    between ranks 0 and 1.
+
+    GIN page, one-sided transfers: a put copies bytes of the caller's slice
+    into the peer's slice. Reading (the pages describe the put and the
+    signal wait, not this exchange): a round is rank 0's put of
+    ``[off, off+nbytes)`` to the same range at rank 1, then rank 1's put of
+    that range of its slice to ``[off+nbytes, off+2*nbytes)`` at rank 0.
+    Every round moves the same bytes, so the result is that of one round;
+    other ranks are untouched.
+    """
+    out = [np.array(b, dtype=np.uint8, copy=True).reshape(-1) for b in slices]
+    out[1][off:off + nbytes] = out[0][off:off + nbytes]
+    out[0][off + nbytes:off + 2 * nbytes] = out[1][off:off + nbytes]
+    return out
+
+
 # -- MoE token dispatch --------------------------------------------------------
 def dispatch(topk_idx: np.ndarray, x_rows: np.ndarray, num_experts: int,
              capacity_rows: int | None = None):

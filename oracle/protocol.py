@@ -410,6 +410,30 @@ def ring_programs(world: World, send: int, recv: int, puts_per_rank: int, put_by
     return [prog(r) for r in range(R)]
 
 
+def pingpong_programs(world: World, win: int, off: int, nbytes: int, iters: int, sig: int):
+    """Signal ping-pong (GIN page: put with a SignalInc, then a wait on the
+    signal): rank 0 pings rank 1 and waits for the pong, ``iters`` times;
+    rank 1 waits for each ping and answers it one message further on in
+    rank 0's slice."""
+    R = world.nranks
+    if R < 2 or iters < 1:
+        raise InvalidArgument("ping-pong needs two ranks and at least one round")
+
+    def prog(rank):
+        base = yield ReadSignal(sig)
+        yield Barrier()
+        for i in range(iters if rank < 2 else 0):
+            if rank == 0:
+                yield Put(1, win, off, win, off, nbytes, SignalInc(sig, True))
+                yield WaitSignal(sig, base + i + 1)
+            else:
+                yield WaitSignal(sig, base + i + 1)
+                yield Put(0, win, off + nbytes, win, off, nbytes, SignalInc(sig, True))
+        yield Barrier()
+
+    return [prog(r) for r in range(R)]
+
+
 class DispatchBuffers:
     """Windows and local arrays one dispatch needs on the oracle's world."""
 

@@ -224,3 +224,15 @@ def test_combine_dedup_reversed_rank_order_is_caught(monkeypatch):
         return orig(np.asarray(pos)[:, :, ::-1], list(y_rows)[::-1], dtype)
     monkeypatch.setattr(D, "combine_dedup", reversed_ranks)
     _fails(TD.test_combine_dedup_hand_worked_rank_order)
+
+
+def test_pingpong_answer_in_place_is_caught(monkeypatch):
+    import test_oracle_protocol as TPR
+
+    def in_place(slices, off, nbytes):  # the pong overwrites rank 0's own bytes
+        out = [np.array(b, dtype=np.uint8, copy=True).reshape(-1) for b in slices]
+        out[1][off:off + nbytes] = out[0][off:off + nbytes]
+        return out
+    monkeypatch.setattr(D, "signal_pingpong", in_place)
+    _fails(TPR.test_pingpong_definition_hand_worked)
+    _fails(TPR.test_pingpong_protocol_matches_definition, 3, 3, 17, 2)

@@ -333,3 +333,53 @@ def test_dedup_dispatch_every_interleaving_two_ranks():
             assert np.array_equal(w.buf(b.recv, d)[:k * rb], rows[d].reshape(-1))
         n += 1
     assert n == 1
+
+
+# -- signal ping-pong --------------------------------------------------------------
+def test_pingpong_definition_hand_worked():
+    # rank 0 holds 0..7, rank 1 holds 100..107; off 1, 3 bytes: rank 1 gets
+    # rank 0's bytes 1..3 in place, rank 0 gets them back at 4..6
+    got = D.signal_pingpong([np.arange(8, dtype=np.uint8), np.arange(100, 108, dtype=np.uint8)], 1, 3)
+    assert list(got[1]) == [100, 1, 2, 3, 104, 105, 106, 107]
+    assert list(got[0]) == [0, 1, 2, 3, 1, 2, 3, 7]
+
+
+def _pingpong_setup(R, init, off, nbytes, iters):
+    def setup():
+        w = World(R, signal_count=2)
+        h = w.register([a.copy() for a in init])
+        return w, pr.pingpong_programs(w, h, off, nbytes, iters, 1)
+    return setup
+
+
+@pytest.mark.parametrize("R,iters,nbytes,seed", [(2, 1, 5, 0), (2, 4, 0, 1), (3, 3, 17, 2), (4, 6, 64, 3)])
+def test_pingpong_protocol_matches_definition(R, iters, nbytes, seed):
+    rng = np.random.default_rng(seed)
+    off = 3
+    init = [rng.integers(0, 256, off + 2 * nbytes + 5, dtype=np.uint8) for _ in range(R)]
+    w, progs = _pingpong_setup(R, init, off, nbytes, iters)()
+    pr.run(w, progs, seed=seed)
+    h = list(w.windows)[0]
+    exp = D.signal_pingpong(init, off, nbytes)
+    assert all(np.array_equal(w.buf(h, r), exp[r]) for r in range(R))
+    assert [w.sig[r][1] for r in range(R)] == [iters, iters] + [0] * (R - 2)
+
+
+def test_pingpong_every_interleaving():
+    R, iters, nbytes, off = 3, 2, 3, 1
+    init = [np.arange(8, dtype=np.uint8) + 50 * r for r in range(R)]
+    exp = D.signal_pingpong(init, off, nbytes)
+    n = 0
+    for w, _ in pr.all_runs(_pingpong_setup(R, init, off, nbytes, iters)):
+        h = list(w.windows)[0]
+        assert all(np.array_equal(w.buf(h, r), exp[r]) for r in range(R))
+        assert [w.sig[r][1] for r in range(R)] == [iters, iters, 0]
+        n += 1
+    assert n > 1
+
+
+def test_pingpong_needs_two_ranks():
+    w = World(1, signal_count=1)
+    h = w.register([np.zeros(8, np.uint8)])
+    with pytest.raises(Exception):
+        pr.pingpong_programs(w, h, 0, 1, 1, 0)
