@@ -41,7 +41,8 @@ def test_allgather_page_segments():
     assert sigs == [R] * R
 
 
-@pytest.mark.parametrize("R,M", [(1, 16), (2, 1), (3, 16385), (4, 16384 * 3), (8, 1000), (16, 32768 + 16), (5, 77)])
+@pytest.mark.parametrize("R,M", [(1, 16), (2, 1), (3, 16385), (4, 16384 * 3), (8, 1000), (16, 32768 + 16), (5, 77),
+                                 (64, 5000)])
 def test_allgather_random_vs_oracle(R, M):
     say(f"allgather R={R} M={M}")
     sends = W.allgather_inputs(R, M, seed=R * 3 + M)

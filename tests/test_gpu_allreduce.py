@@ -44,7 +44,7 @@ def test_allreduce_page_worked_example():
     assert sigs == [R] * R
 
 
-@pytest.mark.parametrize("R", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("R", [1, 2, 3, 8, 16, 64])
 def test_allreduce_rank_fill_closed_form(R):
     say(f"allreduce rank fill R={R}")
     out, _ = _run(W.allreduce_f32_inputs(R, 5000, run="A"), "f32")
@@ -54,7 +54,7 @@ def test_allreduce_rank_fill_closed_form(R):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("R,N", [(2, 1), (3, 1001), (4, 4096), (5, 77777), (8, 2048 * 8 + 3), (16, 40000),
-                                 (7, 123457)])
+                                 (7, 123457), (64, 9000)])
 def test_allreduce_random_bit_exact(dtype, R, N):
     say(f"allreduce {dtype} R={R} N={N}")
     xs = W.allreduce_f32_inputs(R, N, seed=R + N) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + N)

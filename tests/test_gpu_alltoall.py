@@ -42,7 +42,8 @@ def test_alltoall_page_fill_pattern():
     assert sigs == [R] * R
 
 
-@pytest.mark.parametrize("R,B", [(1, 64), (2, 1), (3, 17), (4, 4096), (5, 16385), (8, 65536 + 48), (16, 1000)])
+@pytest.mark.parametrize("R,B", [(1, 64), (2, 1), (3, 17), (4, 4096), (5, 16385), (8, 65536 + 48), (16, 1000),
+                                 (64, 300)])
 def test_alltoall_random_bytes_vs_oracle(R, B):
     say(f"alltoall R={R} B={B}")
     sends = W.alltoall_inputs(R, B, seed=R * 7 + B)

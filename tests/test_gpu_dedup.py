@@ -60,7 +60,8 @@ def _check_dispatch(job, topk, x, E, cap, rv, counts, src, experts, pos, recv_of
 @pytest.mark.parametrize("R,T,H,E,K,seed,drop", [(2, 5, 4, 4, 2, 0, 0.0), (4, 37, 8, 16, 3, 1, 0.2),
                                                   (3, 130, 12, 6, 2, 2, 0.0), (8, 64, 256, 256, 8, 3, 0.0),
                                                   (8, 200, 32, 64, 8, 4, 0.1), (5, 1, 8, 10, 1, 5, 0.0),
-                                                  (4, 1100, 8, 1024, 64, 8, 0.0), (8, 1537, 64, 32, 4, 9, 0.3)])
+                                                  (4, 1100, 8, 1024, 64, 8, 0.0), (8, 1537, 64, 32, 4, 9, 0.3),
+                                                  (64, 50, 8, 128, 4, 12, 0.1)])
 def test_dedup_dispatch_vs_oracle(R, T, H, E, K, seed, drop):
     say(f"dedup dispatch R={R} T={T} H={H} E={E} K={K}")
     topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)

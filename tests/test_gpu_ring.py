@@ -28,7 +28,7 @@ def _run(R, P, pb, C, litmus=True, repeats=1, flags=0):
 
 
 @pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 2), (3, 96, 256, 4), (4, 1000, 48, 10), (16, 4096, 256, 64),
-                                      (5, 64, 8192, 2)])
+                                      (5, 64, 8192, 2), (64, 256, 16, 4)])
 def test_ring_vs_oracle(R, P, pb, C):
     say(f"ring R={R} P={P} pb={pb} C={C}")
     sends, out, sigs, cnts, lit, err = _run(R, P, pb, C)

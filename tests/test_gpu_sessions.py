@@ -95,7 +95,7 @@ def _alltoall_sessions(R, B, seed, repeats=1, extra_barriers=0):
     return sends, res
 
 
-@pytest.mark.parametrize("R,B", [(2, 16), (3, 1000), (4, 32768), (8, 100003), (5, 65536 * 3 + 17)])
+@pytest.mark.parametrize("R,B", [(2, 16), (3, 1000), (4, 32768), (8, 100003), (5, 65536 * 3 + 17), (64, 200)])
 def test_alltoall_sessions_vs_oracle(R, B):
     say(f"alltoall with barrier sessions R={R} B={B}")
     sends, res = _alltoall_sessions(R, B, seed=R * 31 + B)
