@@ -137,7 +137,7 @@ def row_entry(name, bytes_alg, times_ms, kernel, workload, extra=None):
 def run_allreduce_headline(b: Bench, steps: int, warmup: int):
     import workloads as W
     vr = b.vr
-    c = W.CONFIGS["c2"]
+    c = W.CONFIGS["allreduce_bf16_r8_64Mi"]
     R, N = c["ranks"], c["count"]
     log(f"generating AllReduce inputs R={R} N={N} bf16")
     xs = W.allreduce_bf16_inputs(R, N, seed=c["seed"])
@@ -235,7 +235,7 @@ def comm_for(vr, R, **kw):
 def run_allreduce_f32_row(b, reps, rows):
     import workloads as W
     vr, stream = b.vr, b.stream.cuda_stream
-    c = W.CONFIGS["c1"]
+    c = W.CONFIGS["allreduce_f32_r4_1Mi"]
     R, N = c["ranks"], c["count"]
     xs = W.allreduce_f32_inputs(R, N, run="B", seed=c["seed"])
     comm = comm_for(vr, R, signal_count=2)
@@ -257,7 +257,7 @@ def run_allreduce_f32_row(b, reps, rows):
 def run_alltoall_row(b, reps, rows, sessions=False, copy_engine=False):
     import workloads as W
     vr, stream = b.vr, b.stream.cuda_stream
-    c = W.CONFIGS["c3"]
+    c = W.CONFIGS["alltoall_r8_4MiB"]
     R, B = c["ranks"], c["block_bytes"]
     sends = W.alltoall_inputs(R, B, seed=c["seed"])
     comm = comm_for(vr, R, signal_count=2, barrier_count=1)
@@ -288,7 +288,7 @@ def run_alltoall_row(b, reps, rows, sessions=False, copy_engine=False):
 def run_dispatch_row(b, reps, rows):
     import workloads as W
     vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
-    c = W.CONFIGS["c4"]
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
     R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
     topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
     rb = H * 2
@@ -318,7 +318,7 @@ def run_dispatch_row(b, reps, rows):
 def run_combine_row(b, reps, rows):
     import workloads as W
     vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
-    c = W.CONFIGS["c4"]
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
     R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
     topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
     weights = W.router_weights(topk, E, c["zipf_s"])
@@ -359,7 +359,7 @@ def run_dedup_rows(b, reps, rows):
     """The per-rank (dedup) dispatch and its combine on the dispatch workload."""
     import workloads as W
     vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
-    c = W.CONFIGS["c4"]
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
     R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
     topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
     rb = H * 2
@@ -405,7 +405,7 @@ def run_dedup_rows(b, reps, rows):
 def run_allgather_row(b, reps, rows, copy_engine=False):
     import workloads as W
     vr, stream = b.vr, b.stream.cuda_stream
-    c = W.CONFIGS["c5a"]
+    c = W.CONFIGS["allgather_r16_64MiB"]
     R, M = c["ranks"], c["bytes_per_rank"]
     sends = W.allgather_inputs(R, M, seed=c["seed"])
     comm = comm_for(vr, R, signal_count=2)
@@ -481,7 +481,7 @@ def run_pingpong_rows(b, reps, rows):
 def run_ring_row(b, reps, rows, weak=False):
     import workloads as W
     vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
-    c = W.CONFIGS["c5b"]
+    c = W.CONFIGS["ring_r16_1Mi_x_256B"]
     R, P, pb, C = c["ranks"], c["puts_per_rank"], c["put_bytes"], c["contexts"]
     sends = W.ring_inputs(R, P, pb, seed=c["seed"])
     comm = comm_for(vr, R, signal_count=C, counter_count=C, context_count=C)
@@ -597,16 +597,16 @@ def cpu_rows():
             best = dt if best is None else min(best, dt)
         out[name] = {"GBps": round(nbytes / best / 1e9, 3), "seconds": round(best, 4), "sample": sample}
 
-    c = W.CONFIGS["c1"]
+    c = W.CONFIGS["allreduce_f32_r4_1Mi"]
     xs = W.allreduce_f32_inputs(c["ranks"], c["count"], run="B", seed=c["seed"])
     clock("allreduce_f32_r4_1Mi", lambda: D.allreduce(xs, "f32"), 2 * c["ranks"] * c["count"] * 4, "whole workload",
           runs=5)
-    c = W.CONFIGS["c3"]
+    c = W.CONFIGS["alltoall_r8_4MiB"]
     R, B = c["ranks"], c["block_bytes"]
     sends = W.alltoall_inputs(R, B, seed=c["seed"])
     clock("alltoall_r8_4MiB", lambda: D.alltoall(sends, B), 2 * R * R * B, "whole workload", runs=3)
     del sends
-    c = W.CONFIGS["c4"]
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
     R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
     topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
     n = int((topk >= 0).sum())
@@ -624,12 +624,12 @@ def cpu_rows():
     ns = int((ts >= 0).sum())
     clock("combine_r8_t4096_e256_k8", lambda: D.combine(ts, wts, pos, y, E),
           ns * H * 2 + R * Ts * H * 2 + 3 * ts.nbytes, f"{Ts} of {T} tokens per rank")
-    c = W.CONFIGS["c5a"]
+    c = W.CONFIGS["allgather_r16_64MiB"]
     R, M = c["ranks"], c["bytes_per_rank"] // 4
     sends = W.allgather_inputs(R, M, seed=c["seed"])
     clock("allgather_r16_64MiB", lambda: D.allgather(sends), R * M + R * R * M, "16 MiB per rank (of 64 MiB)")
     del sends
-    c = W.CONFIGS["c5b"]
+    c = W.CONFIGS["ring_r16_1Mi_x_256B"]
     R, P, pb = c["ranks"], c["puts_per_rank"], c["put_bytes"]
     sends = W.ring_inputs(R, P, pb, seed=c["seed"])
     zero = [np.zeros(P * pb, np.uint8)] * R
@@ -650,8 +650,8 @@ def main():
                     help="first run a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the R virtual ranks share one device, and no collectives cross "
-              "GPUs in this build", file=sys.stderr)
+        print("bench.py runs on one GPU only: the R virtual ranks share one device; runs across several GPUs "
+              "are not supported", file=sys.stderr)
         sys.exit(2)
     b = Bench()
     if args.calib:

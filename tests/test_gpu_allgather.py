@@ -64,10 +64,10 @@ def test_allgather_offsets():
         assert np.all(out[d][:4099] == 0x5A)
 
 
-def test_allgather_config_c5a_full_size():
-    c = W.CONFIGS["c5a"]
+def test_allgather_r16_64MiB_full_size():
+    c = W.CONFIGS["allgather_r16_64MiB"]
     R, M = c["ranks"], c["bytes_per_rank"]
-    say(f"allgather c5a full R={R} M={M}")
+    say(f"allgather full size R={R} M={M}")
     sends = W.allgather_inputs(R, M, seed=c["seed"])
     with Job(R) as job:
         sw, sv = job.window(M, fill=None, arrays=sends)

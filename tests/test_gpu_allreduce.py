@@ -99,9 +99,9 @@ def test_allreduce_repeated_signal_accumulates():
     assert sigs == [12] * 4
 
 
-def test_allreduce_config_c1_run_b():
-    c = W.CONFIGS["c1"]
-    say("allreduce c1 run B")
+def test_allreduce_f32_r4_1Mi_run_b():
+    c = W.CONFIGS["allreduce_f32_r4_1Mi"]
+    say("allreduce f32 R=4 1 Mi run B")
     xs = W.allreduce_f32_inputs(c["ranks"], c["count"], run="B", seed=c["seed"])
     out, _ = _run(xs, "f32")
     exp = D.allreduce(xs, "f32").view(np.uint8)
@@ -109,10 +109,10 @@ def test_allreduce_config_c1_run_b():
         assert np.array_equal(out[d][:exp.size], exp)
 
 
-def test_allreduce_config_c2_full_size():
-    c = W.CONFIGS["c2"]
+def test_allreduce_bf16_r8_64Mi_full_size():
+    c = W.CONFIGS["allreduce_bf16_r8_64Mi"]
     R, N = c["ranks"], c["count"]
-    say(f"allreduce c2 full R={R} N={N}")
+    say(f"allreduce bf16 full size R={R} N={N}")
     xs = W.allreduce_bf16_inputs(R, N, seed=c["seed"])
     exp = D.allreduce(xs, "bf16").view(np.uint8)
     out, sigs = _run(xs, "bf16")

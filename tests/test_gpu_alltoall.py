@@ -75,7 +75,7 @@ def test_alltoall_repeated_signal_accumulates():
 
 
 def test_alltoall_full_size_config():
-    c = W.CONFIGS["c3"]
+    c = W.CONFIGS["alltoall_r8_4MiB"]
     R, B = c["ranks"], c["block_bytes"]
     say(f"alltoall full R={R} B={B}")
     sends = W.alltoall_inputs(R, B, seed=c["seed"])

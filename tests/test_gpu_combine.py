@@ -147,13 +147,13 @@ def test_combine_bad_position_and_expert_reported():
     assert all(np.array_equal(res["out"][s], want[s]) for s in range(R))
 
 
-def test_combine_config_c4_full_size_sampled():
-    c = W.CONFIGS["c4"]
+def test_combine_r8_t4096_e256_k8_full_size_sampled():
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
     R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
     topk, _ = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
     weights = W.router_weights(topk, E, c["zipf_s"])
     y = W.expert_outputs(D.dispatch_rows_per_rank(topk, E), H, seed=c["seed"] + 2)
-    say("combine c4 full size")
+    say("combine full size R=8 T=4096 E=256 K=8")
     res = _run(topk, weights, y, E, H)
     sample = np.sort(np.random.default_rng(0).choice(T, 256, replace=False))
     _check(res, topk, weights, y, E, tokens=np.concatenate([sample, [T - 1]]))

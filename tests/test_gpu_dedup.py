@@ -131,12 +131,12 @@ def test_dedup_combine_vs_oracle(R, T, H, E, K, seed, dtype):
         job.assert_no_async_error()
 
 
-def test_dedup_config_c4_full_size():
-    c = W.CONFIGS["c4"]
+def test_dedup_r8_t4096_e256_k8_full_size():
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
     R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
     topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
     cap = R * T
-    say("dedup dispatch c4 full size")
+    say("dedup dispatch full size R=8 T=4096 E=256 K=8")
     with Job(R) as job:
         rw, rv, counts, src, experts, pos = _dispatch(job, topk, x, E, cap)
         _check_dispatch(job, topk, x, E, cap, rv, counts, src, experts, pos)

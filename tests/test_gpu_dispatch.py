@@ -128,9 +128,9 @@ def test_dispatch_repeated_signals_accumulate():
     _check(res, topk, x, E, repeats=3)
 
 
-def test_dispatch_config_c4_full_size():
-    c = W.CONFIGS["c4"]
-    say("dispatch c4 full")
+def test_dispatch_r8_t4096_e256_k8_full_size():
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
+    say("dispatch full size R=8 T=4096 E=256 K=8")
     topk, x = W.dispatch_inputs(c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"], c["zipf_s"],
                                 seed=c["seed"])
     res = _run(topk, x, c["experts"])

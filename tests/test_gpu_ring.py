@@ -49,9 +49,9 @@ def test_ring_repeated_accumulates():
     assert err[0] == vr.VR_OK
 
 
-def test_ring_config_c5b_full_size():
-    c = W.CONFIGS["c5b"]
-    say("ring c5b full")
+def test_ring_r16_1Mi_x_256B_full_size():
+    c = W.CONFIGS["ring_r16_1Mi_x_256B"]
+    say("ring full size R=16 2^20 puts x 256 B")
     R, P, pb, C = c["ranks"], c["puts_per_rank"], c["put_bytes"], c["contexts"]
     sends, out, sigs, cnts, lit, err = _run(R, P, pb, C)
     exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
@@ -79,9 +79,9 @@ def test_ring_weak_vs_oracle(R, P, pb, C):
     print(f"weak ring: {lit[0]} checks, {lit[1]} observed reorders")
 
 
-def test_ring_weak_config_c5b_full_size():
-    c = W.CONFIGS["c5b"]
-    say("ring weak c5b full")
+def test_ring_weak_r16_1Mi_x_256B_full_size():
+    c = W.CONFIGS["ring_r16_1Mi_x_256B"]
+    say("ring weak full size R=16 2^20 puts x 256 B")
     R, P, pb, C = c["ranks"], c["puts_per_rank"], c["put_bytes"], c["contexts"]
     sends, out, sigs, cnts, lit, err = _run(R, P, pb, C, flags=vr.VR_RING_WEAK)
     exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
@@ -89,4 +89,4 @@ def test_ring_weak_config_c5b_full_size():
         assert np.array_equal(out[d], exp[d]), d
     assert sigs == [[P // C] * C] * R and cnts == [[P // C] * C] * R
     assert err[0] == vr.VR_OK
-    print(f"weak ring c5b: {lit[0]} checks, {lit[1]} observed reorders")
+    print(f"weak ring full size: {lit[0]} checks, {lit[1]} observed reorders")

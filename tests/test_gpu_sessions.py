@@ -118,9 +118,9 @@ def test_alltoall_sessions_repeated_and_mixed_with_barriers():
     assert res["err"][0] == vr.VR_OK
 
 
-def test_alltoall_sessions_config_c3_full_size():
-    c = W.CONFIGS["c3"]
-    say("alltoall sessions c3 full size")
+def test_alltoall_sessions_r8_4MiB_full_size():
+    c = W.CONFIGS["alltoall_r8_4MiB"]
+    say("alltoall sessions full size R=8 4 MiB blocks")
     sends, res = _alltoall_sessions(c["ranks"], c["block_bytes"], seed=c["seed"])
     want = D.alltoall(sends, c["block_bytes"])
     for d in range(c["ranks"]):

@@ -24,16 +24,16 @@ __all__ = [
     "zipf_expert_probs", "f32_to_bf16_bits_torch",
 ]
 
-# Workload shapes. c2 is the large AllReduce (the headline throughput workload).
+# Workload shapes, named by what they are. The large bf16 AllReduce is the headline throughput workload.
 CONFIGS = {
-    "c1": dict(kind="allreduce", ranks=4, count=1 << 20, dtype="f32", seed=101),
-    "c2": dict(kind="allreduce", ranks=8, count=64 << 20, dtype="bf16", seed=102),
-    "c3": dict(kind="alltoall", ranks=8, block_bytes=4 << 20, seed=103),
-    "c4": dict(kind="dispatch", ranks=8, tokens=4096, hidden=256, experts=256,
-               topk=8, zipf_s=1.1, seed=104),
-    "c5a": dict(kind="allgather", ranks=16, bytes_per_rank=64 << 20, seed=105),
-    "c5b": dict(kind="ring", ranks=16, puts_per_rank=1 << 16, put_bytes=256,
-                contexts=64, seed=105),
+    "allreduce_f32_r4_1Mi": dict(kind="allreduce", ranks=4, count=1 << 20, dtype="f32", seed=101),
+    "allreduce_bf16_r8_64Mi": dict(kind="allreduce", ranks=8, count=64 << 20, dtype="bf16", seed=102),
+    "alltoall_r8_4MiB": dict(kind="alltoall", ranks=8, block_bytes=4 << 20, seed=103),
+    "dispatch_r8_t4096_e256_k8": dict(kind="dispatch", ranks=8, tokens=4096, hidden=256, experts=256,
+                                      topk=8, zipf_s=1.1, seed=104),
+    "allgather_r16_64MiB": dict(kind="allgather", ranks=16, bytes_per_rank=64 << 20, seed=105),
+    "ring_r16_1Mi_x_256B": dict(kind="ring", ranks=16, puts_per_rank=1 << 16, put_bytes=256,
+                                contexts=64, seed=105),
 }
 
 
