@@ -67,6 +67,28 @@ vrResult_t hip_ok(hipError_t e) { return e == hipSuccess ? VR_OK : VR_ERR_HIP; }
 
 size_t sidx(const vrComm* c, int rank, uint32_t id) { return (size_t)rank * c->req.signal_count + id; }
 
+// [p, p + bytes) lies in one device allocation on the communicator's device
+// (nothing to check when bytes is 0). Kernels dereference these pointers, so
+// a host or foreign pointer is refused here instead of faulting the GPU.
+bool dev_span_ok(const vrComm* c, const void* p, size_t bytes) {
+  if (!bytes) return true;
+  if (!p) return false;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (attr.type != hipMemoryTypeDevice || attr.device != c->device) return false;
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return static_cast<const char*>(p) >= static_cast<const char*>(base) &&
+         bytes <= size - (size_t)(static_cast<const char*>(p) - static_cast<const char*>(base));
+}
+
 // Whether [off, off + n) of rank's slice (any rank when rank < 0) touches a
 // word in use as a VA signal: such words are accessed by signal operations
 // only (GIN page, VA signals).
@@ -831,6 +853,12 @@ static vrResult_t dispatch_common(vrComm_t c, vrWindow_t x, size_t x_off, size_t
     return VR_ERR_INVALID_USAGE;
   if (sig_counts >= c->req.signal_count || sig_rows >= c->req.signal_count || sig_counts == sig_rows)
     return VR_ERR_INVALID_ARGUMENT;
+  const size_t RT = (size_t)R * T, n4 = sizeof(int32_t);
+  if (!dev_span_ok(c, topk, RT * K * n4) || !dev_span_ok(c, counts_out, (size_t)E * n4) ||
+      !dev_span_ok(c, src_out, (size_t)R * cap * n4) ||
+      (send_pos && !dev_span_ok(c, send_pos, RT * (dedup ? (size_t)R : (size_t)K) * n4)) ||
+      (dedup && !dev_span_ok(c, experts_out, (size_t)R * cap * K * n4)))
+    return VR_ERR_INVALID_ARGUMENT;
   const bool wait = !(flags & VR_COLL_NO_WAIT);
   U64Tab tc;
   vrResult_t r = inc_targets(c, sig_counts, R, true, &tc);
@@ -882,6 +910,10 @@ static vrResult_t combine_common(vrComm_t c, vrWindow_t y, size_t y_off, size_t 
   if (any_overlap(y, y_off, row_bytes * cap, out, out_off, row_bytes * T, R)) return VR_ERR_INVALID_ARGUMENT;
   if (va_touch(y, -1, y_off, row_bytes * cap) || va_touch(out, -1, out_off, row_bytes * T))
     return VR_ERR_INVALID_USAGE;
+  const size_t RT = (size_t)R * T;
+  if (!dev_span_ok(c, send_pos, RT * (dedup ? (size_t)R : (size_t)K) * sizeof(int32_t)) ||
+      (!dedup && (!dev_span_ok(c, topk, RT * K * sizeof(int32_t)) || !dev_span_ok(c, weights, RT * K * sizeof(float)))))
+    return VR_ERR_INVALID_ARGUMENT;
   const bool wait = !(flags & VR_COLL_NO_WAIT);
   U64Tab t;
   vrResult_t r = inc_targets(c, sig, R, wait, &t);
@@ -913,6 +945,7 @@ vrResult_t vr_ring_exchange(vrComm_t c, vrWindow_t send, vrWindow_t recv, size_t
                             size_t sig_window_off, uint64_t* litmus, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
   if (flags & ~(VR_COLL_NO_WAIT | VR_RING_WEAK)) return VR_ERR_INVALID_ARGUMENT;
+  if (litmus && !dev_span_ok(c, litmus, 2 * sizeof(uint64_t))) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (contexts < 1 || (uint32_t)contexts > c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
   if (put_bytes == 0 || put_bytes % 16 || put_bytes > 65536) return VR_ERR_INVALID_ARGUMENT;

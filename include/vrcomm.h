@@ -27,6 +27,13 @@
  *   - Memory: windows, inputs and outputs are owned by the caller; the
  *     library owns only its signal/counter words and small scratch buffers.
  *   - Device pointers are plain device addresses on the communicator's device.
+ *     Array arguments (routing ids, weights, positions, counts, tags, the
+ *     litmus words) must lie, for their whole stated size, inside one device
+ *     allocation on that device; a host pointer, a buffer on another device or
+ *     a span that runs past the end of its allocation is
+ *     VR_ERR_INVALID_ARGUMENT. (A buffer carved from a larger allocation, as
+ *     torch's caching allocator does, is only checked against that
+ *     allocation.)
  *     A stream is a hipStream_t passed as void* (NULL = the null stream).
  *   - A communicator is not thread-safe, and the operations issued on one
  *     communicator must execute in issue order: use one stream per
