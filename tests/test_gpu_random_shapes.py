@@ -90,3 +90,29 @@ def test_random_dispatch_and_combine(R, T, H, E, K, seed):
     res = TC._run(topk, weights, y, E, H)
     TC._check(res, topk, weights, y, E)
     assert res["err"][0] == vr.VR_OK
+
+
+DEDUP_CASES = _draw(5, lambda i: _dispatch_case(100 + i) + (["bf16", "f32"][i % 2],))
+RING_CASES = _draw(5, lambda i: (lambda R, C: (R, C * int(_rng.integers(1, 300)), 16 * int(_rng.integers(1, 64)), C))(
+    int(_rng.integers(2, 17)), int(_rng.integers(1, 9))))
+SESS_CASES = _draw(4, lambda i: (int(_rng.integers(2, 13)), int(_rng.integers(1, 80000))))
+
+
+@pytest.mark.parametrize("R,T,H,E,K,seed,dtype", DEDUP_CASES)
+def test_random_dedup_dispatch_and_combine(R, T, H, E, K, seed, dtype):
+    import test_gpu_dedup as TDD
+    TDD.test_dedup_dispatch_vs_oracle(R, T, H, E, K, seed, 0.1)
+    TDD.test_dedup_combine_vs_oracle(R, T, H, E, K, seed, dtype)
+
+
+@pytest.mark.parametrize("R,P,pb,C", RING_CASES)
+def test_random_ring_strong_and_weak(R, P, pb, C):
+    import test_gpu_ring as TR
+    TR.test_ring_vs_oracle(R, P, pb, C)
+    TR.test_ring_weak_vs_oracle(R, P, pb, C)
+
+
+@pytest.mark.parametrize("R,B", SESS_CASES)
+def test_random_alltoall_sessions(R, B):
+    import test_gpu_sessions as TS
+    TS.test_alltoall_sessions_vs_oracle(R, B)
