@@ -104,6 +104,11 @@ class Bench:
         # of dirty lines to be written back inside the next timed kernel).
         self.flush_buf.view(self.torch.int64).sum()
 
+    def warm(self, fn, n: int = 5):
+        """Untimed warm-up calls before a row's timed repetitions."""
+        for _ in range(n):
+            fn()
+
     def timed(self, fn, reps: int, flush: bool):
         """Per-repetition durations (ms) from events recorded on the launch stream."""
         torch = self.torch
@@ -244,7 +249,7 @@ def run_allreduce_f32_row(b, reps, rows):
     sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], N * 4)
     rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], N * 4)
     f = lambda: vr.vr_allreduce(comm, sw, 0, rw, 0, N, vr.VR_DT_F32, sig=0, stream=stream)  # noqa: E731
-    f()
+    b.warm(f)
     rows["allreduce_f32_r4_1Mi"] = row_entry("AllReduce fp32 R=4 N=1Mi", 2 * R * N * 4, b.timed(f, reps, True),
                                              "k_allreduce", "allreduce_f32_r4_1Mi")
     vr.vr_window_deregister(comm, sw)
@@ -276,7 +281,7 @@ def run_alltoall_row(b, reps, rows, sessions=False, copy_engine=False):
     else:
         f = lambda: vr.vr_alltoall(comm, sw, 0, rw, 0, B, sig=0, stream=stream)  # noqa: E731
         name, kernel, label = "alltoall_r8_4MiB", "k_alltoall", "AlltoAll R=8 B=4MiB"
-    f()
+    b.warm(f)
     rows[name] = row_entry(label, 2 * R * R * B, b.timed(f, reps, True), kernel, name)
     vr.vr_window_deregister(comm, sw)
     vr.vr_window_deregister(comm, rw)
@@ -302,7 +307,7 @@ def run_dispatch_row(b, reps, rows):
     counts = torch.zeros(R, E // R, dtype=torch.int32, device="cuda")
     src = torch.zeros(R, cap, dtype=torch.int32, device="cuda")
     f = lambda: vr.vr_dispatch(comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, None, 0, 1, stream=stream)  # noqa
-    f()
+    b.warm(f)
     nrows = int((topk >= 0).sum())
     bytes_alg = R * T * rb + topk.nbytes + nrows * rb + nrows * 4 + R * (E // R) * 4
     rows["dispatch_r8_t4096_e256_k8"] = row_entry("dispatch R=8 T=4096 512B E=256 K=8", bytes_alg,
@@ -340,7 +345,7 @@ def run_combine_row(b, reps, rows):
     vr.vr_dispatch(comm, xw, 0, rb, tk, T, K, E, yw, 0, cap, counts, src, pos, 0, 1, stream=stream)
     f = lambda: vr.vr_combine(comm, yw, 0, cap, rb, vr.VR_DT_BF16, tk, wt, pos, T, K, E, ow, 0, 2,  # noqa: E731
                               stream=stream)
-    f()
+    b.warm(f)
     nrows = int((topk >= 0).sum())
     bytes_alg = nrows * rb + R * T * rb + 3 * topk.nbytes
     rows["combine_r8_t4096_e256_k8"] = row_entry("combine R=8 T=4096 512B E=256 K=8", bytes_alg,
@@ -378,7 +383,7 @@ def run_dedup_rows(b, reps, rows):
     pos = torch.zeros(R, T, R, dtype=torch.int32, device="cuda")
     fd = lambda: vr.vr_dispatch_dedup(comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, experts,  # noqa: E731
                                       pos, 0, 1, stream=stream)
-    fd()
+    b.warm(fd)
     epr = E // R
     nrows = int(sum(len({int(e) // epr for e in topk[s, t] if e >= 0}) for s in range(R) for t in range(T)))
     bytes_d = R * T * rb + topk.nbytes + nrows * (rb + 4 + 4 * K) + R * epr * 4 + pos.numel() * 4
@@ -420,7 +425,7 @@ def run_allgather_row(b, reps, rows, copy_engine=False):
     else:
         f = lambda: vr.vr_allgather(comm, sw, 0, rw, 0, M, sig=0, stream=stream)  # noqa: E731
         name, kernel, label, n = "allgather_r16_64MiB", "k_allgather", "AllGather R=16 M=64MiB", max(3, reps // 2)
-    f()
+    b.warm(f)
     rows[name] = row_entry(label, R * M + R * R * M, b.timed(f, n, True), kernel, name)
     vr.vr_window_deregister(comm, sw)
     vr.vr_window_deregister(comm, rw)
@@ -442,7 +447,7 @@ def run_put_get_rows(b, reps, rows):
     fp = lambda: vr.vr_put(comm, 0, 0, 1, rw, 0, sw, 0, n, vr.SignalInc(0), vr.CounterInc(0), stream=stream)  # noqa
     fg = lambda: vr.vr_get(comm, 0, 1, 0, sw, 0, rw, 0, n, vr.CounterInc(1), stream=stream)  # noqa: E731
     for name, label, f in (("put_1GiB", "put 1 GiB", fp), ("get_1GiB", "get 1 GiB", fg)):
-        f()
+        b.warm(f)
         rows[name] = row_entry(label, 2 * n, b.timed(f, max(3, reps // 2), True), "k_put", name)
     code, bits = vr.vr_comm_get_async_error(comm)
     if code != vr.VR_OK:
@@ -465,7 +470,7 @@ def run_pingpong_rows(b, reps, rows):
     for name, label, flags in (("pingpong_cross_xcd_256B", "ping-pong 256 B, other XCD", 0),
                                ("pingpong_same_xcd_256B", "ping-pong 256 B, same XCD", vr.VR_PINGPONG_SAME_XCD)):
         f = lambda: vr.vr_signal_pingpong(comm, w, 0, n, iters, sig=0, flags=flags, stream=stream)  # noqa: E731
-        f()
+        b.warm(f)
         t = b.timed(f, max(3, reps // 2), False)
         med = float(np.median(t))
         rows[name] = row_entry(label, 4 * n * iters, t, "k_pingpong", name,
@@ -492,7 +497,7 @@ def run_ring_row(b, reps, rows, weak=False):
     lit = torch.zeros(2, dtype=torch.int64, device="cuda")
     flags = vr.VR_RING_WEAK if weak else 0
     f = lambda: vr.vr_ring_exchange(comm, sw, rw, pb, P, C, 0, 0, litmus=lit, flags=flags, stream=stream)  # noqa: E731
-    f()
+    b.warm(f)
     t = b.timed(f, reps, True)
     med = float(np.median(t))
     lh = lit.cpu().numpy()
@@ -542,6 +547,17 @@ def copy_ceiling(b: Bench, reps: int = 5):
 
 
 # ---- the CPU oracle beside it ---------------------------------------------------------------------
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(xs, R: int, N: int, budget_s: float = 20.0):
     """Time the oracle's protocol simulation of the same AllReduce on one host core.
 
@@ -576,7 +592,7 @@ def cpu_baseline(xs, R: int, N: int, budget_s: float = 20.0):
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"protocol simulation of the bf16 AllReduce, R={R}, first {n} of {N} elements per rank "
                       f"({dt:.2f} s on one pinned host core, numpy single-threaded)",
-            "seconds": round(dt, 3), "host_cpu_count": os.cpu_count()}
+            "seconds": round(dt, 3), "host_cpu_count": os.cpu_count(), "host_cpu_model": cpu_model()}
 
 
 def cpu_rows():
