@@ -19,7 +19,7 @@ AlltoAll by compute units, in barrier sessions and by the copy engines,
 dispatch, combine, their per-rank-dedup forms, AllGather by compute units
 and by the copy engines, ring exchange with strong and weak signals) each
 measured the same way, with the 256 MiB Infinity Cache flushed before every
-timed repetition.
+timed repetition, and again back to back (no flush) as the headline is.
 """
 from __future__ import annotations
 
@@ -110,9 +110,18 @@ class Bench:
             fn()
 
     def timed(self, fn, reps: int, flush: bool):
-        """Per-repetition durations (ms) from events recorded on the launch stream."""
+        """Per-repetition durations (ms) from events recorded on the launch stream.
+
+        With flush, the caches are evicted by a read before every repetition,
+        and the result also carries `b2b_ms`: the same call timed `reps`
+        times back to back between two events (the headline's timing mode).
+        The two bracket the HBM-bound time from both sides: after a read
+        flush the Infinity Cache is clean, so up to 256 MiB of a call's last
+        writes can still sit there when the timer stops; back to back, each
+        call pays for the write-back of the previous call's dirty lines, but
+        may find some of its inputs still cached."""
         torch = self.torch
-        out = []
+        out = Times()
         for _ in range(reps):
             if flush:
                 self.flush_cache()
@@ -123,7 +132,22 @@ class Bench:
             e1.record(self.stream)
             e1.synchronize()
             out.append(e0.elapsed_time(e1))
+        if flush:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            fn()
+            e0.record(self.stream)
+            for _ in range(reps):
+                fn()
+            e1.record(self.stream)
+            e1.synchronize()
+            out.b2b_ms = e0.elapsed_time(e1) / reps
         return out
+
+
+class Times(list):
+    """Durations (ms) of the flushed repetitions; b2b_ms: back-to-back mean."""
+    b2b_ms = None
 
 
 def row_entry(name, bytes_alg, times_ms, kernel, workload, extra=None):
@@ -132,9 +156,14 @@ def row_entry(name, bytes_alg, times_ms, kernel, workload, extra=None):
     d = {"algorithmic_bytes": int(bytes_alg), "median_ms": round(med, 5), "min_ms": round(float(np.min(times_ms)), 5),
          "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "kernel": kernel,
          "traffic_bytes_per_launch": measured_traffic(kernel, workload) if kernel in KERNEL_SOURCES else None}
+    b2b = getattr(times_ms, "b2b_ms", None)
+    if b2b:
+        d["back_to_back_ms"] = round(b2b, 5)
+        d["back_to_back_GBps"] = round(bytes_alg / (b2b * 1e-3) / 1e9, 1)
     if extra:
         d.update(extra)
-    log(f"{name}: {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), median {med:.4f} ms")
+    log(f"{name}: {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak), median {med:.4f} ms"
+        + (f"; back to back {d['back_to_back_GBps']:.1f} GB/s, {b2b:.4f} ms" if b2b else ""))
     return d
 
 
@@ -543,7 +572,48 @@ def copy_ceiling(b: Bench, reps: int = 5):
     t = b.timed(lambda: dst.copy_(src), reps, False)
     med = float(np.median(t))
     del src, dst
-    return {"GBps": round(2 * n / (med * 1e-3) / 1e9, 1), "how": f"torch copy_ of 1 GiB on the device, median of {reps}"}
+    out = {"GBps": round(2 * n / (med * 1e-3) / 1e9, 1), "how": f"torch copy_ of 1 GiB on the device, median of {reps}"}
+    out["library_put_1GiB_back_to_back_GBps"] = library_put_back_to_back(b)
+    return out
+
+
+def library_put_back_to_back(b: Bench, steps: int = 20):
+    """The library's 1 GiB put (rank 0 -> 1, SignalInc) timed as the headline
+    is: back to back between two events, no flush, so the dirty lines each
+    call leaves in the Infinity Cache are written back inside the next. The
+    flushed put rows run faster because their last writes still sit in that
+    cache when the timer stops."""
+    vr, stream = b.vr, b.stream.cuda_stream
+    R, n = 2, 1 << 30
+    comm = comm_for(vr, R, signal_count=1)
+    s1, sv = b.slices(R, n, fill=7)
+    r1, rv = b.slices(R, n, fill=0)
+    sw = vr.vr_window_register(comm, [v.data_ptr() for v in sv], n)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], n)
+
+    def f():
+        vr.vr_put(comm, 0, 0, 1, rw, 0, sw, 0, n, vr.SignalInc(0), stream=stream)
+
+    b.warm(f)
+    e0 = b.torch.cuda.Event(enable_timing=True)
+    e1 = b.torch.cuda.Event(enable_timing=True)
+    b.torch.cuda.synchronize()
+    e0.record(b.stream)
+    for _ in range(steps):
+        f()
+    e1.record(b.stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    code, bits = vr.vr_comm_get_async_error(comm)
+    if code != vr.VR_OK:
+        raise RuntimeError(f"device error in the put: {vr.vr_error_string(code)} bits={bits:#x}")
+    vr.vr_window_deregister(comm, sw)
+    vr.vr_window_deregister(comm, rw)
+    vr.vr_comm_destroy(comm)
+    del s1, r1
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    log(f"library put 1 GiB back to back: {gbs:.1f} GB/s ({ms:.4f} ms)")
+    return round(gbs, 1)
 
 
 # ---- the CPU oracle beside it ---------------------------------------------------------------------
