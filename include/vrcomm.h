@@ -26,6 +26,14 @@
  *     with vr_comm_get_async_error after synchronizing the stream.
  *   - Memory: windows, inputs and outputs are owned by the caller; the
  *     library owns only its signal/counter words and small scratch buffers.
+ *     The dispatch scratch (count rows, block prefixes: about
+ *     R*(T/64)*E*4 bytes) and the ring's snapshot words are grown on the
+ *     first vr_dispatch, vr_dispatch_dedup or vr_ring_exchange that needs
+ *     more than any call before it on the communicator: that call
+ *     synchronizes the device, frees the old buffer and allocates
+ *     (hipMalloc) before enqueuing. Later calls of that size or smaller
+ *     allocate nothing, so a caller that must not allocate (graph capture,
+ *     a serving loop) makes one call of its largest shape first.
  *   - Device pointers are plain device addresses on the communicator's device.
  *     Array arguments (routing ids, weights, positions, counts, tags, the
  *     litmus words) must lie, for their whole stated size, inside one device
@@ -462,6 +470,11 @@ vrResult_t vr_combine(vrComm_t comm, vrWindow_t y, size_t y_off, size_t y_capaci
  * missing message once the signal reads the context's full count sets
  * VR_ASYNC_LITMUS.
  * puts_per_rank must be a multiple of contexts; put_bytes a multiple of 16. */
+vrResult_t vr_ring_exchange(vrComm_t comm, vrWindow_t send, vrWindow_t recv, size_t put_bytes,
+                            size_t puts_per_rank, int contexts, uint32_t sig_base,
+                            uint32_t cnt_base, vrWindow_t sig_window, size_t sig_window_off,
+                            uint64_t* litmus, uint32_t flags, void* stream);
+
 /* Signal ping-pong (GIN page, one-sided transfers: put with a SignalInc, and
  * the signal methods: wait; GDA survey, opening section: for messages of a few
  * hundred bytes the control path sets the time): ranks 0 and 1 make `iters`
@@ -479,11 +492,6 @@ vrResult_t vr_combine(vrComm_t comm, vrWindow_t y, size_t y_off, size_t y_capaci
  * VR_ASYNC_TIMEOUT and ends the exchange. */
 vrResult_t vr_signal_pingpong(vrComm_t comm, vrWindow_t win, size_t off, size_t bytes, uint32_t iters,
                               uint32_t sig, uint32_t flags, void* stream);
-
-vrResult_t vr_ring_exchange(vrComm_t comm, vrWindow_t send, vrWindow_t recv, size_t put_bytes,
-                            size_t puts_per_rank, int contexts, uint32_t sig_base,
-                            uint32_t cnt_base, vrWindow_t sig_window, size_t sig_window_off,
-                            uint64_t* litmus, uint32_t flags, void* stream);
 
 #ifdef __cplusplus
 }
