@@ -34,6 +34,7 @@ struct ARArgs {
   uint64_t count;   // elements
   uint64_t csz;     // elements per owner chunk (multiple of the tile)
   uint32_t tpc;     // tiles per chunk
+  uint32_t nwg;     // work workgroups: R * tpc (one tile each), or fewer looping over tiles
   uint64_t* sig;
   uint32_t sig_stride;
   uint32_t* relay;  // [R] per chunk, then [R][8] per (chunk, XCD); rstride words apart
@@ -157,15 +158,122 @@ __device__ void reduce_tile(const ARArgs& a, uint64_t start, uint64_t end) {
   }
 }
 
-template <int DT, int RT, bool ALIGNED>
+// relay_arrive for a workgroup that brings `n` of the `parts` at once: true
+// in the one that completes the set (which resets the counter); a
+// workgroup holding every part touches no counter.
+__device__ inline bool relay_arrive_n(uint32_t* counter, uint32_t n, uint32_t parts, bool acquire) {
+  if (n >= parts) return true;
+  const uint32_t prev = atomic_add_u32(counter, n);
+  if (prev + n != parts) return false;
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (acquire) acquire_agent();
+  return true;
+}
+
+// Thread 0 of a workgroup whose stores have completed: `n` units of chunk c
+// done on XCD x, `per_tile` units to a tile. Two-level relay when the tiles
+// split evenly over the XCDs: first the tiles of chunk c on this XCD
+// (arrivals from one XCD only), then the XCDs that hold part of chunk c (one
+// for R = 8); the workgroup that completes the chunk applies one SignalInc
+// at every rank.
+__device__ void chunk_done(const ARArgs& a, uint32_t R, uint32_t c, uint32_t x, uint32_t n, uint32_t per_tile) {
+  const uint32_t nwork = R * a.tpc;
+  bool last;
+  if ((nwork & 7u) == 0) {
+    const uint32_t per = nwork >> 3;
+    const uint32_t lo = std::max(x * per, c * a.tpc), hi = std::min((x + 1) * per, (c + 1) * a.tpc);
+    const uint32_t nx = ((c + 1) * a.tpc - 1) / per - (c * a.tpc) / per + 1;
+    last = relay_arrive_n(a.relay + (R + c * 8 + x) * a.rstride, n, (hi - lo) * per_tile, false) &&
+           relay_arrive(a.relay + c * a.rstride, nx, false);
+  } else {
+    last = relay_arrive_n(a.relay + c * a.rstride, n, a.tpc * per_tile, false);
+  }
+  if (last)
+    for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
+}
+
+// Sum of one 256-vector slab in rank order, stored to every rank.
+template <int DT, int RT>
+__device__ inline void sum_store_slab(const ARArgs& a, uint64_t start, const v4u (&x)[RT]) {
+  using E = Elem<DT>;
+  float acc[E::kPerVec];
+  E::widen(x[0], acc);
+#pragma unroll
+  for (int r = 1; r < RT; ++r) {
+    float f[E::kPerVec];
+    E::widen(x[r], f);
+#pragma unroll
+    for (int j = 0; j < E::kPerVec; ++j) acc[j] = acc[j] + f[j];
+  }
+  const v4u out = E::narrow(acc);
+  constexpr uint32_t nbytes = 256u * 16u;
+#pragma unroll
+  for (int d = 0; d < RT; ++d)
+    store16_agent_stream(rsrc(a.recv.p[d] + a.recv_off + start * E::kSize, nbytes), threadIdx.x * 16u, out);
+}
+
+template <int DT, int RT>
+__device__ inline void load_slab(const ARArgs& a, uint64_t start, v4u (&x)[RT]) {
+  const uint64_t sb = a.send_off + (start + threadIdx.x * Elem<DT>::kPerVec) * Elem<DT>::kSize;
+#pragma unroll
+  for (int r = 0; r < RT; ++r) x[r] = load16_stream(reinterpret_cast<const v4u*>(a.send.p[r] + sb));
+}
+
+// Looping form, used when every tile is full and 16-byte aligned and the
+// tiles split evenly over the XCDs. A tile is kU slabs of 256 vectors per
+// rank; XCD x (x = b mod 8) owns slabs [x, x+1) * S (S = slabs / 8), and
+// workgroup b takes slabs x*S + b/8, + a.nwg/8, ..., issuing the next slab's
+// loads before this slab's sums and stores. The relay counts slabs.
+// Measured back to back at 8 ranks x 64 Mi bf16, alternating on one box:
+// 0.385 ms against 0.400 ms for one workgroup per tile; taking a tile's two
+// slabs in a row before striding was 3 % slower than one workgroup per tile.
+template <int DT, int RT>
+__device__ void persistent_tiles(const ARArgs& a, uint32_t b) {
+  constexpr uint64_t slab = 256ull * Elem<DT>::kPerVec;  // elements
+  const uint32_t S = ((RT * a.tpc) >> 3) * kU;           // slabs per XCD
+  const uint32_t spc = a.tpc * kU;                         // slabs per chunk
+  const uint32_t x = b & 7u, step = a.nwg >> 3;
+  uint32_t q = b >> 3;
+  if (q >= S) return;
+  uint32_t c = (x * S + q) / spc;
+  uint32_t n = 0;  // slabs of chunk c finished by this workgroup
+  v4u cur[RT], nxt[RT];
+  load_slab<DT, RT>(a, (uint64_t)(x * S + q) * slab, cur);
+  for (;;) {
+    const uint32_t q2 = q + step;
+    const bool more = q2 < S;
+    if (more) load_slab<DT, RT>(a, (uint64_t)(x * S + q2) * slab, nxt);
+    sum_store_slab<DT, RT>(a, (uint64_t)(x * S + q) * slab, cur);
+    ++n;
+    if (!more) break;
+    const uint32_t c2 = (x * S + q2) / spc;
+    if (c2 != c) {  // next slab is in another chunk: close this one
+      wg_stores_complete();
+      if (threadIdx.x == 0) chunk_done(a, RT, c, x, n, kU);
+      c = c2;
+      n = 0;
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) cur[r] = nxt[r];
+    q = q2;
+  }
+  wg_stores_complete();
+  if (threadIdx.x == 0) chunk_done(a, RT, c, x, n, kU);
+}
+
+template <int DT, int RT, bool ALIGNED, bool LOOP>
 __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
   const uint32_t R = RT ? RT : a.R;
   const uint32_t nwork = R * a.tpc;
   const uint32_t b = blockIdx.x;
-  if (b >= nwork) {  // receiver d waits for one SignalInc per owner
-    const uint32_t d = b - nwork;
+  if (b >= a.nwg) {  // receiver d waits for one SignalInc per owner
+    const uint32_t d = b - a.nwg;
     if (threadIdx.x == 0)
       wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
+    return;
+  }
+  if (LOOP) {
+    if (RT) persistent_tiles<DT, RT ? RT : 1>(a, b);
     return;
   }
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs (b % 8);
@@ -181,39 +289,28 @@ __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
   const uint64_t end = std::min<uint64_t>(cend, start + tile);
   if (start < end) reduce_tile<DT, RT, ALIGNED>(a, start, end);
   wg_stores_complete();
-  if (threadIdx.x != 0) return;
-  bool last;
-  if ((nwork & 7u) == 0) {
-    // two-level relay: first the tiles of chunk c on this XCD (arrivals from
-    // one XCD only), then the XCDs that hold part of chunk c (one for R = 8)
-    const uint32_t x = b & 7u, per = nwork >> 3;
-    const uint32_t lo = std::max(x * per, c * a.tpc), hi = std::min((x + 1) * per, (c + 1) * a.tpc);
-    const uint32_t nx = ((c + 1) * a.tpc - 1) / per - (c * a.tpc) / per + 1;
-    last = relay_arrive(a.relay + (R + c * 8 + x) * a.rstride, hi - lo, false) &&
-           relay_arrive(a.relay + c * a.rstride, nx, false);
-  } else {
-    last = relay_arrive(a.relay + c * a.rstride, a.tpc, false);
-  }
-  if (last)
-    for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
+  if (threadIdx.x == 0) chunk_done(a, R, c, b & 7u, 1, 1);
 }
 
 template <int DT, int RT, bool AL>
-void launch_t(const ARArgs& a, uint32_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_allreduce<DT, RT, AL>), dim3(grid), dim3(256), 0, st, a);
+void launch_t(const ARArgs& a, bool loop, uint32_t grid, hipStream_t st) {
+  if (loop) hipLaunchKernelGGL((k_allreduce<DT, RT, AL, true>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_allreduce<DT, RT, AL, false>), dim3(grid), dim3(256), 0, st, a);
 }
 
 template <int DT>
-void launch_dt(const ARArgs& a, bool aligned, uint32_t grid, hipStream_t st) {
-  if (!aligned) return launch_t<DT, 0, false>(a, grid, st);
+void launch_dt(const ARArgs& a, bool aligned, bool loop, uint32_t grid, hipStream_t st) {
+  if (!aligned) return launch_t<DT, 0, false>(a, false, grid, st);
   switch (a.R) {
-    case 2: return launch_t<DT, 2, true>(a, grid, st);
-    case 4: return launch_t<DT, 4, true>(a, grid, st);
-    case 8: return launch_t<DT, 8, true>(a, grid, st);
-    case 16: return launch_t<DT, 16, true>(a, grid, st);
-    default: return launch_t<DT, 0, true>(a, grid, st);
+    case 2: return launch_t<DT, 2, true>(a, loop, grid, st);
+    case 4: return launch_t<DT, 4, true>(a, loop, grid, st);
+    case 8: return launch_t<DT, 8, true>(a, loop, grid, st);
+    case 16: return launch_t<DT, 16, true>(a, loop, grid, st);
+    default: return launch_t<DT, 0, true>(a, false, grid, st);
   }
 }
+
+constexpr uint32_t kLoopWorkgroups = 4096;  // workgroups of the looping form
 
 }  // namespace
 
@@ -244,9 +341,16 @@ vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, co
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;
   a.wait = wait;
-  const uint32_t grid = a.tpc * R + (wait ? R : 0);
-  if (dtype == VR_DT_F32) launch_dt<VR_DT_F32>(a, aligned, grid, st);
-  else launch_dt<VR_DT_BF16>(a, aligned, grid, st);
+  // looping form: every tile full (count = R * csz), aligned, a rank count
+  // with a compiled kernel, tiles split evenly over the XCDs, and at least
+  // two tiles per looping workgroup
+  const uint32_t nwork = a.tpc * R;
+  const bool loop = aligned && (R == 2 || R == 4 || R == 8 || R == 16) && count == (uint64_t)R * a.csz &&
+                    (nwork & 7u) == 0 && nwork >= 2 * kLoopWorkgroups;
+  a.nwg = loop ? kLoopWorkgroups : nwork;
+  const uint32_t grid = a.nwg + (wait ? R : 0);
+  if (dtype == VR_DT_F32) launch_dt<VR_DT_F32>(a, aligned, loop, grid, st);
+  else launch_dt<VR_DT_BF16>(a, aligned, loop, grid, st);
   return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;
 }
 

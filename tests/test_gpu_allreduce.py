@@ -119,3 +119,20 @@ def test_allreduce_bf16_r8_64Mi_full_size():
     for d in range(R):
         assert np.array_equal(out[d][:N * 2], exp), d
     assert sigs == [R] * R
+
+
+@pytest.mark.parametrize("dtype,R,N", [("bf16", 16, 32 << 20), ("f32", 4, 16 << 20), ("bf16", 2, 48 << 20)])
+def test_allreduce_looping_form(dtype, R, N):
+    # Large, evenly tiled shapes run the looping form (4096 workgroups, each
+    # taking several tiles of its XCD's range): R=16 crosses an owner chunk
+    # inside a workgroup's loop, R=4 and R=2 spread one chunk over several
+    # XCDs. Two calls in a row check that the relay counters come back to 0.
+    say(f"allreduce looping form {dtype} R={R} N={N}")
+    xs = W.allreduce_f32_inputs(R, N, seed=R + 11) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + 11)
+    es = 4 if dtype == "f32" else 2
+    exp = D.allreduce(xs, dtype).view(np.uint8)
+    out, sigs = _run(xs, dtype, repeats=2)
+    for d in range(R):
+        assert np.array_equal(out[d][:N * es], exp), d
+        assert np.all(out[d][N * es:] == 0xCD)
+    assert sigs == [2 * R] * R
