@@ -93,3 +93,23 @@ def test_allgather_copy_engine_vs_oracle(R, M, send_off, recv_off):
         assert np.array_equal(out[d][recv_off:], exp[d]), d
         assert np.all(out[d][:recv_off] == 0x5A)
     assert sigs == [R] * R
+
+
+@pytest.mark.parametrize("R,M", [(16, 2 << 20), (8, (4 << 20) + 3 * 4096), (4, 8 << 20)])
+def test_allgather_whole_tiles_twice(R, M):
+    # Shapes of whole 4 KiB tiles, 512 to 2051 tiles per source; two calls in
+    # a row check that every source's relay counter comes back to 0.
+    say(f"allgather whole tiles twice R={R} M={M}")
+    sends = W.allgather_inputs(R, M, seed=R + M)
+    exp = D.allgather(sends)
+    with Job(R) as job:
+        sw, sv = job.window(M, arrays=sends)
+        rw, rv = job.window(R * M, fill=0x5A)
+        for _ in range(2):
+            vr.vr_allgather(job.comm, sw, 0, rw, 0, M, sig=1)
+        out = job.host(rv)
+        sigs = [job.sig(d, 1) for d in range(R)]
+        job.assert_no_async_error()
+    for d in range(R):
+        assert np.array_equal(out[d], exp[d]), d
+    assert sigs == [2 * R] * R
