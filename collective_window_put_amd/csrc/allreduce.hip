@@ -272,8 +272,9 @@ __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
       wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
     return;
   }
-  if (LOOP) {
-    if (RT) persistent_tiles<DT, RT ? RT : 1>(a, b);
+  if constexpr (LOOP) {
+    static_assert(RT != 0 && ALIGNED, "the looping form needs a compiled rank count and aligned tiles");
+    persistent_tiles<DT, RT>(a, b);
     return;
   }
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs (b % 8);
@@ -292,21 +293,26 @@ __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
   if (threadIdx.x == 0) chunk_done(a, R, c, b & 7u, 1, 1);
 }
 
-template <int DT, int RT, bool AL>
-void launch_t(const ARArgs& a, bool loop, uint32_t grid, hipStream_t st) {
-  if (loop) hipLaunchKernelGGL((k_allreduce<DT, RT, AL, true>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_allreduce<DT, RT, AL, false>), dim3(grid), dim3(256), 0, st, a);
+template <int DT, int RT, bool AL, bool LOOP>
+void launch_t(const ARArgs& a, uint32_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_allreduce<DT, RT, AL, LOOP>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int DT, int RT>
+void launch_r(const ARArgs& a, bool loop, uint32_t grid, hipStream_t st) {
+  if (loop) launch_t<DT, RT, true, true>(a, grid, st);
+  else launch_t<DT, RT, true, false>(a, grid, st);
 }
 
 template <int DT>
 void launch_dt(const ARArgs& a, bool aligned, bool loop, uint32_t grid, hipStream_t st) {
-  if (!aligned) return launch_t<DT, 0, false>(a, false, grid, st);
+  if (!aligned) return launch_t<DT, 0, false, false>(a, grid, st);
   switch (a.R) {
-    case 2: return launch_t<DT, 2, true>(a, loop, grid, st);
-    case 4: return launch_t<DT, 4, true>(a, loop, grid, st);
-    case 8: return launch_t<DT, 8, true>(a, loop, grid, st);
-    case 16: return launch_t<DT, 16, true>(a, loop, grid, st);
-    default: return launch_t<DT, 0, true>(a, false, grid, st);
+    case 2: return launch_r<DT, 2>(a, loop, grid, st);
+    case 4: return launch_r<DT, 4>(a, loop, grid, st);
+    case 8: return launch_r<DT, 8>(a, loop, grid, st);
+    case 16: return launch_r<DT, 16>(a, loop, grid, st);
+    default: return launch_t<DT, 0, true, false>(a, grid, st);
   }
 }
 
