@@ -222,11 +222,12 @@ __device__ inline void load_slab(const ARArgs& a, uint64_t start, v4u (&x)[RT]) 
 // Looping form, used when every tile is full and 16-byte aligned and the
 // tiles split evenly over the XCDs. A tile is kU slabs of 256 vectors per
 // rank; XCD x (x = b mod 8) owns slabs [x, x+1) * S (S = slabs / 8), and
-// workgroup b takes slabs x*S + b/8, + a.nwg/8, ..., issuing the next slab's
-// loads before this slab's sums and stores. The relay counts slabs.
-// Measured back to back at 8 ranks x 64 Mi bf16, alternating on one box:
-// 0.385 ms against 0.400 ms for one workgroup per tile; taking a tile's two
-// slabs in a row before striding was 3 % slower than one workgroup per tile.
+// workgroup b takes slabs x*S + b/8, + a.nwg/8, ..., with the loads of the
+// next two slabs in flight while a slab is summed and stored. The relay
+// counts slabs. Measured back to back at 8 ranks x 64 Mi bf16, alternating
+// on one box: 0.385 ms with one slab in flight ahead against 0.400 ms for
+// one workgroup per tile, and 0.381 ms with two; taking a tile's two slabs
+// in a row before striding was 3 % slower than one workgroup per tile.
 template <int DT, int RT>
 __device__ void persistent_tiles(const ARArgs& a, uint32_t b) {
   constexpr uint64_t slab = 256ull * Elem<DT>::kPerVec;  // elements
@@ -237,15 +238,15 @@ __device__ void persistent_tiles(const ARArgs& a, uint32_t b) {
   if (q >= S) return;
   uint32_t c = (x * S + q) / spc;
   uint32_t n = 0;  // slabs of chunk c finished by this workgroup
-  v4u cur[RT], nxt[RT];
-  load_slab<DT, RT>(a, (uint64_t)(x * S + q) * slab, cur);
+  v4u v0[RT], v1[RT], v2[RT];  // slabs q, q + step, q + 2 step
+  load_slab<DT, RT>(a, (uint64_t)(x * S + q) * slab, v0);
+  if (q + step < S) load_slab<DT, RT>(a, (uint64_t)(x * S + q + step) * slab, v1);
   for (;;) {
-    const uint32_t q2 = q + step;
-    const bool more = q2 < S;
-    if (more) load_slab<DT, RT>(a, (uint64_t)(x * S + q2) * slab, nxt);
-    sum_store_slab<DT, RT>(a, (uint64_t)(x * S + q) * slab, cur);
+    const uint32_t q2 = q + step, q3 = q2 + step;
+    if (q3 < S) load_slab<DT, RT>(a, (uint64_t)(x * S + q3) * slab, v2);
+    sum_store_slab<DT, RT>(a, (uint64_t)(x * S + q) * slab, v0);
     ++n;
-    if (!more) break;
+    if (q2 >= S) break;
     const uint32_t c2 = (x * S + q2) / spc;
     if (c2 != c) {  // next slab is in another chunk: close this one
       wg_stores_complete();
@@ -254,7 +255,10 @@ __device__ void persistent_tiles(const ARArgs& a, uint32_t b) {
       n = 0;
     }
 #pragma unroll
-    for (int r = 0; r < RT; ++r) cur[r] = nxt[r];
+    for (int r = 0; r < RT; ++r) {
+      v0[r] = v1[r];
+      v1[r] = v2[r];
+    }
     q = q2;
   }
   wg_stores_complete();
