@@ -6,15 +6,17 @@
 // get pulls a peer's window bytes, put pushes them with a SignalInc.
 //
 // Owner c reduces elements [c*csz, (c+1)*csz) (csz = ceil(N/R) rounded up to
-// a whole number of tiles). Each workgroup takes one tile of one owner's
-// chunk: it reads the tile from every rank's send window (the gets of the
-// reduce-scatter), sums in rank order in fp32 -- acc = x_0, then acc += x_r
-// for r = 1..R-1, each an IEEE binary32 addition rounded to nearest even --
-// converts, and stores the tile into every rank's receive window (the puts of
-// the all-gather). The workgroup completing the chunk's relay applies one
-// SignalInc at every rank, so each rank's signal rises by R (one per owner).
-// Output stores are agent-coherent and streaming (sc1 nt): measured 2-3%
-// faster than sc1 alone for this write-once pattern.
+// a whole number of tiles). A workgroup reads a tile from every rank's send
+// window (the gets of the reduce-scatter), sums in rank order in fp32 --
+// acc = x_0, then acc += x_r for r = 1..R-1, each an IEEE binary32 addition
+// rounded to nearest even -- converts, and stores the tile into every rank's
+// receive window (the puts of the all-gather). Small or ragged shapes run
+// one tile per workgroup; large evenly tiled ones run the looping form
+// below (a fixed grid striding over slabs, loads two slabs ahead). The
+// workgroup completing a chunk's relay applies one SignalInc at every rank,
+// so each rank's signal rises by R (one per owner). Output stores are
+// agent-coherent and streaming (sc1 nt): measured back to back 0.7 % faster
+// than sc1 alone in the looping form.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
