@@ -770,7 +770,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": workload, "ranks": head["R"], "count_per_rank": head["N"], "elem": "bf16",
                    "accumulate": "f32 in rank order", "algorithmic_bytes": head["bytes_alg"],
                    "frac_of_peak": round(value / HBM_PEAK_GBS, 4), "inputs": "seeded normal(0,1) -> bf16"},
