@@ -121,7 +121,8 @@ def test_allreduce_bf16_r8_64Mi_full_size():
     assert sigs == [R] * R
 
 
-@pytest.mark.parametrize("dtype,R,N", [("bf16", 16, 32 << 20), ("f32", 4, 16 << 20), ("bf16", 2, 48 << 20)])
+@pytest.mark.parametrize("dtype,R,N", [("bf16", 16, 32 << 20), ("f32", 4, 16 << 20), ("bf16", 2, 48 << 20),
+                                     ("f32", 8, 16 << 20), ("bf16", 4, 32 << 20)])
 def test_allreduce_looping_form(dtype, R, N):
     # Large, evenly tiled shapes run the looping form (4096 workgroups, each
     # taking several tiles of its XCD's range): R=16 crosses an owner chunk
