@@ -136,3 +136,53 @@ def test_dispatch_r8_t4096_e256_k8_full_size():
     res = _run(topk, x, c["experts"])
     _check(res, topk, x, c["experts"])
     assert res["err"][0] == vr.VR_OK
+
+
+def test_dispatch_shapes_interleaved_on_one_comm():
+    # One communicator: dispatches of two shapes, a per-rank-layout dispatch
+    # and a ring exchange (which reuses the library's scratch) in between, each
+    # dispatch checked against the oracle: nothing a dispatch leaves in the
+    # scratch may leak into the next one.
+    import torch
+    R, H, K = 4, 16, 4
+    rb = H * 2
+    shapes = [(300, 64, 1), (100, 32, 2), (300, 64, 3), (100, 32, 4), (300, 64, 5)]
+    with Job(R, signal_count=16, counter_count=16, context_count=2) as job:
+        xw, xv = job.window(300 * rb, fill=0)
+        cap = R * 300 * K
+        rw, rv = job.window(cap * rb, fill=0)
+        rs, _ = job.window(4096, fill=3)
+        rr, _ = job.window(4096, fill=0)
+        steps = []
+        for i, (T, E, seed) in enumerate(shapes):
+            topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+            for r in range(R):
+                xv[r][:T * rb].copy_(torch.from_numpy(np.ascontiguousarray(x[r]).reshape(-1).view(np.uint8)))
+            tk = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).cuda()
+            counts = torch.zeros(R, E // R, dtype=torch.int32, device="cuda")
+            src = torch.full((R, cap), -1, dtype=torch.int32, device="cuda")
+            vr.vr_dispatch(job.comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, None, 0, 1)
+            out = job.host(rv)
+            rows, tags, cnts, _ = D.dispatch(topk, x, E, cap)
+            for d in range(R):
+                n = rows[d].shape[0]
+                assert np.array_equal(out[d][:n * rb], rows[d].reshape(-1)), (i, d)
+                assert np.array_equal(src[d, :n].cpu().numpy(), tags[d]), (i, d)
+                assert np.array_equal(counts[d].cpu().numpy(), cnts[d]), (i, d)
+            steps.append(i)
+            if i == 1:  # the per-rank layout on the same communicator
+                cd = torch.zeros(R, E // R, dtype=torch.int32, device="cuda")
+                sd = torch.full((R, cap), -1, dtype=torch.int32, device="cuda")
+                ed = torch.full((R, cap, K), -2, dtype=torch.int32, device="cuda")
+                vr.vr_dispatch_dedup(job.comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, cd, sd, ed, None, 2, 3)
+                out = job.host(rv)
+                drows, dtags, _, dcnts, _ = D.dispatch_dedup(topk, x, E, cap)[:5]
+                for d in range(R):
+                    n = drows[d].shape[0]
+                    assert np.array_equal(out[d][:n * rb], drows[d].reshape(-1)), ("dedup", d)
+                    assert np.array_equal(sd[d, :n].cpu().numpy(), dtags[d]), ("dedup", d)
+            if i == 2:  # a ring exchange reuses the scratch words
+                vr.vr_ring_exchange(job.comm, rs, rr, 256, 8, 2, 4, 0)
+                job.torch.cuda.synchronize()
+        job.assert_no_async_error()
+    assert steps == list(range(len(shapes)))
