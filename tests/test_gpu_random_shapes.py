@@ -116,3 +116,33 @@ def test_random_ring_strong_and_weak(R, P, pb, C):
 def test_random_alltoall_sessions(R, B):
     import test_gpu_sessions as TS
     TS.test_alltoall_sessions_vs_oracle(R, B)
+
+
+def _loop_case(i):
+    # evenly tiled shapes past the looping form's threshold (at least 8192
+    # tiles of 4096 bf16 / 2048 fp32 elements), 16-byte aligned offsets
+    R = [2, 4, 8, 16][int(_rng.integers(0, 4))]
+    dtype = ["f32", "bf16"][i % 2]
+    tile = 2048 if dtype == "f32" else 4096
+    tpc = -(-8192 // R) + int(_rng.integers(0, 1024 // R + 1))
+    step = 8 // int(np.gcd(R, 8))  # tiles split evenly over the 8 XCDs
+    tpc = -(-tpc // step) * step
+    vec = 4 if dtype == "f32" else 8  # elements per 16 bytes
+    return R, R * tpc * tile, dtype, vec * int(_rng.integers(0, 64)), vec * int(_rng.integers(0, 64))
+
+
+LOOP_CASES = _draw(4, _loop_case)
+
+
+@pytest.mark.parametrize("R,N,dtype,so,ro", LOOP_CASES)
+def test_random_allreduce_looping_form(R, N, dtype, so, ro):
+    es = 4 if dtype == "f32" else 2
+    so, ro = so * es, ro * es
+    say(f"random allreduce looping form R={R} N={N} {dtype} send_off={so} recv_off={ro}")
+    xs = W.allreduce_f32_inputs(R, N, seed=N + R) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=N + R)
+    out, sigs = TAR._run(xs, dtype, send_off=so, recv_off=ro, repeats=2)
+    want = D.allreduce(xs, dtype).view(np.uint8)
+    for d in range(R):
+        assert np.array_equal(out[d][ro:ro + N * es], want), d
+        assert np.all(out[d][:ro] == 0xCD) and np.all(out[d][ro + N * es:] == 0xCD)
+    assert sigs == [2 * R] * R
