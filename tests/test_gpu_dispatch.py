@@ -186,3 +186,16 @@ def test_dispatch_shapes_interleaved_on_one_comm():
                 job.torch.cuda.synchronize()
         job.assert_no_async_error()
     assert steps == list(range(len(shapes)))
+
+
+@pytest.mark.parametrize("zipf_s,seed", [(1.1, 205), (1.1, 306), (0.0, 407)])
+def test_dispatch_full_shape_other_routings(zipf_s, seed):
+    # the full 8 x 4096 x top-8-of-256 shape under other routing draws: two
+    # more Zipf(1.1) seeds and uniform expert popularity (s = 0), where every
+    # rank receives about the same number of rows
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
+    say(f"dispatch full shape zipf_s={zipf_s} seed={seed}")
+    topk, x = W.dispatch_inputs(c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"], zipf_s, seed=seed)
+    res = _run(topk, x, c["experts"])
+    _check(res, topk, x, c["experts"])
+    assert res["err"][0] == vr.VR_OK
