@@ -78,6 +78,8 @@ def test_allreduce_unaligned_offsets(dtype):
         assert np.array_equal(out[d][es * 5:es * 5 + N * es], exp)
 
 
+@pytest.mark.filterwarnings("ignore:overflow encountered in add:RuntimeWarning")
+@pytest.mark.filterwarnings("ignore:invalid value encountered in add:RuntimeWarning")
 def test_allreduce_special_values_bf16():
     # ties, overflow to inf, inf + -inf = NaN (canonical 0x7FC0), signed zeros
     R = 3
