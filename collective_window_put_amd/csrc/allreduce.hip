@@ -227,7 +227,7 @@ __device__ inline void load_slab(const ARArgs& a, uint64_t start, v4u (&x)[RT]) 
 // workgroup b takes slabs x*S + b/8, + a.nwg/8, ..., with the loads of the
 // next two slabs in flight while a slab is summed and stored. The relay
 // counts slabs. Measured back to back at 8 ranks x 64 Mi bf16, alternating
-// on one box: 0.385 ms with one slab in flight ahead against 0.400 ms for
+// on one machine: 0.385 ms with one slab in flight ahead against 0.400 ms for
 // one workgroup per tile, and 0.381 ms with two; taking a tile's two slabs
 // in a row before striding was 3 % slower than one workgroup per tile.
 template <int DT, int RT>
