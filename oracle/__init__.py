@@ -38,9 +38,19 @@ Every function is pinned by tests under ``tests/`` (``-m "not gpu"``)
 against the pages' worked examples, closed forms, library routines,
 brute force and invariants. Parity unpinned: none of the functions here
 is left without a pin; the dispatch result and its per-entry positions are
-pinned by brute force, a library stable sort and invariants only, and the
-combine by hand-worked binary32 cases (product rounding, k order), a closed
-form checked against torch's bf16 rounding, and the one-hot special case,
-since the pages give no worked example for either.
+pinned by brute force (a token may name one expert more than once: one row
+per routing entry, in k order), a library stable sort and invariants only,
+and the combine by hand-worked binary32 cases (product rounding, k order,
+a repeated expert), a closed form checked against torch's bf16 rounding,
+and the one-hot special case, since the pages give no worked example for
+either. ``allgather_for_rank`` is pinned by the Symmetric-memory page's
+segments and brute force over small rank counts and sizes;
+``signal_increment`` by the final signals of each collective's
+step-by-step protocol and the GIN page's nRanks rule.
+
+``protocol`` computes every element value itself (its own rank-order owner
+sum and its own bf16 widening and rounding, pinned against torch), so its
+agreement with ``definitions`` checks the arithmetic as well as the data
+movement.
 """
 from . import primitives, definitions, protocol, ordering  # noqa: F401

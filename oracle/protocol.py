@@ -42,6 +42,34 @@ from .primitives import (COUNTER_BITS, SIGNAL_BITS, CounterInc, Deadlock,
                          InvalidArgument, SignalAdd, SignalInc, World)
 
 
+# -- element conversions (written here again, not imported from definitions, so
+# that agreement between the protocol and the definitions also checks them) --
+def _bf16_widen(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns to fp32 values, exactly: each value is ``bits * 2^16``
+    read as a binary32 pattern."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) * np.uint32(65536)).view(np.float32)
+
+
+def _bf16_round(x: np.ndarray) -> np.ndarray:
+    """fp32 values to bf16 bit patterns, round to nearest, ties to even.
+
+    Written as the comparison it stands for: keep the high half, and step it
+    up by one when the dropped low half is above one half of a unit in the
+    last kept place, or exactly one half and the kept half is odd. A carry out
+    of the mantissa lands in the exponent (overflow reaches infinity). NaN
+    (exponent all ones, mantissa nonzero) gives 0x7FC0.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    hi = u >> np.uint32(16)
+    lo = u & np.uint32(0xFFFF)
+    up = (lo > np.uint32(0x8000)) | ((lo == np.uint32(0x8000)) & ((hi & np.uint32(1)) == np.uint32(1)))
+    out = (hi + up.astype(np.uint32)).astype(np.uint16)
+    is_nan = ((u >> np.uint32(23)) & np.uint32(0xFF)) == np.uint32(0xFF)
+    is_nan &= (u & np.uint32(0x7FFFFF)) != np.uint32(0)
+    out[is_nan] = np.uint16(0x7FC0)
+    return out
+
+
 # -- operations ----------------------------------------------------------------
 @dataclass
 class Put:
@@ -344,6 +372,16 @@ def allreduce_scratch_bytes(count: int, nranks: int, dtype: str) -> int:
     return nranks * per * esize + per * esize
 
 
+def _owner_sum(vals):
+    """An owner's sum of its R received slots: slot 0, then each later slot
+    added in rank order, every addition one binary32 operation rounded to
+    nearest even."""
+    acc = np.array(vals[0], dtype=np.float32, copy=True)
+    for v in vals[1:]:
+        acc = (acc + np.asarray(v, dtype=np.float32)).astype(np.float32)
+    return acc
+
+
 def allreduce_programs(world: World, send: int, recv: int, scratch: int, count: int,
                        dtype: str, sig: int):
     """Reduce-scatter by gets into per-owner scratch slots, then all-gather by puts.
@@ -351,7 +389,6 @@ def allreduce_programs(world: World, send: int, recv: int, scratch: int, count: 
     Scratch layout per rank: R slots of ``ceil(count/R)`` input elements,
     followed by one slot holding the reduced chunk in the output type.
     """
-    from .definitions import allreduce  # the rank-order sum of one chunk
     R = world.nranks
     esize = 4 if dtype == "f32" else 2
     per = -(-count // R)
@@ -367,9 +404,16 @@ def allreduce_programs(world: World, send: int, recv: int, scratch: int, count: 
             yield Get(r, send, start * esize, scratch, r * per * esize, n * esize)
 
         def reduce_chunk(w, me, n=n):
+            # the owner's sum over its R slots, one rank at a time in rank
+            # order: acc = slot 0, then acc = acc + slot r (binary32, nearest
+            # even) for r = 1 .. R-1; bf16 slots widened exactly, the sum
+            # rounded once to bf16
             buf = w.buf(scratch, me)
             slots = [buf[r * per * esize:(r * per + n) * esize].view(np_t) for r in range(R)]
-            buf[res_off:res_off + n * esize] = allreduce(slots, dtype).view(np.uint8)
+            vals = [_bf16_widen(v) if dtype == "bf16" else v.astype(np.float32) for v in slots]
+            acc = _owner_sum(vals)
+            res = _bf16_round(acc) if dtype == "bf16" else acc
+            buf[res_off:res_off + n * esize] = res.view(np.uint8)
 
         yield Local(reduce_chunk, "sum in rank order")
         for peer in range(R):
@@ -570,7 +614,6 @@ def combine_programs(world: World, b: CombineBuffers, sig: int):
                     yield Get(e // epr, b.y, p * rb, b.stage, (t * K + k) * rb, rb)
 
         def mix(w, me):
-            from .definitions import bf16_bits_to_f32, f32_to_bf16_bits_rne
             st = w.buf(b.stage, me).reshape(T, K, rb)
             out = np.zeros((T, rb // b.esize), dtype=np.float32)
             for t in range(T):
@@ -578,10 +621,10 @@ def combine_programs(world: World, b: CombineBuffers, sig: int):
                 for k in range(K):
                     if b.topk[me, t, k] < 0 or b.pos[me, t, k] < 0:
                         continue
-                    y = bf16_bits_to_f32(st[t, k].view(np.uint16)) if b.dtype == "bf16" else st[t, k].view(np.float32)
+                    y = _bf16_widen(st[t, k].view(np.uint16)) if b.dtype == "bf16" else st[t, k].view(np.float32)
                     acc = acc + b.w[me, t, k] * y  # one rounded product, one rounded sum
                 out[t] = acc
-            res = f32_to_bf16_bits_rne(out) if b.dtype == "bf16" else out
+            res = _bf16_round(out) if b.dtype == "bf16" else out
             w.buf(b.out, me)[:] = res.view(np.uint8).reshape(-1)
 
         yield Local(mix, "mix")
@@ -694,17 +737,16 @@ def combine_dedup_programs(world: World, y_win: int, out_win: int, pos: np.ndarr
                     yield Get(d, y_win, int(pos[s, t, d]) * row_bytes, stage, (t * R + d) * row_bytes, row_bytes)
 
         def mix(w, me):
-            from .definitions import bf16_bits_to_f32, f32_to_bf16_bits_rne
             st = w.buf(stage, me).reshape(T, R, row_bytes)
             out = np.zeros((T, row_bytes // esize), dtype=np.float32)
             for t in range(T):
                 acc = np.zeros(row_bytes // esize, dtype=np.float32)
                 for d in range(R):
                     if pos[me, t, d] >= 0:
-                        acc = acc + (bf16_bits_to_f32(st[t, d].view(np.uint16)) if dtype == "bf16"
+                        acc = acc + (_bf16_widen(st[t, d].view(np.uint16)) if dtype == "bf16"
                                      else st[t, d].view(np.float32))
                 out[t] = acc
-            res = f32_to_bf16_bits_rne(out) if dtype == "bf16" else out
+            res = _bf16_round(out) if dtype == "bf16" else out
             w.buf(out_win, me)[:T * row_bytes] = res.view(np.uint8).reshape(-1)
 
         yield Local(mix, "mix")

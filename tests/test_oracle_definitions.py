@@ -174,6 +174,78 @@ def test_allgather_matches_tile():
     assert all(np.array_equal(out[d], ref[d]) for d in range(3))
 
 
+def test_allgather_for_rank_page_segments_and_brute_force():
+    # Symmetric-memory page, AllGather example: segment k of every rank's
+    # receive buffer holds rank k's contribution (4 ranks, 1 Mi fp32 each)
+    g = _load("allgather_segments.json")
+    R, n = g["ranks"], g["send_bytes"] // 4
+    sends = [np.full(n, float(r), dtype=np.float32).view(np.uint8) for r in range(R)]
+    for d in range(R):
+        got = D.allgather_for_rank(sends, d)
+        assert got.nbytes == g["recv_bytes"]
+        segs = got.view(np.float32).reshape(R, n)
+        for k, v in enumerate(g["segment_values"]):
+            assert np.all(segs[k] == np.float32(v)), (d, k)
+    # every destination, every small rank count and size: byte j of segment s
+    # at rank d is byte j of rank s's send buffer
+    for R in range(1, 5):
+        for M in range(0, 7):
+            sends = [np.array([(s * 16 + j) & 0xFF for j in range(M)], dtype=np.uint8) for s in range(R)]
+            for d in range(R):
+                got = D.allgather_for_rank(sends, d)
+                assert got.shape == (R * M,)
+                for s in range(R):
+                    for j in range(M):
+                        assert got[s * M + j] == sends[s][j], (R, M, d, s, j)
+
+
+def _final_signal_of(kind, R):
+    """Run one collective's protocol from zeroed signals and return every
+    rank's final value of the completion signal it uses."""
+    from oracle import protocol as pr
+    from oracle.primitives import World
+    w = World(R, signal_count=2)
+    if kind == "alltoall":
+        B = 4
+        s = w.register([np.arange(R * B, dtype=np.uint8) for _ in range(R)])
+        r = w.register_zeros(R * B)
+        progs, sig = pr.alltoall_programs(w, s, r, B, 1), 1
+    elif kind == "allgather":
+        M = 3
+        s = w.register([np.full(M, q, dtype=np.uint8) for q in range(R)])
+        r = w.register_zeros(R * M)
+        progs, sig = pr.allgather_programs(w, s, r, M, 1), 1
+    elif kind == "allreduce":
+        N = 2 * R + 1
+        s = w.register([np.full(N, q, dtype=np.float32).view(np.uint8) for q in range(R)])
+        r = w.register_zeros(N * 4)
+        sc = w.register_zeros(pr.allreduce_scratch_bytes(N, R, "f32"))
+        progs, sig = pr.allreduce_programs(w, s, r, sc, N, "f32", 1), 1
+    elif kind == "dispatch_counts":
+        T, H, E, K = 3, 2, 2 * R, 2
+        topk, x = W.dispatch_inputs(R, T, H, E, K, seed=R)
+        b = pr.DispatchBuffers(w, x, topk, E, R * T * K)
+        progs, sig = pr.dispatch_programs(w, b, 0, 1), 0
+    else:
+        raise ValueError(kind)
+    pr.run(w, progs, seed=R)
+    return [w.sig[d][sig] for d in range(R)]
+
+
+@pytest.mark.parametrize("kind", ["alltoall", "allgather", "allreduce", "dispatch_counts"])
+def test_signal_increment_equals_protocol_totals(kind):
+    # the final signal value is the number of SignalIncs aimed at the rank in
+    # the step-by-step protocol, loopback included (GIN page, pure-GIN
+    # AlltoAll kernel: the receiver waits for nRanks increments)
+    g = _load("alltoall_fill.json")
+    assert g["signal_increments_per_receiver"] == "nRanks"
+    for R in range(1, 6):
+        assert _final_signal_of(kind, R) == [D.signal_increment(kind, R)] * R, (kind, R)
+    assert D.signal_increment("alltoall", 7) == 7  # nRanks, the page's rule
+    with pytest.raises(ValueError):
+        D.signal_increment("ring", 4)
+
+
 # -- Ring --------------------------------------------------------------------------------
 def test_ring_is_cyclic_shift():
     R, P, pb = 5, 6, 8
@@ -188,7 +260,9 @@ def test_ring_is_cyclic_shift():
 
 # -- Dispatch ------------------------------------------------------------------------------
 def _dispatch_by_loops(topk, x, E):
-    """Destination-major loops: for d, for expert e of d, for source s, for token t."""
+    """Destination-major loops: for d, for expert e of d, for source s, for
+    token t, for entry k -- one row per routing entry naming e, so a token
+    whose top-k names e twice sends two rows (in k order)."""
     R, T, K = topk.shape
     epr = E // R
     res = []
@@ -197,17 +271,19 @@ def _dispatch_by_loops(topk, x, E):
         for e in range(d * epr, (d + 1) * epr):
             for s in range(R):
                 for t in range(T):
-                    if e in list(topk[s, t]):
-                        rows.append(x[s, t].view(np.uint8))
-                        tags.append((s << 16) | t)
+                    for k in range(K):
+                        if topk[s, t, k] == e:
+                            rows.append(x[s, t].view(np.uint8))
+                            tags.append((s << 16) | t)
         res.append((rows, tags))
     return res
 
 
 def test_dispatch_brute_force_all_routings_tiny():
-    # Every routing for R=2, T=2, K=2, E=4 with distinct experts per token.
+    # Every routing for R=2, T=2, K=2, E=4, a token's two entries allowed to
+    # name one expert twice (reading: one row per routing entry).
     R, T, K, E = 2, 2, 2, 4
-    pairs = [p for p in itertools.permutations(range(E), K)]
+    pairs = list(itertools.product(range(E), repeat=K))
     x = np.arange(R * T * 2, dtype=np.uint16).reshape(R, T, 2)
     n = 0
     for choice in itertools.product(pairs, repeat=R * T):
@@ -224,6 +300,19 @@ def test_dispatch_brute_force_all_routings_tiny():
             assert not over[d]
         n += 1
     assert n == len(pairs) ** (R * T)
+
+
+def test_dispatch_duplicate_expert_sends_one_row_per_entry():
+    # R=2, T=1, K=2, E=4: the token names expert 1 twice -> two rows at rank 0,
+    # both tagged (0, 0); counts and the row total count entries
+    topk = np.array([[[1, 1]], [[3, -1]]], dtype=np.int32)
+    x = np.array([[[7, 8]], [[9, 10]]], dtype=np.uint16)
+    rows, src, counts, over = D.dispatch(topk, x, 4)
+    assert src[0].tolist() == [0, 0] and src[1].tolist() == [1 << 16]
+    assert rows[0].shape == (2, 4) and np.array_equal(rows[0][0], rows[0][1])
+    assert counts[0].tolist() == [0, 2] and counts[1].tolist() == [0, 1]
+    assert D.dispatch_rows_per_rank(topk, 4).tolist() == [2, 1]
+    assert D.dispatch_positions(topk, 4).tolist() == [[[0, 1]], [[0, -1]]]
 
 
 def test_dispatch_brute_force_three_ranks_one_slot():
@@ -297,7 +386,7 @@ def _positions_by_loops(topk, E, cap=None):
 
 def test_dispatch_positions_brute_force_tiny():
     R, T, K, E = 2, 2, 2, 4
-    pairs = list(itertools.permutations(range(E), K)) + [(-1, 1), (2, -1)]
+    pairs = list(itertools.product(range(E), repeat=K)) + [(-1, 1), (2, -1)]  # repeats included
     for choice in itertools.product(pairs, repeat=R * T):
         topk = np.array(choice, dtype=np.int32).reshape(R, T, K)
         assert np.array_equal(D.dispatch_positions(topk, E), _positions_by_loops(topk, E))
@@ -356,6 +445,18 @@ def test_combine_hand_worked_rounding_each_product():
     # A fused multiply-add would keep the 2^-27 and give 2^-20 + 2^-27.
     got = _one_token_combine([1.0, 1.0 + 2.0 ** -20], [-(1.0 + 2.0 ** -7), 1.0 + 2.0 ** -7])
     assert got == 2.0 ** -20
+
+
+def test_combine_duplicate_expert_mixes_both_rows():
+    # R=1, T=1, K=2, both entries name expert 0: the dispatch sent two rows
+    # (positions 0 and 1), and the combine mixes each with its own weight:
+    # 0.5 * 3 + 0.25 * 3 = 2.25 (reading one row once would give 1.5)
+    topk = np.array([[[0, 0]]], dtype=np.int32)
+    pos = D.dispatch_positions(topk, 1)
+    assert pos.tolist() == [[[0, 1]]]
+    y = [np.array([[3.0], [3.0]], dtype=np.float32)]
+    w = np.array([[[0.5, 0.25]]], dtype=np.float32)
+    assert D.combine(topk, w, pos, y, 1, "f32")[0, 0, 0] == np.float32(2.25)
 
 
 def test_combine_hand_worked_k_order():
@@ -421,17 +522,24 @@ def test_combine_skips_entries_without_rows():
 
 
 # -- per-rank (dedup) dispatch and its combine -----------------------------------------
-def _dedup_case(R, T, H, E, K, seed, drop=0.0):
+def _dedup_case(R, T, H, E, K, seed, drop=0.0, repeat=0.0):
     topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    rng = np.random.default_rng(seed)
+    if repeat:  # entry k names the same expert as entry k-1
+        rep = rng.random(topk.shape) < repeat
+        rep[:, :, 0] = False
+        for k in range(1, K):
+            topk[:, :, k] = np.where(rep[:, :, k], topk[:, :, k - 1], topk[:, :, k])
     if drop:
-        topk[np.random.default_rng(seed).random(topk.shape) < drop] = -1
+        topk[rng.random(topk.shape) < drop] = -1
     return topk, x
 
 
-@pytest.mark.parametrize("R,T,H,E,K,seed,drop", [(2, 30, 4, 4, 2, 1, 0.0), (4, 80, 2, 16, 3, 2, 0.25),
-                                                  (3, 50, 3, 6, 2, 3, 0.1), (8, 40, 2, 64, 8, 4, 0.0)])
-def test_dedup_dispatch_against_the_per_expert_dispatch(R, T, H, E, K, seed, drop):
-    topk, x = _dedup_case(R, T, H, E, K, seed, drop)
+@pytest.mark.parametrize("R,T,H,E,K,seed,drop,repeat", [(2, 30, 4, 4, 2, 1, 0.0, 0.0), (4, 80, 2, 16, 3, 2, 0.25, 0.0),
+                                                         (3, 50, 3, 6, 2, 3, 0.1, 0.0), (8, 40, 2, 64, 8, 4, 0.0, 0.0),
+                                                         (4, 60, 2, 16, 4, 5, 0.1, 0.4)])
+def test_dedup_dispatch_against_the_per_expert_dispatch(R, T, H, E, K, seed, drop, repeat):
+    topk, x = _dedup_case(R, T, H, E, K, seed, drop, repeat)
     epr = E // R
     rows, src, experts, counts, over = D.dispatch_dedup(topk, x, E)
     prow, psrc, pcounts, _ = D.dispatch(topk, x, E)

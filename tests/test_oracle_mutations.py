@@ -214,7 +214,7 @@ def test_dedup_token_major_order_is_caught(monkeypatch):
             rows[d], src[d], experts[d] = rows[d][order], src[d][order], experts[d][order]
         return rows, src, experts, counts, over
     monkeypatch.setattr(D, "dispatch_dedup", token_major)
-    _fails(TD.test_dedup_dispatch_against_the_per_expert_dispatch, 4, 80, 2, 16, 3, 2, 0.25)
+    _fails(TD.test_dedup_dispatch_against_the_per_expert_dispatch, 4, 80, 2, 16, 3, 2, 0.25, 0.0)
 
 
 def test_combine_dedup_reversed_rank_order_is_caught(monkeypatch):
@@ -236,3 +236,49 @@ def test_pingpong_answer_in_place_is_caught(monkeypatch):
     monkeypatch.setattr(D, "signal_pingpong", in_place)
     _fails(TPR.test_pingpong_definition_hand_worked)
     _fails(TPR.test_pingpong_protocol_matches_definition, 3, 3, 17, 2)
+
+
+def test_allgather_for_rank_rotated_segments_are_caught(monkeypatch):
+    def rotated(sends, d):  # segment k of rank d holding rank (k + d) mod R's bytes
+        R = len(sends)
+        return np.concatenate([np.asarray(sends[(k + d) % R], dtype=np.uint8).reshape(-1) for k in range(R)])
+    monkeypatch.setattr(D, "allgather_for_rank", rotated)
+    _fails(TD.test_allgather_for_rank_page_segments_and_brute_force)
+
+
+def test_signal_increment_without_loopback_is_caught(monkeypatch):
+    monkeypatch.setattr(D, "signal_increment", lambda kind, R: R - 1)
+    _fails(TD.test_signal_increment_equals_protocol_totals, "alltoall")
+    _fails(TD.test_signal_increment_equals_protocol_totals, "allreduce")
+
+
+def test_dispatch_one_row_per_repeated_expert_is_caught(monkeypatch):
+    orig = D.dispatch
+
+    def once(topk, x, E, capacity_rows=None):  # a token naming e twice sends one row
+        t = np.array(topk, copy=True)
+        for k in range(1, t.shape[2]):
+            for q in range(k):
+                t[:, :, k] = np.where(t[:, :, k] == t[:, :, q], -1, t[:, :, k])
+        return orig(t, x, E, capacity_rows)
+    monkeypatch.setattr(D, "dispatch", once)
+    _fails(TD.test_dispatch_brute_force_all_routings_tiny)
+    _fails(TD.test_dispatch_duplicate_expert_sends_one_row_per_entry)
+
+
+def test_protocol_reversed_owner_sum_is_caught(monkeypatch):
+    from oracle import protocol as pr
+    import test_oracle_protocol as TPR
+    orig = pr._owner_sum
+    monkeypatch.setattr(pr, "_owner_sum", lambda vals: orig(list(vals)[::-1]))
+    _fails(TPR.test_allreduce_random_interleavings, 8, 257, "f32", 2)
+    _fails(TPR.test_protocol_owner_sum_is_rank_order)
+
+
+def test_protocol_bf16_truncation_is_caught(monkeypatch):
+    from oracle import protocol as pr
+    import test_oracle_protocol as TPR
+    monkeypatch.setattr(pr, "_bf16_round",
+                        lambda x: (np.ascontiguousarray(x, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16))
+    _fails(TPR.test_protocol_bf16_conversions_match_torch)
+    _fails(TPR.test_allreduce_random_interleavings, 4, 300, "bf16", 1)

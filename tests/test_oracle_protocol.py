@@ -383,3 +383,56 @@ def test_pingpong_needs_two_ranks():
     h = w.register([np.zeros(8, np.uint8)])
     with pytest.raises(Exception):
         pr.pingpong_programs(w, h, 0, 1, 1, 0)
+
+
+# -- the protocol's own element conversions and owner sum --------------------------
+def test_protocol_bf16_conversions_match_torch():
+    import torch
+    # widening: every bf16 pattern, against torch's exact bf16 -> fp32
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    got = pr._bf16_widen(bits)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # rounding: random patterns plus ties and the overflow edge, non-NaN, against
+    # torch's round-to-nearest-even fp32 -> bf16
+    rng = np.random.default_rng(5)
+    u = rng.integers(0, 1 << 32, 1 << 18, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 1 << 16, 4096, dtype=np.uint64).astype(np.uint32) << np.uint32(16)) | np.uint32(0x8000)
+    edge = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7FFFFF, 0xFF7F8000, 0x7F800000, 0x00008000, 0x00018000,
+                     0x80000000, 0x00000001], dtype=np.uint32)
+    u = np.concatenate([u, ties, edge])
+    is_nan = (((u >> np.uint32(23)) & np.uint32(0xFF)) == np.uint32(0xFF)) & ((u & np.uint32(0x7FFFFF)) != 0)
+    u = u[~is_nan]
+    f = u.view(np.float32)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(pr._bf16_round(f), ref)
+    # NaN reading: any NaN becomes the canonical quiet NaN 0x7FC0
+    nans = np.array([0x7FC00000, 0xFFC00001, 0x7F800001, 0xFFFFFFFF], dtype=np.uint32).view(np.float32)
+    assert pr._bf16_round(nans).tolist() == [0x7FC0] * 4
+
+
+def test_protocol_owner_sum_is_rank_order():
+    # 2^24 + 1 + 1: rank order rounds each +1 away (ties to even), a reversed
+    # or pairwise order keeps 2; -0.0 alone stays -0.0 (acc starts at slot 0)
+    big = np.float32(2.0 ** 24)
+    vals = [np.array([big], np.float32), np.array([1.0], np.float32), np.array([1.0], np.float32)]
+    assert pr._owner_sum(vals)[0] == big
+    assert np.signbit(pr._owner_sum([np.array([-0.0], np.float32)])[0])
+
+
+def test_allreduce_protocol_bf16_special_values_match_definition():
+    # ties at the bf16 rounding point, overflow to infinity, inf - inf, NaN
+    R, N = 3, 8
+    f = np.array([[1.0, 3.0e38, np.inf, np.nan, 1.0, -2.0, 0.0, -0.0],
+                  [2.0 ** -8, 3.0e38, -np.inf, 1.0, 2.0 ** -8 + 2.0 ** -16, 2.0 ** -7, -0.0, -0.0],
+                  [0.0, 0.0, 1.0, 1.0, 0.0, 0.0, 0.0, -0.0]], dtype=np.float32)
+    xs = [pr._bf16_round(f[r]) for r in range(R)]
+    w = World(R)
+    s = w.register([x.view(np.uint8).copy() for x in xs])
+    r = w.register_zeros(N * 2)
+    sc = w.register_zeros(pr.allreduce_scratch_bytes(N, R, "bf16"))
+    with np.errstate(invalid="ignore", over="ignore"):
+        pr.run(w, pr.allreduce_programs(w, s, r, sc, N, "bf16", 0), seed=2)
+        exp = D.allreduce(xs, "bf16")
+    for d in range(R):
+        assert np.array_equal(w.buf(r, d).view(np.uint16), exp)
