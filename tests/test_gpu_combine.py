@@ -147,7 +147,8 @@ def test_combine_bad_position_and_expert_reported():
     assert all(np.array_equal(res["out"][s], want[s]) for s in range(R))
 
 
-def test_combine_r8_t4096_e256_k8_full_size_sampled():
+def test_combine_r8_t4096_e256_k8_full_size():
+    # every token of every rank compared with the oracle
     c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
     R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
     topk, _ = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
@@ -155,6 +156,21 @@ def test_combine_r8_t4096_e256_k8_full_size_sampled():
     y = W.expert_outputs(D.dispatch_rows_per_rank(topk, E), H, seed=c["seed"] + 2)
     say("combine full size R=8 T=4096 E=256 K=8")
     res = _run(topk, weights, y, E, H)
-    sample = np.sort(np.random.default_rng(0).choice(T, 256, replace=False))
-    _check(res, topk, weights, y, E, tokens=np.concatenate([sample, [T - 1]]))
+    _check(res, topk, weights, y, E)
+    assert res["err"][0] == vr.VR_OK
+
+
+@pytest.mark.parametrize("R,T,H,E,K,seed,dtype", [(4, 90, 16, 16, 4, 30, "bf16"), (8, 200, 256, 256, 8, 31, "bf16"),
+                                                  (3, 50, 8, 6, 3, 32, "f32")])
+def test_combine_duplicate_expert_ids(R, T, H, E, K, seed, dtype):
+    # entries naming one expert twice each have their own row (the dispatch
+    # sent one per entry), mixed with their own weights in k order
+    topk, weights, y = _inputs(R, T, H, E, K, seed, dtype)
+    rep = np.random.default_rng(seed).random(topk.shape) < 0.4
+    for k in range(1, K):
+        topk[:, :, k] = np.where(rep[:, :, k], topk[:, :, k - 1], topk[:, :, k])
+    y = W.expert_outputs(D.dispatch_rows_per_rank(topk, E), H, seed=seed + 50, dtype=dtype)
+    say(f"combine with repeated expert ids R={R} T={T} E={E} K={K} {dtype}")
+    res = _run(topk, weights, y, E, H, dtype)
+    _check(res, topk, weights, y, E, dtype)
     assert res["err"][0] == vr.VR_OK

@@ -99,13 +99,29 @@ def test_dedup_dispatch_unaligned_rows():
         _check_dispatch(job, topk, x, E, R * T, rv, counts, src, experts, pos, recv_off=3)
 
 
-@pytest.mark.parametrize("R,T,H,E,K,seed,dtype", [(4, 37, 16, 16, 3, 1, "bf16"), (3, 130, 8, 6, 2, 2, "f32"),
-                                                  (8, 200, 256, 64, 8, 3, "bf16"), (5, 1, 8, 10, 1, 4, "bf16")])
-def test_dedup_combine_vs_oracle(R, T, H, E, K, seed, dtype):
+@pytest.mark.parametrize("R,T,H,E,K,seed,frac", [(4, 100, 8, 16, 4, 40, 0.4), (8, 300, 256, 256, 8, 41, 0.3),
+                                                  (2, 3, 4, 4, 2, 42, 1.0)])
+def test_dedup_dispatch_duplicate_expert_ids(R, T, H, E, K, seed, frac):
+    # a token naming one expert twice reaches that rank once; its expert list
+    # shows the local expert at both entries, and the counts count both
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    rep = np.random.default_rng(seed).random(topk.shape) < frac
+    for k in range(1, K):
+        topk[:, :, k] = np.where(rep[:, :, k], topk[:, :, k - 1], topk[:, :, k])
+    say(f"dedup dispatch with repeated expert ids R={R} T={T} E={E} K={K}")
+    cap = max(1, R * T)
+    with Job(R) as job:
+        rw, rv, counts, src, experts, pos = _dispatch(job, topk, x, E, cap)
+        over = _check_dispatch(job, topk, x, E, cap, rv, counts, src, experts, pos)
+        assert not any(over)
+        job.assert_no_async_error()
+
+
+def _dedup_combine_case(R, T, H, E, K, seed, dtype, drop=0.15, topk=None):
     import torch
-    say(f"dedup combine R={R} T={T} H={H} {dtype}")
-    topk, x = W.dispatch_inputs(R, T, 4, E, K, seed=seed)
-    topk[np.random.default_rng(seed).random(topk.shape) < 0.15] = -1
+    if topk is None:
+        topk, _ = W.dispatch_inputs(R, T, 4, E, K, seed=seed)
+        topk[np.random.default_rng(seed).random(topk.shape) < drop] = -1
     es = 2 if dtype == "bf16" else 4
     rb = H * es
     cap = max(1, R * T)
@@ -129,6 +145,22 @@ def test_dedup_combine_vs_oracle(R, T, H, E, K, seed, dtype):
             assert np.all(out[s][T * rb:] == 0xEE)
         assert [job.sig(d, SIG_COMB) for d in range(R)] == [R] * R
         job.assert_no_async_error()
+
+
+@pytest.mark.parametrize("R,T,H,E,K,seed,dtype", [(4, 37, 16, 16, 3, 1, "bf16"), (3, 130, 8, 6, 2, 2, "f32"),
+                                                  (8, 200, 256, 64, 8, 3, "bf16"), (5, 1, 8, 10, 1, 4, "bf16")])
+def test_dedup_combine_vs_oracle(R, T, H, E, K, seed, dtype):
+    say(f"dedup combine R={R} T={T} H={H} {dtype}")
+    _dedup_combine_case(R, T, H, E, K, seed, dtype)
+
+
+def test_dedup_combine_r8_t4096_e256_k8_full_size():
+    # every token of every rank, at the full dispatch shape and routing
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
+    R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
+    topk, _ = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
+    say("dedup combine full size R=8 T=4096 E=256 K=8")
+    _dedup_combine_case(R, T, H, E, K, c["seed"], "bf16", topk=topk)
 
 
 def test_dedup_r8_t4096_e256_k8_full_size():

@@ -199,3 +199,27 @@ def test_dispatch_full_shape_other_routings(zipf_s, seed):
     res = _run(topk, x, c["experts"])
     _check(res, topk, x, c["experts"])
     assert res["err"][0] == vr.VR_OK
+
+
+def _with_repeats(topk, frac, seed):
+    """Entry k names the same expert as entry k-1 with probability frac."""
+    t = topk.copy()
+    rep = np.random.default_rng(seed).random(t.shape) < frac
+    for k in range(1, t.shape[2]):
+        t[:, :, k] = np.where(rep[:, :, k], t[:, :, k - 1], t[:, :, k])
+    return t
+
+
+@pytest.mark.parametrize("R,T,H,E,K,seed,frac", [(2, 3, 4, 4, 2, 20, 1.0), (4, 100, 8, 16, 4, 21, 0.4),
+                                                  (8, 300, 256, 256, 8, 22, 0.3), (3, 70, 8, 6, 3, 23, 0.5)])
+def test_dispatch_duplicate_expert_ids_send_one_row_per_entry(R, T, H, E, K, seed, frac):
+    # a token whose top-k names one expert more than once sends one row per
+    # entry, in k order, and the counts and the row signal count entries
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    topk = _with_repeats(topk, frac, seed)
+    assert any(len(set(topk[s, t].tolist())) < K for s in range(R) for t in range(T))
+    say(f"dispatch with repeated expert ids R={R} T={T} E={E} K={K}")
+    res = _run(topk, x, E)
+    over = _check(res, topk, x, E)
+    assert not any(over)
+    assert res["err"][0] == vr.VR_OK
