@@ -30,7 +30,7 @@ __all__ = [
     "vr_put", "vr_get", "vr_signal", "vr_signal_wait", "vr_signal_read", "vr_signal_reset",
     "vr_signal_expected", "vr_counter_wait", "vr_counter_read", "vr_counter_reset",
     "vr_allreduce", "vr_alltoall", "vr_allgather", "vr_dispatch", "vr_combine", "vr_ring_exchange",
-    "vr_signal_pingpong",
+    "vr_signal_pingpong", "vr_dispatch_noalloc", "VR_DISPATCH_NOALLOC_SCRATCH_BYTES",
 ]
 
 # The in-tree build; VRCOMM_LIB may name another build of the same library.
@@ -60,6 +60,7 @@ VR_COLL_COPY_ENGINE = 0x4
 VR_CE_STREAMS = 8
 VR_RING_WEAK = 0x8
 VR_PINGPONG_SAME_XCD = 0x10
+VR_DISPATCH_NOALLOC_SCRATCH_BYTES = 4 << 20
 VR_FENCE_NONE, VR_FENCE_PUT, VR_FENCE_GET = 0x0, 0x1, 0x2
 VR_ASYNC_TIMEOUT, VR_ASYNC_CAPACITY, VR_ASYNC_BAD_EXPERT, VR_ASYNC_LITMUS = 0x1, 0x2, 0x4, 0x8
 
@@ -149,6 +150,8 @@ SYMBOLS = {
     "vr_allgather": (_R, [_P, _P, c_size_t, _P, c_size_t, c_size_t, c_uint32, c_uint32, _P]),
     "vr_dispatch": (_R, [_P, _P, c_size_t, c_size_t, _P, c_int, c_int, c_int, _P, c_size_t, c_size_t, _P, _P,
                          _P, c_uint32, c_uint32, c_uint32, _P]),
+    "vr_dispatch_noalloc": (_R, [_P, _P, c_size_t, c_size_t, _P, c_int, c_int, c_int, _P, c_size_t, c_size_t, _P,
+                                 _P, _P, c_uint32, c_uint32, c_uint32, _P]),
     "vr_combine": (_R, [_P, _P, c_size_t, c_size_t, c_size_t, c_int, _P, _P, _P, c_int, c_int, c_int, _P,
                         c_size_t, c_uint32, c_uint32, _P]),
     "vr_dispatch_dedup": (_R, [_P, _P, c_size_t, c_size_t, _P, c_int, c_int, c_int, _P, c_size_t, c_size_t, _P, _P,
@@ -392,6 +395,13 @@ def vr_dispatch(comm, x, x_off, row_bytes, topk_idx, T, K, num_experts, recv, re
     _check(lib().vr_dispatch(comm, x, x_off, row_bytes, _ptr(topk_idx), T, K, num_experts, recv, recv_off,
                              capacity_rows, _ptr(recv_expert_counts), _ptr(recv_src), _ptr(send_pos), sig_counts,
                              sig_rows, flags, _stream(stream)), "vr_dispatch")
+
+
+def vr_dispatch_noalloc(comm, x, x_off, row_bytes, topk_idx, T, K, num_experts, recv, recv_off, capacity_rows,
+                        recv_expert_counts, recv_src, send_pos, sig_counts, sig_rows, flags=0, stream=None):
+    _check(lib().vr_dispatch_noalloc(comm, x, x_off, row_bytes, _ptr(topk_idx), T, K, num_experts, recv, recv_off,
+                                     capacity_rows, _ptr(recv_expert_counts), _ptr(recv_src), _ptr(send_pos),
+                                     sig_counts, sig_rows, flags, _stream(stream)), "vr_dispatch_noalloc")
 
 
 def vr_dispatch_dedup(comm, x, x_off, row_bytes, topk_idx, T, K, num_experts, recv, recv_off, capacity_rows,

@@ -24,6 +24,36 @@ namespace {
 std::mutex g_mu;
 std::set<vrComm*> g_comms;
 
+// Scratch of vr_dispatch_noalloc: a file-scope device array, so each GPU the
+// library runs on holds its own copy (allocated with the code object and kept
+// until the process ends). In host code `scratch` names a host-side stand-in,
+// not a device address: the device address of each GPU's copy is taken once
+// per device with hipGetSymbolAddress (in vr_comm_create, with that device
+// current) and only that address is ever handed to a kernel.
+static __device__ __align__(256) char scratch[VR_DISPATCH_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 256;
+char* g_noalloc_scratch[kMaxDevices];  // per device, under g_mu; null until looked up
+
+// The current device's copy of `scratch` (looked up on the first call per
+// device). Called with the device current; VR_ERR_HIP if the lookup fails.
+vrResult_t noalloc_scratch_init(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return VR_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_mu);
+  if (g_noalloc_scratch[dev]) return VR_OK;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return VR_ERR_HIP;
+  }
+  g_noalloc_scratch[dev] = static_cast<char*>(p);
+  return VR_OK;
+}
+char* noalloc_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(g_mu);
+  return g_noalloc_scratch[dev];
+}
+
 constexpr uint32_t kPutTile = 16384;  // bytes per workgroup of a put
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -404,7 +434,8 @@ vrResult_t vr_comm_create(int nranks, const vrCommRequirements* req, void* works
     }
     c->ws = static_cast<char*>(p);
   }
-  if (hipMemset(c->ws, 0, l.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+  if (hipMemset(c->ws, 0, l.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+      noalloc_scratch_init(dev) != VR_OK) {
     if (c->owns_ws) (void)hipFree(c->ws);
     delete c;
     return VR_ERR_HIP;
@@ -838,7 +869,8 @@ vrResult_t vr_allgather(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t
 static vrResult_t dispatch_common(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes, const int32_t* topk,
                                   int T, int K, int E, vrWindow_t recv, size_t recv_off, size_t cap,
                                   int32_t* counts_out, int32_t* src_out, int32_t* experts_out, int32_t* send_pos,
-                                  bool dedup, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags, void* stream) {
+                                  bool dedup, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags, void* stream,
+                                  bool noalloc = false) {
   if (!live(c) || !has_win(c, x) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
   if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
@@ -865,10 +897,20 @@ static vrResult_t dispatch_common(vrComm_t c, vrWindow_t x, size_t x_off, size_t
   if (r != VR_OK) return r;
   for (int d = 0; d < R; ++d)
     if (check_signal_mode(c, d, sig_rows, VR_SIGNAL_ADD) != VR_OK) return VR_ERR_INVALID_USAGE;
-  r = ensure_scratch(c, dispatch_scratch_bytes(R, T, dedup ? R : E, dedup ? E : 0));
-  if (r != VR_OK) return r;
+  const size_t need = dispatch_scratch_bytes(R, T, dedup ? R : E, dedup ? E : 0);
+  char* scr = nullptr;
+  if (noalloc) {
+    // the GPU's fixed scratch array; nothing is allocated
+    if (need > VR_DISPATCH_NOALLOC_SCRATCH_BYTES) return VR_ERR_INVALID_ARGUMENT;
+    scr = noalloc_scratch(c->device);
+    if (!scr) return VR_ERR_HIP;
+  } else {
+    r = ensure_scratch(c, need);
+    if (r != VR_OK) return r;
+    scr = c->scratch;
+  }
   r = launch_dispatch(c, x, x_off, row_bytes, topk, T, K, E, recv, recv_off, cap, counts_out, src_out, send_pos,
-                      experts_out, dedup, sig_counts, sig_rows, tc, wait, S(stream));
+                      experts_out, dedup, sig_counts, sig_rows, tc, wait, scr, S(stream));
   if (r == VR_OK) {
     commit_inc(c, sig_counts, R);
     for (int d = 0; d < R; ++d) note_signal(c, d, sig_rows, VR_SIGNAL_ADD, 0, false);
@@ -882,6 +924,14 @@ vrResult_t vr_dispatch(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes,
                        void* stream) {
   return dispatch_common(c, x, x_off, row_bytes, topk, T, K, E, recv, recv_off, cap, counts_out, src_out, nullptr,
                          send_pos, false, sig_counts, sig_rows, flags, stream);
+}
+
+vrResult_t vr_dispatch_noalloc(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes, const int32_t* topk,
+                               int T, int K, int E, vrWindow_t recv, size_t recv_off, size_t cap,
+                               int32_t* counts_out, int32_t* src_out, int32_t* send_pos, uint32_t sig_counts,
+                               uint32_t sig_rows, uint32_t flags, void* stream) {
+  return dispatch_common(c, x, x_off, row_bytes, topk, T, K, E, recv, recv_off, cap, counts_out, src_out, nullptr,
+                         send_pos, false, sig_counts, sig_rows, flags, stream, true);
 }
 
 vrResult_t vr_dispatch_dedup(vrComm_t c, vrWindow_t x, size_t x_off, size_t row_bytes, const int32_t* topk,

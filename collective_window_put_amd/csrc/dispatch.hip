@@ -623,7 +623,8 @@ size_t dispatch_scratch_bytes(int R, int T, int E, int Eo) { return scratch_layo
 vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t row_bytes, const int32_t* topk, int T,
                            int K, int E, const vrWindow* recv, size_t recv_off, size_t cap, int32_t* counts_out,
                            int32_t* src_out, int32_t* pos_out, int32_t* experts_out, bool dedup, uint32_t sig_counts,
-                           uint32_t sig_rows, const U64Tab& target_counts, bool wait, hipStream_t st) {
+                           uint32_t sig_rows, const U64Tab& target_counts, bool wait, char* scratch,
+                           hipStream_t st) {
   DispArgs a;
   const int R = c->nranks;
   // dedup: the layout's keys are the destination ranks (E = R, one per rank)
@@ -654,16 +655,16 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.NB1 = std::max(1, (T + kCountBlock - 1) / kCountBlock);
   a.NB2 = a.NB1 * kSubs;
   const Layout l = scratch_layout(R, T, E, dedup ? Eo : 0);
-  if (dedup) a.counts_out = reinterpret_cast<int32_t*>(c->scratch + l.rows);
-  a.eblk = reinterpret_cast<int32_t*>(c->scratch + l.eblk);
-  a.ecw = reinterpret_cast<int32_t*>(c->scratch + l.ecw);
+  if (dedup) a.counts_out = reinterpret_cast<int32_t*>(scratch + l.rows);
+  a.eblk = reinterpret_cast<int32_t*>(scratch + l.eblk);
+  a.ecw = reinterpret_cast<int32_t*>(scratch + l.ecw);
   int nbo = 1;
   while ((1 << nbo) < Eo) ++nbo;
   a.nbits_o = nbo;
-  a.subpfx = reinterpret_cast<int32_t*>(c->scratch + l.subpfx);
-  a.blktot = reinterpret_cast<int32_t*>(c->scratch + l.blktot);
-  a.cwin = reinterpret_cast<int32_t*>(c->scratch + l.cwin);
-  a.base_rows = reinterpret_cast<uint64_t*>(c->scratch + l.base_rows);
+  a.subpfx = reinterpret_cast<int32_t*>(scratch + l.subpfx);
+  a.blktot = reinterpret_cast<int32_t*>(scratch + l.blktot);
+  a.cwin = reinterpret_cast<int32_t*>(scratch + l.cwin);
+  a.base_rows = reinterpret_cast<uint64_t*>(scratch + l.base_rows);
   a.sig_counts = c->sig + sig_counts;
   a.sig_rows = c->sig + sig_rows;
   a.sig_stride = c->req.signal_count;

@@ -94,11 +94,13 @@ vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, co
 vrResult_t launch_allgather(vrComm* c, const vrWindow* send, size_t send_off, const vrWindow* recv,
                             size_t recv_off, size_t bytes, uint32_t sig, const U64Tab& target,
                             bool wait, hipStream_t st);
+// scratch: device memory of at least dispatch_scratch_bytes() bytes, 256-byte aligned
 vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t row_bytes,
                            const int32_t* topk, int T, int K, int E, const vrWindow* recv,
                            size_t recv_off, size_t cap, int32_t* counts_out, int32_t* src_out,
                            int32_t* pos_out, int32_t* experts_out, bool dedup, uint32_t sig_counts,
-                           uint32_t sig_rows, const U64Tab& target_counts, bool wait, hipStream_t st);
+                           uint32_t sig_rows, const U64Tab& target_counts, bool wait, char* scratch,
+                           hipStream_t st);
 // dedup: pos is [R][T][R] (a row per destination rank), weights are 1, topk unused
 vrResult_t launch_combine(vrComm* c, const vrWindow* y, size_t y_off, size_t cap, size_t row_bytes, int dtype,
                           const int32_t* topk, const float* weights, const int32_t* pos, int T, int K, int E,

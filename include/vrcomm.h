@@ -390,6 +390,29 @@ vrResult_t vr_dispatch(vrComm_t comm, vrWindow_t x, size_t x_off, size_t row_byt
                        int32_t* recv_src, int32_t* send_pos, uint32_t sig_counts, uint32_t sig_rows,
                        uint32_t flags, void* stream);
 
+/* vr_dispatch without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Arguments, results, signals and device checks are those of
+ * vr_dispatch. Its scratch (count rows, block prefixes) is not the
+ * communicator's growable buffer but a fixed array of
+ * VR_DISPATCH_NOALLOC_SCRATCH_BYTES in the library's code object, one copy per
+ * GPU, held until the process ends; the call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine). Every call on one GPU shares that
+ * GPU's array, whatever its communicator: calls whose executions overlap on
+ * one GPU (other streams, other communicators) race on it and must be
+ * stream-ordered; each call writes every scratch word it reads, so nothing
+ * needs clearing between calls. Limit: with NB = max(1, ceil(T / 256)), the
+ * scratch R*NB*E*16 + R*NB*E*4 + R*R*E*4 + R*8 + R*4 bytes (each term rounded
+ * up to a multiple of 256) must not exceed VR_DISPATCH_NOALLOC_SCRATCH_BYTES
+ * (R = 8, E = 256: up to 25,600 tokens per rank); larger shapes return
+ * VR_ERR_INVALID_ARGUMENT before anything is enqueued. */
+#define VR_DISPATCH_NOALLOC_SCRATCH_BYTES (4u << 20)
+vrResult_t vr_dispatch_noalloc(vrComm_t comm, vrWindow_t x, size_t x_off, size_t row_bytes,
+                               const int32_t* topk_idx, int T, int K, int num_experts, vrWindow_t recv,
+                               size_t recv_off, size_t recv_capacity_rows, int32_t* recv_expert_counts,
+                               int32_t* recv_src, int32_t* send_pos, uint32_t sig_counts, uint32_t sig_rows,
+                               uint32_t flags, void* stream);
+
 /* MoE dispatch in the per-rank (dedup) layout (reading: the GDA survey's
  * dispatch, sending each token once to every rank that owns at least one of
  * its experts instead of once per expert). Rank d's rows are ordered by
