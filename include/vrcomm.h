@@ -374,7 +374,10 @@ vrResult_t vr_allgather(vrComm_t comm, vrWindow_t send, size_t send_off, vrWindo
  *                   not routed or whose row fell past the capacity (the
  *                   metadata vr_combine uses to find the rows again)
  * Layout of rank d's rows: by expert, then source rank, then token (a stable
- * sort of the routing entries on (expert, source, token)).
+ * sort of the routing entries on (expert, source, token)). A token whose
+ * top-k names one expert more than once sends one row per entry, in k order
+ * (reading; the pages do not say), and the counts and the row signal count
+ * entries.
  * Method: (1) each rank counts its tokens per expert and puts its count row
  * to every rank with a SignalInc on sig_counts (each rises by R); (2) every
  * rank computes its offsets from the full count matrix; (3) each rank puts
