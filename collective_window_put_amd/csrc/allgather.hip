@@ -33,8 +33,43 @@ struct AGArgs {
   uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
+  uint64_t* lit;       // litmus words [2], or null
+  uint64_t* lit_last;  // [R]: tile that completed source s's relay
+  uint32_t lit_seed;
   int R;
 };
+
+// Receiver d, litmus on: the tile that completed each source's relay, whole,
+// then one seeded 16-byte sample in every tile of every source, each against
+// the source's send bytes.
+__device__ void ag_litmus(const AGArgs& a, uint32_t R, uint32_t d) {
+  const uint32_t tid = threadIdx.x;
+  uint32_t checks = 0, bad = 0;
+  auto check = [&](uint32_t s, uint64_t o, uint32_t n) {
+    ++checks;
+    bad += !equal_upto16(a.recv.p[d] + a.recv_off + (uint64_t)s * a.bytes + o, a.send.p[s] + a.send_off + o, n);
+  };
+  if (a.bytes) {
+    for (uint32_t s = 0; s < R; ++s) {
+      const uint64_t t0 = load_relaxed_u64(a.lit_last + s) * kTile;
+      if (t0 >= a.bytes) {
+        if (tid == 0) ++checks, ++bad;
+        continue;
+      }
+      const uint64_t n = std::min<uint64_t>(kTile, a.bytes - t0);
+      for (uint64_t o = (uint64_t)tid * 16; o < n; o += 256 * 16)
+        check(s, t0 + o, static_cast<uint32_t>(std::min<uint64_t>(16, n - o)));
+    }
+    for (uint32_t p = tid; p < R * a.tiles; p += 256) {
+      const uint32_t s = p % R;
+      const uint64_t t0 = (uint64_t)(p / R) * kTile;
+      const uint32_t n = static_cast<uint32_t>(std::min<uint64_t>(kTile, a.bytes - t0));
+      const uint32_t o = (mix32(a.lit_seed + p * 0x9E3779B9u) % n) & ~15u;
+      check(s, t0 + o, std::min(16u, n - o));
+    }
+  }
+  litmus_report(a.lit, a.err, checks, bad);
+}
 
 template <int RT, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_allgather(const AGArgs a) {
@@ -43,8 +78,12 @@ __global__ __launch_bounds__(256) void k_allgather(const AGArgs a) {
   const uint32_t b = blockIdx.x;
   if (b >= nwork) {
     const uint32_t d = b - nwork;
-    if (threadIdx.x == 0)
-      wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
+    if (!a.lit) {
+      if (threadIdx.x == 0)
+        wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
+    } else if (receiver_wait(a.sig + (size_t)d * a.sig_stride, a.target.v[d], a.timeout_ns, a.err)) {
+      ag_litmus(a, R, d);
+    }
     return;
   }
   const uint32_t s = b % R, tile = b / R;  // consecutive workgroups: different sources (even relay load)
@@ -68,8 +107,10 @@ __global__ __launch_bounds__(256) void k_allgather(const AGArgs a) {
     }
   }
   wg_stores_complete();
-  if (threadIdx.x == 0 && relay_arrive(a.relay + s * a.rstride, a.tiles, false))
+  if (threadIdx.x == 0 && relay_arrive(a.relay + s * a.rstride, a.tiles, false)) {
+    if (a.lit) litmus_record(a.lit_last + s, tile);
     for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
+  }
 }
 
 template <int RT, bool AL>
@@ -100,6 +141,9 @@ vrResult_t launch_allgather(vrComm* c, const vrWindow* send, size_t send_off, co
   a.rstride = relay_stride(R);
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
+  a.lit = c->litmus;
+  a.lit_last = c->lit_last;
+  a.lit_seed = c->lit_seed++;
   a.R = R;
   const bool aligned = ((send_off | recv_off | bytes) & 15) == 0;
   const uint32_t grid = a.tiles * R + (wait ? R : 0);

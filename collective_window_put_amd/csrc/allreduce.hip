@@ -43,6 +43,9 @@ struct ARArgs {
   uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
+  uint64_t* lit;       // litmus words [2], or null
+  uint64_t* lit_last;  // [R]: first element of the piece that completed chunk c's relay
+  uint32_t lit_seed;
   int R;
   int wait;
 };
@@ -178,7 +181,8 @@ __device__ inline bool relay_arrive_n(uint32_t* counter, uint32_t n, uint32_t pa
 // (arrivals from one XCD only), then the XCDs that hold part of chunk c (one
 // for R = 8); the workgroup that completes the chunk applies one SignalInc
 // at every rank.
-__device__ void chunk_done(const ARArgs& a, uint32_t R, uint32_t c, uint32_t x, uint32_t n, uint32_t per_tile) {
+__device__ void chunk_done(const ARArgs& a, uint32_t R, uint32_t c, uint32_t x, uint32_t n, uint32_t per_tile,
+                           uint64_t piece) {
   const uint32_t nwork = R * a.tpc;
   bool last;
   if ((nwork & 7u) == 0) {
@@ -190,8 +194,55 @@ __device__ void chunk_done(const ARArgs& a, uint32_t R, uint32_t c, uint32_t x, 
   } else {
     last = relay_arrive_n(a.relay + c * a.rstride, n, a.tpc * per_tile, false);
   }
-  if (last)
+  if (last) {
+    if (a.lit) litmus_record(a.lit_last + c, piece);
     for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
+  }
+}
+
+// Element k of rank d's receive slice equals the rank-order sum of element k
+// of every send slice, recomputed here (binary32 adds, then the element type).
+template <int DT>
+__device__ bool elem_ok(const ARArgs& a, uint32_t R, uint32_t d, uint64_t k) {
+  using E = Elem<DT>;
+  const uint64_t sb = a.send_off + k * E::kSize;
+  float acc = E::load1(a.send.p[0] + sb);
+  for (uint32_t r = 1; r < R; ++r) acc = acc + E::load1(a.send.p[r] + sb);
+  const char* got = a.recv.p[d] + a.recv_off + k * E::kSize;
+  if (DT == VR_DT_F32) return *reinterpret_cast<const uint32_t*>(got) == __float_as_uint(acc);
+  return *reinterpret_cast<const uint16_t*>(got) == static_cast<uint16_t>(bf16_rne(acc));
+}
+
+// Receiver d, litmus on: from the piece that completed each chunk's relay,
+// a whole tile's elements, then one seeded element in every tile.
+template <int DT>
+__device__ void ar_litmus(const ARArgs& a, uint32_t R, uint32_t d) {
+  constexpr uint64_t tile = 256ull * kU * Elem<DT>::kPerVec;
+  const uint32_t tid = threadIdx.x;
+  uint32_t checks = 0, bad = 0;
+  for (uint32_t c = 0; c < R; ++c) {
+    const uint64_t cbeg = (uint64_t)c * a.csz, cend = std::min<uint64_t>(a.count, cbeg + a.csz);
+    if (cbeg >= cend) continue;  // an empty chunk
+    const uint64_t p0 = load_relaxed_u64(a.lit_last + c);
+    if (p0 < cbeg || p0 >= cend) {
+      if (tid == 0) ++checks, ++bad;
+      continue;
+    }
+    for (uint64_t k = p0 + tid; k < std::min<uint64_t>(cend, p0 + tile); k += 256) {
+      ++checks;
+      bad += !elem_ok<DT>(a, R, d, k);
+    }
+  }
+  for (uint32_t w = tid; w < R * a.tpc; w += 256) {
+    const uint32_t c = w / a.tpc, j = w % a.tpc;
+    const uint64_t cend = std::min<uint64_t>(a.count, (uint64_t)c * a.csz + a.csz);
+    const uint64_t start = (uint64_t)c * a.csz + (uint64_t)j * tile;
+    const uint64_t end = std::min<uint64_t>(cend, start + tile);
+    if (start >= end) continue;
+    ++checks;
+    bad += !elem_ok<DT>(a, R, d, start + mix32(a.lit_seed + w * 0x9E3779B9u) % (end - start));
+  }
+  litmus_report(a.lit, a.err, checks, bad);
 }
 
 // Sum of one 256-vector slab in rank order, stored to every rank.
@@ -240,19 +291,21 @@ __device__ void persistent_tiles(const ARArgs& a, uint32_t b) {
   if (q >= S) return;
   uint32_t c = (x * S + q) / spc;
   uint32_t n = 0;  // slabs of chunk c finished by this workgroup
+  uint64_t piece = 0;  // first element of the last slab stored
   v4u v0[RT], v1[RT], v2[RT];  // slabs q, q + step, q + 2 step
   load_slab<DT, RT>(a, (uint64_t)(x * S + q) * slab, v0);
   if (q + step < S) load_slab<DT, RT>(a, (uint64_t)(x * S + q + step) * slab, v1);
   for (;;) {
     const uint32_t q2 = q + step, q3 = q2 + step;
     if (q3 < S) load_slab<DT, RT>(a, (uint64_t)(x * S + q3) * slab, v2);
-    sum_store_slab<DT, RT>(a, (uint64_t)(x * S + q) * slab, v0);
+    piece = (uint64_t)(x * S + q) * slab;
+    sum_store_slab<DT, RT>(a, piece, v0);
     ++n;
     if (q2 >= S) break;
     const uint32_t c2 = (x * S + q2) / spc;
     if (c2 != c) {  // next slab is in another chunk: close this one
       wg_stores_complete();
-      if (threadIdx.x == 0) chunk_done(a, RT, c, x, n, kU);
+      if (threadIdx.x == 0) chunk_done(a, RT, c, x, n, kU, piece);
       c = c2;
       n = 0;
     }
@@ -264,7 +317,7 @@ __device__ void persistent_tiles(const ARArgs& a, uint32_t b) {
     q = q2;
   }
   wg_stores_complete();
-  if (threadIdx.x == 0) chunk_done(a, RT, c, x, n, kU);
+  if (threadIdx.x == 0) chunk_done(a, RT, c, x, n, kU, piece);
 }
 
 template <int DT, int RT, bool ALIGNED, bool LOOP>
@@ -274,8 +327,12 @@ __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
   const uint32_t b = blockIdx.x;
   if (b >= a.nwg) {  // receiver d waits for one SignalInc per owner
     const uint32_t d = b - a.nwg;
-    if (threadIdx.x == 0)
-      wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
+    if (!a.lit) {
+      if (threadIdx.x == 0)
+        wait_reached(a.sig + (size_t)d * a.sig_stride, a.target.v[d], 64, a.timeout_ns, a.err, VR_ASYNC_TIMEOUT);
+    } else if (receiver_wait(a.sig + (size_t)d * a.sig_stride, a.target.v[d], a.timeout_ns, a.err)) {
+      ar_litmus<DT>(a, R, d);
+    }
     return;
   }
   if constexpr (LOOP) {
@@ -296,7 +353,7 @@ __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
   const uint64_t end = std::min<uint64_t>(cend, start + tile);
   if (start < end) reduce_tile<DT, RT, ALIGNED>(a, start, end);
   wg_stores_complete();
-  if (threadIdx.x == 0) chunk_done(a, R, c, b & 7u, 1, 1);
+  if (threadIdx.x == 0) chunk_done(a, R, c, b & 7u, 1, 1, start);
 }
 
 template <int DT, int RT, bool AL, bool LOOP>
@@ -351,6 +408,9 @@ vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, co
   a.rstride = relay_stride(9 * R);
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
+  a.lit = c->litmus;
+  a.lit_last = c->lit_last;
+  a.lit_seed = c->lit_seed++;
   a.R = R;
   a.wait = wait;
   // looping form: every tile full (count = R * csz), aligned, a rank count

@@ -68,7 +68,7 @@ bool valid_req(int nranks, const vrCommRequirements* req) {
 }
 
 struct Layout {
-  size_t sig, cnt, err, relay, bar, total;
+  size_t sig, cnt, err, relay, bar, lit, total;
 };
 Layout layout(int R, const vrCommRequirements& q) {
   Layout l;
@@ -77,7 +77,8 @@ Layout layout(int R, const vrCommRequirements& q) {
   l.err = align_up(l.cnt + sizeof(uint64_t) * R * std::max<uint32_t>(q.counter_count, 1), 256);
   l.relay = align_up(l.err + 256, 256);
   l.bar = align_up(l.relay + sizeof(uint32_t) * kRelaySlots, 256);
-  l.total = align_up(l.bar + sizeof(uint64_t) * std::max<uint32_t>(q.barrier_count, 1), 256);
+  l.lit = align_up(l.bar + sizeof(uint64_t) * std::max<uint32_t>(q.barrier_count, 1), 256);
+  l.total = align_up(l.lit + sizeof(uint64_t) * R * R, 256);
   return l;
 }
 
@@ -445,6 +446,9 @@ vrResult_t vr_comm_create(int nranks, const vrCommRequirements* req, void* works
   c->err = reinterpret_cast<uint32_t*>(c->ws + l.err);
   c->relay = reinterpret_cast<uint32_t*>(c->ws + l.relay);
   c->bar = reinterpret_cast<uint64_t*>(c->ws + l.bar);
+  c->lit_last = reinterpret_cast<uint64_t*>(c->ws + l.lit);
+  c->litmus = nullptr;
+  c->lit_seed = 0;
   c->bar_expect.assign(req->barrier_count, 0);
   c->scratch = nullptr;
   c->scratch_bytes = 0;
@@ -486,6 +490,13 @@ vrResult_t vr_comm_get_async_error(vrComm_t c, vrResult_t* out, uint32_t* bits) 
   else if (b & VR_ASYNC_CAPACITY) *out = VR_ERR_OUT_OF_RESOURCES;
   else if (b) *out = VR_ERR_DEVICE_CHECK;
   else *out = VR_OK;
+  return VR_OK;
+}
+
+vrResult_t vr_comm_set_litmus(vrComm_t c, uint64_t* litmus) {
+  if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
+  if (litmus && !dev_span_ok(c, litmus, 2 * sizeof(uint64_t))) return VR_ERR_INVALID_ARGUMENT;
+  c->litmus = litmus;
   return VR_OK;
 }
 

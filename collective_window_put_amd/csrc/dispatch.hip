@@ -85,6 +85,9 @@ struct DispArgs {
   uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
+  uint64_t* lit;         // litmus words [2], or null
+  uint64_t* lit_last;    // [R][R]: a row the block completing source s's relay sent to d (~0: none)
+  uint32_t lit_seed;
   char* span_base;       // lowest receive address, when the span path is on
   uint32_t span_bytes;
   uint32_t dspan[VR_MAX_RANKS];  // recv.p[d] + recv_off - span_base
@@ -554,8 +557,58 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     const int d = tid;
     uint64_t rows = 0;
     for (int e = d * epr; e < (d + 1) * epr; ++e) rows += crow[e];
+    if (a.lit) {  // the last receive row this block wrote at d, for the receiver's litmus
+      uint64_t last = ~0ull;
+      for (int slot = 0; slot < kSub * K; ++slot) {
+        if (b2 * kSub + slot / K >= a.T || dexp[slot] < 0 || dexp[slot] / epr != d) continue;
+        const int32_t pos = dpos[slot];
+        if (pos >= 0 && (uint64_t)pos < a.cap && (last == ~0ull || (uint64_t)pos > last)) last = (uint64_t)pos;
+      }
+      litmus_record(a.lit_last + (size_t)s * R + d, last);
+    }
     if (rows) atomic_add_u64(a.sig_rows + (size_t)d * a.sig_stride, rows);
   }
+}
+
+// Receiver d, litmus on, after its row signal has reached its target: the
+// row each source's completing block wrote last at d, whole, then one
+// seeded 16-byte sample of every received row, each against the token row
+// its source tag names (and the tag itself checked).
+__device__ void dispatch_litmus(const DispArgs& a, int d, int32_t rows) {
+  const int R = a.R, tid = threadIdx.x;
+  const uint64_t rb = a.row_bytes;
+  const uint64_t n = std::min<uint64_t>(static_cast<uint64_t>(rows), a.cap);
+  const char* rbase = a.recv.p[d] + a.recv_off;
+  const int32_t* tags = a.src_out + (size_t)d * a.cap;
+  uint32_t checks = 0, bad = 0;
+  for (int s = 0; s < R; ++s) {
+    const uint64_t i = load_relaxed_u64(a.lit_last + (size_t)s * R + d);
+    if (i == ~0ull) continue;  // source s's completing block sent nothing to d
+    const int32_t tag = i < n ? tags[i] : -1;
+    const int ts = tag >> 16, tt = tag & 0xFFFF;
+    if (i >= n || ts != s || tt >= a.T) {
+      if (tid == 0) ++checks, ++bad;
+      continue;
+    }
+    for (uint64_t o = (uint64_t)tid * 16; o < rb; o += kThreads * 16) {
+      ++checks;
+      bad += !equal_upto16(rbase + i * rb + o, a.x.p[ts] + a.x_off + (uint64_t)tt * rb + o,
+                           static_cast<uint32_t>(std::min<uint64_t>(16, rb - o)));
+    }
+  }
+  for (uint64_t i = tid; i < n; i += kThreads) {
+    const int32_t tag = tags[i];
+    const int ts = tag >> 16, tt = tag & 0xFFFF;
+    ++checks;
+    if (ts < 0 || ts >= R || tt >= a.T) {
+      ++bad;
+      continue;
+    }
+    const uint32_t o = (mix32(a.lit_seed + static_cast<uint32_t>(i) * 0x9E3779B9u) % static_cast<uint32_t>(rb)) & ~15u;
+    bad += !equal_upto16(rbase + i * rb + o, a.x.p[ts] + a.x_off + (uint64_t)tt * rb + o,
+                         std::min(16u, static_cast<uint32_t>(rb) - o));
+  }
+  litmus_report(a.lit, a.err, checks, bad);
 }
 
 // Receiver d: waits for the count exchange (which fixes how many rows are
@@ -578,10 +631,16 @@ __device__ void receiver_block(const DispArgs& a, int32_t* lds, int d) {
     if (tid < w) lds[tid] += lds[tid + w];
     __syncthreads();
   }
-  if (tid == 0) {
-    const uint64_t base = load_relaxed_u64(a.base_rows + d);
-    wait_reached(a.sig_rows + (size_t)d * a.sig_stride, base + static_cast<uint64_t>(lds[0]), 64, a.timeout_ns,
-                 a.err, VR_ASYNC_TIMEOUT);
+  const int32_t rows = lds[0];
+  if (!a.lit) {
+    if (tid == 0) {
+      const uint64_t base = load_relaxed_u64(a.base_rows + d);
+      wait_reached(a.sig_rows + (size_t)d * a.sig_stride, base + static_cast<uint64_t>(rows), 64, a.timeout_ns,
+                   a.err, VR_ASYNC_TIMEOUT);
+    }
+  } else if (receiver_wait(a.sig_rows + (size_t)d * a.sig_stride,
+                           load_relaxed_u64(a.base_rows + d) + static_cast<uint64_t>(rows), a.timeout_ns, a.err)) {
+    dispatch_litmus(a, d, rows);
   }
 }
 
@@ -674,6 +733,9 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.rstride = relay_stride(19 * R + 2, kRelayDispatchWords);
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
+  a.lit = c->litmus;
+  a.lit_last = c->lit_last;
+  a.lit_seed = c->lit_seed++;
   a.R = R;
   a.T = T;
   a.K = K;

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "vrcomm.h"  // VR_ASYNC_* bits
+
 namespace vr {
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -216,6 +218,72 @@ __device__ inline uint32_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
   return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+// ---- strong-signal litmus of the collectives' receivers ---------------------------
+// GIN page, strong and weak signals: a signal seen at the peer means the
+// payload of every earlier put of the context to that peer is visible there.
+// With a communicator's litmus on, the workgroup that completes a relay
+// records the piece it stored last (a tile, a slab, a row) before applying
+// the signal; each receiver, once its wait has ended and it has acquired,
+// checks those pieces in full first, then one seeded sample in every piece
+// aimed at it. A signal applied before its pieces were visible would show up
+// as a mismatch.
+
+__device__ inline uint32_t mix32(uint32_t x) {  // an integer hash (xorshift-multiply rounds)
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// The n <= 16 bytes at `got` equal those at `want`.
+__device__ inline bool equal_upto16(const char* got, const char* want, uint32_t n) {
+  if (n == 16 && ((reinterpret_cast<uintptr_t>(got) | reinterpret_cast<uintptr_t>(want)) & 15) == 0) {
+    const v4u x = *reinterpret_cast<const v4u*>(got), y = *reinterpret_cast<const v4u*>(want);
+    return x[0] == y[0] && x[1] == y[1] && x[2] == y[2] && x[3] == y[3];
+  }
+  bool eq = true;
+  for (uint32_t i = 0; i < n; ++i) eq &= got[i] == want[i];
+  return eq;
+}
+
+// From the thread that completed a relay: record the piece it stored last;
+// the record has landed before the signal the caller applies next.
+__device__ inline void litmus_record(uint64_t* slot, uint64_t piece) {
+  store8_agent(slot, piece);
+  wait_vmem();
+}
+
+// Adds the workgroup's counts to words[0] (checks) and words[1] (mismatches);
+// a mismatch also sets VR_ASYNC_LITMUS. Every thread of the workgroup calls it.
+__device__ inline void litmus_report(uint64_t* words, uint32_t* err, uint32_t checks, uint32_t bad) {
+  __shared__ uint32_t tot[2];
+  if (threadIdx.x == 0) tot[0] = tot[1] = 0;
+  __syncthreads();
+  if (checks) atomicAdd(&tot[0], checks);
+  if (bad) atomicAdd(&tot[1], bad);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomic_add_u64(words, tot[0]);
+    if (tot[1]) {
+      atomic_add_u64(words + 1, tot[1]);
+      atomic_or_u32(err, VR_ASYNC_LITMUS);
+    }
+  }
+}
+
+// A receiver's wait, then (litmus on) an acquire by every thread: true when
+// the wait ended before its timeout. Every thread of the workgroup calls it.
+__device__ inline bool receiver_wait(const uint64_t* word, uint64_t least, uint64_t timeout_ns, uint32_t* err) {
+  __shared__ int ok;
+  if (threadIdx.x == 0) ok = wait_reached(word, least, 64, timeout_ns, err, VR_ASYNC_TIMEOUT);
+  __syncthreads();
+  if (!ok) return false;
+  acquire_agent();
+  return true;
 }
 
 // ---- wave helpers -------------------------------------------------------------------

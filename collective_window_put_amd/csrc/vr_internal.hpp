@@ -68,6 +68,9 @@ struct vrComm {
   uint32_t* err;    // error bits
   uint32_t* relay;  // [kRelaySlots]
   uint64_t* bar;    // [barrier_count] barrier-session slots
+  uint64_t* lit_last;  // [R][R] litmus records: the piece that completed each relay
+  uint64_t* litmus;    // caller's litmus words [2] (checks, mismatches), or null: litmus off
+  uint32_t lit_seed;   // per-launch seed of the litmus samples
   // growable scratch for dispatch (histograms, count exchange)
   char* scratch;
   size_t scratch_bytes;

@@ -202,6 +202,25 @@ vrResult_t vr_comm_destroy(vrComm_t comm);
 #define VR_ASYNC_LITMUS        0x8u
 vrResult_t vr_comm_get_async_error(vrComm_t comm, vrResult_t* out, uint32_t* bits);
 
+/* Strong-signal litmus for the collectives (GIN page, strong and weak
+ * signals: a signal seen at the peer means every earlier put of the context to
+ * that peer is visible there). litmus: device uint64[2] or NULL (off, the
+ * default). While it is set, the receivers of later vr_allreduce,
+ * vr_alltoall, vr_allgather (compute-unit paths), vr_dispatch,
+ * vr_dispatch_noalloc and vr_dispatch_dedup calls on the communicator check,
+ * inside the kernel, right after their wait on the completion signal has ended
+ * and they have acquired, that what the signal announced is visible: first,
+ * whole, the piece (tile, slab or row) that the workgroup completing each
+ * relay stored last, which it records before applying the signal; then one
+ * seeded sample in every tile (every received row for the dispatch), each
+ * against the senders' windows (for the AllReduce, the rank-order sum
+ * recomputed from the send windows; for the dispatch, the token row named by
+ * the row's source tag). litmus[0] counts the checks and litmus[1] the
+ * mismatches; a mismatch also sets VR_ASYNC_LITMUS. The checks lengthen the
+ * receivers' part of the kernel; calls with VR_COLL_NO_WAIT have no receivers
+ * and check nothing. */
+vrResult_t vr_comm_set_litmus(vrComm_t comm, uint64_t* litmus);
+
 /* Rank count and requirements of a communicator. */
 vrResult_t vr_comm_query(vrComm_t comm, int* nranks, vrCommRequirements* req);
 
