@@ -202,6 +202,9 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
     b.torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [e0.elapsed_time(e1) / steps]
+    # the same step timed cold as well: 20 repetitions, each after a 1 GiB
+    # read that evicts the caches, events around each (untimed by the headline)
+    flushed = b.timed(step, 20, flush=True)
     code, bits = vr.vr_comm_get_async_error(comm)
     if code != vr.VR_OK:
         raise RuntimeError(f"device error during the AllReduce: {vr.vr_error_string(code)} bits={bits:#x}")
@@ -222,7 +225,98 @@ def run_allreduce_headline(b: Bench, steps: int, warmup: int):
     vr.vr_window_deregister(comm, rw)
     vr.vr_comm_destroy(comm)
     del s_slab, r_slab
-    return dict(xs=xs, R=R, N=N, bytes_alg=bytes_alg, ms_per_step=ms_per_step, kern_ms=kern_ms)
+    return dict(xs=xs, R=R, N=N, bytes_alg=bytes_alg, ms_per_step=ms_per_step, kern_ms=kern_ms,
+                flushed_ms=[float(t) for t in flushed])
+
+
+# ---- the dispatch's phase timeline -----------------------------------------------------------------
+PHASES = {"count": ["start", "histograms stored", "count row published (last block of a source)"],
+          "put": ["start", "entries ranked, token-row loads issued", "count signal seen",
+                  "count rows loaded, offsets computed", "source tags stored", "row stores issued",
+                  "row stores complete", "row signals applied (last block of a source)"],
+          "receiver": ["start", "count signal seen", "row signal seen"]}
+
+
+def dispatch_phases(b: Bench, reps: int, dedup: bool = False) -> str:
+    """Markdown timeline of the dispatch workload (8 ranks x 4096 tokens of
+    512 B, top-8 of 256 Zipf(1.1) experts): every workgroup's phase
+    timestamps (vr_comm_set_trace, device real-time clock) over `reps`
+    launches, each after a 1 GiB read flush; times are from the first
+    workgroup's start in the same launch. Per phase: the median over launches
+    of the median, the earliest and the latest workgroup."""
+    import workloads as W
+    vr, stream, torch = b.vr, b.stream.cuda_stream, b.torch
+    c = W.CONFIGS["dispatch_r8_t4096_e256_k8"]
+    R, T, H, E, K = c["ranks"], c["tokens"], c["hidden"], c["experts"], c["topk"]
+    topk, x = W.dispatch_inputs(R, T, H, E, K, c["zipf_s"], seed=c["seed"])
+    rb = H * 2
+    cap = R * T * (1 if dedup else min(K, E // R))
+    comm = comm_for(vr, R, signal_count=4)
+    s1, xv = b.slices(R, T * rb, arrays=[x[r] for r in range(R)])
+    r1, rv = b.slices(R, cap * rb, fill=0)
+    xw = vr.vr_window_register(comm, [v.data_ptr() for v in xv], T * rb)
+    rw = vr.vr_window_register(comm, [v.data_ptr() for v in rv], cap * rb)
+    tk = torch.from_numpy(topk).cuda()
+    counts = torch.zeros(R, E // R, dtype=torch.int32, device="cuda")
+    src = torch.zeros(R, cap, dtype=torch.int32, device="cuda")
+    ex = torch.zeros(R, cap, K, dtype=torch.int32, device="cuda")
+    nb1 = (T + 255) // 256
+    ncount, nput = R * nb1, R * 4 * nb1
+    grid = ncount + nput + R
+    stamps = torch.zeros(grid * 8, dtype=torch.int64, device="cuda")
+
+    def f():
+        if dedup:
+            vr.vr_dispatch_dedup(comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, ex, None, 0, 1, stream=stream)
+        else:
+            vr.vr_dispatch(comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, None, 0, 1, stream=stream)
+
+    b.warm(f)
+    vr.vr_comm_set_trace(comm, stamps)
+    per = {k: [[] for _ in v] for k, v in PHASES.items()}
+    events = []
+    for _ in range(reps):
+        stamps.zero_()
+        b.flush_cache()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(b.stream)
+        f()
+        e1.record(b.stream)
+        e1.synchronize()
+        events.append(e0.elapsed_time(e1))
+        st = stamps.view(grid, 8).cpu().numpy().astype(np.int64)
+        t0 = st[:, 0][st[:, 0] > 0].min()
+        kinds = {"count": st[:ncount], "put": st[ncount:ncount + nput], "receiver": st[ncount + nput:]}
+        for k, arr in kinds.items():
+            for ph in range(len(PHASES[k])):
+                col = arr[:, ph]
+                col = (col[col > 0] - t0) / 1e3  # us
+                if col.size:
+                    per[k][ph].append((np.median(col), col.min(), col.max(), col.size))
+    vr.vr_comm_set_trace(comm, None)
+    code, bits = vr.vr_comm_get_async_error(comm)
+    if code != vr.VR_OK:
+        raise RuntimeError(f"device error during the traced dispatch: {vr.vr_error_string(code)} bits={bits:#x}")
+    vr.vr_window_deregister(comm, xw)
+    vr.vr_window_deregister(comm, rw)
+    vr.vr_comm_destroy(comm)
+    lines = [f"{'Per-rank (dedup) dispatch' if dedup else 'Dispatch'}: R={R}, T={T}, {rb} B rows, E={E}, K={K}, "
+             f"{reps} launches, each after a 1 GiB read flush; event time per launch (median) "
+             f"{np.median(events) * 1e3:.1f} us", "",
+             "| Workgroups | Phase | median WG (us) | first WG (us) | last WG (us) | WGs |",
+             "|---|---|---|---|---|---|"]
+    for k, names in PHASES.items():
+        for ph, name in enumerate(names):
+            v = per[k][ph]
+            if not v:
+                continue
+            med = np.median([q[0] for q in v])
+            lo = np.median([q[1] for q in v])
+            hi = np.median([q[2] for q in v])
+            n = int(np.median([q[3] for q in v]))
+            lines.append(f"| {k} | {ph} {name} | {med:.2f} | {lo:.2f} | {hi:.2f} | {n} |")
+    return "\n".join(lines)
 
 
 # ---- the other workloads ------------------------------------------------------------------------
@@ -752,6 +846,8 @@ def main():
     ap.add_argument("--rows", default=",".join(ROW_NAMES), help="comma-separated subset of " + ",".join(ROW_NAMES))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--reps", type=int, default=20, help="repetitions per other workload")
+    ap.add_argument("--dispatch-phases", action="store_true",
+                    help="print the dispatch's phase timeline (markdown) instead of the JSON line")
     ap.add_argument("--calib", action="store_true",
                     help="first run a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
@@ -760,10 +856,16 @@ def main():
               "are not supported", file=sys.stderr)
         sys.exit(2)
     b = Bench()
+    if args.dispatch_phases:
+        print(dispatch_phases(b, args.reps))
+        print()
+        print(dispatch_phases(b, args.reps, dedup=True))
+        return
     if args.calib:
         calib_copy(b)
     head = run_allreduce_headline(b, args.steps, args.warmup)
     kern = float(np.mean(head["kern_ms"]))
+    fl_med = float(np.median(head["flushed_ms"]))
     achieved = head["bytes_alg"] / (kern * 1e-3) / 1e9
     value = head["bytes_alg"] / (head["ms_per_step"] * 1e-3) / 1e9
     workload = "allreduce_bf16_r8_64Mi"
@@ -777,7 +879,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("k_allreduce", workload), "kernel": "k_allreduce",
-                     "kernel_ms_mean": round(kern, 5)},
+                     "kernel_ms_mean": round(kern, 5),
+                     # cold figure: median of 20 launches, each after a 1 GiB read flush (events
+                     # around each launch, so the launch latency is included)
+                     "kernel_ms_median_flushed": round(fl_med, 5), "reps_flushed": len(head["flushed_ms"]),
+                     "frac_flushed": round(head["bytes_alg"] / (fl_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_rows:
         out["rows"] = run_rows(b, args.reps, tuple(args.rows.split(",")))

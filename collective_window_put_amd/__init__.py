@@ -30,7 +30,7 @@ __all__ = [
     "vr_put", "vr_get", "vr_signal", "vr_signal_wait", "vr_signal_read", "vr_signal_reset",
     "vr_signal_expected", "vr_counter_wait", "vr_counter_read", "vr_counter_reset",
     "vr_allreduce", "vr_alltoall", "vr_allgather", "vr_dispatch", "vr_combine", "vr_ring_exchange",
-    "vr_signal_pingpong", "vr_dispatch_noalloc", "vr_comm_set_litmus", "VR_DISPATCH_NOALLOC_SCRATCH_BYTES",
+    "vr_signal_pingpong", "vr_dispatch_noalloc", "vr_comm_set_litmus", "vr_comm_set_trace", "VR_DISPATCH_NOALLOC_SCRATCH_BYTES",
 ]
 
 # The in-tree build; VRCOMM_LIB may name another build of the same library.
@@ -133,6 +133,7 @@ SYMBOLS = {
     "vr_comm_get_async_error": (_R, [_P, POINTER(c_int), POINTER(c_uint32)]),
     "vr_comm_query": (_R, [_P, POINTER(c_int), POINTER(vrCommRequirements)]),
     "vr_comm_set_litmus": (_R, [_P, _P]),
+    "vr_comm_set_trace": (_R, [_P, _P, c_size_t]),
     "vr_window_register": (_R, [_P, POINTER(_P), c_size_t, c_uint32, POINTER(_P)]),
     "vr_window_deregister": (_R, [_P, _P]),
     "vr_put": (_R, [_P, c_int, c_int, c_int, _P, c_size_t, _P, c_size_t, c_size_t, vrRemoteAction,
@@ -402,6 +403,13 @@ def vr_comm_set_litmus(comm, litmus=None):
     """Turn the collectives' in-kernel strong-signal litmus on (litmus: a device
     uint64 tensor of 2 words: checks, mismatches) or off (None)."""
     _check(lib().vr_comm_set_litmus(comm, _ptr(litmus) or None), "vr_comm_set_litmus")
+
+
+def vr_comm_set_trace(comm, stamps=None):
+    """Record the dispatch's per-workgroup phase timestamps into `stamps` (a
+    device uint64/int64 tensor; 8 words per workgroup), or stop (None)."""
+    _check(lib().vr_comm_set_trace(comm, _ptr(stamps) or None, 0 if stamps is None else stamps.numel()),
+           "vr_comm_set_trace")
 
 
 def vr_dispatch_noalloc(comm, x, x_off, row_bytes, topk_idx, T, K, num_experts, recv, recv_off, capacity_rows,

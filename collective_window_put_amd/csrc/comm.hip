@@ -449,6 +449,8 @@ vrResult_t vr_comm_create(int nranks, const vrCommRequirements* req, void* works
   c->lit_last = reinterpret_cast<uint64_t*>(c->ws + l.lit);
   c->litmus = nullptr;
   c->lit_seed = 0;
+  c->trace = nullptr;
+  c->trace_words = 0;
   c->bar_expect.assign(req->barrier_count, 0);
   c->scratch = nullptr;
   c->scratch_bytes = 0;
@@ -497,6 +499,14 @@ vrResult_t vr_comm_set_litmus(vrComm_t c, uint64_t* litmus) {
   if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
   if (litmus && !dev_span_ok(c, litmus, 2 * sizeof(uint64_t))) return VR_ERR_INVALID_ARGUMENT;
   c->litmus = litmus;
+  return VR_OK;
+}
+
+vrResult_t vr_comm_set_trace(vrComm_t c, uint64_t* stamps, size_t words) {
+  if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
+  if (stamps && (!words || !dev_span_ok(c, stamps, words * sizeof(uint64_t)))) return VR_ERR_INVALID_ARGUMENT;
+  c->trace = stamps;
+  c->trace_words = stamps ? words : 0;
   return VR_OK;
 }
 

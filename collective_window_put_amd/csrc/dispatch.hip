@@ -85,6 +85,8 @@ struct DispArgs {
   uint32_t rstride;
   uint32_t* err;
   uint64_t timeout_ns;
+  uint64_t* trace;       // phase timestamps [grid][kTracePhases] (ns), or null
+  uint64_t trace_n;      // words of trace
   uint64_t* lit;         // litmus words [2], or null
   uint64_t* lit_last;    // [R][R]: a row the block completing source s's relay sent to d (~0: none)
   uint32_t lit_seed;
@@ -93,7 +95,18 @@ struct DispArgs {
   uint32_t dspan[VR_MAX_RANKS];  // recv.p[d] + recv_off - span_base
   int R, T, K, E, NB1, NB2, nbits;
   int mode;              // 2: 16-byte lanes via the span; 1: 8-byte lanes; 0: bytes
+  int rowbuf;            // count rows loaded with 16-byte lanes through LDS
 };
+
+// Phase timestamps of this workgroup, for the timeline a traced call records:
+// word blockIdx.x * kTracePhases + phase receives the real-time clock in ns.
+constexpr int kTracePhases = 8;
+__device__ inline void stamp(const DispArgs& a, int phase) {
+  if (a.trace && threadIdx.x == 0) {
+    const uint64_t i = (uint64_t)blockIdx.x * kTracePhases + phase;
+    if (i < a.trace_n) a.trace[i] = now_ns();
+  }
+}
 
 __device__ inline int32_t load_topk(const DispArgs& a, int s, int t, int k) {
   return a.topk[((size_t)s * a.T + t) * a.K + k];
@@ -214,6 +227,7 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
   const int s = wg % R, blk = wg / R;  // interleaved: sources' relays hit in parallel
   const int tid = threadIdx.x;
   int32_t* hist = lds;  // [kSubs][E]
+  stamp(a, 0);
   for (int i = tid; i < kSubs * E; i += kThreads) hist[i] = 0;
   if (blk == 0 && tid == 0)
     store8_agent(a.base_rows + s, load_relaxed_u64(a.sig_rows + (size_t)s * a.sig_stride));
@@ -259,9 +273,13 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
     store4_agent(reinterpret_cast<uint32_t*>(a.blktot + ((size_t)s * a.NB1 + blk) * E + e), run);
   }
   wg_stores_complete();
+  stamp(a, 1);
   if (tid == 0) *last_flag = relay_arrive(a.relay + s * a.rstride, a.NB1, false);
   __syncthreads();
-  if (*last_flag) count_exchange(a, s);
+  if (*last_flag) {
+    count_exchange(a, s);
+    stamp(a, 2);
+  }
   if (DEDUP) expert_counts(a, lds, last_flag, s, blk);
 }
 
@@ -322,6 +340,7 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
   int32_t* dorig = crow + E;  // dedup: [kSub*K] each entry's expert id
   const int s = wg % R, b2 = wg / R;  // interleaved sources
   const int b1 = b2 / kSubs;
+  stamp(a, 0);
   const int tpr = 64 / K;  // tokens per ballot round
   const int tw0 = b2 * kSub + wave * kTokPerWave;
   const int rounds = (kTokPerWave + tpr - 1) / tpr;
@@ -400,14 +419,44 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
   }
   // count exchange: rank s waits until every source's count row has arrived;
   // the rows and prefixes are then read with agent-coherent loads.
+  stamp(a, 1);
   if (tid == 0)
     wait_reached(a.sig_counts + (size_t)s * a.sig_stride, a.target_counts.v[s], 64, a.timeout_ns, a.err,
                  VR_ASYNC_TIMEOUT, false);
+  stamp(a, 2);
   __syncthreads();
   compiler_fence();
   const int32_t* cw = a.cwin + (size_t)s * R * E;  // rank s's copy: cw[s'][e]
   const int32_t* pb = a.blktot + ((size_t)s * a.NB1 + b1) * E;  // rows of source s's earlier count blocks
   const int32_t* ps = a.subpfx + ((size_t)s * a.NB1 * kSubs + b2) * E;
+  if (a.rowbuf) {
+    // the R count rows and the two prefix rows, 16-byte agent-coherent loads
+    // (one or two per thread, all in flight together), staged in LDS
+    int32_t* rb4 = dorig + (DEDUP ? kSub * K : 0);  // [(R + 2)][E]
+    const int n4 = E >> 2;
+    const __amdgpu_buffer_rsrc_t rcw = rsrc(cw, (uint32_t)(R * E * 4));
+    const __amdgpu_buffer_rsrc_t rps = rsrc(ps, (uint32_t)(E * 4)), rpb = rsrc(pb, (uint32_t)(E * 4));
+    for (int i = tid; i < (R + 2) * n4; i += kThreads) {
+      const int q = i / n4, e4 = i - q * n4;
+      const v4u v = q < R ? __builtin_amdgcn_raw_buffer_load_b128(rcw, (uint32_t)(i * 16), 0, kStoreAgent)
+                          : __builtin_amdgcn_raw_buffer_load_b128(q == R ? rps : rpb, (uint32_t)(e4 * 16), 0,
+                                                                  kStoreAgent);
+      *reinterpret_cast<v4u*>(rb4 + i * 4) = v;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kThreads) {
+      int32_t t = 0, pre = 0, own = 0;
+      for (int j = 0; j < R; ++j) {
+        const int32_t x = rb4[j * E + e];
+        t += x;
+        if (j < s) pre += x;
+        if (j == s) own = x;
+      }
+      tot[e] = t;
+      crow[e] = own;
+      base[e] = pre + rb4[R * E + e] + rb4[(R + 1) * E + e];
+    }
+  } else
   for (int e = tid; e < E; e += kThreads) {
     // count rows of every source, the prefix over this source's earlier count
     // blocks and over the earlier sub-blocks of this one: independent loads
@@ -433,6 +482,7 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     base[e] = pre + before;
   }
   __syncthreads();
+  stamp(a, 3);
   // seg[e]: rows of the experts before e on the same rank. When the rank's
   // experts tile the waves (epr a power of two up to 64), a shuffle scan
   // within each group of epr lanes; otherwise a loop over LDS.
@@ -507,6 +557,7 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
         if (dexp[tlb * K + k] == d) pos = dpos[tlb * K + k];
       a.pos_out[((size_t)s * a.T + b2 * kSub) * R + i] = (uint64_t)pos < a.cap ? pos : -1;
     }
+  stamp(a, 4);
   // copy: the wave's 8 token rows, each once per routed expert
   if (a.mode == 2) {
     const __amdgpu_buffer_rsrc_t rd = rsrc(a.span_base, a.span_bytes);
@@ -542,8 +593,10 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
       }
     }
   }
+  stamp(a, 5);
   if (DEDUP && b2 == 0) put_expert_counts(a, s);
   wg_stores_complete();
+  stamp(a, 6);
   if (tid == 0) {
     // two-level relay: 16 first-level counters per source, then one per source
     const int g = b2 % kRelayFan;
@@ -568,6 +621,7 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     }
     if (rows) atomic_add_u64(a.sig_rows + (size_t)d * a.sig_stride, rows);
   }
+  if (*last_flag) stamp(a, 7);
 }
 
 // Receiver d, litmus on, after its row signal has reached its target: the
@@ -617,9 +671,11 @@ __device__ void dispatch_litmus(const DispArgs& a, int d, int32_t rows) {
 __device__ void receiver_block(const DispArgs& a, int32_t* lds, int d) {
   const int R = a.R, E = a.E, epr = a.E / a.R;
   const int tid = threadIdx.x;
+  stamp(a, 0);
   if (tid == 0)
     wait_reached(a.sig_counts + (size_t)d * a.sig_stride, a.target_counts.v[d], 64, a.timeout_ns, a.err,
                  VR_ASYNC_TIMEOUT, false);
+  stamp(a, 1);
   __syncthreads();
   compiler_fence();
   int32_t part = 0;
@@ -638,6 +694,7 @@ __device__ void receiver_block(const DispArgs& a, int32_t* lds, int d) {
       wait_reached(a.sig_rows + (size_t)d * a.sig_stride, base + static_cast<uint64_t>(rows), 64, a.timeout_ns,
                    a.err, VR_ASYNC_TIMEOUT);
     }
+    stamp(a, 2);
   } else if (receiver_wait(a.sig_rows + (size_t)d * a.sig_stride,
                            load_relaxed_u64(a.base_rows + d) + static_cast<uint64_t>(rows), a.timeout_ns, a.err)) {
     dispatch_litmus(a, d, rows);
@@ -736,6 +793,8 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   a.lit = c->litmus;
   a.lit_last = c->lit_last;
   a.lit_seed = c->lit_seed++;
+  a.trace = c->trace;
+  a.trace_n = c->trace_words;
   a.R = R;
   a.T = T;
   a.K = K;
@@ -760,9 +819,12 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   } else {
     a.mode = (row_bytes % 8 == 0 && x_off % 8 == 0 && recv_off % 8 == 0) ? 1 : 0;
   }
+  // count rows through LDS when E splits into 16-byte lanes and the rows fit 16 KiB
+  a.rowbuf = (E % 4) == 0 && (size_t)(R + 2) * E * 4 <= 16384;
   const size_t lds = sizeof(int32_t) * std::max<size_t>({(size_t)kSubs * E + (dedup ? (size_t)Eo : 0),
                                                          (3 + kWaves) * (size_t)E + 2 * (size_t)kSub * K +
-                                                             (dedup ? (size_t)kSub * K : 0),
+                                                             (dedup ? (size_t)kSub * K : 0) +
+                                                             (a.rowbuf ? (size_t)(R + 2) * E : 0),
                                                          (size_t)kThreads});
   const int grid = R * a.NB1 + R * a.NB2 + (wait ? R : 0);
   if (dedup) hipLaunchKernelGGL(k_dispatch<true>, dim3(grid), dim3(kThreads), lds, st, a);

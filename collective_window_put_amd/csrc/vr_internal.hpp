@@ -71,6 +71,8 @@ struct vrComm {
   uint64_t* lit_last;  // [R][R] litmus records: the piece that completed each relay
   uint64_t* litmus;    // caller's litmus words [2] (checks, mismatches), or null: litmus off
   uint32_t lit_seed;   // per-launch seed of the litmus samples
+  uint64_t* trace;     // caller's dispatch phase timestamps, or null: tracing off
+  uint64_t trace_words;
   // growable scratch for dispatch (histograms, count exchange)
   char* scratch;
   size_t scratch_bytes;

@@ -221,6 +221,23 @@ vrResult_t vr_comm_get_async_error(vrComm_t comm, vrResult_t* out, uint32_t* bit
  * and check nothing. */
 vrResult_t vr_comm_set_litmus(vrComm_t comm, uint64_t* litmus);
 
+/* Phase timeline of the dispatch (a measuring aid: where the time of the
+ * count exchange, the offsets and the row copies goes). stamps: device
+ * uint64[words] or NULL (off, the default). While it is set, every workgroup
+ * of a vr_dispatch, vr_dispatch_noalloc or vr_dispatch_dedup kernel writes the
+ * device real-time clock (ns) at its phase boundaries into
+ * stamps[w * 8 + phase], w its index in the grid -- the count workgroups
+ * (R * ceil(T / 256), source-interleaved), then the put workgroups
+ * (R * 4 * ceil(T / 256)), then the R receivers; words past `words` are not
+ * written, and phases a workgroup does not reach keep their old value.
+ * Count workgroup: 0 start, 1 histograms stored, 2 count row published (the
+ * source's last block only). Put workgroup: 0 start, 1 entries ranked and
+ * token-row loads issued, 2 count signal seen, 3 count rows loaded and
+ * offsets computed, 4 source tags stored, 5 row stores issued, 6 row stores
+ * complete, 7 row signals applied (the source's last block only). Receiver:
+ * 0 start, 1 count signal seen, 2 row signal seen. */
+vrResult_t vr_comm_set_trace(vrComm_t comm, uint64_t* stamps, size_t words);
+
 /* Rank count and requirements of a communicator. */
 vrResult_t vr_comm_query(vrComm_t comm, int* nranks, vrCommRequirements* req);
 

@@ -223,3 +223,46 @@ def test_dispatch_duplicate_expert_ids_send_one_row_per_entry(R, T, H, E, K, see
     over = _check(res, topk, x, E)
     assert not any(over)
     assert res["err"][0] == vr.VR_OK
+
+
+def test_dispatch_trace_records_every_workgroups_phases():
+    # vr_comm_set_trace: every workgroup stamps its phases, in order; the
+    # result is unchanged
+    import torch
+    R, T, H, E, K = 4, 600, 16, 32, 4
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=31)
+    rb = H * 2
+    cap = R * T * K
+    nb1 = (T + 255) // 256
+    ncount, nput = R * nb1, R * 4 * nb1
+    with Job(R) as job:
+        xw, _ = job.window(T * rb, fill=None, arrays=[x[r] for r in range(R)])
+        rw, rv = job.window(cap * rb, fill=0)
+        tk = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).cuda()
+        counts = torch.zeros((R, E // R), dtype=torch.int32, device="cuda")
+        src = torch.full((R, cap), -1, dtype=torch.int32, device="cuda")
+        stamps = torch.zeros((ncount + nput + R) * 8, dtype=torch.int64, device="cuda")
+        vr.vr_comm_set_trace(job.comm, stamps)
+        say("dispatch with a phase trace")
+        vr.vr_dispatch(job.comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, None, 0, 1)
+        st = stamps.view(-1, 8).cpu().numpy()
+        vr.vr_comm_set_trace(job.comm, None)
+        out = job.host(rv)
+        job.assert_no_async_error()
+    cnt, put, rcv = st[:ncount], st[ncount:ncount + nput], st[ncount + nput:]
+    assert np.all(cnt[:, :2] > 0) and np.all(cnt[:, 1] >= cnt[:, 0])
+    assert (cnt[:, 2] > 0).sum() == R  # one count-row publisher per source
+    assert np.all(put[:, :7] > 0) and np.all(np.diff(put[:, :7], axis=1) >= 0)
+    assert (put[:, 7] > 0).sum() == R  # one row-signal applier per source
+    assert np.all(rcv[:, :3] > 0) and np.all(np.diff(rcv[:, :3], axis=1) >= 0)
+    # receiver d's wait ends after every put workgroup of every source sending
+    # rows to d has completed its stores (stamped before its relay arrival)
+    epr = E // R
+    for d in range(R):
+        srcs = [s for s in range(R) if np.any(topk[s] // epr == d)]
+        last = max(put[b2 * R + s, 6] for s in srcs for b2 in range(4 * nb1))
+        assert rcv[d, 2] >= last, d
+    rows, tags, _, _ = D.dispatch(topk, x, E, cap)
+    for d in range(R):
+        n = rows[d].shape[0]
+        assert np.array_equal(out[d][:n * rb].reshape(n, rb), rows[d]), d
