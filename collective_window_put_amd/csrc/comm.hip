@@ -68,7 +68,7 @@ bool valid_req(int nranks, const vrCommRequirements* req) {
 }
 
 struct Layout {
-  size_t sig, cnt, err, relay, bar, lit, total;
+  size_t sig, cnt, err, relay, bar, lit, ring, total;
 };
 Layout layout(int R, const vrCommRequirements& q) {
   Layout l;
@@ -78,7 +78,8 @@ Layout layout(int R, const vrCommRequirements& q) {
   l.relay = align_up(l.err + 256, 256);
   l.bar = align_up(l.relay + sizeof(uint32_t) * kRelaySlots, 256);
   l.lit = align_up(l.bar + sizeof(uint64_t) * std::max<uint32_t>(q.barrier_count, 1), 256);
-  l.total = align_up(l.lit + sizeof(uint64_t) * R * R, 256);
+  l.ring = align_up(l.lit + sizeof(uint64_t) * R * R, 256);
+  l.total = align_up(l.ring + 2 * sizeof(uint64_t) * R * q.context_count, 256);
   return l;
 }
 
@@ -451,6 +452,9 @@ vrResult_t vr_comm_create(int nranks, const vrCommRequirements* req, void* works
   c->lit_seed = 0;
   c->trace = nullptr;
   c->trace_words = 0;
+  c->ring_bases = reinterpret_cast<uint64_t*>(c->ws + l.ring);
+  c->ring_gens = c->ring_bases + (size_t)nranks * req->context_count;
+  c->ring_gen = 0;
   c->bar_expect.assign(req->barrier_count, 0);
   c->scratch = nullptr;
   c->scratch_bytes = 0;

@@ -19,8 +19,14 @@
 // by one wave took 225 us, 64 KiB rounds by one wave 119 us, 64 KiB rounds
 // by a 256-thread workgroup 98 us (32 KiB: 155 us; 128 KiB: 97 us): the time
 // follows the number of serial rounds per issuer and the loads in flight.
-// One waiting wavefront per receiving (rank, context) polls the signal until
-// it has grown by the context's message count; with the litmus on, each time
+// Before its first signal, the producer of (rank, context) -- the only writer
+// of that signal during the exchange -- reads the signal's value and
+// publishes it, followed by the call's generation number, in the
+// communicator's workspace; the receiver waits for the generation, reads the
+// value and from it the target. One waiting wavefront per receiving (rank,
+// context) then polls the signal until it has grown by the context's message
+// count (replacing a separate snapshot kernel before the exchange: one launch
+// less per call); with the litmus on, each time
 // it sees a new value v it acquires and checks that message v-1 and one
 // earlier message of the context are present, counting violations.
 //
@@ -53,20 +59,14 @@ struct RingArgs {
   uint64_t* sigp[VR_MAX_RANKS];  // rank d's signal of context 0; context k at sigp[d] + k
   uint64_t* cnt;        // &cnt[0][cnt_base]
   uint32_t cnt_stride;
-  uint64_t* bases;      // [R][C] signal values before this exchange
+  uint64_t* bases;      // [R][C] signal values before this exchange, published by the producers
+  uint64_t* gens;       // [R][C] generation of the exchange whose base bases[] holds
+  uint64_t gen;
   uint64_t* litmus;     // [2] checks, violations; or null
   uint32_t* err;
   uint64_t timeout_ns;
   int R, C, waiters;
 };
-
-__global__ void k_ring_snapshot(const RingArgs a) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < a.R * a.C) {
-    const int d = i / a.C, k = i % a.C;
-    store8_agent(a.bases + i, load_relaxed_u64(a.sigp[d] + k));
-  }
-}
 
 // Compare message m at receiver d with its source at sender; true if equal.
 __device__ bool message_present(const RingArgs& a, int d, int sender, uint64_t m) {
@@ -94,6 +94,15 @@ __global__ __launch_bounds__(kThreads) void k_ring(const RingArgs a) {
     const uint64_t m0 = (uint64_t)k * a.per_ctx, m1 = m0 + a.per_ctx;
     uint64_t* sig = a.sigp[peer] + k;
     uint64_t* cnt = a.cnt + (size_t)r * a.cnt_stride + k;
+    if (a.waiters) {  // publish the signal's value before any of this exchange's signals
+      if (tid == 0) {
+        const size_t i = (size_t)peer * C + k;
+        store8_agent(a.bases + i, load_relaxed_u64(sig));
+        wait_vmem();  // the value has landed before the generation that announces it
+        store8_agent(a.gens + i, a.gen);
+      }
+      __syncthreads();  // no wave signals before the value has been read
+    }
     if (WEAK) {  // wave v: chunks v, v + 4, ... of the context; lane j signals message j of a chunk
       const uint32_t lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addresses
       const uint64_t per_chunk = std::min<uint64_t>(64, std::max<uint64_t>(1, kRoundBytes / kWaves / P));
@@ -126,10 +135,18 @@ __global__ __launch_bounds__(kThreads) void k_ring(const RingArgs a) {
   const int i = w - R * C;
   if (i >= a.waiters) return;
   const int d = i / C, k = i % C, sender = (d + R - 1) % R;
-  const uint64_t base = a.bases[(size_t)d * C + k];
+  const uint64_t t0 = now_ns();
+  // this exchange's base, once the producer has published it
+  while (load_relaxed_u64(a.gens + (size_t)d * C + k) != a.gen) {
+    if (now_ns() - t0 > a.timeout_ns) {
+      if (lane == 0) atomic_or_u32(a.err, VR_ASYNC_TIMEOUT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  const uint64_t base = load_relaxed_u64(a.bases + (size_t)d * C + k);
   const uint64_t* sig = a.sigp[d] + k;
   const uint64_t m0 = (uint64_t)k * a.per_ctx;
-  const uint64_t t0 = now_ns();
   uint64_t seen = 0;
   for (;;) {
     const uint64_t v = load_relaxed_u64(sig);
@@ -166,8 +183,6 @@ vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, si
                        int contexts, uint64_t* const* sig_ctx0, uint32_t cnt_base, bool wait, bool weak,
                        uint64_t* litmus, hipStream_t st) {
   const int R = c->nranks;
-  vrResult_t r = ensure_scratch(c, sizeof(uint64_t) * R * contexts);
-  if (r != VR_OK) return r;
   RingArgs a;
   for (int q = 0; q < VR_MAX_RANKS; ++q) {
     a.send.p[q] = send->base[q];
@@ -178,18 +193,15 @@ vrResult_t launch_ring(vrComm* c, const vrWindow* send, const vrWindow* recv, si
   for (int q = 0; q < VR_MAX_RANKS; ++q) a.sigp[q] = q < R ? sig_ctx0[q] : nullptr;
   a.cnt = c->cnt + cnt_base;
   a.cnt_stride = c->req.counter_count;
-  a.bases = reinterpret_cast<uint64_t*>(c->scratch);
+  a.bases = c->ring_bases;
+  a.gens = c->ring_gens;
+  a.gen = ++c->ring_gen;
   a.litmus = litmus;
   a.err = c->err;
   a.timeout_ns = kDefaultTimeoutNs;
   a.R = R;
   a.C = contexts;
   a.waiters = wait ? R * contexts : 0;
-  if (a.waiters) {
-    const int n = R * contexts;
-    hipLaunchKernelGGL(k_ring_snapshot, dim3((n + 255) / 256), dim3(256), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return VR_ERR_HIP;
-  }
   if (weak) hipLaunchKernelGGL(k_ring<true>, dim3(R * contexts + a.waiters), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(k_ring<false>, dim3(R * contexts + a.waiters), dim3(kThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;

@@ -71,6 +71,9 @@ struct vrComm {
   uint64_t* lit_last;  // [R][R] litmus records: the piece that completed each relay
   uint64_t* litmus;    // caller's litmus words [2] (checks, mismatches), or null: litmus off
   uint32_t lit_seed;   // per-launch seed of the litmus samples
+  uint64_t* ring_bases;  // [R][context_count] ring signal values published by the producers
+  uint64_t* ring_gens;   // [R][context_count] exchange generation of each published value
+  uint64_t ring_gen;     // generation of the last ring exchange enqueued
   uint64_t* trace;     // caller's dispatch phase timestamps, or null: tracing off
   uint64_t trace_words;
   // growable scratch for dispatch (histograms, count exchange)

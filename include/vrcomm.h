@@ -27,13 +27,13 @@
  *   - Memory: windows, inputs and outputs are owned by the caller; the
  *     library owns only its signal/counter words and small scratch buffers.
  *     The dispatch scratch (count rows, block prefixes: about
- *     R*(T/64)*E*4 bytes) and the ring's snapshot words are grown on the
- *     first vr_dispatch, vr_dispatch_dedup or vr_ring_exchange that needs
- *     more than any call before it on the communicator: that call
- *     synchronizes the device, frees the old buffer and allocates
- *     (hipMalloc) before enqueuing. Later calls of that size or smaller
- *     allocate nothing, so a caller that must not allocate (graph capture,
- *     a serving loop) makes one call of its largest shape first.
+ *     R*(T/64)*E*4 bytes) is grown on the first vr_dispatch or
+ *     vr_dispatch_dedup that needs more than any call before it on the
+ *     communicator: that call synchronizes the device, frees the old buffer
+ *     and allocates (hipMalloc) before enqueuing. Later calls of that size or
+ *     smaller allocate nothing, so a caller that must not allocate (graph
+ *     capture, a serving loop) makes one call of its largest shape first, or
+ *     uses vr_dispatch_noalloc. Every other operation allocates nothing.
  *   - Device pointers are plain device addresses on the communicator's device.
  *     Array arguments (routing ids, weights, positions, counts, tags, the
  *     litmus words) must lie, for their whole stated size, inside one device

@@ -140,7 +140,7 @@ def test_dispatch_r8_t4096_e256_k8_full_size():
 
 def test_dispatch_shapes_interleaved_on_one_comm():
     # One communicator: dispatches of two shapes, a per-rank-layout dispatch
-    # and a ring exchange (which reuses the library's scratch) in between, each
+    # and a ring exchange in between, each
     # dispatch checked against the oracle: nothing a dispatch leaves in the
     # scratch may leak into the next one.
     import torch
@@ -181,7 +181,7 @@ def test_dispatch_shapes_interleaved_on_one_comm():
                     n = drows[d].shape[0]
                     assert np.array_equal(out[d][:n * rb], drows[d].reshape(-1)), ("dedup", d)
                     assert np.array_equal(sd[d, :n].cpu().numpy(), dtags[d]), ("dedup", d)
-            if i == 2:  # a ring exchange reuses the scratch words
+            if i == 2:  # a ring exchange on the same communicator
                 vr.vr_ring_exchange(job.comm, rs, rr, 256, 8, 2, 4, 0)
                 job.torch.cuda.synchronize()
         job.assert_no_async_error()
