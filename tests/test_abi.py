@@ -80,6 +80,11 @@ def test_argument_errors_without_gpu(lib):
         assert e.value.code == vr.VR_ERR_INVALID_ARGUMENT
     rc = lib.vr_allreduce(None, None, 0, None, 0, 0, 0, 0, 0, 0, None)
     assert rc == vr.VR_ERR_INVALID_ARGUMENT
+    # the communicator switches and the allocation-free dispatch refuse unknown handles too
+    assert lib.vr_comm_set_litmus(0x10, None) == vr.VR_ERR_INVALID_ARGUMENT
+    assert lib.vr_comm_set_trace(0x10, None, 0) == vr.VR_ERR_INVALID_ARGUMENT
+    assert lib.vr_dispatch_noalloc(0x10, 0x20, 0, 16, None, 0, 1, 8, 0x30, 0, 0, None, None, None, 0, 1, 0,
+                                   None) == vr.VR_ERR_INVALID_ARGUMENT
 
 
 def test_struct_layouts_match_header():
