@@ -840,8 +840,8 @@ def cpu_rows():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     ap.add_argument("--rows", default=",".join(ROW_NAMES), help="comma-separated subset of " + ",".join(ROW_NAMES))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
