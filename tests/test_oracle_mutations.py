@@ -282,3 +282,136 @@ def test_protocol_bf16_truncation_is_caught(monkeypatch):
                         lambda x: (np.ascontiguousarray(x, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16))
     _fails(TPR.test_protocol_bf16_conversions_match_torch)
     _fails(TPR.test_allreduce_random_interleavings, 4, 300, "bf16", 1)
+
+
+# -- the remaining definitions, primitives and protocol programs ------------------------
+def test_bf16_widening_off_by_one_bit_is_caught(monkeypatch):
+    monkeypatch.setattr(D, "bf16_bits_to_f32",
+                        lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(15)).view(np.float32))
+    _fails(TD.test_bf16_widening_is_exact)
+
+
+def test_ring_to_the_wrong_successor_is_caught(monkeypatch):
+    def two_ahead(sends, recv_before, puts_per_rank, put_bytes):
+        R, n = len(sends), puts_per_rank * put_bytes
+        out = [np.array(b, dtype=np.uint8, copy=True).reshape(-1) for b in recv_before]
+        for r in range(R):
+            out[(r + 2) % R][:n] = np.asarray(sends[r], dtype=np.uint8).reshape(-1)[:n]
+        return out
+    monkeypatch.setattr(D, "ring", two_ahead)
+    _fails(TD.test_ring_is_cyclic_shift)
+
+
+def test_rows_per_rank_counting_tokens_is_caught(monkeypatch):
+    def per_token(topk, E):  # one row per (token, rank) instead of per entry
+        topk = np.asarray(topk)
+        R, T, _ = topk.shape
+        epr = E // R
+        out = np.zeros(R, np.int64)
+        for s in range(R):
+            for t in range(T):
+                for d in {int(e) // epr for e in topk[s, t] if e >= 0}:
+                    out[d] += 1
+        return out
+    monkeypatch.setattr(D, "dispatch_rows_per_rank", per_token)
+    _fails(TD.test_dispatch_duplicate_expert_sends_one_row_per_entry)
+
+
+def test_dedup_positions_in_token_major_order_are_caught(monkeypatch):
+    def token_major(topk, E, capacity_rows=None):
+        topk = np.asarray(topk)
+        R, T, _ = topk.shape
+        epr = E // R
+        pos = np.full((R, T, R), -1, dtype=np.int32)
+        for d in range(R):
+            n = 0
+            for t in range(T):  # token before source: a plausible slip
+                for s in range(R):
+                    if any(e >= 0 and e // epr == d for e in topk[s, t]):
+                        if capacity_rows is None or n < capacity_rows:
+                            pos[s, t, d] = n
+                        n += 1
+        return pos
+    monkeypatch.setattr(D, "dispatch_dedup_positions", token_major)
+    _fails(TD.test_dedup_positions_point_at_the_rows_and_capacity)
+
+
+def test_put_dropping_its_last_byte_is_caught(monkeypatch):
+    from oracle.primitives import World
+    orig = World.put
+
+    def short(self, rank, peer, dst, doff, src, soff, nbytes, remote=None, local=None):
+        return orig(self, rank, peer, dst, doff, src, soff, max(0, nbytes - 1), remote, local)
+    monkeypatch.setattr(World, "put", short)
+    _fails(TP.test_put_get_brute_force_tiny_windows)
+
+
+def test_counter_counting_twice_is_caught(monkeypatch):
+    from oracle.primitives import World, COUNTER_BITS
+
+    def twice(self, rank, action):
+        if action is None:
+            return
+        self._validate_local(rank, action)
+        self.cnt[rank][action.id] = (self.cnt[rank][action.id] + 2) % (1 << COUNTER_BITS)
+    monkeypatch.setattr(World, "apply_local", twice)
+    _fails(TP.test_counter_counts_local_completions_only)
+
+
+def test_protocol_alltoall_at_the_peers_offset_is_caught(monkeypatch):
+    from oracle import protocol as pr
+    import test_oracle_protocol as TPR
+
+    def transposed(world, send, recv, block, sig, strong=True):
+        R = world.nranks
+
+        def prog(rank):
+            base = yield pr.ReadSignal(sig)
+            yield pr.Barrier()
+            for peer in range(R):  # receive offset of the peer instead of the sender's own
+                yield pr.Put(peer, recv, peer * block, send, peer * block, block, pr.SignalInc(sig, strong))
+            yield pr.WaitSignal(sig, base + R)
+            yield pr.Barrier()
+        return [prog(r) for r in range(R)]
+    monkeypatch.setattr(pr, "alltoall_programs", transposed)
+    _fails(TPR.test_alltoall_random_interleavings, 3)
+
+
+def test_protocol_allgather_wrong_segment_is_caught(monkeypatch):
+    from oracle import protocol as pr
+    import test_oracle_protocol as TPR
+
+    def wrong(world, send, recv, nbytes, sig):
+        R = world.nranks
+
+        def prog(rank):
+            base = yield pr.ReadSignal(sig)
+            yield pr.Barrier()
+            for peer in range(R):  # segment of the destination instead of the source
+                yield pr.Put(peer, recv, peer * nbytes, send, 0, nbytes, pr.SignalInc(sig))
+            yield pr.WaitSignal(sig, base + R)
+            yield pr.Barrier()
+        return [prog(r) for r in range(R)]
+    monkeypatch.setattr(pr, "allgather_programs", wrong)
+    _fails(TPR.test_allgather_protocol, 0)
+
+
+def test_protocol_allreduce_chunk_bounds_off_by_one_is_caught(monkeypatch):
+    from oracle import protocol as pr
+    import test_oracle_protocol as TPR
+    orig = pr.chunk_bounds
+    monkeypatch.setattr(pr, "chunk_bounds", lambda count, R, owner: (lambda a, b: (min(a + 1, b), b))(
+        *orig(count, R, owner)))
+    _fails(TPR.test_allreduce_random_interleavings, 3, 1001, "f32", 0)
+
+
+def test_protocol_ring_signalling_one_context_is_caught(monkeypatch):
+    from oracle import protocol as pr
+    import test_oracle_protocol as TPR
+    orig_inc = pr.SignalInc
+    # every SignalInc of the exchange lands on the first context's signal: the
+    # other contexts' waits can never end, which the scheduler reports
+    from oracle.primitives import Deadlock
+    monkeypatch.setattr(pr, "SignalInc", lambda sid, strong=True: orig_inc(0, strong))
+    with pytest.raises(Deadlock):
+        TPR.test_ring_protocol_signals_and_counters(0)
