@@ -537,7 +537,9 @@ def dispatch_programs(world: World, b: DispatchBuffers, sig_counts: int, sig_row
         my_rows = int(tot[s * epr:(s + 1) * epr].sum())
         b.overflow[s] = my_rows > b.cap
 
-        # step 3: one put per expert of the packed rows (ascending token), no signal
+        # step 3: one put per expert of the packed rows, one per routing entry
+        # naming it (ascending token, then k: a token naming e twice sends two
+        # rows), no signal
         rows_to = [0] * R
         so = 0
         for e in range(E):
@@ -545,19 +547,19 @@ def dispatch_programs(world: World, b: DispatchBuffers, sig_counts: int, sig_row
             if n == 0:
                 continue
             d = e // epr
-            toks = [t for t in range(T) if e in b.topk[s, t]]
+            ents = [(t, k) for t in range(T) for k in range(K) if b.topk[s, t, k] == e]
 
-            def pack(w, me, toks=toks, so=so):
+            def pack(w, me, ents=ents, so=so):
                 xs = w.buf(b.x, me).reshape(T, rb)
-                w.buf(b.stage, me)[so * rb:(so + len(toks)) * rb] = xs[toks].reshape(-1)
+                toks = [t for (t, _) in ents]
+                w.buf(b.stage, me)[so * rb:(so + len(ents)) * rb] = xs[toks].reshape(-1)
                 tags = np.array([(me << 16) | t for t in toks], dtype=np.int32)
-                w.buf(b.stage_src, me)[so * 4:(so + len(toks)) * 4] = tags.view(np.uint8)
+                w.buf(b.stage_src, me)[so * 4:(so + len(ents)) * 4] = tags.view(np.uint8)
 
             yield Local(pack, f"pack e={e}")
-            for i, t in enumerate(toks):
-                for k in range(K):
-                    if b.topk[s, t, k] == e and off[e] + i < b.cap:
-                        b.pos[s, t, k] = off[e] + i
+            for i, (t, k) in enumerate(ents):
+                if off[e] + i < b.cap:
+                    b.pos[s, t, k] = off[e] + i
             keep = max(0, min(n, b.cap - int(off[e])))  # rows past the capacity are dropped
             if keep:
                 yield Put(d, b.recv, int(off[e]) * rb, b.stage, so * rb, keep * rb)

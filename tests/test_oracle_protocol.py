@@ -161,8 +161,19 @@ def test_ring_with_reset_returns_signals_to_zero():
     assert w.cnt == [[P // C] * C] * R
 
 
-def _run_dispatch(R, T, H, E, K, seed, cap=None):
+def _with_repeats(topk, frac, seed):
+    """Entry k names the same expert as entry k-1 with probability frac."""
+    t = topk.copy()
+    rep = np.random.default_rng(seed + 1).random(t.shape) < frac
+    for k in range(1, t.shape[2]):
+        t[:, :, k] = np.where(rep[:, :, k], t[:, :, k - 1], t[:, :, k])
+    return t
+
+
+def _run_dispatch(R, T, H, E, K, seed, cap=None, repeat=0.0):
     topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    if repeat:
+        topk = _with_repeats(topk, repeat, seed)
     cap = cap if cap is not None else R * T * min(K, E // R)
     w = World(R)
     b = pr.DispatchBuffers(w, x, topk, E, cap)
@@ -436,3 +447,77 @@ def test_allreduce_protocol_bf16_special_values_match_definition():
         exp = D.allreduce(xs, "bf16")
     for d in range(R):
         assert np.array_equal(w.buf(r, d).view(np.uint16), exp)
+
+
+
+# -- a token naming one expert more than once: one row per routing entry -------------------
+@pytest.mark.parametrize("R,T,H,E,K,seed,cap", [(3, 30, 4, 6, 3, 11, None), (4, 25, 2, 16, 4, 12, None),
+                                                (2, 40, 2, 4, 2, 13, 30)])
+def test_dispatch_protocol_repeated_experts_match_definition(R, T, H, E, K, seed, cap):
+    topk, x, w, b, cap = _run_dispatch(R, T, H, E, K, seed, cap, repeat=0.5)
+    assert any(len(set(topk[s, t].tolist())) < K for s in range(R) for t in range(T))
+    rows, src, counts, over = D.dispatch(topk, x, E, cap)
+    for d in range(R):
+        n, rb = rows[d].shape
+        assert np.array_equal(w.buf(b.recv, d)[:n * rb], rows[d].reshape(-1)), d
+        assert np.array_equal(w.buf(b.recv_src, d)[:n * 4].view(np.int32), src[d]), d
+        assert np.array_equal(b.counts[d], counts[d])
+        assert w.sig[d][1] == D.dispatch_rows_per_rank(topk, E)[d]
+        assert b.overflow[d] == over[d]
+    assert np.array_equal(b.pos, D.dispatch_positions(topk, E, cap))
+
+
+def test_dispatch_protocol_repeated_expert_every_interleaving():
+    R, T, H, E, K = 2, 2, 1, 4, 2
+    topk = np.array([[[1, 1], [2, 1]], [[1, 3], [0, 0]]], dtype=np.int32)
+    x = np.arange(R * T * H, dtype=np.uint16).reshape(R, T, H) + 1
+    rows, src, counts, _ = D.dispatch(topk, x, E, R * T * K)
+    bufs = []
+
+    def setup():
+        w = World(R)
+        b = pr.DispatchBuffers(w, x, topk, E, R * T * K)
+        bufs.append(b)
+        return w, pr.dispatch_programs(w, b, 0, 1)
+
+    n = 0
+    for w in pr.distinct_final_states(setup):
+        b = bufs[-1]
+        for d in range(R):
+            k, rb = rows[d].shape
+            assert np.array_equal(w.buf(b.recv, d)[:k * rb], rows[d].reshape(-1))
+            assert np.array_equal(w.buf(b.recv_src, d)[:k * 4].view(np.int32), src[d])
+        assert np.array_equal(b.pos, D.dispatch_positions(topk, E))
+        n += 1
+    assert n == 1
+
+
+def test_combine_protocol_repeated_experts_match_definition():
+    R, T, H, E, K, seed = 3, 20, 4, 6, 3, 21
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    topk = _with_repeats(topk, 0.5, seed)
+    weights = W.router_weights(topk, E)
+    pos = D.dispatch_positions(topk, E)
+    y = W.expert_outputs(D.dispatch_rows_per_rank(topk, E), H, seed=seed + 7)
+    want = D.combine(topk, weights, pos, y, E)
+    w = World(R)
+    b = pr.CombineBuffers(w, y, topk, weights, pos, E, "bf16")
+    pr.run(w, pr.combine_programs(w, b, 3), seed=seed)
+    for s in range(R):
+        assert np.array_equal(w.buf(b.out, s).view(np.uint16).reshape(T, H), want[s])
+
+
+def test_dedup_protocol_repeated_experts_match_definition():
+    R, T, H, E, K, seed = 4, 30, 2, 16, 4, 22
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
+    topk = _with_repeats(topk, 0.5, seed)
+    w = World(R)
+    b = pr.DedupBuffers(w, x, topk, E, R * T)
+    pr.run(w, pr.dispatch_dedup_programs(w, b, 0, 1), seed=seed)
+    rows, src, experts, counts, over = D.dispatch_dedup(topk, x, E, R * T)
+    for d in range(R):
+        n, rb = rows[d].shape
+        assert np.array_equal(w.buf(b.recv, d)[:n * rb], rows[d].reshape(-1))
+        meta = w.buf(b.recv_meta, d)[:n * 4 * (1 + K)].view(np.int32).reshape(n, 1 + K)
+        assert np.array_equal(meta[:, 0], src[d]) and np.array_equal(meta[:, 1:], experts[d])
+    assert np.array_equal(b.pos, D.dispatch_dedup_positions(topk, E, R * T))
