@@ -22,7 +22,9 @@ namespace vr {
 constexpr uint32_t kRelaySpread = 64;
 constexpr uint32_t kRelaySingle = 0;  // vr_put / vr_get: 8 per-XCD counters and a total, spread
 constexpr uint32_t kRelayColl = 9 * kRelaySpread;  // collectives: up to R*R counters
-constexpr uint32_t kRelayCollWords = VR_MAX_RANKS * VR_MAX_RANKS;
+// (and the AllReduce's rank-split form: 73 counters per rank for R <= 8, spread)
+constexpr uint32_t kRelayCollWords =
+    VR_MAX_RANKS * VR_MAX_RANKS > 73 * 8 * kRelaySpread ? VR_MAX_RANKS * VR_MAX_RANKS : 73 * 8 * kRelaySpread;
 constexpr uint32_t kRelayDispatch = kRelayColl + kRelayCollWords;  // 18 counters per source rank
 constexpr uint32_t kRelayDispatchWords = 18 * VR_MAX_RANKS * 8;
 constexpr uint32_t kRelaySlots = kRelayDispatch + kRelayDispatchWords;

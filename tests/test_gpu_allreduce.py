@@ -123,15 +123,56 @@ def test_allreduce_bf16_r8_64Mi_full_size():
     assert sigs == [R] * R
 
 
-@pytest.mark.parametrize("dtype,R,N", [("bf16", 16, 32 << 20), ("f32", 4, 16 << 20), ("bf16", 2, 48 << 20),
-                                     ("f32", 8, 16 << 20), ("bf16", 4, 32 << 20)])
-def test_allreduce_looping_form(dtype, R, N):
-    # Large, evenly tiled shapes run the looping form (4096 workgroups, each
-    # taking several tiles of its XCD's range): R=16 crosses an owner chunk
-    # inside a workgroup's loop, R=4 and R=2 spread one chunk over several
-    # XCDs. Two calls in a row check that the relay counters come back to 0.
-    say(f"allreduce looping form {dtype} R={R} N={N}")
+@pytest.mark.parametrize("dtype,R,N", [("f32", 4, 16 << 20), ("bf16", 2, 48 << 20), ("f32", 8, 16 << 20),
+                                     ("bf16", 4, 32 << 20)])
+def test_allreduce_rank_split_form_large(dtype, R, N):
+    # Large, evenly tiled shapes with R <= 8 whose chunk splits into a
+    # multiple of 64 pieces run the rank-split form (one piece of 512/R
+    # vectors per rank per workgroup, three relay levels); a piece is 4 KiB
+    # per rank for R=2. Two calls in a row check that the relay counters come
+    # back to 0.
+    say(f"allreduce rank-split form {dtype} R={R} N={N}")
     xs = W.allreduce_f32_inputs(R, N, seed=R + 11) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + 11)
+    es = 4 if dtype == "f32" else 2
+    exp = D.allreduce(xs, dtype).view(np.uint8)
+    out, sigs = _run(xs, dtype, repeats=2)
+    for d in range(R):
+        assert np.array_equal(out[d][:N * es], exp), d
+        assert np.all(out[d][N * es:] == 0xCD)
+    assert sigs == [2 * R] * R
+
+
+def _tile(dtype):
+    return 2048 if dtype == "f32" else 4096  # elements of a tile (8 KiB per rank)
+
+
+@pytest.mark.parametrize("dtype,R,tpc", [("bf16", 2, 32), ("bf16", 4, 16), ("bf16", 8, 8), ("f32", 4, 48),
+                                         ("f32", 8, 24), ("bf16", 8, 72), ("f32", 2, 96)])
+def test_allreduce_rank_split_form_small(dtype, R, tpc):
+    # The smallest rank-split shapes: R * tpc pieces per chunk, 64 of them
+    # (one per first-level relay counter, which is then skipped) up to 576.
+    N = R * tpc * _tile(dtype)
+    say(f"allreduce rank-split form {dtype} R={R} tiles per chunk {tpc} N={N}")
+    xs = W.allreduce_f32_inputs(R, N, seed=R + tpc) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + tpc)
+    es = 4 if dtype == "f32" else 2
+    exp = D.allreduce(xs, dtype).view(np.uint8)
+    out, sigs = _run(xs, dtype, repeats=3)
+    for d in range(R):
+        assert np.array_equal(out[d][:N * es], exp), d
+        assert np.all(out[d][N * es:] == 0xCD)
+    assert sigs == [3 * R] * R
+
+
+@pytest.mark.parametrize("dtype,R,tpc", [("bf16", 16, 512), ("bf16", 16, 513), ("f32", 4, 2050)])
+def test_allreduce_looping_form(dtype, R, tpc):
+    # Evenly tiled shapes with at least 8192 tiles that split over the 8 XCDs
+    # run the looping form (4096 workgroups, each taking several slabs of its
+    # XCD's range) when R = 16, or when R <= 8 and a chunk's R * tpc pieces
+    # are not a multiple of 64. R=16 crosses an owner chunk inside a
+    # workgroup's loop, R=4 spreads one chunk over two XCDs. Two calls in a row check that the relay counters come back to 0.
+    N = R * tpc * _tile(dtype)
+    say(f"allreduce looping form {dtype} R={R} N={N}")
+    xs = W.allreduce_f32_inputs(R, N, seed=R + 13) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + 13)
     es = 4 if dtype == "f32" else 2
     exp = D.allreduce(xs, dtype).view(np.uint8)
     out, sigs = _run(xs, dtype, repeats=2)

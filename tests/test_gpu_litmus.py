@@ -49,7 +49,7 @@ def test_litmus_allreduce_bf16_r8_64Mi():
         for r in range(R):
             sv[r].copy_(_device_bf16(torch, N, 1000 + r))
         words = _litmus(job)
-        say("litmus allreduce bf16 R=8 N=64Mi (looping form)")
+        say("litmus allreduce bf16 R=8 N=64Mi (rank-split form)")
         vr.vr_allreduce(job.comm, sw, 0, rw, 0, N, vr.VR_DT_BF16, sig=1)
         checks, bad = _read(job, words)
         job.assert_no_async_error()

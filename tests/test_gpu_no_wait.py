@@ -23,7 +23,8 @@ def _wait_all(job, sig, least):
 
 
 @pytest.mark.parametrize("dtype,R,N,send_off,recv_off", [
-    ("bf16", 8, 32 << 20, 4096, 16),   # looping form, offset windows
+    ("bf16", 8, 32 << 20, 4096, 16),   # rank-split form, offset windows
+    ("f32", 4, 4 * 2050 * 2048, 4096, 16),  # looping form (8200 tiles, not a multiple of 64)
     ("f32", 4, 100003, 0, 0),          # one tile per workgroup, ragged
 ])
 def test_allreduce_no_wait(dtype, R, N, send_off, recv_off):

@@ -120,7 +120,9 @@ def test_random_alltoall_sessions(R, B):
 
 def _loop_case(i):
     # evenly tiled shapes past the looping form's threshold (at least 8192
-    # tiles of 4096 bf16 / 2048 fp32 elements), 16-byte aligned offsets
+    # tiles of 4096 bf16 / 2048 fp32 elements), 16-byte aligned offsets: the
+    # rank-split form where R <= 8 and R * tpc is a multiple of 64, else the
+    # looping form
     R = [2, 4, 8, 16][int(_rng.integers(0, 4))]
     dtype = ["f32", "bf16"][i % 2]
     tile = 2048 if dtype == "f32" else 4096
@@ -134,11 +136,26 @@ def _loop_case(i):
 LOOP_CASES = _draw(4, _loop_case)
 
 
-@pytest.mark.parametrize("R,N,dtype,so,ro", LOOP_CASES)
-def test_random_allreduce_looping_form(R, N, dtype, so, ro):
+def _split_case(i):
+    # evenly tiled shapes of the rank-split form at small sizes: R <= 8 and
+    # R * tpc a multiple of 64 (64 to 1024 pieces per chunk), 16-byte
+    # aligned offsets
+    R = [2, 4, 8][int(_rng.integers(0, 3))]
+    dtype = ["f32", "bf16"][i % 2]
+    tile = 2048 if dtype == "f32" else 4096
+    tpc = (64 // R) * int(_rng.integers(1, 17))
+    vec = 4 if dtype == "f32" else 8
+    return R, R * tpc * tile, dtype, vec * int(_rng.integers(0, 64)), vec * int(_rng.integers(0, 64))
+
+
+SPLIT_CASES = _draw(6, _split_case)
+
+
+@pytest.mark.parametrize("R,N,dtype,so,ro", LOOP_CASES + SPLIT_CASES)
+def test_random_allreduce_full_tiles(R, N, dtype, so, ro):
     es = 4 if dtype == "f32" else 2
     so, ro = so * es, ro * es
-    say(f"random allreduce looping form R={R} N={N} {dtype} send_off={so} recv_off={ro}")
+    say(f"random allreduce full tiles R={R} N={N} {dtype} send_off={so} recv_off={ro}")
     xs = W.allreduce_f32_inputs(R, N, seed=N + R) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=N + R)
     out, sigs = TAR._run(xs, dtype, send_off=so, recv_off=ro, repeats=2)
     want = D.allreduce(xs, dtype).view(np.uint8)
