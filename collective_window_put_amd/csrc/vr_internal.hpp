@@ -20,11 +20,12 @@ namespace vr {
 // gfx950, returning atomics on one 256-byte span serialize at ~12 ns each,
 // while separate spans proceed in parallel.
 constexpr uint32_t kRelaySpread = 64;
-constexpr uint32_t kRelaySingle = 0;  // vr_put / vr_get: 8 per-XCD counters and a total, spread
-constexpr uint32_t kRelayColl = 9 * kRelaySpread;  // collectives: up to R*R counters
-// (and the AllReduce's rank-split form: 73 counters per rank for R <= 8, spread)
+constexpr uint32_t kRelaySingle = 0;  // vr_put / vr_get: a total, 8 per XCD, 64 first-level, spread
+constexpr uint32_t kRelayColl = 73 * kRelaySpread;  // collectives: up to R*R counters
+// (and the AllReduce's rank-split and the AllGather's piece forms: 73
+// counters per rank, spread 256 bytes apart up to R = 16)
 constexpr uint32_t kRelayCollWords =
-    VR_MAX_RANKS * VR_MAX_RANKS > 73 * 8 * kRelaySpread ? VR_MAX_RANKS * VR_MAX_RANKS : 73 * 8 * kRelaySpread;
+    VR_MAX_RANKS * VR_MAX_RANKS > 73 * 16 * kRelaySpread ? VR_MAX_RANKS * VR_MAX_RANKS : 73 * 16 * kRelaySpread;
 constexpr uint32_t kRelayDispatch = kRelayColl + kRelayCollWords;  // 18 counters per source rank
 constexpr uint32_t kRelayDispatchWords = 18 * VR_MAX_RANKS * 8;
 constexpr uint32_t kRelaySlots = kRelayDispatch + kRelayDispatchWords;

@@ -97,8 +97,9 @@ def test_allgather_copy_engine_vs_oracle(R, M, send_off, recv_off):
 
 @pytest.mark.parametrize("R,M", [(16, 2 << 20), (8, (4 << 20) + 3 * 4096), (4, 8 << 20)])
 def test_allgather_whole_tiles_twice(R, M):
-    # Shapes of whole 4 KiB tiles, 512 to 2051 tiles per source; two calls in
-    # a row check that every source's relay counter comes back to 0.
+    # Shapes of whole 4 KiB tiles, 512 to 2051 tiles per source (R=8 is not
+    # a multiple of 64 KiB, so it runs the tile form; the others the piece
+    # form); two calls in a row check that every relay counter comes back to 0.
     say(f"allgather whole tiles twice R={R} M={M}")
     sends = W.allgather_inputs(R, M, seed=R + M)
     exp = D.allgather(sends)
@@ -112,4 +113,31 @@ def test_allgather_whole_tiles_twice(R, M):
         job.assert_no_async_error()
     for d in range(R):
         assert np.array_equal(out[d], exp[d]), d
+    assert sigs == [2 * R] * R
+
+
+@pytest.mark.parametrize("R,M,send_off,recv_off", [(1, 64 << 10, 0, 0), (2, 128 << 10, 16, 4096), (3, 5 * (64 << 10), 0, 16),
+                                                   (5, 3 * (64 << 10), 4096, 0), (8, 1 << 20, 0, 0),
+                                                   (16, 64 << 10, 32, 48), (64, 64 << 10, 0, 0)])
+def test_allgather_piece_form(R, M, send_off, recv_off):
+    # Sizes that are a multiple of 64 KiB with 16-byte aligned offsets run the
+    # piece form (1 KiB of one source per workgroup, wave w storing to ranks
+    # w, w + 4, ...; 64 pieces per source at least, one per first-level relay
+    # counter). Twice in a row: the relay counters come back to 0.
+    say(f"allgather piece form R={R} M={M} offsets {send_off},{recv_off}")
+    sends = W.allgather_inputs(R, M, seed=R * 7 + M)
+    exp = D.allgather(sends)
+    with Job(R) as job:
+        sw, sv = job.window(send_off + M, fill=0)
+        rw, rv = job.window(recv_off + R * M + 16, fill=0x5A)
+        for r in range(R):
+            sv[r][send_off:].copy_(job.torch.from_numpy(sends[r]))
+        for _ in range(2):
+            vr.vr_allgather(job.comm, sw, send_off, rw, recv_off, M, sig=1)
+        out = job.host(rv)
+        sigs = [job.sig(d, 1) for d in range(R)]
+        job.assert_no_async_error()
+    for d in range(R):
+        assert np.array_equal(out[d][recv_off:recv_off + R * M], exp[d]), d
+        assert np.all(out[d][:recv_off] == 0x5A) and np.all(out[d][recv_off + R * M:] == 0x5A)
     assert sigs == [2 * R] * R

@@ -124,13 +124,14 @@ def test_allreduce_bf16_r8_64Mi_full_size():
 
 
 @pytest.mark.parametrize("dtype,R,N", [("f32", 4, 16 << 20), ("bf16", 2, 48 << 20), ("f32", 8, 16 << 20),
-                                     ("bf16", 4, 32 << 20)])
-def test_allreduce_rank_split_form_large(dtype, R, N):
-    # Large, evenly tiled shapes with R <= 8 whose chunk splits into a
-    # multiple of 64 pieces run the rank-split form (one piece of 512/R
-    # vectors per rank per workgroup, three relay levels); a piece is 4 KiB
-    # per rank for R=2. Two calls in a row check that the relay counters come
-    # back to 0.
+                                     ("bf16", 4, 32 << 20), ("f32", 2, 2 * 4096 * 2048)])
+def test_allreduce_rank_split_form(dtype, R, N):
+    # Evenly tiled shapes of at least 8192 tiles with R <= 8 whose chunk
+    # splits into a multiple of 64 pieces run the rank-split form (one piece
+    # of 512/R vectors per rank per workgroup, three relay levels); a piece is
+    # 4 KiB per rank for R=2, and the last shape is the smallest that
+    # qualifies. Two calls in a row check that the relay counters come back
+    # to 0.
     say(f"allreduce rank-split form {dtype} R={R} N={N}")
     xs = W.allreduce_f32_inputs(R, N, seed=R + 11) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + 11)
     es = 4 if dtype == "f32" else 2
@@ -148,11 +149,12 @@ def _tile(dtype):
 
 @pytest.mark.parametrize("dtype,R,tpc", [("bf16", 2, 32), ("bf16", 4, 16), ("bf16", 8, 8), ("f32", 4, 48),
                                          ("f32", 8, 24), ("bf16", 8, 72), ("f32", 2, 96)])
-def test_allreduce_rank_split_form_small(dtype, R, tpc):
-    # The smallest rank-split shapes: R * tpc pieces per chunk, 64 of them
-    # (one per first-level relay counter, which is then skipped) up to 576.
+def test_allreduce_full_tiles_below_the_large_forms(dtype, R, tpc):
+    # Whole, aligned tiles but fewer than 8192 of them: one tile per
+    # workgroup, the XCD-aware order and the two-level relay; three calls in a
+    # row bring every counter back to 0.
     N = R * tpc * _tile(dtype)
-    say(f"allreduce rank-split form {dtype} R={R} tiles per chunk {tpc} N={N}")
+    say(f"allreduce full tiles {dtype} R={R} tiles per chunk {tpc} N={N}")
     xs = W.allreduce_f32_inputs(R, N, seed=R + tpc) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + tpc)
     es = 4 if dtype == "f32" else 2
     exp = D.allreduce(xs, dtype).view(np.uint8)

@@ -67,8 +67,9 @@ def test_alltoall_no_wait():
     assert sigs == [R] * R
 
 
-def test_allgather_no_wait():
-    R, M = 16, (2 << 20) + 4096 * 3
+@pytest.mark.parametrize("M", [(2 << 20) + 4096 * 3, 2 << 20])  # tile form, piece form
+def test_allgather_no_wait(M):
+    R = 16
     say(f"allgather no-wait R={R} M={M}")
     sends = W.allgather_inputs(R, M, seed=4)
     exp = D.allgather(sends)

@@ -40,7 +40,8 @@ def test_put_get_brute_force_small_ranges():
         job.assert_no_async_error()
 
 
-@pytest.mark.parametrize("n", [1, 100, 16384, 16385, 5 * 16384 + 33, 21 * 16384 + 5, 1 << 22])
+@pytest.mark.parametrize("n", [1, 100, 4096, 4097, 5 * 4096 + 33, 15 * 4096 + 1, 16 * 4096, 21 * 4096 + 5,
+                               70 * 4096 - 3, 1 << 22, 16384 * 4096 + 16])
 def test_put_multi_workgroup_with_signal(n):
     say(f"put {n} bytes")
     rng = np.random.default_rng(n)
@@ -58,11 +59,13 @@ def test_put_multi_workgroup_with_signal(n):
 
 
 def test_large_puts_back_to_back_each_signal_once():
-    """Puts of 16 tiles or more count their tiles per XCD, then the XCDs: every
-    counter must be back at zero for the next put (sizes 22, 16 and 300 tiles)."""
+    """Puts of 16 tiles (4 KiB each) or more count their tiles in three relay
+    levels (per XCD and first-level counter, per XCD, then the XCDs): every
+    counter must be back at zero for the next put (sizes 22, 16, 300, 70 and
+    1201 tiles, some leaving first-level counters unused)."""
     say("large puts back to back")
     rng = np.random.default_rng(5)
-    sizes = [21 * 16384 + 5, 16 * 16384, 300 * 16384 - 7]
+    sizes = [21 * 4096 + 5, 16 * 4096, 300 * 4096 - 7, 70 * 4096, 1201 * 4096 - 1]
     n = max(sizes)
     with Job(2, signal_count=2, counter_count=2) as job:
         src = [rng.integers(0, 256, n, dtype=np.uint8) for _ in range(2)]
@@ -73,7 +76,7 @@ def test_large_puts_back_to_back_each_signal_once():
             vr.vr_get(job.comm, 0, 0, 1, sw, 0, dw, 0, m, vr.CounterInc(1))
         out = job.host(dv)
         assert np.array_equal(out[1], src[0]) and np.array_equal(out[0], src[1])
-        assert job.sig(1, 1) == 3 and job.cnt(0, 0) == 3 and job.cnt(0, 1) == 3
+        assert job.sig(1, 1) == len(sizes) and job.cnt(0, 0) == len(sizes) and job.cnt(0, 1) == len(sizes)
         job.assert_no_async_error()
 
 

@@ -137,18 +137,17 @@ LOOP_CASES = _draw(4, _loop_case)
 
 
 def _split_case(i):
-    # evenly tiled shapes of the rank-split form at small sizes: R <= 8 and
-    # R * tpc a multiple of 64 (64 to 1024 pieces per chunk), 16-byte
-    # aligned offsets
+    # evenly tiled shapes of the rank-split form: R <= 8, at least 8192
+    # tiles, R * tpc a multiple of 64; 16-byte aligned offsets
     R = [2, 4, 8][int(_rng.integers(0, 3))]
     dtype = ["f32", "bf16"][i % 2]
     tile = 2048 if dtype == "f32" else 4096
-    tpc = (64 // R) * int(_rng.integers(1, 17))
+    tpc = 8192 // R + (64 // R) * int(_rng.integers(0, 17))
     vec = 4 if dtype == "f32" else 8
     return R, R * tpc * tile, dtype, vec * int(_rng.integers(0, 64)), vec * int(_rng.integers(0, 64))
 
 
-SPLIT_CASES = _draw(6, _split_case)
+SPLIT_CASES = _draw(4, _split_case)
 
 
 @pytest.mark.parametrize("R,N,dtype,so,ro", LOOP_CASES + SPLIT_CASES)
