@@ -162,3 +162,26 @@ def test_random_allreduce_full_tiles(R, N, dtype, so, ro):
         assert np.array_equal(out[d][ro:ro + N * es], want), d
         assert np.all(out[d][:ro] == 0xCD) and np.all(out[d][ro + N * es:] == 0xCD)
     assert sigs == [2 * R] * R
+
+
+def _ag_piece_case(i):
+    # AllGather sizes of the piece form: non-zero multiples of 64 KiB with
+    # 16-byte aligned offsets, any rank count up to 24
+    R = int(_rng.integers(1, 25))
+    M = (64 << 10) * int(_rng.integers(1, 9))
+    return R, M, 16 * int(_rng.integers(0, 300)), 16 * int(_rng.integers(0, 300))
+
+
+AG_PIECE_CASES = _draw(5, _ag_piece_case)
+
+
+@pytest.mark.parametrize("R,M,so,ro", AG_PIECE_CASES)
+def test_random_allgather_piece_form(R, M, so, ro):
+    say(f"random allgather piece form R={R} M={M} send_off={so} recv_off={ro}")
+    sends = W.allgather_inputs(R, M, seed=M + R)
+    out, sigs = TAG._run(sends, M, send_off=so, recv_off=ro)
+    want = D.allgather(sends)
+    for d in range(R):
+        assert np.array_equal(out[d][ro:], want[d]), d
+        assert np.all(out[d][:ro] == 0x5A)
+    assert sigs == [R] * R

@@ -28,8 +28,12 @@ def _run(R, P, pb, C, litmus=True, repeats=1, flags=0):
 
 
 @pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 2), (3, 96, 256, 4), (4, 1000, 48, 10), (16, 4096, 256, 64),
-                                      (5, 64, 8192, 2), (64, 256, 16, 4)])
+                                      (5, 64, 8192, 2), (64, 256, 16, 4), (2, 520, 16, 1), (3, 12, 32768, 3),
+                                      (4, 3000, 64, 3)])
 def test_ring_vs_oracle(R, P, pb, C):
+    # each context's workgroup issues rounds of up to 64 KiB (at most 256
+    # messages) in order: the last three shapes have 3, 2 and 4 rounds per
+    # context, the first and last with a partial last round
     say(f"ring R={R} P={P} pb={pb} C={C}")
     sends, out, sigs, cnts, lit, err = _run(R, P, pb, C)
     exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
@@ -41,11 +45,17 @@ def test_ring_vs_oracle(R, P, pb, C):
     assert err[0] == vr.VR_OK
 
 
-def test_ring_repeated_accumulates():
-    say("ring repeated x2")
-    R, P, pb, C = 4, 64, 256, 4
-    sends, out, sigs, cnts, lit, err = _run(R, P, pb, C, repeats=2)
-    assert sigs == [[2 * P // C] * C] * R and cnts == [[2 * P // C] * C] * R
+@pytest.mark.parametrize("flags", [0, vr.VR_RING_WEAK])
+def test_ring_repeated_accumulates(flags):
+    # two rounds per context, three calls in a row: signals and counters
+    # accumulate, the bytes are the last call's
+    say(f"ring repeated x3 flags={flags}")
+    R, P, pb, C = 4, 1024, 256, 2
+    sends, out, sigs, cnts, lit, err = _run(R, P, pb, C, repeats=3, flags=flags)
+    exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
+    for d in range(R):
+        assert np.array_equal(out[d], exp[d]), d
+    assert sigs == [[3 * P // C] * C] * R and cnts == [[3 * P // C] * C] * R
     assert err[0] == vr.VR_OK
 
 
