@@ -87,6 +87,15 @@ def test_combine_vs_oracle(R, T, H, E, K, seed, dtype):
     assert res["err"][0] == vr.VR_OK
 
 
+def test_combine_maximum_token_count():
+    # T = 65535, the largest token count the dispatch's source tags hold
+    R, T, H, E, K = 2, 65535, 8, 4, 2
+    say(f"combine maximum T R={R} T={T} H={H} E={E} K={K}")
+    topk, weights, y = _inputs(R, T, H, E, K, 23)
+    res = _run(topk, weights, y, E, H)
+    _check(res, topk, weights, y, E)
+
+
 def test_combine_unrouted_entries_and_capacity_drops():
     R, T, H, E, K = 4, 80, 16, 16, 4
     topk, weights, y = _inputs(R, T, H, E, K, 9, drop=0.3)

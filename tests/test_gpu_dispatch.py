@@ -68,6 +68,19 @@ def test_dispatch_small_vs_oracle(R, T, H, E, K, seed):
     assert res["err"][0] == vr.VR_OK
 
 
+def test_dispatch_maximum_token_count():
+    # T = 65535, the largest the source tag's 16-bit token field holds: 256
+    # count blocks and 1024 put blocks per source
+    R, T, H, E, K = 2, 65535, 8, 4, 2
+    say(f"dispatch maximum T R={R} T={T} H={H} E={E} K={K}")
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=21)
+    res = _run(topk, x, E)
+    over = _check(res, topk, x, E)
+    assert not any(over)
+    assert res["err"][0] == vr.VR_OK
+    assert int(res["src"][0].max()) & 0xFFFF == T - 1 or int(res["src"][1].max()) & 0xFFFF == T - 1
+
+
 def test_dispatch_unrouted_entries_and_empty_experts():
     R, T, H, E, K = 4, 50, 8, 16, 4
     topk, x = W.dispatch_inputs(R, T, H, E, K, seed=11)

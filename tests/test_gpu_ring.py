@@ -29,11 +29,12 @@ def _run(R, P, pb, C, litmus=True, repeats=1, flags=0):
 
 @pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 2), (3, 96, 256, 4), (4, 1000, 48, 10), (16, 4096, 256, 64),
                                       (5, 64, 8192, 2), (64, 256, 16, 4), (2, 520, 16, 1), (3, 12, 32768, 3),
-                                      (4, 3000, 64, 3)])
+                                      (4, 3000, 64, 3), (2, 4, 65536, 2)])
 def test_ring_vs_oracle(R, P, pb, C):
     # each context's workgroup issues rounds of up to 64 KiB (at most 256
-    # messages) in order: the last three shapes have 3, 2 and 4 rounds per
-    # context, the first and last with a partial last round
+    # messages) in order: (2, 520, 16, 1), (3, 12, 32768, 3) and
+    # (4, 3000, 64, 3) have 3, 2 and 4 rounds per context, the first and last
+    # with a partial last round; 65536-byte messages are the largest allowed
     say(f"ring R={R} P={P} pb={pb} C={C}")
     sends, out, sigs, cnts, lit, err = _run(R, P, pb, C)
     exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
@@ -73,7 +74,7 @@ def test_ring_r16_1Mi_x_256B_full_size():
 
 
 @pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 2), (3, 96, 256, 4), (4, 1000, 48, 10), (16, 4096, 256, 64),
-                                      (5, 64, 8192, 2), (3, 12, 32768, 3), (2, 520, 16, 1)])
+                                      (5, 64, 8192, 2), (3, 12, 32768, 3), (2, 520, 16, 1), (2, 4, 65536, 2)])
 def test_ring_weak_vs_oracle(R, P, pb, C):
     """Weak SignalIncs: same bytes, signals and counters; the litmus may see
     reorders (allowed), never a missing message at the full count."""
