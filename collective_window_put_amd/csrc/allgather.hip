@@ -8,8 +8,8 @@
 // completing source s's relay applies one SignalInc at every rank, so each
 // rank's signal rises by R. The last R workgroups of the grid are the
 // receivers' waits. Measured on 16 ranks x 64 MiB: 4 KiB tiles 3.35 ms,
-// 8 KiB 3.43 ms, 16 KiB 3.48 ms. When every source splits into a multiple of
-// 64 pieces of 1 KiB, the piece form below runs instead.
+// 8 KiB 3.43 ms, 16 KiB 3.48 ms. From 64 KiB per source up (16-byte
+// aligned), the piece form below runs instead.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -76,8 +76,9 @@ __device__ void ag_litmus(const AGArgs& a, uint32_t R, uint32_t d) {
   litmus_report(a.lit, a.err, checks, bad);
 }
 
-// Piece form, used when the offsets are 16-byte aligned and each source
-// splits into a multiple of 64 pieces of kPiece bytes. Workgroup b takes
+// Piece form, used when the offsets and the size are 16-byte aligned and
+// each source holds at least 64 pieces of kPiece bytes (the last may be
+// partial). Workgroup b takes
 // piece b mod (pieces per source) of source b div (pieces per source), so a
 // source's pieces are consecutive in the grid and at any time the chip
 // writes one narrow band of each receive window. Wave 0 loads the piece
@@ -95,6 +96,7 @@ __device__ void ag_piece(const AGArgs& a, uint32_t R, uint32_t b) {
   const uint32_t pps = a.pieces;
   const uint32_t s = b / pps;
   const uint64_t off = (uint64_t)(b % pps) * kPiece;
+  const uint32_t n = static_cast<uint32_t>(std::min<uint64_t>(kPiece, a.bytes - off));  // a multiple of 16
   __shared__ v4u buf[kPiece / 16];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -103,21 +105,26 @@ __device__ void ag_piece(const AGArgs& a, uint32_t R, uint32_t b) {
   char* dst[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) dst[j] = w + 4 * j < R ? a.recv.p[w + 4 * j] : nullptr;
-  if (w == 0) buf[lane] = load16_stream(reinterpret_cast<const v4u*>(a.send.p[s] + a.send_off + off) + lane);
+  if (w == 0 && lane * 16u < n)
+    buf[lane] = load16_stream(reinterpret_cast<const v4u*>(a.send.p[s] + a.send_off + off) + lane);
   __syncthreads();
   const v4u v = buf[lane];
   const uint64_t doff = a.recv_off + (uint64_t)s * a.bytes + off;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (w + 4 * j < R) store16_agent(rsrc(dst[j] + doff, kPiece), lane * 16u, v);
+  for (int j = 0; j < kPer; ++j)  // lanes past a partial last piece fall outside the descriptor: dropped
+    if (w + 4 * j < R) store16_agent(rsrc(dst[j] + doff, n), lane * 16u, v);
   wg_stores_complete();
   if (threadIdx.x == 0) {
-    // counters of one source sit R apart, so those hit together are spread
-    const uint32_t x = b & 7u, k = (b >> 3) & (kPieceFan - 1);
-    const bool last =
-        relay_arrive(a.relay + (9 * R + (x * kPieceFan + k) * R + s) * a.rstride, pps / (8 * kPieceFan), false) &&
-        relay_arrive(a.relay + (R + x * R + s) * a.rstride, kPieceFan, false) &&
-        relay_arrive(a.relay + s * a.rstride, 8, false);
+    // counters of one source sit R apart, so those hit together are spread.
+    // First level: the source's pieces b with b mod 8F = 8k + x (F =
+    // kPieceFan); with 64 pieces or more every (x, k) has at least one.
+    const uint32_t x = b & 7u, k = (b >> 3) & (kPieceFan - 1), r = 8 * k + x, m = 8 * kPieceFan;
+    const uint32_t lo = s * pps, hi = lo + pps;
+    auto upto = [&](uint32_t e) { return e > r ? (e - 1 - r) / m + 1 : 0u; };  // b < e with b mod m = r
+    const bool last = relay_arrive(a.relay + (9 * R + (x * kPieceFan + k) * R + s) * a.rstride, upto(hi) - upto(lo),
+                                   false) &&
+                      relay_arrive(a.relay + (R + x * R + s) * a.rstride, kPieceFan, false) &&
+                      relay_arrive(a.relay + s * a.rstride, 8, false);
     if (last) {
       if (a.lit) litmus_record(a.lit_last + s, off);
       for (uint32_t d = 0; d < R; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
@@ -204,9 +211,9 @@ vrResult_t launch_allgather(vrComm* c, const vrWindow* send, size_t send_off, co
   a.lit_seed = c->lit_seed++;
   a.R = R;
   const bool aligned = ((send_off | recv_off | bytes) & 15) == 0;
-  const uint64_t pieces = bytes / kPiece;
-  // (an empty AllGather keeps the tile form, whose one empty tile per source still signals)
-  const bool piece = aligned && bytes > 0 && bytes % (64ull * kPiece) == 0 && pieces * R <= 0x7FFFFFFFull;
+  const uint64_t pieces = (bytes + kPiece - 1) / kPiece;
+  // at least 64 pieces per source, so every first-level relay counter has one
+  const bool piece = aligned && pieces >= 64 && pieces * R <= 0x7FFFFFFFull;
   a.pieces = piece ? static_cast<uint32_t>(pieces) : 0;
   a.nwg = piece ? a.pieces * R : a.tiles * R;
   // [R] per source, then (piece form) [8][R] per (XCD, source) and

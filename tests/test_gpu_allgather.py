@@ -97,9 +97,9 @@ def test_allgather_copy_engine_vs_oracle(R, M, send_off, recv_off):
 
 @pytest.mark.parametrize("R,M", [(16, 2 << 20), (8, (4 << 20) + 3 * 4096), (4, 8 << 20)])
 def test_allgather_whole_tiles_twice(R, M):
-    # Shapes of whole 4 KiB tiles, 512 to 2051 tiles per source (R=8 is not
-    # a multiple of 64 KiB, so it runs the tile form; the others the piece
-    # form); two calls in a row check that every relay counter comes back to 0.
+    # Shapes of whole 4 KiB tiles, 512 to 2051 tiles per source (all of them
+    # run the piece form, 1 KiB pieces); two calls in a row check that every
+    # relay counter comes back to 0.
     say(f"allgather whole tiles twice R={R} M={M}")
     sends = W.allgather_inputs(R, M, seed=R + M)
     exp = D.allgather(sends)
@@ -118,12 +118,15 @@ def test_allgather_whole_tiles_twice(R, M):
 
 @pytest.mark.parametrize("R,M,send_off,recv_off", [(1, 64 << 10, 0, 0), (2, 128 << 10, 16, 4096), (3, 5 * (64 << 10), 0, 16),
                                                    (5, 3 * (64 << 10), 4096, 0), (8, 1 << 20, 0, 0),
-                                                   (16, 64 << 10, 32, 48), (64, 64 << 10, 0, 0)])
+                                                   (16, 64 << 10, 32, 48), (64, 64 << 10, 0, 0),
+                                                   (3, (64 << 10) + 16, 0, 16), (16, 100000, 16, 32),
+                                                   (5, (2 << 20) + 1024 + 48, 4096, 0), (7, 200000 - 16 * 3, 0, 0)])
 def test_allgather_piece_form(R, M, send_off, recv_off):
-    # Sizes that are a multiple of 64 KiB with 16-byte aligned offsets run the
+    # 16-byte aligned sizes of 64 KiB or more with aligned offsets run the
     # piece form (1 KiB of one source per workgroup, wave w storing to ranks
-    # w, w + 4, ...; 64 pieces per source at least, one per first-level relay
-    # counter). Twice in a row: the relay counters come back to 0.
+    # w, w + 4, ...; 64 pieces per source at least, so every first-level relay
+    # counter has one); the last four end in a partial piece, so the counters
+    # take unequal arrivals. Twice in a row: the counters come back to 0.
     say(f"allgather piece form R={R} M={M} offsets {send_off},{recv_off}")
     sends = W.allgather_inputs(R, M, seed=R * 7 + M)
     exp = D.allgather(sends)

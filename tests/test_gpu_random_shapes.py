@@ -165,10 +165,10 @@ def test_random_allreduce_full_tiles(R, N, dtype, so, ro):
 
 
 def _ag_piece_case(i):
-    # AllGather sizes of the piece form: non-zero multiples of 64 KiB with
-    # 16-byte aligned offsets, any rank count up to 24
+    # AllGather sizes of the piece form: 16-byte multiples of at least 64 KiB
+    # with 16-byte aligned offsets, any rank count up to 24
     R = int(_rng.integers(1, 25))
-    M = (64 << 10) * int(_rng.integers(1, 9))
+    M = 16 * int(_rng.integers(4096, 40000))
     return R, M, 16 * int(_rng.integers(0, 300)), 16 * int(_rng.integers(0, 300))
 
 
