@@ -100,19 +100,23 @@ __device__ void ag_piece(const AGArgs& a, uint32_t R, uint32_t b) {
   __shared__ v4u buf[kPiece / 16];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // this wave's receive pointers, read before the barrier: read inside the
-  // store loop, each store waited for its pointer's load
+  // this wave's store addresses, computed before the barrier: with the
+  // pointer (or offset) loads inside the store loop, each store waited for
+  // one (measured 3.16 against 3.06 ms at 16 x 64 MiB)
+  const uint64_t doff = a.recv_off + (uint64_t)s * a.bytes + off;
   char* dst[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) dst[j] = w + 4 * j < R ? a.recv.p[w + 4 * j] : nullptr;
+  for (int j = 0; j < kPer; ++j) {
+    dst[j] = w + 4 * j < R ? a.recv.p[w + 4 * j] + doff : nullptr;
+    asm volatile("" : "+s"(dst[j]));  // keeps the address computed here, above the barrier
+  }
   if (w == 0 && lane * 16u < n)
     buf[lane] = load16_stream(reinterpret_cast<const v4u*>(a.send.p[s] + a.send_off + off) + lane);
   __syncthreads();
   const v4u v = buf[lane];
-  const uint64_t doff = a.recv_off + (uint64_t)s * a.bytes + off;
 #pragma unroll
   for (int j = 0; j < kPer; ++j)  // lanes past a partial last piece fall outside the descriptor: dropped
-    if (w + 4 * j < R) store16_agent(rsrc(dst[j] + doff, n), lane * 16u, v);
+    if (w + 4 * j < R) store16_agent(rsrc(dst[j], n), lane * 16u, v);
   wg_stores_complete();
   if (threadIdx.x == 0) {
     // counters of one source sit R apart, so those hit together are spread.

@@ -11,7 +11,7 @@
 // acc = x_0, then acc += x_r for r = 1..R-1, each an IEEE binary32 addition
 // rounded to nearest even -- converts, and stores the tile into every rank's
 // receive window (the puts of the all-gather). Ragged or unaligned shapes
-// run one tile per workgroup; evenly tiled ones with R = 2, 4 or 8 run the
+// run one tile per workgroup; large aligned ones with R = 2, 4 or 8 run the
 // rank-split form below (one piece per workgroup, ranks split across its
 // waves, the sum through LDS), and the remaining large evenly tiled ones the
 // looping form (a fixed grid striding over slabs, loads two slabs ahead).
@@ -231,7 +231,9 @@ __device__ void ar_litmus(const ARArgs& a, uint32_t R, uint32_t d) {
   for (uint32_t c = 0; c < R; ++c) {
     const uint64_t cbeg = (uint64_t)c * a.csz, cend = std::min<uint64_t>(a.count, cbeg + a.csz);
     if (cbeg >= cend) continue;  // an empty chunk
-    const uint64_t p0 = load_relaxed_u64(a.lit_last + c);
+    uint64_t p0 = load_relaxed_u64(a.lit_last + c);
+    // an empty tile or piece past the data may complete the relay: check the chunk's last tile then
+    if (p0 >= cend && p0 < cbeg + a.csz) p0 = std::max<uint64_t>(cbeg, cend >= tile ? cend - tile : 0);
     if (p0 < cbeg || p0 >= cend) {
       if (tid == 0) ++checks, ++bad;
       continue;
@@ -328,9 +330,10 @@ __device__ void persistent_tiles(const ARArgs& a, uint32_t b) {
   if (threadIdx.x == 0) chunk_done(a, RT, c, x, n, kU, piece);
 }
 
-// Rank-split form, used when every tile is full and 16-byte aligned, R is 2,
-// 4 or 8, there are at least 8192 tiles, and each chunk's pieces split
-// evenly over the relay counters.
+// Rank-split form, used when the offsets are 16-byte aligned, R is 2, 4 or
+// 8, there are at least 8192 tiles, and each chunk's pieces split evenly
+// over the relay counters. The piece holding the end of the vector is summed
+// element by element; pieces past it move nothing but still join the relay.
 // Workgroup w takes piece w: 512/R vectors of every rank (1 KiB per rank for
 // R = 8), 512 vectors in all, rank-major. Each wave loads two 64-vector runs
 // of it (each within one rank, so the rank's window pointer is a scalar) into
@@ -345,6 +348,25 @@ __device__ void persistent_tiles(const ARArgs& a, uint32_t b) {
 // levels ((chunk, XCD), then chunk) took 0.411 ms: 2048 arrivals on each
 // first-level counter queue behind each other, so the first level is spread
 // over kSplitFan counters per (chunk, XCD).
+// Piece w's stores are done in every wave: three relay levels, (chunk, XCD,
+// k) with k = (w / 8) mod kSplitFan, then (chunk, XCD), then chunk; the
+// pieces of a chunk split evenly over them. The workgroup completing a chunk
+// applies one SignalInc at every rank.
+template <int RT>
+__device__ inline void split_done(const ARArgs& a, uint32_t w, uint64_t start) {
+  wg_stores_complete();
+  if (threadIdx.x != 0) return;
+  const uint32_t c = w / a.ppc, x = w & 7u, k = (w >> 3) & (kSplitFan - 1);
+  const bool last =
+      relay_arrive(a.relay + (9 * RT + (c * 8 + x) * kSplitFan + k) * a.rstride, a.ppc / (8 * kSplitFan), false) &&
+      relay_arrive(a.relay + (RT + c * 8 + x) * a.rstride, kSplitFan, false) &&
+      relay_arrive(a.relay + c * a.rstride, 8, false);
+  if (last) {
+    if (a.lit) litmus_record(a.lit_last + c, start);
+    for (uint32_t d = 0; d < RT; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
+  }
+}
+
 template <int DT, int RT>
 __device__ void split_piece(const ARArgs& a, uint32_t w) {
   using E = Elem<DT>;
@@ -356,6 +378,22 @@ __device__ void split_piece(const ARArgs& a, uint32_t w) {
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint64_t start = (uint64_t)w * pe;
+  if (start + pe > a.count) {
+    // the piece holding the end of the vector (element by element, rank
+    // order) or one past it (nothing to move); it still joins the relay
+    const uint32_t nbytes = static_cast<uint32_t>(pe * E::kSize);
+    for (uint64_t k = start + tid; k < a.count; k += 256) {
+      const uint64_t sb = a.send_off + k * E::kSize;
+      float acc = E::load1(a.send.p[0] + sb);
+#pragma unroll
+      for (int r = 1; r < RT; ++r) acc = acc + E::load1(a.send.p[r] + sb);
+      const uint32_t off = static_cast<uint32_t>((k - start) * E::kSize);
+#pragma unroll
+      for (int d = 0; d < RT; ++d) E::store1(rsrc(a.recv.p[d] + a.recv_off + start * E::kSize, nbytes), off, acc);
+    }
+    split_done<RT>(a, w, start);
+    return;
+  }
   v4u x[2];
   char* dst[2];  // read before the barriers, so the stores need not wait for them
 #pragma unroll
@@ -395,20 +433,7 @@ __device__ void split_piece(const ARArgs& a, uint32_t w) {
     const __amdgpu_buffer_rsrc_t rd = rsrc(dst[u] + a.recv_off + start * E::kSize, V * 16u);
     store16_agent_stream(rd, (q % V + lane) * 16u, total[q % V + lane]);
   }
-  wg_stores_complete();
-  if (tid == 0) {
-    // three relay levels: (chunk, XCD, k) with k = (w / 8) mod kSplitFan,
-    // then (chunk, XCD), then chunk; the pieces of a chunk split evenly
-    const uint32_t c = w / a.ppc, x = w & 7u, k = (w >> 3) & (kSplitFan - 1);
-    const bool last =
-        relay_arrive(a.relay + (9 * RT + (c * 8 + x) * kSplitFan + k) * a.rstride, a.ppc / (8 * kSplitFan), false) &&
-        relay_arrive(a.relay + (RT + c * 8 + x) * a.rstride, kSplitFan, false) &&
-        relay_arrive(a.relay + c * a.rstride, 8, false);
-    if (last) {
-      if (a.lit) litmus_record(a.lit_last + c, start);
-      for (uint32_t d = 0; d < RT; ++d) atomic_add_u64(a.sig + (size_t)d * a.sig_stride, 1ull);
-    }
-  }
+  split_done<RT>(a, w, start);
 }
 
 template <int DT, int RT, bool ALIGNED, int FORM>
@@ -514,9 +539,9 @@ vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, co
   a.lit_seed = c->lit_seed++;
   a.R = R;
   a.wait = wait;
-  // rank-split form: every tile full (count = R * csz), aligned, R = 2, 4 or
-  // 8, at least 8192 tiles, and each chunk's R * tpc pieces (a tile is R
-  // pieces) a multiple of the 8 * kSplitFan first-level relay counters.
+  // rank-split form: aligned offsets, R = 2, 4 or 8, at least 8192 tiles,
+  // and each chunk's R * tpc pieces (a tile is R pieces) a multiple of the
+  // 8 * kSplitFan first-level relay counters (the count need not fill them).
   // Looping form: every tile full, aligned, a rank count with a compiled
   // kernel (2, 4, 8, 16), the tiles splitting evenly over the XCDs, and at
   // least two tiles per looping workgroup. Smaller shapes run one tile per
@@ -526,7 +551,7 @@ vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, co
   const bool full = aligned && (R == 2 || R == 4 || R == 8 || R == 16) && count == (uint64_t)R * a.csz;
   int form = kOneTile;
   a.ppc = 0;
-  if (full && R <= 8 && nwork % (8 * kSplitFan) == 0 && nwork >= 2 * kLoopWorkgroups &&
+  if (aligned && (R == 2 || R == 4 || R == 8) && nwork % (8 * kSplitFan) == 0 && nwork >= 2 * kLoopWorkgroups &&
       (uint64_t)nwork * R <= 0x7FFFFFFFull) {
     form = kSplit;
     a.ppc = nwork;  // pieces per chunk: tpc tiles of R pieces

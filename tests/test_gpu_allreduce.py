@@ -147,6 +147,20 @@ def _tile(dtype):
     return 2048 if dtype == "f32" else 4096  # elements of a tile (8 KiB per rank)
 
 
+def _form(dtype, R, N, send_off=0, recv_off=0):
+    """The kernel form the library picks (its launch rule, restated)."""
+    tile = _tile(dtype)
+    per = -(-N // R)
+    tpc = max(1, -(-per // tile))
+    nwork = R * tpc
+    aligned = (send_off | recv_off) % 16 == 0
+    if aligned and R in (2, 4, 8) and nwork % 64 == 0 and nwork >= 8192:
+        return "split"
+    if aligned and R in (2, 4, 8, 16) and N == R * tpc * tile and nwork % 8 == 0 and nwork >= 8192:
+        return "loop"
+    return "tile"
+
+
 @pytest.mark.parametrize("dtype,R,tpc", [("bf16", 2, 32), ("bf16", 4, 16), ("bf16", 8, 8), ("f32", 4, 48),
                                          ("f32", 8, 24), ("bf16", 8, 72), ("f32", 2, 96)])
 def test_allreduce_full_tiles_below_the_large_forms(dtype, R, tpc):
@@ -182,3 +196,31 @@ def test_allreduce_looping_form(dtype, R, tpc):
         assert np.array_equal(out[d][:N * es], exp), d
         assert np.all(out[d][N * es:] == 0xCD)
     assert sigs == [2 * R] * R
+
+
+@pytest.mark.parametrize("dtype,R,N,off", [("bf16", 8, (64 << 20) - 3, 0), ("f32", 4, (16 << 20) - 1000, 16),
+                                         ("bf16", 2, 2 * 4096 * 4096 - 3 * 2048 - 7, 4096),
+                                         ("f32", 8, (16 << 20) - 4 * 256 - 5, 0)])
+def test_allreduce_rank_split_form_ragged(dtype, R, N, off):
+    # Counts that do not fill the last chunk: the piece holding the end is
+    # summed element by element, the pieces past it (up to a few whole tiles'
+    # worth) move nothing but still complete the relay. Two calls in a row.
+    assert _form(dtype, R, N, off, off) == "split"
+    say(f"allreduce rank-split form ragged {dtype} R={R} N={N} off={off}")
+    xs = W.allreduce_f32_inputs(R, N, seed=R + N) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + N)
+    es = 4 if dtype == "f32" else 2
+    exp = D.allreduce(xs, dtype).view(np.uint8)
+    out, sigs = _run(xs, dtype, send_off=off, recv_off=off, repeats=2)
+    for d in range(R):
+        assert np.array_equal(out[d][off:off + N * es], exp), d
+        assert np.all(out[d][:off] == 0xCD) and np.all(out[d][off + N * es:] == 0xCD)
+    assert sigs == [2 * R] * R
+
+
+def test_allreduce_form_rule_covers_the_tested_shapes():
+    # every form is exercised by the shapes above (the rule restated in _form)
+    assert _form("bf16", 8, 64 << 20) == "split"
+    assert _form("bf16", 16, 16 * 513 * 4096) == "loop"
+    assert _form("f32", 4, 4 * 2050 * 2048) == "loop"
+    assert _form("f32", 4, 1 << 20) == "tile"
+    assert _form("bf16", 8, 64 << 20, 8, 0) == "tile"
