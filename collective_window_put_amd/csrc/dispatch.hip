@@ -70,6 +70,9 @@ struct DispArgs {
   int32_t* eblk;         // dedup: [R][NB1][Eo] entries per expert of each count block
   int32_t* ecw;          // dedup: [R][Eo] entries per expert of each source
   int Eo, epro;          // dedup: keys are destination ranks (E = R); Eo experts, epro per rank
+  uint64_t epro_mul;     // ceil(2^32 / epro): e / epro as a multiply (see div_by)
+  uint64_t epr_mul;      // ceil(2^32 / (E / R)), for the keys' rank
+  int kbits;             // bits holding every key value up to E (dedup: rank or the non-key E)
   int wave_tokens;       // 64 % K == 0: a wave's 64 entries hold whole tokens
   int gbits;             // bits naming a token within a wave: 2^gbits >= ceil(64 / K)
   int nbits_o;           // dedup: bits of an expert id
@@ -108,6 +111,13 @@ __device__ inline void stamp(const DispArgs& a, int phase) {
   }
 }
 
+// n / d for 0 <= n < 2^16 and 1 <= d <= 2^16, with mul = ceil(2^32 / d)
+// computed on the host: exact, since n * (mul * d - 2^32) < n * d <= 2^32.
+// (A 32-bit division by a runtime value expands to some twenty instructions.)
+__device__ inline int32_t div_by(int32_t n, uint64_t mul) {
+  return static_cast<int32_t>((static_cast<uint64_t>(static_cast<uint32_t>(n)) * mul) >> 32);
+}
+
 __device__ inline int32_t load_topk(const DispArgs& a, int s, int t, int k) {
   return a.topk[((size_t)s * a.T + t) * a.K + k];
 }
@@ -122,26 +132,27 @@ __device__ inline int32_t entry_key(const DispArgs& a, int s, int t, int k) {
   const int32_t e = load_topk(a, s, t, k);
   if (!DEDUP || e == -1) return e;
   if (e < 0 || e >= a.Eo) return a.E;
-  const int32_t d = e / a.epro;
+  const int32_t d = div_by(e, a.epro_mul);
   for (int q = 0; q < k; ++q) {
     const int32_t f = load_topk(a, s, t, q);
-    if (f >= 0 && f < a.Eo && f / a.epro == d) return -1;
+    if (f >= 0 && f < a.Eo && div_by(f, a.epro_mul) == d) return -1;
   }
   return d;
 }
 
-// Dedup key of an entry whose token's entries sit in neighbouring lanes of
-// this wave (`group` < 2^gbits names the token within the wave): the
-// destination rank if no lower lane of the same token names that rank, -1
-// for such a later entry and for unrouted ones; ids outside [-1, E) map to
-// the out-of-range key a.E, which the callers flag and skip. All lanes of
-// the wave call it.
+// Dedup key of an entry whose token's K entries sit in lanes [group*K,
+// group*K + K) of this wave: the destination rank if no lower lane of the
+// same token names that rank, -1 for such a later entry and for unrouted
+// ones; ids outside [-1, E) map to the out-of-range key a.E, which the
+// callers flag and skip. The rank is matched over the wave (kbits ballots)
+// and the match then kept to the token's lanes; matching (token, rank) over
+// the wave took gbits + 8 ballots. All lanes of the wave call it.
 __device__ inline int32_t dedup_rep(const DispArgs& a, int32_t e, int group, bool active) {
-  const int32_t d = (e >= 0 && e < a.Eo) ? e / a.epro : (e == -1 ? -1 : a.E);
+  const int32_t d = (e >= 0 && e < a.Eo) ? div_by(e, a.epro_mul) : (e == -1 ? -1 : a.E);
   const bool cand = active && d >= 0 && d < a.E;
-  // (token, rank) in gbits + 7 bits (ranks < 128); non-candidates share the value above them all
-  const uint32_t key = cand ? static_cast<uint32_t>((group << 7) | d) : (1u << (a.gbits + 7));
-  const uint64_t m = match_any(key, a.gbits + 8);
+  const uint32_t key = cand ? static_cast<uint32_t>(d) : static_cast<uint32_t>(a.E);  // non-candidates: no rank
+  const uint64_t token = a.K >= 64 ? ~0ull : (((1ull << a.K) - 1ull) << (group * a.K));
+  const uint64_t m = match_any(key, a.kbits) & token;
   const uint64_t lt = (1ull << lane_id()) - 1ull;
   if (!active) return -1;
   return cand ? ((m & lt) == 0 ? d : -1) : d;
@@ -238,24 +249,35 @@ __device__ void count_block(const DispArgs& a, int32_t* lds, int* last_flag, int
   // wave instruction with ballots)
   const int lane = tid & 63;
   const int iters = (ntok * a.K + kThreads - 1) / kThreads;
+  // entry i = step * kThreads + tid is (token i / K, k = i % K); both advance
+  // by a fixed amount per step, so no division by K inside the loop
+  const int sq = kThreads / a.K, sr = kThreads - sq * a.K;
+  int cq = tid / a.K, cr = tid - cq * a.K;  // for step 0
+  const int group = lane / a.K;             // the token's place in the wave (K divides 64 when used)
   for (int it0 = 0; it0 < iters; it0 += 8) {  // 8 loads in flight per thread, then the adds
-    int ev[8];
+    int ev[8], tq[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = (it0 + u) * kThreads + tid;
       const bool in = it0 + u < iters && i < ntok * a.K;
+      tq[u] = cq;
       // dedup with whole tokens per wave: the raw id now, the key below; otherwise the key now
-      ev[u] = in ? ((DEDUP && a.wave_tokens) ? load_topk(a, s, t0 + i / a.K, i % a.K)
-                                             : entry_key<DEDUP>(a, s, t0 + i / a.K, i % a.K))
+      ev[u] = in ? ((DEDUP && a.wave_tokens) ? load_topk(a, s, t0 + cq, cr) : entry_key<DEDUP>(a, s, t0 + cq, cr))
                  : -1;
+      cq += sq;
+      cr += sr;
+      if (cr >= a.K) {
+        cr -= a.K;
+        ++cq;
+      }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (it0 + u >= iters) break;
       const int i = (it0 + u) * kThreads + tid;
-      const int tl = i / a.K;
+      const int tl = tq[u];
       int e = ev[u];
-      if (DEDUP && a.wave_tokens) e = dedup_rep(a, e, (i / a.K) & ((64 / a.K) - 1), i < ntok * a.K);
+      if (DEDUP && a.wave_tokens) e = dedup_rep(a, e, group, i < ntok * a.K);
       if (e != -1 && (e < 0 || e >= E)) atomic_or_u32(a.err, VR_ASYNC_BAD_EXPERT);
       if (e >= 0 && e < E) {
         const int key = (tl / kSub) * E + e;
@@ -522,13 +544,13 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     }
     const int32_t pos = base[e] + dpos[slot];
     dpos[slot] = pos;
-    const int d = e / epr;
+    const int d = div_by(e, a.epr_mul);
     const bool kept = (uint64_t)pos < a.cap;
     if (DEDUP && kept) {  // the row's entries as rank d sees them (an output: plain stores)
       int32_t* xo = a.experts_out + ((size_t)d * a.cap + pos) * K;
       auto local = [&](int k) {
         const int32_t f = dorig[tlb * K + k];
-        return (f >= 0 && f < a.Eo && f / a.epro == d) ? f - d * a.epro : -1;
+        return (f >= 0 && f < a.Eo && div_by(f, a.epro_mul) == d) ? f - d * a.epro : -1;
       };
       if (a.xo_vec) {
         for (int k = 0; k < K; k += 4)
@@ -746,6 +768,7 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   // dedup: the layout's keys are the destination ranks (E = R, one per rank)
   a.Eo = E;
   a.epro = E / R;
+  a.epro_mul = ((1ull << 32) + a.epro - 1) / a.epro;
   a.experts_out = experts_out;
   a.ecounts_out = dedup ? counts_out : nullptr;
   a.wave_tokens = 64 % K == 0;
@@ -802,6 +825,10 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
   int nb = 1;
   while ((1 << nb) < E) ++nb;
   a.nbits = nb;
+  int kb = 1;
+  while ((1 << kb) <= E) ++kb;
+  a.kbits = kb;  // values 0..E
+  a.epr_mul = ((1ull << 32) + E / R - 1) / (E / R);
   // copy path: one buffer resource over all receive slices when they fit a 4 GiB span
   char* lo = recv->base[0] + recv_off;
   char* hi = lo + cap * row_bytes;
