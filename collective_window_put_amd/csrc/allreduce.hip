@@ -11,8 +11,8 @@
 // acc = x_0, then acc += x_r for r = 1..R-1, each an IEEE binary32 addition
 // rounded to nearest even -- converts, and stores the tile into every rank's
 // receive window (the puts of the all-gather). Ragged or unaligned shapes
-// run one tile per workgroup; large aligned ones with R = 2, 4 or 8 run the
-// rank-split form below (one piece per workgroup, ranks split across its
+// run one tile per workgroup; large aligned ones with R = 2, 4, 8 or 16 run
+// the rank-split form below (one piece per workgroup, ranks split across its
 // waves, the sum through LDS), and the remaining large evenly tiled ones the
 // looping form (a fixed grid striding over slabs, loads two slabs ahead).
 // The workgroup completing a chunk's relay applies one SignalInc at every
@@ -330,18 +330,19 @@ __device__ void persistent_tiles(const ARArgs& a, uint32_t b) {
   if (threadIdx.x == 0) chunk_done(a, RT, c, x, n, kU, piece);
 }
 
-// Rank-split form, used when the offsets are 16-byte aligned, R is 2, 4 or
-// 8, there are at least 8192 tiles, and each chunk's pieces split evenly
+// Rank-split form, used when the offsets are 16-byte aligned, R is 2, 4, 8
+// or 16, there are at least 8192 tiles, and each chunk's pieces split evenly
 // over the relay counters. The piece holding the end of the vector is summed
 // element by element; pieces past it move nothing but still join the relay.
-// Workgroup w takes piece w: 512/R vectors of every rank (1 KiB per rank for
-// R = 8), 512 vectors in all, rank-major. Each wave loads two 64-vector runs
-// of it (each within one rank, so the rank's window pointer is a scalar) into
-// LDS; after a barrier every thread sums 32-bit words across the ranks in
-// rank order; after another, each wave stores the same two runs' positions of
-// the sum to their ranks. So each thread issues two loads and two stores, and
-// the workgroup ends; pieces run in grid order, so at any time the chip reads
-// and writes one narrow band of each rank's slice. Measured back to back at
+// Workgroup w takes piece w: max(512/R, 64) vectors of every rank (1 KiB per
+// rank for R = 8 and 16), rank-major. Each wave loads two (four for R = 16)
+// 64-vector runs of it (each within one rank, so the rank's window pointer is
+// a scalar) into LDS; after a barrier every thread sums 32-bit words across
+// the ranks in rank order; after another, each wave stores the same runs'
+// positions of the sum to their ranks. So each thread issues two loads and
+// two stores (four for R = 16), and the workgroup ends; pieces run in grid
+// order, so at any time the chip reads and writes one narrow band of each
+// rank's slice. Measured back to back at
 // 8 ranks x 64 Mi bf16 in a stand-alone copy of the data path: 0.341 ms
 // without the relay, 0.348 ms with it, against 0.389 ms for one tile per
 // workgroup with eight loads and eight stores per thread. A relay of two
@@ -370,7 +371,8 @@ __device__ inline void split_done(const ARArgs& a, uint32_t w, uint64_t start) {
 template <int DT, int RT>
 __device__ void split_piece(const ARArgs& a, uint32_t w) {
   using E = Elem<DT>;
-  constexpr uint32_t V = 512 / RT;  // vectors per rank in a piece
+  constexpr uint32_t V = RT <= 8 ? 512 / RT : 64;  // vectors per rank in a piece
+  constexpr int kRuns = RT * V / 256;               // 64-vector runs per wave: 2, or 4 for R = 16
   static_assert(V % 64 == 0, "a 64-lane run must lie within one rank");
   constexpr uint64_t pe = (uint64_t)V * E::kPerVec;  // elements per piece
   __shared__ v4u part[RT * V];  // rank-major
@@ -394,17 +396,17 @@ __device__ void split_piece(const ARArgs& a, uint32_t w) {
     split_done<RT>(a, w, start);
     return;
   }
-  v4u x[2];
-  char* dst[2];  // read before the barriers, so the stores need not wait for them
+  v4u x[kRuns];
+  char* dst[kRuns];  // read before the barriers, so the stores need not wait for them
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const uint32_t q = (2 * wave + u) * 64;  // first rank-major vector of the run
+  for (int u = 0; u < kRuns; ++u) {
+    const uint32_t q = (kRuns * wave + u) * 64;  // first rank-major vector of the run
     const char* src = a.send.p[q / V] + a.send_off + start * E::kSize;
     x[u] = load16_stream(reinterpret_cast<const v4u*>(src + (q % V + lane) * 16u));
     dst[u] = a.recv.p[q / V];
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) part[(2 * wave + u) * 64 + lane] = x[u];
+  for (int u = 0; u < kRuns; ++u) part[(kRuns * wave + u) * 64 + lane] = x[u];
   __syncthreads();
   const uint32_t* p32 = reinterpret_cast<const uint32_t*>(part);
   uint32_t* t32 = reinterpret_cast<uint32_t*>(total);
@@ -428,8 +430,8 @@ __device__ void split_piece(const ARArgs& a, uint32_t w) {
   }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const uint32_t q = (2 * wave + u) * 64;
+  for (int u = 0; u < kRuns; ++u) {
+    const uint32_t q = (kRuns * wave + u) * 64;
     const __amdgpu_buffer_rsrc_t rd = rsrc(dst[u] + a.recv_off + start * E::kSize, V * 16u);
     store16_agent_stream(rd, (q % V + lane) * 16u, total[q % V + lane]);
   }
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(256) void k_allreduce(const ARArgs a) {
     return;
   }
   if constexpr (FORM == kSplit) {
-    static_assert(RT != 0 && RT <= 8 && ALIGNED, "the rank-split form needs R <= 8, compiled, and aligned tiles");
+    static_assert(RT != 0 && RT <= 16 && ALIGNED, "the rank-split form needs R <= 16, compiled, and aligned tiles");
     split_piece<DT, RT>(a, b);
     return;
   }
@@ -484,10 +486,8 @@ void launch_t(const ARArgs& a, uint32_t grid, hipStream_t st) {
 
 template <int DT, int RT>
 void launch_r(const ARArgs& a, int form, uint32_t grid, hipStream_t st) {
-  if constexpr (RT <= 8) {
-    if (form == kSplit) return launch_t<DT, RT, true, kSplit>(a, grid, st);
-  }
-  if (form == kLoop) launch_t<DT, RT, true, kLoop>(a, grid, st);
+  if (form == kSplit) launch_t<DT, RT, true, kSplit>(a, grid, st);
+  else if (form == kLoop) launch_t<DT, RT, true, kLoop>(a, grid, st);
   else launch_t<DT, RT, true, kOneTile>(a, grid, st);
 }
 
@@ -539,9 +539,10 @@ vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, co
   a.lit_seed = c->lit_seed++;
   a.R = R;
   a.wait = wait;
-  // rank-split form: aligned offsets, R = 2, 4 or 8, at least 8192 tiles,
-  // and each chunk's R * tpc pieces (a tile is R pieces) a multiple of the
-  // 8 * kSplitFan first-level relay counters (the count need not fill them).
+  // rank-split form: aligned offsets, R = 2, 4, 8 or 16, at least 8192
+  // tiles, and each chunk's pieces (a tile is min(R, 8) pieces) a multiple
+  // of the 8 * kSplitFan first-level relay counters (the count need not
+  // fill them).
   // Looping form: every tile full, aligned, a rank count with a compiled
   // kernel (2, 4, 8, 16), the tiles splitting evenly over the XCDs, and at
   // least two tiles per looping workgroup. Smaller shapes run one tile per
@@ -551,11 +552,12 @@ vrResult_t launch_allreduce(vrComm* c, const vrWindow* send, size_t send_off, co
   const bool full = aligned && (R == 2 || R == 4 || R == 8 || R == 16) && count == (uint64_t)R * a.csz;
   int form = kOneTile;
   a.ppc = 0;
-  if (aligned && (R == 2 || R == 4 || R == 8) && nwork % (8 * kSplitFan) == 0 && nwork >= 2 * kLoopWorkgroups &&
-      (uint64_t)nwork * R <= 0x7FFFFFFFull) {
+  const uint32_t ppt = std::min(R, 8);  // rank-split pieces per tile
+  if (aligned && (R == 2 || R == 4 || R == 8 || R == 16) && (a.tpc * ppt) % (8 * kSplitFan) == 0 &&
+      nwork >= 2 * kLoopWorkgroups && (uint64_t)a.tpc * ppt * R <= 0x7FFFFFFFull) {
     form = kSplit;
-    a.ppc = nwork;  // pieces per chunk: tpc tiles of R pieces
-    a.nwg = nwork * R;
+    a.ppc = a.tpc * ppt;  // pieces per chunk
+    a.nwg = a.ppc * R;
   } else if (full && (nwork & 7u) == 0 && nwork >= 2 * kLoopWorkgroups) {
     form = kLoop;
     a.nwg = kLoopWorkgroups;

@@ -124,14 +124,16 @@ def test_allreduce_bf16_r8_64Mi_full_size():
 
 
 @pytest.mark.parametrize("dtype,R,N", [("f32", 4, 16 << 20), ("bf16", 2, 48 << 20), ("f32", 8, 16 << 20),
-                                     ("bf16", 4, 32 << 20), ("f32", 2, 2 * 4096 * 2048)])
+                                     ("bf16", 4, 32 << 20), ("f32", 2, 2 * 4096 * 2048), ("bf16", 16, 32 << 20),
+                                     ("f32", 16, 16 * 520 * 2048)])
 def test_allreduce_rank_split_form(dtype, R, N):
-    # Evenly tiled shapes of at least 8192 tiles with R <= 8 whose chunk
-    # splits into a multiple of 64 pieces run the rank-split form (one piece
-    # of 512/R vectors per rank per workgroup, three relay levels); a piece is
-    # 4 KiB per rank for R=2, and the last shape is the smallest that
-    # qualifies. Two calls in a row check that the relay counters come back
-    # to 0.
+    # Evenly tiled shapes of at least 8192 tiles whose chunk splits into a
+    # multiple of 64 pieces run the rank-split form (one piece of
+    # max(512/R, 64) vectors per rank per workgroup, three relay levels); a
+    # piece is 4 KiB per rank for R=2, R=16 takes four runs per wave, and the
+    # fifth shape is the smallest that qualifies. Two calls in a row check
+    # that the relay counters come back to 0.
+    assert _form(dtype, R, N) == "split"
     say(f"allreduce rank-split form {dtype} R={R} N={N}")
     xs = W.allreduce_f32_inputs(R, N, seed=R + 11) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + 11)
     es = 4 if dtype == "f32" else 2
@@ -154,7 +156,7 @@ def _form(dtype, R, N, send_off=0, recv_off=0):
     tpc = max(1, -(-per // tile))
     nwork = R * tpc
     aligned = (send_off | recv_off) % 16 == 0
-    if aligned and R in (2, 4, 8) and nwork % 64 == 0 and nwork >= 8192:
+    if aligned and R in (2, 4, 8, 16) and (tpc * min(R, 8)) % 64 == 0 and nwork >= 8192:
         return "split"
     if aligned and R in (2, 4, 8, 16) and N == R * tpc * tile and nwork % 8 == 0 and nwork >= 8192:
         return "loop"
@@ -179,14 +181,16 @@ def test_allreduce_full_tiles_below_the_large_forms(dtype, R, tpc):
     assert sigs == [3 * R] * R
 
 
-@pytest.mark.parametrize("dtype,R,tpc", [("bf16", 16, 512), ("bf16", 16, 513), ("f32", 4, 2050)])
+@pytest.mark.parametrize("dtype,R,tpc", [("f32", 16, 514), ("bf16", 16, 513), ("f32", 4, 2050)])
 def test_allreduce_looping_form(dtype, R, tpc):
     # Evenly tiled shapes with at least 8192 tiles that split over the 8 XCDs
-    # run the looping form (4096 workgroups, each taking several slabs of its
-    # XCD's range) when R = 16, or when R <= 8 and a chunk's R * tpc pieces
-    # are not a multiple of 64. R=16 crosses an owner chunk inside a
-    # workgroup's loop, R=4 spreads one chunk over two XCDs. Two calls in a row check that the relay counters come back to 0.
+    # but whose chunks do not split into a multiple of 64 pieces run the
+    # looping form (4096 workgroups, each taking several slabs of its XCD's
+    # range). R=16 crosses an owner chunk inside a workgroup's loop, R=4
+    # spreads one chunk over two XCDs. Two calls in a row check that the
+    # relay counters come back to 0.
     N = R * tpc * _tile(dtype)
+    assert _form(dtype, R, N) == "loop"
     say(f"allreduce looping form {dtype} R={R} N={N}")
     xs = W.allreduce_f32_inputs(R, N, seed=R + 13) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + 13)
     es = 4 if dtype == "f32" else 2
@@ -200,7 +204,8 @@ def test_allreduce_looping_form(dtype, R, tpc):
 
 @pytest.mark.parametrize("dtype,R,N,off", [("bf16", 8, (64 << 20) - 3, 0), ("f32", 4, (16 << 20) - 1000, 16),
                                          ("bf16", 2, 2 * 4096 * 4096 - 3 * 2048 - 7, 4096),
-                                         ("f32", 8, (16 << 20) - 4 * 256 - 5, 0)])
+                                         ("f32", 8, (16 << 20) - 4 * 256 - 5, 0),
+                                         ("bf16", 16, (32 << 20) - 3 * 512 - 1, 32)])
 def test_allreduce_rank_split_form_ragged(dtype, R, N, off):
     # Counts that do not fill the last chunk: the piece holding the end is
     # summed element by element, the pieces past it (up to a few whole tiles'
@@ -221,6 +226,7 @@ def test_allreduce_form_rule_covers_the_tested_shapes():
     # every form is exercised by the shapes above (the rule restated in _form)
     assert _form("bf16", 8, 64 << 20) == "split"
     assert _form("bf16", 16, 16 * 513 * 4096) == "loop"
+    assert _form("bf16", 16, 32 << 20) == "split"
     assert _form("f32", 4, 4 * 2050 * 2048) == "loop"
     assert _form("f32", 4, 1 << 20) == "tile"
     assert _form("bf16", 8, 64 << 20, 8, 0) == "tile"
