@@ -116,11 +116,12 @@ def test_allgather_whole_tiles_twice(R, M):
     assert sigs == [2 * R] * R
 
 
-@pytest.mark.parametrize("R,M,send_off,recv_off", [(1, 64 << 10, 0, 0), (2, 128 << 10, 16, 4096), (3, 5 * (64 << 10), 0, 16),
-                                                   (5, 3 * (64 << 10), 4096, 0), (8, 1 << 20, 0, 0),
-                                                   (16, 64 << 10, 32, 48), (64, 64 << 10, 0, 0),
-                                                   (3, (64 << 10) + 16, 0, 16), (16, 100000, 16, 32),
-                                                   (5, (2 << 20) + 1024 + 48, 4096, 0), (7, 200000 - 16 * 3, 0, 0)])
+PIECE_CASES = [(1, 64 << 10, 0, 0), (2, 128 << 10, 16, 4096), (3, 5 * (64 << 10), 0, 16), (5, 3 * (64 << 10), 4096, 0),
+               (8, 1 << 20, 0, 0), (16, 64 << 10, 32, 48), (64, 64 << 10, 0, 0), (3, (64 << 10) + 16, 0, 16),
+               (16, 100000, 16, 32), (5, (2 << 20) + 1024 + 48, 4096, 0), (7, 200000 - 16 * 3, 0, 0)]
+
+
+@pytest.mark.parametrize("R,M,send_off,recv_off", PIECE_CASES)
 def test_allgather_piece_form(R, M, send_off, recv_off):
     # 16-byte aligned sizes of 64 KiB or more with aligned offsets run the
     # piece form (1 KiB of one source per workgroup, wave w storing to ranks
