@@ -123,7 +123,8 @@ def test_litmus_allgather_r16_64MiB():
 # -- small, ragged and unaligned shapes: litmus on, results still the oracle's -------------
 @pytest.mark.parametrize("dtype,R,N,off", [("f32", 3, 1001, 0), ("bf16", 8, 2048 * 8 + 3, 0), ("f32", 4, 3000, 12),
                                            ("bf16", 16, 40000, 0), ("bf16", 8, 8 * 4096 * 16, 0), ("f32", 64, 900, 4),
-                                           ("bf16", 2, 4 * 4096 + 1, 0), ("f32", 4, (16 << 20) - 1000, 16)])
+                                           ("bf16", 2, 4 * 4096 + 1, 0), ("f32", 4, (16 << 20) - 1000, 16),
+                                           ("bf16", 16, (32 << 20) - 5, 0)])
 def test_litmus_allreduce_shapes(dtype, R, N, off):
     es = 4 if dtype == "f32" else 2
     xs = W.allreduce_f32_inputs(R, N, seed=R + N) if dtype == "f32" else W.allreduce_bf16_inputs(R, N, seed=R + N)
