@@ -78,10 +78,10 @@ __device__ void ag_litmus(const AGArgs& a, uint32_t R, uint32_t d) {
 
 // Piece form, used when the offsets and the size are 16-byte aligned and
 // each source holds at least 64 pieces of kPiece bytes (the last may be
-// partial). Workgroup b takes
-// piece b mod (pieces per source) of source b div (pieces per source), so a
-// source's pieces are consecutive in the grid and at any time the chip
-// writes one narrow band of each receive window. Wave 0 loads the piece
+// partial). Workgroup b takes piece b mod (pieces per source) of source
+// b div (pieces per source), so a source's pieces are consecutive in the
+// grid and at any time the chip writes one narrow band of each receive
+// window. Wave 0 loads the piece
 // (64 lanes x 16 bytes) into LDS; after a barrier wave w stores it to ranks
 // w, w + 4, ...: four stores per thread for R = 16, and 16 KiB written per
 // workgroup. Measured stand-alone at 16 ranks x 64 MiB, back to back on one
