@@ -169,7 +169,7 @@ def test_litmus_alltoall_shapes(R, B, soff, roff):
 
 @pytest.mark.parametrize("R,M,soff,roff", [(3, 16385, 0, 0), (16, 32768 + 16, 0, 0), (4, 20000, 7, 4099),
                                            (2, 1, 0, 0), (64, 5000, 0, 0), (8, 256 << 10, 16, 4096),
-                                           (16, 64 << 10, 0, 0)])
+                                           (16, 64 << 10, 0, 0), (5, 200000 - 48, 16, 32)])
 def test_litmus_allgather_shapes(R, M, soff, roff):
     sends = W.allgather_inputs(R, M, seed=R * 3 + M)
     with Job(R) as job:
