@@ -32,11 +32,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTokPerWave = 8;
 constexpr int kTok = kWaves * kTokPerWave;  // tokens per workgroup
-// Row loads per batch (two batches in flight per lane). 4: 70 VGPRs, 6
-// waves per SIMD; 8: 105 VGPRs, 4 waves. Measured flushed, alternating on
-// one machine: combine 34.1-34.4 us against 34.5-34.9 us, per-rank combine
-// 22.1-22.2 us against 22.7 us.
-constexpr int kBatch = 4;
+constexpr int kLoads = 8;                   // row loads in flight per lane: one batch of a token's entries
 
 struct CombArgs {
   WinTab y;
@@ -54,6 +50,9 @@ struct CombArgs {
   uint64_t timeout_ns;
   int R, T, K, E, nblk;
   int dedup;  // entries are destination ranks (k = d), weight 1, no topk or weights
+  int lpr;        // 16-byte path: lanes per row (a power of two, at most 64)
+  int staged;     // 16-byte path: output rows staged in LDS, stored per column chunk
+  uint32_t wt_off, stage_off;  // byte offsets of the weights and the staging rows in dynamic LDS
 };
 
 template <int DT> struct CElem;
@@ -97,68 +96,14 @@ template <> struct CElem<VR_DT_BF16> {
   }
 };
 
-// One lane group's walk over (token, batch-of-kBatch-entries) items for one
-// 16-byte column: load() issues an item's row loads, mix() folds them into
-// the accumulator in k order and, after a token's last batch, stores the
-// token's output column and clears the accumulator.
-template <int DT>
-struct Mixer {
-  const char* const* src;
-  const float* wt;
-  char* out;
-  int t0, tl0, rpi, K, nb, col;
-  uint64_t rb;
-  __device__ __forceinline__ int token(int it) const { return tl0 + (it / nb) * rpi; }
-  __device__ __forceinline__ void reset(float (&acc)[CElem<DT>::kPerVec]) const {
-#pragma unroll
-    for (int j = 0; j < CElem<DT>::kPerVec; ++j) acc[j] = 0.0f;
-  }
-  // returns the mask of entries that have a row
-  __device__ __forceinline__ uint32_t load(int it, v4u (&v)[kBatch]) const {
-    const int tl = token(it), k0 = (it % nb) * kBatch;
-    // entries without a row issue no load (the lanes are masked off);
-    // mix() drops them by a select
-    const char* p[kBatch];
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) p[q] = k0 + q < K ? src[tl * K + k0 + q] : nullptr;
-    uint32_t m = 0;
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      m |= p[q] ? 1u << q : 0u;
-      v[q] = p[q] ? load16_stream_global(p[q] + col * 16) : v4u{0, 0, 0, 0};
-    }
-    return m;
-  }
-  __device__ __forceinline__ void mix(int it, const v4u (&v)[kBatch], uint32_t m,
-                                      float (&acc)[CElem<DT>::kPerVec]) const {
-    using EL = CElem<DT>;
-    const int tl = token(it), kb = it % nb, k0 = kb * kBatch;
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      const float w = k0 + q < K ? wt[tl * K + k0 + q] : 0.0f;
-      float f[EL::kPerVec];
-      EL::widen(v[q], f);
-#pragma unroll
-      for (int j = 0; j < EL::kPerVec; ++j) {
-        const float sum = acc[j] + w * f[j];
-        acc[j] = (m >> q) & 1u ? sum : acc[j];
-      }
-    }
-    if (kb == nb - 1) {
-      store16_agent_stream(rsrc(out + (uint64_t)(t0 + tl) * rb, static_cast<uint32_t>(rb)), col * 16,
-                           EL::narrow(acc));
-      reset(acc);
-    }
-  }
-};
-
 // VEC: 16-byte lanes (row_bytes and both offsets multiples of 16); otherwise
 // one element per lane.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_combine(const CombArgs a) {
   using EL = CElem<DT>;
-  __shared__ const char* src[kTok * 64];  // row address of each entry (nullptr: no row)
-  __shared__ float wt[kTok * 64];
+  extern __shared__ __align__(16) char smem[];
+  const char** src = reinterpret_cast<const char**>(smem);  // [kTok][K] row address of each entry (nullptr: no row)
+  float* wt = reinterpret_cast<float*>(smem + a.wt_off);    // [kTok][K]
   __shared__ int last;
   const int R = a.R, K = a.K;
   const int nwork = R * a.nblk;
@@ -213,31 +158,63 @@ __global__ __launch_bounds__(kThreads) void k_combine(const CombArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   char* out = a.out_base[s] + a.out_off;
   if (VEC) {
+    // A lane group of lpr lanes takes one column chunk (lpr 16-byte vectors)
+    // of a token's row; the wave's rpi = 64 / lpr groups take its tokens in
+    // turn. Per token: its entries' rows in batches of kLoads loads in flight,
+    // mixed in k order, the output vector staged in LDS; after each chunk the
+    // workgroup stores the staged rows together (contiguous runs of the
+    // output), or, where a buffer descriptor cannot span the workgroup's rows,
+    // each group stores its own vector. Measured at 8 ranks x 4096 tokens,
+    // 512-byte rows, K = 8 (flushed, alternating on one machine): 31.2-31.3
+    // us against 34.6-34.8 us with two batches of four loads in flight and
+    // each vector stored as soon as it was mixed; per-rank combine 20.7-20.8
+    // against 22.1-22.2 us. A stand-alone probe put the gather alone at
+    // 25.4 us and its stores, unstaged, at +5 us.
     const int nv = static_cast<int>(rb >> 4);
-    int lpr = 1;
-    while (lpr < nv && lpr < 64) lpr <<= 1;
-    const int rpi = 64 / lpr;
+    const int lpr = a.lpr, rpi = 64 / lpr;
     const int l = lane & (lpr - 1), grp = lane / lpr;
-    const int nb = (K + kBatch - 1) / kBatch;  // load batches per token
+    v4u* stage = reinterpret_cast<v4u*>(smem + a.stage_off);  // [kTok][lpr]
     for (int c0 = 0; c0 < nv; c0 += lpr) {
       const int col = c0 + l;
-      // this lane group's tokens: ti = grp, grp + rpi, ... (within the wave's share)
-      int ntl = 0;
-      for (int ti = grp; ti < kTokPerWave && wave * kTokPerWave + ti < ntok; ti += rpi) ++ntl;
-      const int items = col < nv ? ntl * nb : 0;  // (token, batch) pairs, in order
-      // two register buffers: the loads of item i+1 are in flight while item i is mixed
-      float acc[CElem<DT>::kPerVec];
-      v4u va[kBatch], vb[kBatch];
-      uint32_t ma = 0, mb = 0;
-      Mixer<DT> mx{src, wt, out, t0, wave * kTokPerWave + grp, rpi, K, nb, col, rb};
-      mx.reset(acc);
-      if (items > 0) ma = mx.load(0, va);
-      for (int it = 0; it < items; it += 2) {
-        if (it + 1 < items) mb = mx.load(it + 1, vb);
-        mx.mix(it, va, ma, acc);
-        if (it + 1 >= items) break;
-        if (it + 2 < items) ma = mx.load(it + 2, va);
-        mx.mix(it + 1, vb, mb, acc);
+      for (int ti = grp; ti < kTokPerWave && col < nv; ti += rpi) {
+        const int tl = wave * kTokPerWave + ti;
+        if (tl >= ntok) break;
+        float acc[EL::kPerVec];
+#pragma unroll
+        for (int j = 0; j < EL::kPerVec; ++j) acc[j] = 0.0f;
+        for (int k0 = 0; k0 < K; k0 += kLoads) {
+          v4u v[kLoads];
+#pragma unroll
+          for (int q = 0; q < kLoads; ++q) {
+            const char* p = k0 + q < K ? src[tl * K + k0 + q] : nullptr;
+            v[q] = p ? load16_stream_global(p + col * 16) : v4u{0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int q = 0; q < kLoads; ++q) {
+            if (k0 + q < K && src[tl * K + k0 + q]) {  // entries without a row are skipped
+              const float w = wt[tl * K + k0 + q];
+              float f[EL::kPerVec];
+              EL::widen(v[q], f);
+#pragma unroll
+              for (int j = 0; j < EL::kPerVec; ++j) acc[j] = acc[j] + w * f[j];
+            }
+          }
+        }
+        if (a.staged) stage[tl * lpr + l] = EL::narrow(acc);
+        else store16_agent(rsrc(out + (uint64_t)(t0 + tl) * rb, static_cast<uint32_t>(rb)), col * 16, EL::narrow(acc));
+      }
+      if (a.staged) {
+        __syncthreads();
+        if (ntok > 0) {
+          const int w16 = min(lpr, nv - c0);  // vectors of this chunk
+          const __amdgpu_buffer_rsrc_t ro =
+              rsrc(out + (uint64_t)t0 * rb + (uint64_t)c0 * 16, static_cast<uint32_t>((ntok - 1) * rb + w16 * 16));
+          for (int i = tid; i < ntok * lpr; i += kThreads) {
+            const int tl = i / lpr, l2 = i & (lpr - 1);
+            if (l2 < w16) store16_agent(ro, static_cast<uint32_t>(tl * rb + l2 * 16), stage[i]);
+          }
+        }
+        __syncthreads();  // the stage is rewritten by the next chunk
       }
     }
   } else {
@@ -254,16 +231,18 @@ __global__ __launch_bounds__(kThreads) void k_combine(const CombArgs a) {
       }
     }
   }
-  wg_stores_complete();
+  // the signal says that the rows have been read: every row load has
+  // returned (its value is in the output), so no wait for the stores
+  __syncthreads();
   if (tid == 0) last = relay_arrive(a.relay + s * a.rstride, a.nblk, false);
   __syncthreads();
   if (last && tid < R) atomic_add_u64(a.sig + (size_t)tid * a.sig_stride, 1ull);  // SignalInc at each rank
 }
 
 template <int DT>
-void launch_dt(const CombArgs& a, bool vec, int grid, hipStream_t st) {
-  if (vec) hipLaunchKernelGGL((k_combine<DT, true>), dim3(grid), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((k_combine<DT, false>), dim3(grid), dim3(kThreads), 0, st, a);
+void launch_dt(const CombArgs& a, bool vec, int grid, uint32_t lds, hipStream_t st) {
+  if (vec) hipLaunchKernelGGL((k_combine<DT, true>), dim3(grid), dim3(kThreads), lds, st, a);
+  else hipLaunchKernelGGL((k_combine<DT, false>), dim3(grid), dim3(kThreads), lds, st, a);
 }
 
 }  // namespace
@@ -299,9 +278,17 @@ vrResult_t launch_combine(vrComm* c, const vrWindow* y, size_t y_off, size_t cap
   a.dedup = dedup ? 1 : 0;
   a.nblk = std::max(1, (T + kTok - 1) / kTok);
   const bool vec = row_bytes % 16 == 0 && y_off % 16 == 0 && out_off % 16 == 0;
+  const uint64_t nv = row_bytes / 16;
+  a.lpr = 1;
+  while (a.lpr < 64 && (uint64_t)a.lpr < nv) a.lpr <<= 1;
+  // staging: one descriptor spans the workgroup's kTok rows of a chunk
+  a.staged = vec && (uint64_t)(kTok - 1) * row_bytes + 16ull * a.lpr <= 0xFFFFFFFFull;
+  a.wt_off = static_cast<uint32_t>(kTok * K * sizeof(const char*));
+  a.stage_off = (a.wt_off + kTok * K * sizeof(float) + 15) & ~15u;
+  const uint32_t lds = a.stage_off + (a.staged ? kTok * a.lpr * 16u : 0u);  // at most 56 KiB (K <= 64)
   const int grid = R * a.nblk + (wait ? R : 0);
-  if (dtype == VR_DT_F32) launch_dt<VR_DT_F32>(a, vec, grid, st);
-  else launch_dt<VR_DT_BF16>(a, vec, grid, st);
+  if (dtype == VR_DT_F32) launch_dt<VR_DT_F32>(a, vec, grid, lds, st);
+  else launch_dt<VR_DT_BF16>(a, vec, grid, lds, st);
   return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;
 }
 

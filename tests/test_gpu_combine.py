@@ -115,6 +115,19 @@ def test_combine_element_path_unaligned(H, dtype, y_off, out_off):
     _check(res, topk, weights, y, E, dtype)
 
 
+def test_combine_rows_too_long_to_stage():
+    # rows of 140,000,000 bytes: the 32 rows of a workgroup span more than a
+    # 32-bit buffer range, so each lane group stores its own output vectors
+    # instead of staging the rows in LDS
+    R, T, E, K, H = 2, 2, 2, 1, 70_000_000
+    say(f"combine rows of {2 * H} bytes R={R} T={T} E={E} K={K}")
+    topk, weights, y = _inputs(R, T, 8, E, K, 11)
+    y = W.expert_outputs(D.dispatch_rows_per_rank(topk, E), H, seed=61)
+    res = _run(topk, weights, y, E, H)
+    _check(res, topk, weights, y, E)
+    assert res["err"][0] == vr.VR_OK
+
+
 def test_combine_zero_tokens():
     R, E, K, H = 4, 8, 2, 8
     topk = np.zeros((R, 0, K), np.int32)
