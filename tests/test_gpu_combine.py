@@ -78,7 +78,10 @@ def _check(res, topk, weights, y, E, dtype="bf16", repeats=1, tokens=None):
     (2, 5, 8, 4, 2, 0, "bf16"), (4, 37, 16, 16, 3, 1, "bf16"), (3, 130, 8, 6, 2, 2, "f32"),
     (8, 64, 256, 256, 8, 3, "bf16"), (5, 1, 8, 10, 1, 4, "bf16"), (4, 100, 64, 32, 4, 5, "f32"),
     (8, 200, 136, 64, 8, 6, "bf16"), (4, 70, 1024, 16, 2, 7, "bf16"), (4, 300, 8, 1024, 64, 8, "bf16"),
-    (64, 40, 8, 128, 4, 9, "bf16")])
+    (64, 40, 8, 128, 4, 9, "bf16"),
+    # K = 12 and 10: a full and a partial batch of row loads; 137 and 68
+    # vectors per row: chunks of 64 lanes with a partial last one
+    (4, 45, 1096, 16, 12, 12, "bf16"), (3, 70, 272, 12, 10, 13, "f32")])
 def test_combine_vs_oracle(R, T, H, E, K, seed, dtype):
     say(f"combine R={R} T={T} H={H} E={E} K={K} {dtype}")
     topk, weights, y = _inputs(R, T, H, E, K, seed, dtype)
