@@ -322,18 +322,35 @@ struct CeCopy {
   const char* src;
   size_t bytes;
 };
+// The internal streams and events, created on first use: all of them or
+// none (a partial set would be indexed past its end by the next call).
+static vrResult_t ce_setup(vrComm* c) {
+  hipStream_t ss[VR_CE_STREAMS];
+  hipEvent_t es[VR_CE_STREAMS + 1];
+  int nss = 0, nes = 0;
+  while (nss < VR_CE_STREAMS && hipStreamCreateWithFlags(&ss[nss], hipStreamNonBlocking) == hipSuccess) ++nss;
+  while (nss == VR_CE_STREAMS && nes <= VR_CE_STREAMS && hipEventCreateWithFlags(&es[nes], hipEventDisableTiming) == hipSuccess)
+    ++nes;
+  const bool ok = nss == VR_CE_STREAMS && nes == VR_CE_STREAMS + 1;
+  if (ok) {
+    try {
+      c->ce_streams.assign(ss, ss + nss);
+      c->ce_events.assign(es, es + nes);
+      return VR_OK;
+    } catch (...) {
+      c->ce_streams.clear();
+      c->ce_events.clear();
+    }
+  }
+  for (int i = 0; i < nss; ++i) (void)hipStreamDestroy(ss[i]);
+  for (int i = 0; i < nes; ++i) (void)hipEventDestroy(es[i]);
+  return ok ? VR_ERR_OUT_OF_RESOURCES : VR_ERR_HIP;
+}
+
 vrResult_t ce_puts(vrComm* c, const std::vector<CeCopy>& ops, hipStream_t st) {
   if (c->ce_streams.empty()) {
-    for (int i = 0; i < VR_CE_STREAMS; ++i) {
-      hipStream_t s;
-      if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return VR_ERR_HIP;
-      c->ce_streams.push_back(s);
-    }
-    for (int i = 0; i <= VR_CE_STREAMS; ++i) {
-      hipEvent_t e;
-      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return VR_ERR_HIP;
-      c->ce_events.push_back(e);
-    }
+    const vrResult_t r = ce_setup(c);
+    if (r != VR_OK) return r;
   }
   const int n = std::min<int>(VR_CE_STREAMS, std::max<int>(1, (int)ops.size()));
   if (hipEventRecord(c->ce_events[0], st) != hipSuccess) return VR_ERR_HIP;
@@ -465,16 +482,20 @@ vrResult_t vr_comm_create(int nranks, const vrCommRequirements* req, void* works
   c->ring_bases = reinterpret_cast<uint64_t*>(c->ws + l.ring);
   c->ring_gens = c->ring_bases + (size_t)nranks * req->context_count;
   c->ring_gen = 0;
-  c->bar_expect.assign(req->barrier_count, 0);
   c->scratch = nullptr;
   c->scratch_bytes = 0;
   const size_t ns = (size_t)nranks * req->signal_count;
-  c->expect.assign(ns, 0);
-  c->expect_known.assign(ns, 1);
-  c->sig_mode.assign(ns, 0);
-  {
+  try {  // host tables: a failed allocation is an error code, never an exception through the C ABI
+    c->bar_expect.assign(req->barrier_count, 0);
+    c->expect.assign(ns, 0);
+    c->expect_known.assign(ns, 1);
+    c->sig_mode.assign(ns, 0);
     std::lock_guard<std::mutex> g(g_mu);
     g_comms.insert(c);
+  } catch (...) {
+    if (c->owns_ws) (void)hipFree(c->ws);
+    delete c;
+    return VR_ERR_OUT_OF_RESOURCES;
   }
   *out = c;
   return VR_OK;
@@ -557,7 +578,12 @@ vrResult_t vr_window_register(vrComm_t c, void* const* bases, size_t bytes, uint
   w->flags = flags;
   w->nranks = R;
   for (int r = 0; r < VR_MAX_RANKS; ++r) w->base[r] = r < R ? static_cast<char*>(bases[r]) : nullptr;
-  c->windows.insert(w);
+  try {
+    c->windows.insert(w);
+  } catch (...) {
+    delete w;
+    return VR_ERR_OUT_OF_RESOURCES;
+  }
   *out = w;
   return VR_OK;
 }
@@ -642,7 +668,11 @@ static vrResult_t va_prepare(vrComm* c, vrWindow* w, int rank, size_t off) {
   if (!live(c) || !rank_ok(c, rank)) return VR_ERR_INVALID_ARGUMENT;
   vrResult_t r = check_va_word(c, w, off);
   if (r != VR_OK) return r;
-  w->va_words.emplace(std::make_pair(rank, (uint64_t)off), 0);  // a signal from now on
+  try {
+    w->va_words.emplace(std::make_pair(rank, (uint64_t)off), 0);  // a signal from now on
+  } catch (...) {
+    return VR_ERR_OUT_OF_RESOURCES;
+  }
   return VR_OK;
 }
 
@@ -817,6 +847,11 @@ vrResult_t vr_alltoall(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t 
   if (r != VR_OK) return r;
   if (flags & VR_COLL_COPY_ENGINE) {
     std::vector<CeCopy> ops;
+    try {
+      ops.reserve((size_t)R * R);  // the pushes below then cannot throw
+    } catch (...) {
+      return VR_ERR_OUT_OF_RESOURCES;
+    }
     for (int s = 0; s < R; ++s)  // destination-major, so consecutive copies target different ranks
       for (int d = 0; d < R; ++d)
         ops.push_back({recv->base[(d + s) % R] + recv_off + (size_t)s * block,
@@ -889,6 +924,11 @@ vrResult_t vr_allgather(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t
   if (r != VR_OK) return r;
   if (flags & VR_COLL_COPY_ENGINE) {
     std::vector<CeCopy> ops;
+    try {
+      ops.reserve((size_t)R * R);  // the pushes below then cannot throw
+    } catch (...) {
+      return VR_ERR_OUT_OF_RESOURCES;
+    }
     for (int s = 0; s < R; ++s)
       for (int d = 0; d < R; ++d)
         ops.push_back({recv->base[(d + s) % R] + recv_off + (size_t)s * bytes, send->base[s] + send_off, bytes});
