@@ -19,18 +19,29 @@ from ctypes import POINTER, Structure, c_char_p, c_int, c_size_t, c_uint32, c_ui
 
 __all__ = [
     "VrError", "VrLibraryMissing", "LIB_PATH", "lib", "SYMBOLS",
+    # result codes, flags and limits (values as in include/vrcomm.h)
     "VR_OK", "VR_ERR_INVALID_ARGUMENT", "VR_ERR_INVALID_USAGE", "VR_ERR_OUT_OF_RESOURCES",
     "VR_ERR_HIP", "VR_ERR_TIMEOUT", "VR_ERR_UNSUPPORTED_DEVICE", "VR_ERR_INTERNAL", "VR_ERR_DEVICE_CHECK",
-    "VR_DT_F32", "VR_DT_BF16", "VR_OP_SUM", "VR_COLL_NO_WAIT", "VR_MAX_RANKS",
+    "VR_MAX_RANKS", "VR_SIGNAL_BITS", "VR_COUNTER_BITS", "VR_WIN_DEFAULT", "VR_WIN_COLL_SYMMETRIC", "VR_WIN_STRICT_ORDERING", "VR_WIN_REQUIRED_ALIGNMENT",
+    "VR_ACTION_NONE", "VR_SIGNAL_INC", "VR_SIGNAL_ADD", "VR_COUNTER_INC", "VR_VA_SIGNAL_INC", "VR_VA_SIGNAL_ADD",
+    "VR_DT_F32", "VR_DT_BF16", "VR_OP_SUM", "VR_COLL_NO_WAIT", "VR_COLL_COPY_ENGINE", "VR_CE_STREAMS",
+    "VR_RING_WEAK", "VR_PINGPONG_SAME_XCD", "VR_DISPATCH_NOALLOC_SCRATCH_BYTES",
+    "VR_FENCE_NONE", "VR_FENCE_PUT", "VR_FENCE_GET",
     "VR_ASYNC_TIMEOUT", "VR_ASYNC_CAPACITY", "VR_ASYNC_BAD_EXPERT", "VR_ASYNC_LITMUS",
-    "VR_WIN_DEFAULT", "VR_WIN_COLL_SYMMETRIC", "VR_WIN_STRICT_ORDERING", "VR_WIN_REQUIRED_ALIGNMENT",
-    "SignalInc", "SignalAdd", "CounterInc",
+    # argument structures and action helpers
+    "vrCommRequirements", "vrRemoteAction", "vrLocalAction", "vrDevComm", "vrDevWindow",
+    "SignalInc", "SignalAdd", "CounterInc", "VASignalInc", "VASignalAdd",
+    # entry points
     "vr_error_string", "vr_version", "vr_comm_workspace_bytes", "vr_comm_create", "vr_comm_destroy",
-    "vr_comm_get_async_error", "vr_comm_query", "vr_window_register", "vr_window_deregister",
-    "vr_put", "vr_get", "vr_signal", "vr_signal_wait", "vr_signal_read", "vr_signal_reset",
-    "vr_signal_expected", "vr_counter_wait", "vr_counter_read", "vr_counter_reset",
-    "vr_allreduce", "vr_alltoall", "vr_allgather", "vr_dispatch", "vr_combine", "vr_ring_exchange",
-    "vr_signal_pingpong", "vr_dispatch_noalloc", "vr_comm_set_litmus", "vr_comm_set_trace", "VR_DISPATCH_NOALLOC_SCRATCH_BYTES",
+    "vr_comm_get_async_error", "vr_comm_query", "vr_comm_set_litmus", "vr_comm_set_trace",
+    "vr_comm_device_view", "vr_window_register", "vr_window_deregister", "vr_window_device_view",
+    "vr_put", "vr_get", "vr_signal", "vr_signal_wait", "vr_signal_read", "vr_signal_reset", "vr_signal_expected",
+    "vr_va_signal_wait", "vr_va_signal_read", "vr_va_signal_reset",
+    "vr_counter_wait", "vr_counter_read", "vr_counter_reset",
+    "vr_barrier", "vr_barrier_advance", "vr_barrier_expected",
+    "vr_allreduce", "vr_alltoall", "vr_alltoall_sessions", "vr_allgather",
+    "vr_dispatch", "vr_dispatch_noalloc", "vr_dispatch_dedup", "vr_combine", "vr_combine_dedup",
+    "vr_ring_exchange", "vr_signal_pingpong",
 ]
 
 # The in-tree build; VRCOMM_LIB may name another build of the same library.
@@ -47,6 +58,8 @@ VR_ERR_INTERNAL = 7
 VR_ERR_DEVICE_CHECK = 8
 
 VR_MAX_RANKS = 64
+VR_SIGNAL_BITS = 64
+VR_COUNTER_BITS = 56
 VR_WIN_DEFAULT = 0x0
 VR_WIN_COLL_SYMMETRIC = 0x1
 VR_WIN_STRICT_ORDERING = 0x2

@@ -32,6 +32,23 @@ def test_header_declares_the_binding_symbols():
     assert _declared_functions() == sorted(vr.SYMBOLS)
 
 
+def test_binding_exports_every_declared_function_and_constant():
+    # each C entry point has a wrapper of the same name that the package exports
+    for name in _declared_functions():
+        assert callable(getattr(vr, name, None)), name
+        assert name in vr.__all__, name
+    # each constant the header defines has the same value in the binding, exported
+    text = open(HEADER).read()
+    defines = re.findall(r"^#define\s+(VR_[A-Z0-9_]+)\s+(\(?[0-9xXa-fA-F]+u?(?:\s*<<\s*[0-9]+)?\)?)", text, flags=re.M)
+    assert len(defines) == len(re.findall(r"^#define\s+VR_", text, flags=re.M))  # every one parsed
+    for name, expr in defines:
+        value = eval(re.sub(r"(?<=[0-9a-fA-F])u", "", expr), {"__builtins__": {}})  # literals and << only
+        assert getattr(vr, name) == value, name
+        assert name in vr.__all__, name
+    for name in vr.__all__:
+        assert hasattr(vr, name), name
+
+
 def test_library_exports_every_declared_function(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", vr.LIB_PATH], capture_output=True, text=True, check=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
