@@ -46,6 +46,21 @@ def test_ring_vs_oracle(R, P, pb, C):
     assert err[0] == vr.VR_OK
 
 
+@pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 1), (4, 6400, 16, 64), (3, 200, 32, 100), (2, 520, 16, 130)])
+@pytest.mark.parametrize("flags", [0, vr.VR_RING_WEAK])
+def test_ring_plain_waits_vs_oracle(R, P, pb, C, flags):
+    # without the litmus one wavefront per receiving rank waits, lane j on
+    # contexts j, j + 64, ...: 100 and 130 contexts take a second and third pass
+    say(f"ring plain waits R={R} P={P} pb={pb} C={C} flags={flags}")
+    sends, out, sigs, cnts, lit, err = _run(R, P, pb, C, litmus=False, repeats=2, flags=flags)
+    exp = D.ring(sends, [np.zeros(P * pb, np.uint8)] * R, P, pb)
+    for d in range(R):
+        assert np.array_equal(out[d], exp[d]), d
+    assert sigs == [[2 * (P // C)] * C] * R
+    assert cnts == [[2 * (P // C)] * C] * R
+    assert err[0] == vr.VR_OK, (vr.vr_error_string(err[0]), hex(err[1]))
+
+
 @pytest.mark.parametrize("flags", [0, vr.VR_RING_WEAK])
 def test_ring_repeated_accumulates(flags):
     # two rounds per context, three calls in a row: signals and counters

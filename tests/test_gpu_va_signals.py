@@ -114,10 +114,12 @@ def test_va_signal_wait_in_stream_and_timeout():
         assert code == vr.VR_ERR_TIMEOUT and bits & vr.VR_ASYNC_TIMEOUT
 
 
-@pytest.mark.parametrize("R,Pn,pb,C", [(3, 96, 256, 4), (4, 2048, 256, 16), (16, 4096, 256, 64)])
-def test_ring_with_va_signals_litmus(R, Pn, pb, C):
+@pytest.mark.parametrize("R,Pn,pb,C,litmus", [(3, 96, 256, 4, True), (4, 2048, 256, 16, True),
+                                              (16, 4096, 256, 64, True), (4, 2048, 256, 16, False),
+                                              (2, 400, 64, 100, False)])
+def test_ring_with_va_signals_litmus(R, Pn, pb, C, litmus):
     import torch
-    say(f"ring with VA signals R={R} P={Pn} pb={pb} C={C}")
+    say(f"ring with VA signals R={R} P={Pn} pb={pb} C={C} litmus={litmus}")
     sends = W.ring_inputs(R, Pn, pb, seed=R * 7 + Pn)
     off = 4096  # the signal words live after the messages in the receive window
     with Job(R, signal_count=1, counter_count=C, context_count=C) as job:
@@ -128,7 +130,8 @@ def test_ring_with_va_signals_litmus(R, Pn, pb, C):
         assert _code(vr.vr_ring_exchange, job.comm, sw, rw, pb, Pn, C, sig_window=rw, sig_window_off=0,
                      litmus=lit) == vr.VR_ERR_INVALID_USAGE
         gw, _ = job.window(8 * C, fill=0, flags=STRICT)
-        vr.vr_ring_exchange(job.comm, sw, rw, pb, Pn, C, cnt_base=0, sig_window=gw, sig_window_off=0, litmus=lit)
+        vr.vr_ring_exchange(job.comm, sw, rw, pb, Pn, C, cnt_base=0, sig_window=gw, sig_window_off=0,
+                            litmus=lit if litmus else None)
         out = job.host(rv)
         exp = D.ring(sends, [np.zeros(off + Pn * pb, np.uint8)] * R, Pn, pb)
         for d in range(R):
@@ -137,5 +140,5 @@ def test_ring_with_va_signals_litmus(R, Pn, pb, C):
                 assert vr.vr_va_signal_read(job.comm, gw, d, 8 * k) == Pn // C
                 assert vr.vr_counter_read(job.comm, d, k) == Pn // C
         lh = lit.cpu().numpy()
-        assert lh[1] == 0 and lh[0] > 0
+        assert lh[1] == 0 and (lh[0] > 0) == litmus
         job.assert_no_async_error()
