@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 SIG_COUNTS, SIG_ROWS, SIG_COMB = 4, 5, 6
 
 
-def _dispatch(job, topk, x, E, cap, x_off=0, recv_off=0):
+def _dispatch(job, topk, x, E, cap, x_off=0, recv_off=0, ids_offset=0):
     torch = job.torch
     R, T, K = topk.shape
     rb = x.shape[2] * x.itemsize
@@ -25,7 +25,10 @@ def _dispatch(job, topk, x, E, cap, x_off=0, recv_off=0):
     for r in range(R):
         xv[r][x_off:x_off + T * rb].copy_(torch.from_numpy(xb[r].reshape(-1)))
     rw, rv = job.window(recv_off + cap * rb, fill=0xEE)
-    tk = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).cuda()
+    # ids_offset > 0: the routing ids start that many int32 into their buffer
+    ids = torch.zeros(ids_offset + topk.size, dtype=torch.int32, device="cuda")
+    ids[ids_offset:].copy_(torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32).reshape(-1)))
+    tk = ids[ids_offset:].view(R, T, K)
     counts = torch.full((R, E // R), -7, dtype=torch.int32, device="cuda")
     src = torch.full((R, cap), -1, dtype=torch.int32, device="cuda")
     experts = torch.full((R, cap, K), -9, dtype=torch.int32, device="cuda")
@@ -87,6 +90,23 @@ def test_dedup_dispatch_capacity_and_bad_ids():
         assert any(over)
         code, bits = job.async_error()
         assert bits & vr.VR_ASYNC_CAPACITY and bits & vr.VR_ASYNC_BAD_EXPERT
+
+
+@pytest.mark.parametrize("ids_offset", [0, 1])
+def test_dedup_dispatch_bad_ids_and_id_alignment(ids_offset):
+    # K = 8: a token's ids load as two 16-byte vectors when the routing array
+    # is 16-byte aligned, one by one when it starts 4 bytes in; an id past E
+    # and one below -1 are flagged and skipped either way
+    R, T, H, E, K = 4, 70, 8, 16, 8
+    topk, x = W.dispatch_inputs(R, T, H, E, K, seed=15)
+    topk[2, 5, 3] = 99
+    topk[0, 69, 7] = -3
+    say(f"dedup dispatch bad ids, ids offset {ids_offset} int32")
+    with Job(R) as job:
+        rw, rv, counts, src, experts, pos = _dispatch(job, topk, x, E, R * T, ids_offset=ids_offset)
+        _check_dispatch(job, topk, x, E, R * T, rv, counts, src, experts, pos)
+        code, bits = job.async_error()
+        assert bits & vr.VR_ASYNC_BAD_EXPERT and not bits & vr.VR_ASYNC_CAPACITY
 
 
 def test_dedup_dispatch_unaligned_rows():
