@@ -29,7 +29,7 @@ def _run(R, P, pb, C, litmus=True, repeats=1, flags=0):
 
 @pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 2), (3, 96, 256, 4), (4, 1000, 48, 10), (16, 4096, 256, 64),
                                       (5, 64, 8192, 2), (64, 256, 16, 4), (2, 520, 16, 1), (3, 12, 32768, 3),
-                                      (4, 3000, 64, 3), (2, 4, 65536, 2)])
+                                      (4, 3000, 64, 3), (2, 4, 65536, 2), (1, 64, 16, 2)])
 def test_ring_vs_oracle(R, P, pb, C):
     # each context's workgroup issues rounds of up to 64 KiB (at most 256
     # messages) in order: (2, 520, 16, 1), (3, 12, 32768, 3) and
@@ -46,7 +46,8 @@ def test_ring_vs_oracle(R, P, pb, C):
     assert err[0] == vr.VR_OK
 
 
-@pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 1), (4, 6400, 16, 64), (3, 200, 32, 100), (2, 520, 16, 130)])
+@pytest.mark.parametrize("R,P,pb,C", [(2, 8, 16, 1), (4, 6400, 16, 64), (3, 200, 32, 100), (2, 520, 16, 130),
+                                      (1, 300, 32, 3)])
 @pytest.mark.parametrize("flags", [0, vr.VR_RING_WEAK])
 def test_ring_plain_waits_vs_oracle(R, P, pb, C, flags):
     # without the litmus one wavefront per receiving rank waits, lane j on
