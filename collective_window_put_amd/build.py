@@ -56,5 +56,29 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+NATIVE = os.path.join(ROOT, "tests", "native")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Compile tests/native/allreduce_worked_example.c, a plain C client of the
+    library (gcc, C11, the HIP runtime's C API), next to its source; it finds
+    libvrcomm.so through a path relative to itself. Returns the binary's path."""
+    src = os.path.join(NATIVE, "allreduce_worked_example.c")
+    out = os.path.join(NATIVE, "allreduce_worked_example")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I" + os.path.join(rocm, "include"), "-I" + os.path.join(ROOT, "include"), src,
+           "-L" + PKG, "-lvrcomm", "-L" + os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../collective_window_put_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed for {src}:\n{r.stderr}")
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_client(verbose=True)

@@ -134,6 +134,16 @@ __global__ void ring_once(vrDevComm c, vrDevWindow w, uint64_t block, uint64_t b
 """
 
 
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_c_client_compiles_against_the_header():
+    # the header is plain C: the C client compiles with gcc in C11 mode
+    src = os.path.join(ROOT, "tests", "native", "allreduce_worked_example.c")
+    cmd = ["gcc", "-std=c11", "-fsyntax-only", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"), src]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_device_header_compiles_in_a_user_kernel(tmp_path):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
