@@ -47,6 +47,13 @@
  *     communicator must execute in issue order: use one stream per
  *     communicator, or order the streams yourself. Operations that share a
  *     signal id must be stream-ordered.
+ *   - HIP graphs: an operation whose kernel waits in-kernel takes the
+ *     signal's target from the library's expected value when it is enqueued,
+ *     so a captured call keeps that target on every replay, and from the
+ *     second replay on its waits would find it already reached. Capture a
+ *     vr_signal_reset of the signal at every rank (a kernel, not a memset)
+ *     before the operation, so that every replay starts from 0 and waits for
+ *     exactly its own signals; or capture with VR_COLL_NO_WAIT.
  */
 #ifndef VRCOMM_H
 #define VRCOMM_H
