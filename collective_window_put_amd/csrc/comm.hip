@@ -402,7 +402,10 @@ vrResult_t ensure_scratch(vrComm* c, size_t bytes) {
   }
   void* p = nullptr;
   if (hipMalloc(&p, bytes) != hipSuccess) return VR_ERR_OUT_OF_RESOURCES;
-  if (hipMemset(p, 0, bytes) != hipSuccess) return VR_ERR_HIP;
+  if (hipMemset(p, 0, bytes) != hipSuccess) {
+    (void)hipFree(p);
+    return VR_ERR_HIP;
+  }
   c->scratch = static_cast<char*>(p);
   c->scratch_bytes = bytes;
   return VR_OK;
