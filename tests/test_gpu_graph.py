@@ -51,3 +51,51 @@ def test_allreduce_replayed_from_a_graph_with_signal_resets(dtype, R, N):
                 assert vr.vr_signal_read(job.comm, d, SIG) == R, (rep, d)
             job.assert_no_async_error()
         del graph
+
+
+def test_dispatch_noalloc_replayed_from_a_graph_with_new_routing():
+    # the allocation-free dispatch is for callers such as graph capture: its
+    # count target comes from the reset, and its row target is taken on the
+    # device from the row signal at kernel start, so every replay may route
+    # differently
+    import torch
+    R, T, H, E, K = 8, 300, 64, 64, 4
+    SIGC, SIGR = 4, 5
+    rb, cap = H * 2, R * T * K
+    say(f"dispatch_noalloc in a HIP graph R={R} T={T} E={E} K={K}, three replays with new routing")
+    with Job(R) as job:
+        xw, xv = job.window(T * rb, fill=0)
+        rw, rv = job.window(cap * rb, fill=0xEE)
+        tk = torch.zeros((R, T, K), dtype=torch.int32, device="cuda")
+        counts = torch.zeros((R, E // R), dtype=torch.int32, device="cuda")
+        src = torch.full((R, cap), -1, dtype=torch.int32, device="cuda")
+        pos = torch.full((R, T, K), -5, dtype=torch.int32, device="cuda")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+            for d in range(R):
+                vr.vr_signal_reset(job.comm, d, SIGC)
+                vr.vr_signal_reset(job.comm, d, SIGR)
+            vr.vr_dispatch_noalloc(job.comm, xw, 0, rb, tk, T, K, E, rw, 0, cap, counts, src, pos, SIGC, SIGR)
+        for rep in range(3):
+            topk, x = W.dispatch_inputs(R, T, H, E, K, seed=50 + rep)
+            for r in range(R):  # eager work between the replays: new tokens and routing, cleared outputs
+                xv[r].copy_(torch.from_numpy(np.ascontiguousarray(x[r]).reshape(-1).view(np.uint8)))
+                rv[r].fill_(0xEE)
+            tk.copy_(torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)))
+            src.fill_(-1)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            rows, tags, cnts, _ = D.dispatch(topk, x, E, cap)
+            out = job.host(rv)
+            src_h, cnt_h, pos_h = src.cpu().numpy(), counts.cpu().numpy(), pos.cpu().numpy()
+            assert np.array_equal(pos_h, D.dispatch_positions(topk, E, cap)), rep
+            for d in range(R):
+                n = rows[d].shape[0]
+                assert np.array_equal(out[d][:n * rb], rows[d].reshape(-1)), (rep, d)
+                assert np.array_equal(src_h[d, :n], tags[d]) and np.all(src_h[d, n:] == -1), (rep, d)
+                assert np.array_equal(cnt_h[d], cnts[d]), (rep, d)
+                assert vr.vr_signal_read(job.comm, d, SIGC) == R, (rep, d)
+                assert vr.vr_signal_read(job.comm, d, SIGR) == n, (rep, d)
+            job.assert_no_async_error()
+        del graph
