@@ -453,7 +453,11 @@ vrResult_t vr_dispatch(vrComm_t comm, vrWindow_t x, size_t x_off, size_t row_byt
  * scratch R*NB*E*16 + R*NB*E*4 + R*R*E*4 + R*8 + R*4 bytes (each term rounded
  * up to a multiple of 256) must not exceed VR_DISPATCH_NOALLOC_SCRATCH_BYTES
  * (R = 8, E = 256: up to 25,600 tokens per rank); larger shapes return
- * VR_ERR_INVALID_ARGUMENT before anything is enqueued. */
+ * VR_ERR_INVALID_ARGUMENT before anything is enqueued. In a replayed graph,
+ * capture a vr_signal_reset of sig_counts and of sig_rows at every rank
+ * before it: the count target then holds on every replay, and each
+ * receiver's row target is taken on the device, so every replay may route
+ * differently. */
 #define VR_DISPATCH_NOALLOC_SCRATCH_BYTES (4u << 20)
 vrResult_t vr_dispatch_noalloc(vrComm_t comm, vrWindow_t x, size_t x_off, size_t row_bytes,
                                const int32_t* topk_idx, int T, int K, int num_experts, vrWindow_t recv,
