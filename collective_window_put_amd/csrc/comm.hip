@@ -93,6 +93,14 @@ bool live(vrComm* c) {
   std::lock_guard<std::mutex> g(g_mu);
   return c && g_comms.count(c);
 }
+// A call runs with the communicator's device current: the null stream, a
+// device synchronize and a symbol lookup all resolve against the current
+// device, and a launch there would address this communicator's memory from
+// another GPU.
+bool on_device(const vrComm* c) {
+  int d = -1;
+  return hipGetDevice(&d) == hipSuccess && d == c->device;
+}
 bool has_win(vrComm* c, vrWindow* w) { return w && c->windows.count(w); }
 bool rank_ok(vrComm* c, int r) { return r >= 0 && r < c->nranks; }
 bool span_ok(const vrWindow* w, size_t off, size_t n) { return off <= w->bytes && n <= w->bytes - off; }
@@ -507,6 +515,10 @@ vrResult_t vr_comm_create(int nranks, const vrCommRequirements* req, void* works
 vrResult_t vr_comm_destroy(vrComm_t c) {
   if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
   if (!c->windows.empty()) return VR_ERR_INVALID_USAGE;
+  // any device may be current here: switch to the communicator's for the
+  // synchronize and the frees, then give the caller's back
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(c->device) != hipSuccess) return VR_ERR_HIP;
   (void)hipDeviceSynchronize();
   if (c->owns_ws) (void)hipFree(c->ws);
   if (c->scratch) (void)hipFree(c->scratch);
@@ -517,11 +529,13 @@ vrResult_t vr_comm_destroy(vrComm_t c) {
     g_comms.erase(c);
   }
   delete c;
+  (void)hipSetDevice(prev);
   return VR_OK;
 }
 
 vrResult_t vr_comm_get_async_error(vrComm_t c, vrResult_t* out, uint32_t* bits) {
   if (!live(c) || !out) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   uint32_t b = 0;
   if (hipMemcpy(&b, c->err, sizeof(b), hipMemcpyDeviceToHost) != hipSuccess) return VR_ERR_HIP;
   if (b && hipMemset(c->err, 0, sizeof(uint32_t)) != hipSuccess) return VR_ERR_HIP;
@@ -535,6 +549,7 @@ vrResult_t vr_comm_get_async_error(vrComm_t c, vrResult_t* out, uint32_t* bits) 
 
 vrResult_t vr_comm_set_litmus(vrComm_t c, uint64_t* litmus) {
   if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (litmus && !dev_span_ok(c, litmus, 2 * sizeof(uint64_t))) return VR_ERR_INVALID_ARGUMENT;
   c->litmus = litmus;
   return VR_OK;
@@ -542,6 +557,7 @@ vrResult_t vr_comm_set_litmus(vrComm_t c, uint64_t* litmus) {
 
 vrResult_t vr_comm_set_trace(vrComm_t c, uint64_t* stamps, size_t words) {
   if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (stamps && (!words || !dev_span_ok(c, stamps, words * sizeof(uint64_t)))) return VR_ERR_INVALID_ARGUMENT;
   c->trace = stamps;
   c->trace_words = stamps ? words : 0;
@@ -550,6 +566,7 @@ vrResult_t vr_comm_set_trace(vrComm_t c, uint64_t* stamps, size_t words) {
 
 vrResult_t vr_comm_query(vrComm_t c, int* nranks, vrCommRequirements* req) {
   if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (nranks) *nranks = c->nranks;
   if (req) *req = c->req;
   return VR_OK;
@@ -558,6 +575,7 @@ vrResult_t vr_comm_query(vrComm_t c, int* nranks, vrCommRequirements* req) {
 vrResult_t vr_window_register(vrComm_t c, void* const* bases, size_t bytes, uint32_t flags,
                               vrWindow_t* out) {
   if (!live(c) || !bases || !out || bytes == 0) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (flags & ~(VR_WIN_COLL_SYMMETRIC | VR_WIN_STRICT_ORDERING)) return VR_ERR_INVALID_ARGUMENT;
   *out = nullptr;
   const int R = c->nranks;
@@ -593,6 +611,7 @@ vrResult_t vr_window_register(vrComm_t c, void* const* bases, size_t bytes, uint
 
 vrResult_t vr_window_deregister(vrComm_t c, vrWindow_t w) {
   if (!live(c) || !has_win(c, w)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   (void)hipDeviceSynchronize();  // no enqueued work may still use the window
   c->windows.erase(w);
   delete w;
@@ -603,6 +622,7 @@ vrResult_t vr_put(vrComm_t c, int ctx, int rank, int peer, vrWindow_t dst, size_
                   vrWindow_t src, size_t src_off, size_t bytes, vrRemoteAction remote,
                   vrLocalAction local, void* stream) {
   if (!live(c) || !rank_ok(c, rank) || !rank_ok(c, peer)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (ctx < 0 || (uint32_t)ctx >= c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
   if (!has_win(c, dst) || !has_win(c, src)) return VR_ERR_INVALID_ARGUMENT;
   if (!span_ok(dst, dst_off, bytes) || !span_ok(src, src_off, bytes)) return VR_ERR_INVALID_ARGUMENT;
@@ -627,6 +647,7 @@ vrResult_t vr_put(vrComm_t c, int ctx, int rank, int peer, vrWindow_t dst, size_
 vrResult_t vr_get(vrComm_t c, int ctx, int rank, int peer, vrWindow_t remote, size_t remote_off,
                   vrWindow_t localw, size_t local_off, size_t bytes, vrLocalAction local, void* stream) {
   if (!live(c) || !rank_ok(c, rank) || !rank_ok(c, peer)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (ctx < 0 || (uint32_t)ctx >= c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
   if (!has_win(c, remote) || !has_win(c, localw)) return VR_ERR_INVALID_ARGUMENT;
   if (!span_ok(remote, remote_off, bytes) || !span_ok(localw, local_off, bytes)) return VR_ERR_INVALID_ARGUMENT;
@@ -641,6 +662,7 @@ vrResult_t vr_get(vrComm_t c, int ctx, int rank, int peer, vrWindow_t remote, si
 
 vrResult_t vr_signal(vrComm_t c, int ctx, int rank, int peer, vrRemoteAction remote, void* stream) {
   if (!live(c) || !rank_ok(c, rank) || !rank_ok(c, peer)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (ctx < 0 || (uint32_t)ctx >= c->req.context_count) return VR_ERR_INVALID_ARGUMENT;
   if (remote.kind == VR_ACTION_NONE) return VR_ERR_INVALID_ARGUMENT;
   vrResult_t r = check_remote(c, peer, remote);
@@ -663,12 +685,14 @@ static vrResult_t wait_word(vrComm* c, uint64_t* word, uint64_t least, int bits,
 vrResult_t vr_signal_wait(vrComm_t c, int rank, uint32_t id, uint64_t least, int bits, uint64_t timeout_ns,
                           void* stream) {
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (bits < 1 || bits > VR_SIGNAL_BITS) return VR_ERR_INVALID_ARGUMENT;
   return wait_word(c, c->sig + sidx(c, rank, id), least, bits, timeout_ns, stream);
 }
 
 static vrResult_t va_prepare(vrComm* c, vrWindow* w, int rank, size_t off) {
   if (!live(c) || !rank_ok(c, rank)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   vrResult_t r = check_va_word(c, w, off);
   if (r != VR_OK) return r;
   try {
@@ -690,6 +714,7 @@ vrResult_t vr_va_signal_wait(vrComm_t c, vrWindow_t w, int rank, size_t off, uin
 vrResult_t vr_counter_wait(vrComm_t c, int rank, uint32_t id, uint64_t least, int bits, uint64_t timeout_ns,
                            void* stream) {
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.counter_count) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (bits < 1 || bits > VR_COUNTER_BITS) return VR_ERR_INVALID_ARGUMENT;
   return wait_word(c, c->cnt + (size_t)rank * c->req.counter_count + id, least, bits, timeout_ns, stream);
 }
@@ -703,6 +728,7 @@ static vrResult_t read_word(const uint64_t* word, int bits, uint64_t* out) {
 
 vrResult_t vr_signal_read(vrComm_t c, int rank, uint32_t id, int bits, uint64_t* out) {
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count || !out) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (bits < 1 || bits > VR_SIGNAL_BITS) return VR_ERR_INVALID_ARGUMENT;
   return read_word(c->sig + sidx(c, rank, id), bits, out);
 }
@@ -725,30 +751,35 @@ vrResult_t vr_va_signal_reset(vrComm_t c, vrWindow_t w, int rank, size_t off, vo
 
 vrResult_t vr_comm_device_view(vrComm_t c, vrDevComm* out) {
   if (!live(c) || !out) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   *out = device_view(c);
   return VR_OK;
 }
 
 vrResult_t vr_window_device_view(vrComm_t c, vrWindow_t w, vrDevWindow* out) {
   if (!live(c) || !has_win(c, w) || !out) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   *out = device_view(w);
   return VR_OK;
 }
 
 vrResult_t vr_barrier_expected(vrComm_t c, uint32_t index, uint64_t* out) {
   if (!live(c) || index >= c->req.barrier_count || !out) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   *out = c->bar_expect[index];
   return VR_OK;
 }
 
 vrResult_t vr_barrier_advance(vrComm_t c, uint32_t index, uint64_t arrivals) {
   if (!live(c) || index >= c->req.barrier_count) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   c->bar_expect[index] += arrivals;
   return VR_OK;
 }
 
 vrResult_t vr_barrier(vrComm_t c, uint32_t index, uint32_t fence, uint64_t timeout_ns, void* stream) {
   if (!live(c) || index >= c->req.barrier_count) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (fence & ~(VR_FENCE_PUT | VR_FENCE_GET)) return VR_ERR_INVALID_ARGUMENT;
   const uint64_t target = c->bar_expect[index] + c->nranks;
   vrResult_t r = launch_barrier(c, index, target, fence, timeout_ns ? timeout_ns : kDefaultTimeoutNs, S(stream));
@@ -758,12 +789,14 @@ vrResult_t vr_barrier(vrComm_t c, uint32_t index, uint32_t fence, uint64_t timeo
 
 vrResult_t vr_counter_read(vrComm_t c, int rank, uint32_t id, int bits, uint64_t* out) {
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.counter_count || !out) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (bits < 1 || bits > VR_COUNTER_BITS) return VR_ERR_INVALID_ARGUMENT;
   return read_word(c->cnt + (size_t)rank * c->req.counter_count + id, bits, out);
 }
 
 vrResult_t vr_signal_reset(vrComm_t c, int rank, uint32_t id, void* stream) {
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   hipLaunchKernelGGL(k_store0, dim3(1), dim3(64), 0, S(stream), c->sig + sidx(c, rank, id));
   vrResult_t r = hip_ok(hipGetLastError());
   if (r == VR_OK) {
@@ -777,6 +810,7 @@ vrResult_t vr_signal_reset(vrComm_t c, int rank, uint32_t id, void* stream) {
 
 vrResult_t vr_counter_reset(vrComm_t c, int rank, uint32_t id, void* stream) {
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.counter_count) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   hipLaunchKernelGGL(k_store0, dim3(1), dim3(64), 0, S(stream),
                      c->cnt + (size_t)rank * c->req.counter_count + id);
   return hip_ok(hipGetLastError());
@@ -784,6 +818,7 @@ vrResult_t vr_counter_reset(vrComm_t c, int rank, uint32_t id, void* stream) {
 
 vrResult_t vr_signal_expected(vrComm_t c, int rank, uint32_t id, uint64_t* out) {
   if (!live(c) || !rank_ok(c, rank) || id >= c->req.signal_count || !out) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   const size_t i = sidx(c, rank, id);
   if (!c->expect_known[i]) return VR_ERR_INVALID_USAGE;
   *out = c->expect[i];
@@ -817,6 +852,7 @@ static void commit_inc(vrComm* c, uint32_t sig, uint64_t amount) {
 vrResult_t vr_allreduce(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
                         size_t count, int dtype, int op, uint32_t sig, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if ((dtype != VR_DT_F32 && dtype != VR_DT_BF16) || op != VR_OP_SUM) return VR_ERR_INVALID_ARGUMENT;
   if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
   const size_t es = dtype == VR_DT_F32 ? 4 : 2;
@@ -837,6 +873,7 @@ vrResult_t vr_allreduce(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t
 vrResult_t vr_alltoall(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
                        size_t block, uint32_t sig, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (flags & ~(VR_COLL_NO_WAIT | VR_COLL_COPY_ENGINE)) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (block > (size_t(1) << 40)) return VR_ERR_INVALID_ARGUMENT;
@@ -871,6 +908,7 @@ vrResult_t vr_alltoall(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t 
 vrResult_t vr_alltoall_sessions(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
                                 size_t block, uint32_t sig, uint32_t index, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (flags || index >= c->req.barrier_count) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (block > (size_t(1) << 40)) return VR_ERR_INVALID_ARGUMENT;
@@ -894,6 +932,7 @@ vrResult_t vr_alltoall_sessions(vrComm_t c, vrWindow_t send, size_t send_off, vr
 vrResult_t vr_signal_pingpong(vrComm_t c, vrWindow_t w, size_t off, size_t bytes, uint32_t iters, uint32_t sig,
                               uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, w)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (flags & ~VR_PINGPONG_SAME_XCD) return VR_ERR_INVALID_ARGUMENT;
   if (c->nranks < 2 || iters == 0 || bytes > (size_t(1) << 20)) return VR_ERR_INVALID_ARGUMENT;
   if (!span_ok(w, off, 2 * bytes)) return VR_ERR_INVALID_ARGUMENT;
@@ -914,6 +953,7 @@ vrResult_t vr_signal_pingpong(vrComm_t c, vrWindow_t w, size_t off, size_t bytes
 vrResult_t vr_allgather(vrComm_t c, vrWindow_t send, size_t send_off, vrWindow_t recv, size_t recv_off,
                         size_t bytes, uint32_t sig, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (flags & ~(VR_COLL_NO_WAIT | VR_COLL_COPY_ENGINE)) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (bytes > (size_t(1) << 40)) return VR_ERR_INVALID_ARGUMENT;
@@ -950,6 +990,7 @@ static vrResult_t dispatch_common(vrComm_t c, vrWindow_t x, size_t x_off, size_t
                                   bool dedup, uint32_t sig_counts, uint32_t sig_rows, uint32_t flags, void* stream,
                                   bool noalloc = false) {
   if (!live(c) || !has_win(c, x) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if ((!topk && T > 0) || !counts_out || (!src_out && cap > 0)) return VR_ERR_INVALID_ARGUMENT;
@@ -1025,6 +1066,7 @@ static vrResult_t combine_common(vrComm_t c, vrWindow_t y, size_t y_off, size_t 
                                  int E, bool dedup, vrWindow_t out, size_t out_off, uint32_t sig, uint32_t flags,
                                  void* stream) {
   if (!live(c) || !has_win(c, y) || !has_win(c, out)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (flags & ~VR_COLL_NO_WAIT) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;
   if (dtype != VR_DT_F32 && dtype != VR_DT_BF16) return VR_ERR_INVALID_ARGUMENT;
@@ -1063,6 +1105,7 @@ vrResult_t vr_combine_dedup(vrComm_t c, vrWindow_t y, size_t y_off, size_t cap, 
                             const int32_t* send_pos, int T, vrWindow_t out, size_t out_off, uint32_t sig,
                             uint32_t flags, void* stream) {
   if (!live(c)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   const int R = c->nranks;  // a row per destination rank: K = E = R entries per token
   return combine_common(c, y, y_off, cap, row_bytes, dtype, nullptr, nullptr, send_pos, T, R, R, true, out, out_off,
                         sig, flags, stream);
@@ -1072,6 +1115,7 @@ vrResult_t vr_ring_exchange(vrComm_t c, vrWindow_t send, vrWindow_t recv, size_t
                             int contexts, uint32_t sig_base, uint32_t cnt_base, vrWindow_t sig_window,
                             size_t sig_window_off, uint64_t* litmus, uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, send) || !has_win(c, recv)) return VR_ERR_INVALID_ARGUMENT;
+  if (!on_device(c)) return VR_ERR_INVALID_USAGE;
   if (flags & ~(VR_COLL_NO_WAIT | VR_RING_WEAK)) return VR_ERR_INVALID_ARGUMENT;
   if (litmus && !dev_span_ok(c, litmus, 2 * sizeof(uint64_t))) return VR_ERR_INVALID_ARGUMENT;
   const int R = c->nranks;

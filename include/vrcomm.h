@@ -54,6 +54,10 @@
  *     vr_signal_reset of the signal at every rank (a kernel, not a memset)
  *     before the operation, so that every replay starts from 0 and waits for
  *     exactly its own signals; or capture with VR_COLL_NO_WAIT.
+ *   - Device: a communicator lives on the device current at vr_comm_create.
+ *     Every later call but vr_comm_destroy must be made with that device
+ *     current, else it returns VR_ERR_INVALID_USAGE and does nothing;
+ *     vr_comm_destroy selects the device itself and restores the caller's.
  */
 #ifndef VRCOMM_H
 #define VRCOMM_H

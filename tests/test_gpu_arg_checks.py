@@ -57,3 +57,31 @@ def test_ring_refuses_host_litmus_words():
         out = job.host(rv)
         assert np.array_equal(out[1], sends[0][:P * pb]) and np.array_equal(out[0], sends[1][:P * pb])
         job.assert_no_async_error()
+
+
+def test_calls_with_another_device_current_are_refused():
+    # a communicator belongs to the device current at its creation; with
+    # another device current every call but destroy is refused, and destroy
+    # selects the device itself and gives the caller's back
+    import torch
+    if torch.cuda.device_count() < 2:
+        pytest.skip("needs a second device to make current")
+    say("calls with another device current")
+    torch.cuda.set_device(0)
+    job = Job(2, signal_count=2)
+    w, views = job.window(1024, fill=0)
+    try:
+        torch.cuda.set_device(1)
+        for fn in (lambda: vr.vr_put(job.comm, 0, 0, 1, w, 0, w, 0, 64),
+                   lambda: vr.vr_signal_read(job.comm, 0, 0),
+                   lambda: vr.vr_comm_get_async_error(job.comm)):
+            with pytest.raises(vr.VrError) as e:
+                fn()
+            assert e.value.code == vr.VR_ERR_INVALID_USAGE
+    finally:
+        torch.cuda.set_device(0)
+    vr.vr_window_deregister(job.comm, w)
+    torch.cuda.set_device(1)
+    vr.vr_comm_destroy(job.comm)
+    assert torch.cuda.current_device() == 1
+    torch.cuda.set_device(0)
