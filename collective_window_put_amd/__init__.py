@@ -311,6 +311,10 @@ def vr_barrier(comm: int, index: int, fence: int = VR_FENCE_PUT | VR_FENCE_GET, 
 
 
 def vr_window_register(comm: int, bases, nbytes: int, flags: int = VR_WIN_DEFAULT) -> int:
+    bases = list(bases)
+    nranks, _ = vr_comm_query(comm)
+    if len(bases) != nranks:  # the library reads exactly nranks pointers
+        raise ValueError(f"vr_window_register: {len(bases)} base pointers for {nranks} ranks")
     arr = (c_void_p * len(bases))(*[_ptr(b) for b in bases])
     out = c_void_p()
     _check(lib().vr_window_register(comm, arr, nbytes, flags, ctypes.byref(out)), "vr_window_register")

@@ -189,7 +189,20 @@ uint64_t* remote_word(vrComm* c, int peer, const vrRemoteAction& a, uint64_t* ad
   if (is_va(a.kind)) return reinterpret_cast<uint64_t*>(a.window->base[peer] + a.offset);
   return c->sig + sidx(c, peer, a.id);
 }
-// Host bookkeeping once a remote action has been enqueued.
+// Enters a VA signal word in the window's table before the operation that
+// updates it is enqueued, so that the bookkeeping after a successful launch
+// only assigns to an existing entry and cannot fail. The word counts as a
+// signal from here on, as after a wait or a read of it.
+vrResult_t va_reserve(vrWindow* w, int rank, uint64_t off) {
+  try {
+    w->va_words.emplace(std::make_pair(rank, off), 0);
+  } catch (...) {
+    return VR_ERR_OUT_OF_RESOURCES;
+  }
+  return VR_OK;
+}
+// Host bookkeeping once a remote action has been enqueued (its VA word, if
+// any, entered by va_reserve).
 void note_remote(vrComm* c, int peer, const vrRemoteAction& a, uint64_t add) {
   if (is_va(a.kind)) a.window->va_words[{peer, a.offset}] = a.kind == VR_VA_SIGNAL_INC ? 1 : 2;
   else note_signal(c, peer, a.id, a.kind, add, true);
@@ -635,6 +648,7 @@ vrResult_t vr_put(vrComm_t c, int ctx, int rank, int peer, vrWindow_t dst, size_
                              (remote.window == src && overlap(src->base[rank] + src_off, bytes,
                                                                src->base[peer] + remote.offset, 8))))
     return VR_ERR_INVALID_USAGE;  // the put would move the signal word's own bytes
+  if (is_va(remote.kind) && (r = va_reserve(remote.window, peer, remote.offset)) != VR_OK) return r;
   uint64_t* sig = nullptr;
   uint64_t add = 0;
   if (remote.kind != VR_ACTION_NONE) sig = remote_word(c, peer, remote, &add);
@@ -667,6 +681,7 @@ vrResult_t vr_signal(vrComm_t c, int ctx, int rank, int peer, vrRemoteAction rem
   if (remote.kind == VR_ACTION_NONE) return VR_ERR_INVALID_ARGUMENT;
   vrResult_t r = check_remote(c, peer, remote);
   if (r != VR_OK) return r;
+  if (is_va(remote.kind) && (r = va_reserve(remote.window, peer, remote.offset)) != VR_OK) return r;
   uint64_t add = 0;
   uint64_t* word = remote_word(c, peer, remote, &add);
   hipLaunchKernelGGL(k_signal, dim3(1), dim3(64), 0, S(stream), word, add);
@@ -1147,6 +1162,9 @@ vrResult_t vr_ring_exchange(vrComm_t c, vrWindow_t send, vrWindow_t recv, size_t
       }
       ctx0[d] = reinterpret_cast<uint64_t*>(sig_window->base[d] + sig_window_off);
     }
+    for (int d = 0; d < R; ++d)
+      for (int k = 0; k < contexts; ++k)
+        if (vrResult_t e = va_reserve(sig_window, d, sig_window_off + 8ull * k)) return e;
   } else {
     for (int d = 0; d < R; ++d) {
       for (int k = 0; k < contexts; ++k)

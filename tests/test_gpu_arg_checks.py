@@ -85,3 +85,14 @@ def test_calls_with_another_device_current_are_refused():
     vr.vr_comm_destroy(job.comm)
     assert torch.cuda.current_device() == 1
     torch.cuda.set_device(0)
+
+
+def test_window_register_needs_one_base_per_rank():
+    # the library reads exactly R base pointers; the binding refuses a list
+    # of another length before the call
+    import torch
+    say("window register with a short base list")
+    with Job(4) as job:
+        slab = torch.empty(4 * 4096, dtype=torch.uint8, device="cuda")
+        with pytest.raises(ValueError):
+            vr.vr_window_register(job.comm, [slab.data_ptr()] * 3, 4096)
