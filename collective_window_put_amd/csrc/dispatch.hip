@@ -370,7 +370,7 @@ __device__ void put_expert_counts(const DispArgs& a, int s) {
     __hip_atomic_store(ready, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool DEDUP>
+template <bool DEDUP, int G>
 __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int wg) {
   // LDS: tot[E] (rows of expert e over all sources), base[E] (receive row of
   // this block's first row of expert e), hw[kWaves][E] (per-wave counts, then
@@ -407,25 +407,27 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
     const int tl = rd * tpr + lane / K;
     ent[rd] = (rd < rounds && lane < tpr * K && tl < ntw) ? load_topk(a, s, tw0 + tl, lane % K) : -1;
   }
-  // This wave's token rows (16-byte path) stay in registers until the copy.
-  // Per-expert layout: loaded here, before the ranking, so that the 16 MiB
-  // of row loads are done before the count exchange's round trips instead
-  // of queueing in front of them (measured 40.0 against 41.1 us flushed,
-  // 33.5 against 34.4 us back to back, three alternations on one box). The
-  // dedup layout loads them after its ranking: there the longer live range
-  // took the kernel to 92 VGPRs and 5 waves per SIMD.
-  v4u v[kTokPerWave];
+  // This wave's token rows (16-byte path, at most G vectors per lane) stay
+  // in registers until the copy. They are loaded here, before the ranking,
+  // so that the row loads are done before the count exchange's round trips
+  // instead of queueing in front of them (per-expert layout: 40.0 against
+  // 41.1 us flushed, 33.5 against 34.4 us back to back, three alternations
+  // on one box) -- except in the per-rank layout with G = kTokPerWave, where
+  // the longer live range takes the kernel to 92 VGPRs and 5 waves per SIMD:
+  // there they are loaded after the ranking.
+  v4u v[G];
   auto load_rows = [&]() {
     if (a.mode != 2) return;
 #pragma unroll
-    for (int g = 0; g < kTokPerWave; ++g) {
+    for (int g = 0; g < G; ++g) {
       const int tl = g * rpi + sub;
       v[g] = (g < groups && tl < ntw && l < nv)
                  ? load16_stream(reinterpret_cast<const v4u*>(a.x.p[s] + a.x_off + (uint64_t)(tw0 + tl) * rb + l * 16))
                  : v4u{0, 0, 0, 0};
     }
   };
-  if (!DEDUP) load_rows();
+  constexpr bool kEarly = !DEDUP || G < kTokPerWave;
+  if (kEarly) load_rows();
   // Ranking within the block needs no counts: per-wave counts, their
   // exclusive prefix over the waves, then each entry's rank among the
   // block's entries of its expert (token order). dpos holds that local rank.
@@ -472,7 +474,7 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
       }
     __syncthreads();
   }
-  if (DEDUP) load_rows();  // loaded while the counts are awaited
+  if (!kEarly) load_rows();  // loaded while the counts are awaited
   // count exchange: rank s waits until every source's count row has arrived;
   // the rows and prefixes are then read with agent-coherent loads.
   stamp(a, 1);
@@ -618,7 +620,7 @@ __device__ void put_block(const DispArgs& a, int32_t* lds, int* last_flag, int w
   if (a.mode == 2) {
     const __amdgpu_buffer_rsrc_t rd = rsrc(a.span_base, a.span_bytes);
 #pragma unroll
-    for (int g = 0; g < kTokPerWave; ++g) {
+    for (int g = 0; g < G; ++g) {
       if (g >= groups) break;
       const int tl = g * rpi + sub;
       if (tl < ntw && l < nv) {
@@ -757,14 +759,14 @@ __device__ void receiver_block(const DispArgs& a, int32_t* lds, int d) {
   }
 }
 
-template <bool DEDUP>
+template <bool DEDUP, int G>
 __global__ __launch_bounds__(kThreads) void k_dispatch(const DispArgs a) {
   extern __shared__ int32_t lds[];
   __shared__ int last;
   const int ncount = a.R * a.NB1, nput = a.R * a.NB2;
   const int b = blockIdx.x;
   if (b < ncount) count_block<DEDUP>(a, lds, &last, b);
-  else if (b < ncount + nput) put_block<DEDUP>(a, lds, &last, b - ncount);
+  else if (b < ncount + nput) put_block<DEDUP, G>(a, lds, &last, b - ncount);
   else receiver_block(a, lds, b - ncount - nput);
 }
 
@@ -888,8 +890,18 @@ vrResult_t launch_dispatch(vrComm* c, const vrWindow* x, size_t x_off, size_t ro
                                                              (a.rowbuf ? (size_t)(R + 2) * E : 0),
                                                          (size_t)kThreads});
   const int grid = R * a.NB1 + R * a.NB2 + (wait ? R : 0);
-  if (dedup) hipLaunchKernelGGL(k_dispatch<true>, dim3(grid), dim3(kThreads), lds, st, a);
-  else hipLaunchKernelGGL(k_dispatch<false>, dim3(grid), dim3(kThreads), lds, st, a);
+  // Per-rank layout with rows of up to 512 bytes: two or more rows per wave
+  // instruction, so at most kTokPerWave / 2 row vectors per lane, which lets
+  // its row loads go out before its ranking at 76 VGPRs (30.5-31.0 against
+  // 31.2-31.4 us flushed, three alternations on one box). The per-expert
+  // layout keeps the full bound: with it (58 VGPRs, 7 waves per SIMD) it
+  // measured 0.3 us slower.
+  if (dedup && a.mode == 2 && row_bytes <= 512)
+    hipLaunchKernelGGL((k_dispatch<true, kTokPerWave / 2>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (dedup)
+    hipLaunchKernelGGL((k_dispatch<true, kTokPerWave>), dim3(grid), dim3(kThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((k_dispatch<false, kTokPerWave>), dim3(grid), dim3(kThreads), lds, st, a);
   return hipGetLastError() == hipSuccess ? VR_OK : VR_ERR_HIP;
 }
 

@@ -64,7 +64,9 @@ def _check_dispatch(job, topk, x, E, cap, rv, counts, src, experts, pos, recv_of
                                                   (3, 130, 12, 6, 2, 2, 0.0), (8, 64, 256, 256, 8, 3, 0.0),
                                                   (8, 200, 32, 64, 8, 4, 0.1), (5, 1, 8, 10, 1, 5, 0.0),
                                                   (4, 1100, 8, 1024, 64, 8, 0.0), (8, 1537, 64, 32, 4, 9, 0.3),
-                                                  (64, 50, 8, 128, 4, 12, 0.1)])
+                                                  (64, 50, 8, 128, 4, 12, 0.1),
+                                                  # rows of 528 and 1024 bytes (one row per wave instruction)
+                                                  (4, 90, 264, 16, 4, 13, 0.1), (8, 130, 512, 64, 8, 14, 0.0)])
 def test_dedup_dispatch_vs_oracle(R, T, H, E, K, seed, drop):
     say(f"dedup dispatch R={R} T={T} H={H} E={E} K={K}")
     topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)

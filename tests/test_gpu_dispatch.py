@@ -58,7 +58,10 @@ def _check(res, topk, x, E, repeats=1):
                                              (8, 64, 256, 256, 8, 3), (8, 200, 32, 64, 8, 4), (5, 1, 8, 10, 1, 5),
                                              (4, 65, 3, 8, 4, 6), (2, 300, 256, 8, 8, 7),
                                              (4, 1100, 8, 1024, 64, 8), (8, 1537, 64, 32, 4, 9),
-                                             (3, 50, 8, 9, 2, 10), (2, 70, 8, 128, 4, 11), (64, 50, 8, 128, 4, 12)])
+                                             (3, 50, 8, 9, 2, 10), (2, 70, 8, 128, 4, 11), (64, 50, 8, 128, 4, 12),
+                                             # rows of 528 and 1024 bytes: one row per wave instruction
+                                             # on the 16-byte path, eight row vectors per lane
+                                             (4, 90, 264, 16, 4, 13), (8, 130, 512, 64, 8, 14)])
 def test_dispatch_small_vs_oracle(R, T, H, E, K, seed):
     say(f"dispatch R={R} T={T} H={H} E={E} K={K}")
     topk, x = W.dispatch_inputs(R, T, H, E, K, seed=seed)
