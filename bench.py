@@ -584,14 +584,17 @@ def run_put_get_rows(b, reps, rows):
 def run_pingpong_rows(b, reps, rows):
     """The control path of a small put: 2000 round trips of 256 B between two
     workgroups inside one kernel (put + SignalInc + wait each way), with the
-    second rank on another XCD and on the same XCD."""
+    second rank on another XCD and on the same XCD, and between the two waves
+    of one workgroup."""
     vr, stream = b.vr, b.stream.cuda_stream
     R, n, iters = 2, 256, 2000
     comm = comm_for(vr, R, signal_count=2)
     s1, sv = b.slices(R, 4096, fill=3)
     w = vr.vr_window_register(comm, [v.data_ptr() for v in sv], 4096)
     for name, label, flags in (("pingpong_cross_xcd_256B", "ping-pong 256 B, other XCD", 0),
-                               ("pingpong_same_xcd_256B", "ping-pong 256 B, same XCD", vr.VR_PINGPONG_SAME_XCD)):
+                               ("pingpong_same_xcd_256B", "ping-pong 256 B, same XCD", vr.VR_PINGPONG_SAME_XCD),
+                               ("pingpong_waves_256B", "ping-pong 256 B, two waves of one workgroup",
+                                vr.VR_PINGPONG_WAVES)):
         f = lambda: vr.vr_signal_pingpong(comm, w, 0, n, iters, sig=0, flags=flags, stream=stream)  # noqa: E731
         b.warm(f)
         t = b.timed(f, max(3, reps // 2), False)

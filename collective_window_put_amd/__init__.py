@@ -25,7 +25,7 @@ __all__ = [
     "VR_MAX_RANKS", "VR_SIGNAL_BITS", "VR_COUNTER_BITS", "VR_WIN_DEFAULT", "VR_WIN_COLL_SYMMETRIC", "VR_WIN_STRICT_ORDERING", "VR_WIN_REQUIRED_ALIGNMENT",
     "VR_ACTION_NONE", "VR_SIGNAL_INC", "VR_SIGNAL_ADD", "VR_COUNTER_INC", "VR_VA_SIGNAL_INC", "VR_VA_SIGNAL_ADD",
     "VR_DT_F32", "VR_DT_BF16", "VR_OP_SUM", "VR_COLL_NO_WAIT", "VR_COLL_COPY_ENGINE", "VR_CE_STREAMS",
-    "VR_RING_WEAK", "VR_PINGPONG_SAME_XCD", "VR_DISPATCH_NOALLOC_SCRATCH_BYTES",
+    "VR_RING_WEAK", "VR_PINGPONG_SAME_XCD", "VR_PINGPONG_WAVES", "VR_DISPATCH_NOALLOC_SCRATCH_BYTES",
     "VR_FENCE_NONE", "VR_FENCE_PUT", "VR_FENCE_GET",
     "VR_ASYNC_TIMEOUT", "VR_ASYNC_CAPACITY", "VR_ASYNC_BAD_EXPERT", "VR_ASYNC_LITMUS",
     # argument structures and action helpers
@@ -73,6 +73,7 @@ VR_COLL_COPY_ENGINE = 0x4
 VR_CE_STREAMS = 8
 VR_RING_WEAK = 0x8
 VR_PINGPONG_SAME_XCD = 0x10
+VR_PINGPONG_WAVES = 0x20
 VR_DISPATCH_NOALLOC_SCRATCH_BYTES = 4 << 20
 VR_FENCE_NONE, VR_FENCE_PUT, VR_FENCE_GET = 0x0, 0x1, 0x2
 VR_ASYNC_TIMEOUT, VR_ASYNC_CAPACITY, VR_ASYNC_BAD_EXPERT, VR_ASYNC_LITMUS = 0x1, 0x2, 0x4, 0x8

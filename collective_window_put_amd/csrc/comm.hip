@@ -948,7 +948,9 @@ vrResult_t vr_signal_pingpong(vrComm_t c, vrWindow_t w, size_t off, size_t bytes
                               uint32_t flags, void* stream) {
   if (!live(c) || !has_win(c, w)) return VR_ERR_INVALID_ARGUMENT;
   if (!on_device(c)) return VR_ERR_INVALID_USAGE;
-  if (flags & ~VR_PINGPONG_SAME_XCD) return VR_ERR_INVALID_ARGUMENT;
+  if ((flags & ~(VR_PINGPONG_SAME_XCD | VR_PINGPONG_WAVES)) ||
+      (flags & (VR_PINGPONG_SAME_XCD | VR_PINGPONG_WAVES)) == (VR_PINGPONG_SAME_XCD | VR_PINGPONG_WAVES))
+    return VR_ERR_INVALID_ARGUMENT;
   if (c->nranks < 2 || iters == 0 || bytes > (size_t(1) << 20)) return VR_ERR_INVALID_ARGUMENT;
   if (!span_ok(w, off, 2 * bytes)) return VR_ERR_INVALID_ARGUMENT;
   if (va_touch(w, 0, off, 2 * bytes) || va_touch(w, 1, off, 2 * bytes)) return VR_ERR_INVALID_USAGE;
@@ -959,7 +961,8 @@ vrResult_t vr_signal_pingpong(vrComm_t c, vrWindow_t w, size_t off, size_t bytes
     if (!c->expect_known[sidx(c, r, sig)]) return VR_ERR_INVALID_USAGE;
     base[r] = c->expect[sidx(c, r, sig)];
   }
-  vrResult_t r = launch_pingpong(c, w, off, bytes, iters, sig, base, (flags & VR_PINGPONG_SAME_XCD) != 0, S(stream));
+  vrResult_t r = launch_pingpong(c, w, off, bytes, iters, sig, base, (flags & VR_PINGPONG_SAME_XCD) != 0,
+                                 (flags & VR_PINGPONG_WAVES) != 0, S(stream));
   if (r == VR_OK)
     for (int q = 0; q < 2; ++q) note_signal(c, q, sig, VR_SIGNAL_INC, iters, true);
   return r;

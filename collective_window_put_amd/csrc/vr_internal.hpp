@@ -131,7 +131,7 @@ vrResult_t launch_alltoall_sessions(vrComm* c, const vrDevWindow& send, size_t s
 // helpers in comm.hip
 vrResult_t ensure_scratch(vrComm* c, size_t bytes);
 vrResult_t launch_pingpong(vrComm* c, const vrWindow* w, size_t off, size_t bytes, uint32_t iters, uint32_t sig,
-                           const uint64_t base[2], bool same_xcd, hipStream_t st);
+                           const uint64_t base[2], bool same_xcd, bool waves, hipStream_t st);
 vrDevComm device_view(const vrComm* c);
 vrDevWindow device_view(const vrWindow* w);
 

@@ -364,6 +364,8 @@ vrResult_t vr_counter_reset(vrComm_t comm, int rank, uint32_t id, void* stream);
 #define VR_RING_WEAK         0x8u
 /* vr_signal_pingpong only: rank 1's workgroup on rank 0's XCD */
 #define VR_PINGPONG_SAME_XCD 0x10u
+/* vr_signal_pingpong only: ranks 0 and 1 are the two waves of one workgroup */
+#define VR_PINGPONG_WAVES    0x20u
 
 /* Sum-AllReduce over `count` elements at send_off of every rank's send slice;
  * every rank's recv slice receives the sum at recv_off.
@@ -564,7 +566,9 @@ vrResult_t vr_ring_exchange(vrComm_t comm, vrWindow_t send, vrWindow_t recv, siz
  * [off+bytes, off+2*bytes) of rank 0's slice with a SignalInc on `sig` at
  * rank 0, which waits for it. Each of the two signals rises by iters; other
  * ranks are untouched. flags: VR_PINGPONG_SAME_XCD runs rank 1 on rank 0's
- * XCD (otherwise on the next one). Needs nranks >= 2, iters >= 1,
+ * XCD (otherwise on the next one); VR_PINGPONG_WAVES makes the two ranks the
+ * two waves of one workgroup, each with the wave-level put and publish of
+ * vrcomm_device.hpp (not with VR_PINGPONG_SAME_XCD). Needs nranks >= 2, iters >= 1,
  * bytes <= 1 MiB (0 allowed: signals only), [off, off+2*bytes) inside the
  * window and clear of VA signal words, and both signals' values known to the
  * host (VR_ERR_INVALID_USAGE otherwise). A wait that times out sets

@@ -9,15 +9,17 @@
  * Visibility protocol (the same one the library's own kernels use): payload
  * bytes are stored with agent-coherent stores; before a signal, counter or
  * barrier arrival the issuing workgroup waits for its stores and meets at a
- * workgroup barrier (publish_wg); the signal is then a relaxed agent-scope
+ * workgroup barrier (publish_wg), or the issuing wave waits for its own
+ * stores (publish_wave); the signal is then a relaxed agent-scope
  * atomic, and a waiter that sees the value it needs issues one agent-scope
  * acquire. Every signal is therefore published after all earlier stores of
  * its workgroup: strong and weak signals (GIN page, strong and weak
  * signals) get the same, strong, guarantee.
  *
- * Unit of cooperation: the workgroup. Functions marked "all threads" must be
- * reached by every thread of the workgroup; "one thread" functions by a
- * single thread (any).
+ * Unit of cooperation: the workgroup, or a single wave (put_wave and
+ * publish_wave). Functions marked "all threads" must be reached by every
+ * thread of the workgroup, "all lanes of one wave" by the 64 lanes of the
+ * wave that issues them, and "one thread" functions by a single thread (any).
  */
 #pragma once
 
@@ -62,17 +64,10 @@ __device__ inline void publish_wg() {
   __syncthreads();
 }
 
-/* All threads: put -- copy `bytes` from src (rank's slice, src_off) to dst
- * (peer's slice, dst_off) with agent-coherent stores (GIN page, one-sided
- * transfers: put, with a workgroup as the cooperating group). peer, rank and
- * the offsets must be the same in every thread. Call publish_wg() before
- * announcing it. */
-__device__ inline void put_wg(const vrDevWindow& dst, int peer, uint64_t dst_off, const vrDevWindow& src,
-                              int rank, uint64_t src_off, uint64_t bytes) {
-  char* d = dst.base[peer] + dst_off;
-  const char* s = src.base[rank] + src_off;
-  const uint32_t t = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
-  const uint32_t nthr = blockDim.x * blockDim.y * blockDim.z;
+/* The body of a put, shared by the workgroup and the wave forms: thread t of
+ * the nthr cooperating threads copies its share of [s, s + bytes) to d with
+ * agent-coherent stores. */
+__device__ inline void put_span(char* d, const char* s, uint64_t bytes, uint32_t t, uint32_t nthr) {
   const bool vec = ((reinterpret_cast<uintptr_t>(d) | reinterpret_cast<uintptr_t>(s)) & 15) == 0;
   constexpr uint64_t kChunk = 1ull << 30;  // one buffer resource per GiB
   for (uint64_t c0 = 0; c0 < bytes; c0 += kChunk) {
@@ -99,8 +94,35 @@ __device__ inline void put_wg(const vrDevWindow& dst, int peer, uint64_t dst_off
   }
 }
 
+/* All threads: put -- copy `bytes` from src (rank's slice, src_off) to dst
+ * (peer's slice, dst_off) with agent-coherent stores (GIN page, one-sided
+ * transfers: put, with a workgroup as the cooperating group). peer, rank and
+ * the offsets must be the same in every thread. Call publish_wg() before
+ * announcing it. */
+__device__ inline void put_wg(const vrDevWindow& dst, int peer, uint64_t dst_off, const vrDevWindow& src,
+                              int rank, uint64_t src_off, uint64_t bytes) {
+  const uint32_t t = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
+  const uint32_t nthr = blockDim.x * blockDim.y * blockDim.z;
+  put_span(dst.base[peer] + dst_off, src.base[rank] + src_off, bytes, t, nthr);
+}
+
+/* All 64 lanes of one wave: the same put with the wave as the cooperating
+ * group, so that each wave of a workgroup can issue, publish and announce
+ * its own puts without meeting the others at a workgroup barrier. The
+ * arguments must be the same in every lane. Call publish_wave() before
+ * announcing it. */
+__device__ inline void put_wave(const vrDevWindow& dst, int peer, uint64_t dst_off, const vrDevWindow& src,
+                                int rank, uint64_t src_off, uint64_t bytes) {
+  put_span(dst.base[peer] + dst_off, src.base[rank] + src_off, bytes, __lane_id(), 64);
+}
+
+/* All lanes of one wave: wait until this wave's loads and stores have
+ * completed (the wave's memory counter covers every lane). After it, the
+ * wave's stores are visible at agent scope and one lane may announce them. */
+__device__ inline void publish_wave() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 /* ---- signals and counters ------------------------------------------------------------ */
-/* One thread, after publish_wg(): SignalAdd (SignalInc is value 1) on a
+/* One thread, after publish_wg() or publish_wave(): SignalAdd (SignalInc is value 1) on a
  * signal word, or CounterInc on a counter word (GIN page, signals and
  * counters). */
 __device__ inline void signal_add(uint64_t* word, uint64_t value) {

@@ -131,6 +131,13 @@ __global__ void ring_once(vrDevComm c, vrDevWindow w, uint64_t block, uint64_t b
   vrdev::barrier_sync_wg(vrdev::barrier_word(c, 0), bar_base + c.nranks, VR_FENCE_PUT, 0, c.error);
   if (threadIdx.x == 0) vrdev::wait_word(vrdev::signal_word(c, r, 0), 1, 64, 0, c.error);
 }
+// the wave form: each wave of workgroup r puts its own piece and signals it
+__global__ void ring_waves(vrDevComm c, vrDevWindow w, uint64_t piece) {
+  const int r = blockIdx.x, peer = (r + 1) % c.nranks, wv = threadIdx.x / 64;
+  vrdev::put_wave(w, peer, (uint64_t)wv * piece, w, r, (uint64_t)wv * piece, piece);
+  vrdev::publish_wave();
+  if (threadIdx.x % 64 == 0) vrdev::signal_add(vrdev::signal_word(c, peer, 1), 1);
+}
 """
 
 
