@@ -54,8 +54,6 @@ constexpr int kTokPerWave = 8;    // tokens per wave in a put workgroup
 constexpr int kSub = kWaves * kTokPerWave;  // tokens per put workgroup (sub-block): 64
 constexpr int kCountBlock = 256;  // tokens per count workgroup
 constexpr int kSubs = kCountBlock / kSub;
-constexpr int kSubBits = 2;       // log2(kSubs): key bits above the expert's
-static_assert((1 << kSubBits) == kSubs, "kSubBits");
 constexpr int kRelayFan = 16;     // first-level relay counters per source (put blocks)
 
 struct DispArgs {
